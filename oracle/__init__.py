@@ -1,0 +1,23 @@
+"""CPU oracle for the verification step of tree speculative decoding.
+
+TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
+benchmark's CPU-baseline leg may import or run anything in this package; the
+library never does, and it shares no code, table or helper with the GPU path.
+
+It is plain numpy in float64, written from the defining passages of the pages
+and kept slow and obvious on purpose: masked softmax attention of every
+draft-tree node over the paged context plus its own ancestors, the per-chunk
+attention mass, greedy longest-accepted-path acceptance and the
+recursive-residual rejection walk.  Each function cites the passage it follows.
+
+Every function here is pinned by tests against something other than itself
+(closed forms, library routines, brute force on tiny inputs, exact
+enumeration of the sampler's output law).  None is "parity unpinned".
+"""
+
+from .attention import (bf16_to_f64, ancestor_matrix, gather_kv, tree_attention, attention_rows,
+                        chunk_mass, topk_chunks)
+from .acceptance import argmax_lowest, accept_greedy, target_probs, accept_rejection
+
+__all__ = ["bf16_to_f64", "ancestor_matrix", "gather_kv", "tree_attention", "attention_rows", "chunk_mass",
+           "topk_chunks", "argmax_lowest", "accept_greedy", "target_probs", "accept_rejection"]
