@@ -1,0 +1,236 @@
+/*
+ * spec_verify.h -- C ABI of the tree-verification library for AMD Instinct MI355X (gfx950).
+ *
+ * The library computes the target model's verification step of tree speculative decoding:
+ *
+ *   spec_tree_attention    tree-masked GQA attention of every draft-tree node against a paged
+ *                          bf16 KV cache (split-K over the context, LSE merge of the splits)
+ *   spec_chunk_salience    the attention mass that the verification queries put on each context
+ *                          chunk, optionally accumulated over layers, with top-k chunk selection
+ *   spec_accept_greedy     greedy longest-accepted-path acceptance
+ *   spec_accept_rejection  exact rejection-sampling acceptance against the draft distribution
+ *
+ * Sources (web pages cited by title and section):
+ *   [DS]  "DiffSpec: Accelerating Long Sequence Generation with Differential Speculative Decoding"
+ *         (vllm-diffspec README): "What DiffSpec Does" items 2 and 5, "Architecture"
+ *         (target-guided retrieval from paged target KV), "Configuration" (chunk size 64,
+ *         up to 50 verifier tree nodes).
+ *   [DSC] DiffSpec README (CGCL-codes), "Features": salience-aware chunk encoding, paged KV.
+ *   [AS]  "Adaptive Speculative Decoding": "Correctness first" (exact rejection sampling,
+ *         greedy as its temperature-0 case), "The controller" (acceptance probability
+ *         min(1, p/q); k drafts give up to k+1 tokens), "Layout" (per-row cache mask
+ *         s <= lengths[b] + j).
+ *   [VC]  vllm.cpp "Speculative decoding": "MTP" (accept-if-equal greedy verification),
+ *         "Consuming it programmatically" (a versioned C ABI that refuses what it cannot
+ *         honour, by name, instead of silently downgrading).
+ *
+ * Conventions for every entry point
+ *   - Pointers are device pointers unless marked (host).  The caller owns all memory; the
+ *     library never allocates, frees or keeps a pointer after the call returns.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).  Calls only
+ *     enqueue work and return; there is no host<->device synchronisation, so calls may be
+ *     captured in a HIP graph.
+ *   - Host-visible arguments are validated before anything is enqueued.  On failure the call
+ *     returns a spec_status other than SPEC_OK, enqueues nothing, and spec_last_error()
+ *     (thread-local) names the argument and the accepted values.  A failed HIP launch returns
+ *     SPEC_ERR_HIP with the HIP error text.
+ *   - Device-side preconditions (listed per call) are not checked on the host.  Kernels clamp
+ *     every index they derive from device data to the host bounds, so a violated
+ *     precondition gives wrong results, never an out-of-bounds access.
+ *   - Results are deterministic: fixed reduction orders, no floating-point atomics.
+ *   - No C++ exception crosses this interface.
+ */
+#ifndef SPEC_VERIFY_H
+#define SPEC_VERIFY_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SPEC_ABI_VERSION 1
+
+typedef enum spec_status {
+  SPEC_OK = 0,
+  SPEC_ERR_INVALID_ARGUMENT = 1, /* a null/misaligned pointer, a size out of range, inconsistent shapes */
+  SPEC_ERR_UNSUPPORTED = 2,      /* a well-formed value this build does not implement (e.g. head_dim 96) */
+  SPEC_ERR_WORKSPACE = 3,        /* workspace missing or smaller than the matching *_workspace_size() */
+  SPEC_ERR_HIP = 4,              /* a HIP runtime call or kernel launch failed */
+  SPEC_ERR_STATE = 5             /* call order violated (salience without chunk partials) */
+} spec_status;
+
+typedef enum spec_dtype { SPEC_DTYPE_BF16 = 0, SPEC_DTYPE_F32 = 1 } spec_dtype;
+
+/* == SPEC_ABI_VERSION of the built library. */
+int spec_abi_version(void);
+/* Static text for a status code. */
+const char* spec_status_string(int status);
+/* (host) Thread-local text of the last failure on this thread; "" after a successful call. */
+const char* spec_last_error(void);
+
+/* ------------------------------------------------------------------------------------------
+ * Paged KV cache [DSC "Features": paged KV with a block table; AS "Layout"].
+ * Logical slot t of sequence b is page block_table[b * block_table_stride + t / page_size],
+ * row t % page_size.  Element (page, kv_head, row, d) of K is at
+ *   k_cache + page * page_stride + kv_head * head_stride + row * token_stride + d
+ * (bf16 elements; V uses the same strides).  The layout [pages][kv_heads][page_size][head_dim]
+ * (token_stride = head_dim, head_stride = page_size * head_dim) gives each (page, head) one
+ * contiguous block and is the fastest; others work if every row is 16-byte aligned.
+ * Pages may be shared between sequences (copy-on-write prefixes): the library only reads them.
+ * ------------------------------------------------------------------------------------------ */
+typedef struct spec_paged_kv {
+  const void* k_cache;          /* bf16, 16-byte aligned */
+  const void* v_cache;          /* bf16, 16-byte aligned */
+  int64_t page_stride;          /* elements; multiple of 8 */
+  int64_t head_stride;          /* elements; multiple of 8 */
+  int64_t token_stride;         /* elements; multiple of 8, >= head_dim */
+  int32_t page_size;            /* slots per page: a power of two in [1, 1024] (16 in the workloads) */
+  int32_t num_pages;            /* (host) pages in the pool; ids outside [0, num_pages) read as zeros */
+  const int32_t* block_table;   /* int32 [batch][block_table_stride] physical page ids */
+  int32_t block_table_stride;   /* >= ceil((max_ctx_len + max_nodes) / page_size) */
+} spec_paged_kv;
+
+/* ------------------------------------------------------------------------------------------
+ * spec_tree_attention  [DS "What DiffSpec Does" item 5; AS "Layout"]
+ *
+ * Every node of each sequence's draft tree is a query.  Node i of sequence b (L = ctx_lens[b]
+ * committed tokens) sees the keys {0 .. L-1} and {L + j : j is i or an ancestor of i}; its own
+ * K/V must already be written at logical slot L + i.  Query head h reads KV head
+ * h / (num_q_heads / num_kv_heads).  For a chain of drafts this is ordinary causal decode.
+ *   out[n][h][:] = softmax(scale * q[n][h] . K^T) V  over the visible keys   (bf16, RNE)
+ *   lse[n][h]    = natural log of the softmax denominator                     (fp32)
+ * Arithmetic: bf16 products with fp32 accumulation; probabilities are rounded to bf16 before
+ * the P.V product; split partials are merged in fp32.
+ * With chunk_size > 0 the call also leaves, in the workspace, the per-(query row, context
+ * chunk) partials that spec_chunk_salience reduces [DS "Architecture": chunks are scored from
+ * the paged target KV without materialising the attention matrix].
+ *
+ * Device preconditions: 0 <= ctx_lens[b] <= max_ctx_len; node_offsets non-decreasing with
+ * node_offsets[0] = 0 and at most max_nodes nodes per sequence; parents sequence-local with
+ * parents[first node] = -1 and 0 <= parents[i] < i otherwise; block-table ids < num_pages.
+ * ------------------------------------------------------------------------------------------ */
+typedef struct spec_tree_attention_args {
+  int32_t batch;                /* >= 1 */
+  int32_t num_q_heads;          /* >= 1, multiple of num_kv_heads */
+  int32_t num_kv_heads;         /* >= 1 */
+  int32_t head_dim;             /* 64 or 128 */
+  int32_t max_nodes;            /* (host) bound on tree nodes per sequence, 1..256 */
+  int32_t max_ctx_len;          /* (host) bound on ctx_lens[b], >= 0 */
+  const int32_t* ctx_lens;      /* int32 [batch] committed tokens before the root */
+  const int32_t* node_offsets;  /* int32 [batch + 1] packed node ranges; the first node of a range is the root */
+  const int32_t* parents;       /* int32 [total_nodes] sequence-local parent ids */
+  const void* q;                /* bf16 [total_nodes][num_q_heads][head_dim], 16-byte aligned (post-RoPE) */
+  spec_paged_kv kv;
+  float scale;                  /* finite; usually 1/sqrt(head_dim) */
+  void* out;                    /* bf16 [total_nodes][num_q_heads][head_dim], 16-byte aligned */
+  float* lse;                   /* fp32 [total_nodes][num_q_heads] or NULL */
+  int32_t chunk_size;           /* 0: no salience partials; else 16, 32 or a multiple of 64 */
+  int32_t split_tiles;          /* 0: library choice; else KV tiles of 64 slots per split (tuning knob) */
+  void* workspace;              /* 256-byte aligned, >= spec_tree_attention_workspace_size(args) bytes */
+  size_t workspace_bytes;
+} spec_tree_attention_args;
+
+/* Workspace bytes needed by spec_tree_attention for these host bounds (0 if args are invalid;
+ * spec_last_error() then says why).  Depends only on batch, head counts, head_dim, max_nodes,
+ * max_ctx_len, chunk_size and split_tiles. */
+size_t spec_tree_attention_workspace_size(const spec_tree_attention_args* args);
+int spec_tree_attention(const spec_tree_attention_args* args, void* stream);
+
+/* ------------------------------------------------------------------------------------------
+ * spec_chunk_salience  [DS "What DiffSpec Does" item 2, "Architecture" (target-guided retrieval),
+ * "Configuration" (diffspec_chunk_size); DSC "Features" (salience-aware chunk encoding)]
+ *
+ * For each sequence b and context chunk c = slots [c*chunk_size, min((c+1)*chunk_size, L)):
+ *   mass[b][c] = (1 / (N_b * num_q_heads)) * sum over nodes i, query heads h, keys t in c of
+ *                the attention probability p[i][h][t] of the preceding spec_tree_attention call
+ * (probabilities are normalised over all visible keys, context and tree; tree keys belong to no
+ * chunk).  accumulate = 1 adds to chunk_mass (summing over layers); 0 overwrites it.  Entries
+ * c >= ceil(L / chunk_size) are written as 0 (overwrite) or left unchanged (accumulate).
+ * With top_k > 0 it then writes, per sequence, the top_k chunks of chunk_mass (after the update)
+ * ordered by (mass descending, chunk index ascending), padded with index -1 and mass 0.
+ *
+ * Must follow, on the same stream, the spec_tree_attention call made with *attn (same workspace,
+ * chunk_size > 0) before that workspace is reused.  chunk_size == 0 there -> SPEC_ERR_STATE.
+ * ------------------------------------------------------------------------------------------ */
+typedef struct spec_chunk_salience_args {
+  const spec_tree_attention_args* attn;  /* (host) the arguments of the preceding attention call */
+  float* chunk_mass;            /* fp32 [batch][max_chunks] */
+  int32_t max_chunks;           /* >= ceil(attn->max_ctx_len / attn->chunk_size) */
+  int32_t accumulate;           /* 0 or 1 */
+  int32_t top_k;                /* 0 (none) .. min(max_chunks, 8192) */
+  int32_t* topk_index;          /* int32 [batch][top_k] or NULL when top_k == 0 */
+  float* topk_mass;             /* fp32 [batch][top_k] or NULL when top_k == 0 */
+} spec_chunk_salience_args;
+
+int spec_chunk_salience(const spec_chunk_salience_args* args, void* stream);
+
+/* ------------------------------------------------------------------------------------------
+ * spec_accept_greedy  [VC "MTP": accept a draft iff it equals the target's greedy choice;
+ * AS "The controller": k drafts give up to k+1 tokens]
+ *
+ * a_u = argmax_v target_logits[u][v] (lowest v among exactly equal maxima).  Node j is accepted
+ * iff its parent is accepted and draft_tokens[j] == a_parent(j); the root is always accepted.
+ * The result is the deepest accepted node f (lowest node index among equally deep ones):
+ *   out_num_accepted[b]   = depth(f)  (accepted draft tokens)
+ *   out_path_nodes[b][:]  = sequence-local nodes root .. f, then -1
+ *   out_tokens[b][:]      = draft tokens of path nodes 1.., then a_f (the bonus token), then -1
+ * A path longer than max_path is reported as out_num_accepted[b] = -1 with -1 rows.
+ *
+ * Device preconditions: as for spec_tree_attention (node_offsets, parents); no NaN logits.
+ * ------------------------------------------------------------------------------------------ */
+typedef struct spec_accept_greedy_args {
+  int32_t batch;                /* >= 1 */
+  int32_t vocab;                /* 1 .. 2^24 */
+  int32_t max_nodes;            /* (host) bound on nodes per sequence, 1..256 */
+  int32_t max_path;             /* (host) row length of the path/token outputs, >= 1 (max depth + 1) */
+  const int32_t* node_offsets;  /* int32 [batch + 1] */
+  const int32_t* parents;       /* int32 [total_nodes] sequence-local */
+  const int32_t* draft_tokens;  /* int32 [total_nodes]; the root's entry is ignored */
+  const void* target_logits;    /* [total_nodes][vocab] of logits_dtype; row u = target logits after node u */
+  int32_t logits_dtype;         /* spec_dtype */
+  int32_t* out_num_accepted;    /* int32 [batch] */
+  int32_t* out_path_nodes;      /* int32 [batch][max_path] */
+  int32_t* out_tokens;          /* int32 [batch][max_path] */
+  void* workspace;              /* >= spec_accept_greedy_workspace_size(args) bytes, 256-byte aligned */
+  size_t workspace_bytes;
+} spec_accept_greedy_args;
+
+size_t spec_accept_greedy_workspace_size(const spec_accept_greedy_args* args);
+int spec_accept_greedy(const spec_accept_greedy_args* args, void* stream);
+
+/* ------------------------------------------------------------------------------------------
+ * spec_accept_rejection  [AS "Correctness first", "The controller"; Leviathan et al. and
+ * Chen et al. as cited there]
+ *
+ * p_u = softmax(target_logits[u]) and q_u = draft_probs[u] (the distribution u's children were
+ * drawn from, i.i.d.).  Starting at the root u: res = p_u; visit the children c of u in increasing
+ * node index with x = draft_tokens[c]:
+ *   accept iff u_accept[c] * q_u(x) < res(x)  -> move to c and repeat;
+ *   else res = max(0, res - q_u) / sum(max(0, res - q_u))   (kept unchanged if that sum is 0).
+ * If no child is accepted, the bonus token is the smallest v with
+ *   sum_{w <= v} res(w) > u_sample[u] * sum_w res(w).
+ * With one child per node this is the chain rule of the page; with i.i.d. children the emitted
+ * token has law p_u (lossless).  Outputs as for spec_accept_greedy.  A node with more than
+ * max_children children is reported as out_num_accepted[b] = -1.
+ * Arithmetic: every probability, residual and sum in fp64 (exp evaluated in fp64).
+ *
+ * Device preconditions: as for spec_accept_greedy; draft_probs rows non-negative; uniforms in [0,1).
+ * ------------------------------------------------------------------------------------------ */
+typedef struct spec_accept_rejection_args {
+  spec_accept_greedy_args base; /* topology, target logits, outputs, workspace */
+  int32_t max_children;         /* (host) bound on children of any node, 1 .. max_nodes - 1 (0 if max_nodes == 1) */
+  const float* draft_probs;     /* fp32 [total_nodes][vocab] */
+  const float* u_accept;        /* fp32 [total_nodes]: uniform for the accept test of node c */
+  const float* u_sample;        /* fp32 [total_nodes]: uniform for the bonus draw at stopping node u */
+} spec_accept_rejection_args;
+
+size_t spec_accept_rejection_workspace_size(const spec_accept_rejection_args* args);
+int spec_accept_rejection(const spec_accept_rejection_args* args, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPEC_VERIFY_H */

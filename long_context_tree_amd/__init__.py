@@ -1,0 +1,11 @@
+"""Tree verification for speculative decoding on AMD Instinct MI355X (gfx950).
+
+A thin Python binding over libspec_verify (include/spec_verify.h): tree-masked paged attention,
+per-chunk attention mass with top-k selection, and greedy / rejection-sampling acceptance.
+"""
+
+from .spec import (AttentionHandle, SpecError, accept_greedy, accept_rejection, chunk_salience, last_error, lib,
+                   status_string, tree_attention, tree_attention_args)
+
+__all__ = ["AttentionHandle", "SpecError", "accept_greedy", "accept_rejection", "chunk_salience", "last_error", "lib",
+           "status_string", "tree_attention", "tree_attention_args"]

@@ -1,0 +1,454 @@
+// Greedy and rejection-sampling acceptance over a draft tree, for gfx950.
+//
+// Greedy: a draft is accepted iff it equals the target's greedy choice at its parent (vllm.cpp
+// "Speculative decoding", section MTP); on a tree the result is the deepest accepted node.
+// Rejection: accept x ~ q with probability min(1, p(x)/q(x)); on rejection continue with the
+// normalised residual max(0, res - q) ("Adaptive Speculative Decoding", sections "Correctness
+// first" and "The controller"), generalised to siblings drawn i.i.d. from q.
+//
+// Both are HBM streams over the [nodes][vocab] logits (16-33 MB at vocab 128K), so the work is
+// spread over (vocab segment x node) work-groups with fixed-order reductions, and only the tree
+// walk itself runs in one work-group per sequence:
+//   argmax_seg     per (node, 8192-token segment): the packed key (ordered value, ~index) maximum,
+//                  i.e. the largest logit with the lowest index among exact ties
+//   residual_pass  (rejection) level r = 0: sum exp(l - M); level r >= 1, for nodes with >= r
+//                  children: sum max(0, res_{r-1} - q), with res_{r-1} rebuilt per element from the
+//                  earlier levels' normalisers (all fp64, exp evaluated in fp64)
+//   walk           per sequence: accept tests of every child in parallel (a child is tested only
+//                  after all earlier siblings were rejected, so its residual level is its sibling
+//                  rank), first accepted child per node by LDS atomic-min, walk from the root,
+//                  then the bonus token (greedy: argmax; rejection: inverse CDF of the residual,
+//                  segment found from the segment sums, then an in-segment scan)
+#include "spec_internal.h"
+
+namespace spec {
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ uint32_t ordered(float v) {
+  uint32_t u = __float_as_uint(v);
+  if ((u << 1) == 0) u = 0;                       // -0 == +0
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ unsigned long long pack_key(float v, int idx) {
+  return ((unsigned long long)ordered(v) << 32) | (uint32_t)(~(uint32_t)idx);
+}
+__device__ __forceinline__ float key_value(unsigned long long k) {
+  const uint32_t o = (uint32_t)(k >> 32);
+  return __uint_as_float((o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o);
+}
+__device__ __forceinline__ int key_index(unsigned long long k) { return (int)(~(uint32_t)(k & 0xFFFFFFFFu)); }
+
+__device__ __forceinline__ unsigned long long umax64(unsigned long long a, unsigned long long b) { return a > b ? a : b; }
+
+__device__ __forceinline__ unsigned long long shfl_xor_u64(unsigned long long v, int m) {
+  const uint32_t lo = __shfl_xor((uint32_t)v, m), hi = __shfl_xor((uint32_t)(v >> 32), m);
+  return ((unsigned long long)hi << 32) | lo;
+}
+
+__device__ __forceinline__ float load_logit(const AcceptParams& p, int64_t u, int v) {
+  if (p.bf16) {
+    const uint16_t h = reinterpret_cast<const uint16_t*>(p.logits)[u * p.vocab + v];
+    return __uint_as_float((uint32_t)h << 16);
+  }
+  return reinterpret_cast<const float*>(p.logits)[u * p.vocab + v];
+}
+
+__device__ __forceinline__ int total_nodes(const AcceptParams& p) {
+  int t = p.node_offsets[p.batch];
+  const int cap = p.batch * p.max_nodes;
+  return t < 0 ? 0 : (t > cap ? cap : t);
+}
+
+// Block-wide (256 threads) maximum of a u64 key; result valid in every thread.
+__device__ unsigned long long block_max_u64(unsigned long long v) {
+  __shared__ unsigned long long red[4];
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v = umax64(v, shfl_xor_u64(v, off));
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  v = umax64(umax64(red[0], red[1]), umax64(red[2], red[3]));
+  __syncthreads();
+  return v;
+}
+
+// Block-wide (256 threads) fp64 sum in a fixed order; result valid in every thread.
+__device__ double block_sum_f64(double v) {
+  __shared__ double red[4];
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  v = (red[0] + red[1]) + (red[2] + red[3]);
+  __syncthreads();
+  return v;
+}
+
+// ---- per (segment, node): maximum logit with the lowest index among exact ties ----
+__global__ __launch_bounds__(256) void argmax_seg_kernel(AcceptParams p) {
+  const int seg = blockIdx.x;
+  const int64_t u = blockIdx.y;
+  if (u >= total_nodes(p)) return;
+  const int v0 = seg * kSegment;
+  const int v1 = min(p.vocab, v0 + kSegment);
+  unsigned long long best = 0;
+  const int esz = p.bf16 ? 2 : 4;
+  const int per = 16 / esz;                       // elements per 16-byte load
+  const char* row = reinterpret_cast<const char*>(p.logits) + u * (int64_t)p.vocab * esz;
+  const bool vec = ((((uintptr_t)row) & 15) == 0) && (v0 % per == 0);
+  int v = v0;
+  if (vec) {
+    const int nvec = (v1 - v0) / per;
+    for (int i = threadIdx.x; i < nvec; i += 256) {
+      const u32x4 w = *reinterpret_cast<const u32x4*>(row + (int64_t)(v0 + i * per) * esz);
+      const int base = v0 + i * per;
+      if (p.bf16) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          best = umax64(best, pack_key(__uint_as_float(w[k] << 16), base + 2 * k));
+          best = umax64(best, pack_key(__uint_as_float(w[k] & 0xFFFF0000u), base + 2 * k + 1));
+        }
+      } else {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) best = umax64(best, pack_key(__uint_as_float(w[k]), base + k));
+      }
+    }
+    v = v0 + nvec * per;
+  }
+  for (int i = v + threadIdx.x; i < v1; i += 256) best = umax64(best, pack_key(load_logit(p, u, i), i));
+  best = block_max_u64(best);
+  if (threadIdx.x == 0) p.seg_key[u * p.nseg + seg] = best;
+}
+
+__device__ __forceinline__ float row_max(const AcceptParams& p, int64_t u) {
+  unsigned long long k = 0;
+  for (int s = 0; s < p.nseg; ++s) k = umax64(k, p.seg_key[u * p.nseg + s]);
+  return key_value(k);
+}
+
+// Normalisers of node u in a fixed order: Z[0] = sum exp(l - M); Z[k] = sum max(0, res_{k-1} - q).
+__device__ __forceinline__ double level_sum(const AcceptParams& p, int64_t u, int k) {
+  const double* s = p.seg_sum + (u * (p.max_children + 1) + k) * p.nseg;
+  double z = 0.0;
+  for (int i = 0; i < p.nseg; ++i) z += s[i];
+  return z;
+}
+
+// ---- rejection: one residual level for every node that needs it ----
+__global__ __launch_bounds__(256) void residual_pass_kernel(AcceptParams p, int r) {
+  const int seg = blockIdx.x;
+  const int64_t u = blockIdx.y;
+  if (u >= total_nodes(p)) return;
+  if (r > 0 && p.n_children[u] < r) return;
+  const double M = (double)row_max(p, u);
+  double Z[9];
+  const int v0 = seg * kSegment;
+  const int v1 = min(p.vocab, v0 + kSegment);
+  double acc = 0.0;
+  if (r == 0) {
+    for (int v = v0 + threadIdx.x; v < v1; v += 256) acc += exp((double)load_logit(p, u, v) - M);
+  } else {
+    // normalisers of the earlier levels (up to 8 held in registers; deeper levels re-summed)
+    for (int k = 0; k < r && k < 9; ++k) Z[k] = level_sum(p, u, k);
+    const float* q = p.draft_probs + u * (int64_t)p.vocab;
+    for (int v = v0 + threadIdx.x; v < v1; v += 256) {
+      const double qv = (double)q[v];
+      double res = exp((double)load_logit(p, u, v) - M) / Z[0];
+      for (int k = 1; k < r; ++k) {
+        const double d = fmax(0.0, res - qv);
+        const double zk = k < 9 ? Z[k] : level_sum(p, u, k);
+        if (zk > 0.0) res = d / zk;
+      }
+      acc += fmax(0.0, res - qv);
+    }
+  }
+  acc = block_sum_f64(acc);
+  if (threadIdx.x == 0) p.seg_sum[(u * (p.max_children + 1) + r) * p.nseg + seg] = acc;
+}
+
+// ---- per sequence: child counts (for the residual passes) ----
+__global__ __launch_bounds__(256) void tree_info_kernel(AcceptParams p) {
+  __shared__ int cnt[kMaxNodes];
+  const int b = blockIdx.x;
+  int n0 = p.node_offsets[b];
+  int N = p.node_offsets[b + 1] - n0;
+  N = N < 0 ? 0 : (N > p.max_nodes ? p.max_nodes : N);
+  n0 = n0 < 0 ? 0 : (n0 > (p.batch - 1) * p.max_nodes ? (p.batch - 1) * p.max_nodes : n0);
+  for (int i = threadIdx.x; i < N; i += 256) cnt[i] = 0;
+  __syncthreads();
+  for (int i = threadIdx.x + 1; i < N; i += 256) {
+    const int pi = p.parents[n0 + i];
+    if (pi >= 0 && pi < i) atomicAdd(&cnt[pi], 1);
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < N; i += 256) p.n_children[n0 + i] = cnt[i];
+}
+
+// ---- per sequence: the walk and the bonus token ----
+template <bool REJECT>
+__global__ __launch_bounds__(256) void walk_kernel(AcceptParams p) {
+  __shared__ int par_s[kMaxNodes], tok_s[kMaxNodes], first_s[kMaxNodes], nch_s[kMaxNodes], rank_s[kMaxNodes];
+  __shared__ int amax_s[kMaxNodes];
+  __shared__ int path_s[kMaxNodes];
+  __shared__ int stop_s, depth_s, bad_s, seg_s, bonus_s;
+  __shared__ double base_s, thr_s;
+  __shared__ double zs[9];
+  __shared__ double scan_s[256];
+  const int b = blockIdx.x;
+  const int tid = threadIdx.x;
+  int n0 = p.node_offsets[b];
+  int N = p.node_offsets[b + 1] - n0;
+  N = N < 0 ? 0 : (N > p.max_nodes ? p.max_nodes : N);
+  n0 = n0 < 0 ? 0 : (n0 > (p.batch - 1) * p.max_nodes ? (p.batch - 1) * p.max_nodes : n0);
+  int32_t* o_path = p.out_path_nodes + (int64_t)b * p.max_path;
+  int32_t* o_tok = p.out_tokens + (int64_t)b * p.max_path;
+  if (N == 0) {
+    for (int i = tid; i < p.max_path; i += 256) { o_path[i] = -1; o_tok[i] = -1; }
+    if (tid == 0) p.out_num_accepted[b] = -1;
+    return;
+  }
+  if (tid == 0) bad_s = 0;
+  for (int i = tid; i < N; i += 256) {
+    int pi = p.parents[n0 + i];
+    par_s[i] = pi;
+    int t = p.draft_tokens[n0 + i];
+    tok_s[i] = t;
+    first_s[i] = 0x7FFFFFFF;
+    if (!REJECT) {
+      unsigned long long k = 0;
+      for (int s = 0; s < p.nseg; ++s) k = umax64(k, p.seg_key[(int64_t)(n0 + i) * p.nseg + s]);
+      amax_s[i] = key_index(k);
+    }
+  }
+  __syncthreads();
+  for (int i = tid; i < N; i += 256) {
+    const int pi = par_s[i];
+    if (i > 0 && !(pi >= 0 && pi < i)) bad_s = 1;
+    if (i == 0 && pi != -1) bad_s = 1;
+    int rank = 0, nch = 0;
+    for (int j = 1; j < N; ++j) {
+      rank += (j < i && par_s[j] == pi) ? 1 : 0;
+      nch += (par_s[j] == i) ? 1 : 0;
+    }
+    rank_s[i] = rank;
+    nch_s[i] = nch;
+    if (REJECT && nch > p.max_children) bad_s = 1;
+  }
+  __syncthreads();
+  if (bad_s) {
+    for (int i = tid; i < p.max_path; i += 256) { o_path[i] = -1; o_tok[i] = -1; }
+    if (tid == 0) p.out_num_accepted[b] = -1;
+    return;
+  }
+  // accept tests of every child, in parallel
+  for (int c = 1 + tid; c < N; c += 256) {
+    const int u = par_s[c];
+    const int x = tok_s[c];
+    bool ok = false;
+    if (x >= 0 && x < p.vocab) {
+      if (!REJECT) {
+        ok = (x == amax_s[u]);
+      } else {
+        const int64_t gu = n0 + u;
+        const int r = rank_s[c];
+        double Z[9];
+        for (int k = 0; k <= r && k < 9; ++k) Z[k] = level_sum(p, gu, k);
+        const double M = (double)row_max(p, gu);
+        const double qx = (double)p.draft_probs[gu * p.vocab + x];
+        const double e = exp((double)load_logit(p, gu, x) - M);
+        double res = e / Z[0];
+        for (int k = 1; k <= r; ++k) {
+          const double d = fmax(0.0, res - qx);
+          const double zk = k < 9 ? Z[k] : level_sum(p, gu, k);
+          if (zk > 0.0) res = d / zk;
+        }
+        ok = (double)p.u_accept[n0 + c] * qx < res;
+      }
+    }
+    if (REJECT) {
+      if (ok) atomicMin(&first_s[u], c);
+    } else {
+      rank_s[c] = ok ? 1 : 0;                     // greedy: the edge test, reused below
+    }
+  }
+  __syncthreads();
+  if (REJECT) {
+    // sampling order: at each node move to its first accepted child
+    if (tid == 0) {
+      int u = 0, d = 0;
+      path_s[0] = 0;
+      while (first_s[u] != 0x7FFFFFFF && d + 1 < kMaxNodes) {
+        u = first_s[u];
+        path_s[++d] = u;
+      }
+      stop_s = u;
+      depth_s = d;
+    }
+  } else {
+    // greedy: node j is accepted iff every edge on its root path passed; keep the deepest
+    // accepted node, the lowest index among equally deep ones
+    unsigned long long best = 0;
+    for (int j = tid; j < N; j += 256) {
+      bool acc = true;
+      int d = 0, x = j;
+      while (x > 0 && d < N) {
+        acc = acc && rank_s[x] != 0;
+        x = par_s[x];
+        ++d;
+      }
+      if (acc) best = umax64(best, ((unsigned long long)d << 32) | (uint32_t)(0xFFFFu - j));
+    }
+    best = block_max_u64(best);
+    if (tid == 0) {
+      const int f = 0xFFFF - (int)(best & 0xFFFFu);
+      const int d = (int)(best >> 32);
+      int x = f;
+      for (int k = d; k >= 0; --k) {
+        path_s[k] = x;
+        x = k > 0 ? par_s[x] : x;
+      }
+      stop_s = f;
+      depth_s = d;
+    }
+  }
+  __syncthreads();
+  const int u = stop_s, depth = depth_s;
+  if (depth + 1 > p.max_path) {
+    for (int i = tid; i < p.max_path; i += 256) { o_path[i] = -1; o_tok[i] = -1; }
+    if (tid == 0) p.out_num_accepted[b] = -1;
+    return;
+  }
+  int bonus;
+  if (!REJECT) {
+    bonus = amax_s[u];
+  } else {
+    // inverse CDF of the residual left at u after all its children were rejected
+    const int64_t gu = n0 + u;
+    const int r = nch_s[u];
+    if (tid == 0) {
+      int lvl = 0;
+      for (int k = 0; k <= r; ++k) {
+        const double z = level_sum(p, gu, k);
+        if (k < 9) zs[k] = z;
+        if (z > 0.0 || k == 0) lvl = k;             // a zero residual keeps the previous level
+      }
+      const double* ss = p.seg_sum + (gu * (p.max_children + 1) + lvl) * p.nseg;
+      const double zl = level_sum(p, gu, lvl);
+      double tot = 0.0;
+      for (int s = 0; s < p.nseg; ++s) tot += ss[s] / zl;
+      const double thr = (double)p.u_sample[gu] * tot;
+      double base = 0.0;
+      int seg = p.nseg - 1;
+      for (int s = 0; s < p.nseg; ++s) {
+        const double w = ss[s] / zl;
+        if (base + w > thr) { seg = s; break; }
+        base += w;
+      }
+      if (base + ss[seg] / zl <= thr) {             // rounding left the threshold past the end:
+        base = tot;                                 // fall back to the last segment with mass
+        for (int s = p.nseg - 1; s >= 0; --s) {
+          base -= ss[s] / zl;
+          if (ss[s] > 0.0) { seg = s; break; }
+        }
+      }
+      seg_s = seg;
+      base_s = base;
+      thr_s = thr;
+      bonus_s = 0x7FFFFFFF;
+    }
+    __syncthreads();
+    const int seg = seg_s;
+    const int v0 = seg * kSegment;
+    const int v1 = min(p.vocab, v0 + kSegment);
+    const int per = kSegment / 256;
+    const int a0 = v0 + tid * per;
+    const int a1 = min(v1, a0 + per);
+    const double M = (double)row_max(p, gu);
+    const float* q = p.draft_probs + gu * (int64_t)p.vocab;
+    double Z[9];
+    for (int k = 0; k <= r && k < 9; ++k) Z[k] = zs[k];
+    auto res_of = [&](int v) -> double {
+      const double qv = (double)q[v];
+      double res = exp((double)load_logit(p, gu, v) - M) / Z[0];
+      for (int k = 1; k <= r; ++k) {
+        const double dd = fmax(0.0, res - qv);
+        const double zk = k < 9 ? Z[k] : level_sum(p, gu, k);
+        if (zk > 0.0) res = dd / zk;
+      }
+      return res;
+    };
+    double mine = 0.0;
+    for (int v = a0; v < a1; ++v) mine += res_of(v);
+    scan_s[tid] = mine;
+    __syncthreads();
+    if (tid == 0) {                                 // exclusive scan in thread order
+      double run = 0.0;
+      for (int i = 0; i < 256; ++i) { const double t = scan_s[i]; scan_s[i] = run; run += t; }
+    }
+    __syncthreads();
+    const double lo = base_s + scan_s[tid];
+    const double thr = thr_s;
+    if (a0 < a1 && lo + mine > thr && lo <= thr) {
+      double run = lo;
+      int pick = a1 - 1;
+      for (int v = a0; v < a1; ++v) {
+        run += res_of(v);
+        if (run > thr) { pick = v; break; }
+      }
+      atomicMin(&bonus_s, pick);                    // rounding may let two threads claim: lowest wins
+    }
+    __syncthreads();
+    if (tid == 0 && bonus_s == 0x7FFFFFFF) {        // rounding: take the last token with mass in the segment
+      int pick = v0;
+      for (int v = v1 - 1; v >= v0; --v)
+        if (res_of(v) > 0.0) { pick = v; break; }
+      bonus_s = pick;
+    }
+    __syncthreads();
+    bonus = bonus_s;
+  }
+  for (int i = tid; i < p.max_path; i += 256) {
+    o_path[i] = i <= depth ? path_s[i] : -1;
+    o_tok[i] = i < depth ? tok_s[path_s[i + 1]] : (i == depth ? bonus : -1);
+  }
+  if (tid == 0) p.out_num_accepted[b] = depth;
+}
+
+}  // namespace
+
+size_t greedy_ws_bytes(int batch, int max_nodes, int nseg) {
+  return align_up(sizeof(unsigned long long) * (size_t)batch * max_nodes * nseg, 256);
+}
+
+size_t rejection_ws_bytes(int batch, int max_nodes, int nseg, int max_children) {
+  return greedy_ws_bytes(batch, max_nodes, nseg) +
+         align_up(sizeof(double) * (size_t)batch * max_nodes * (max_children + 1) * nseg, 256) +
+         align_up(sizeof(int32_t) * (size_t)batch * max_nodes, 256);
+}
+
+hipError_t launch_accept_greedy(const AcceptParams& p, hipStream_t s) {
+  const unsigned rows = (unsigned)(p.batch * p.max_nodes);
+  hipLaunchKernelGGL(argmax_seg_kernel, dim3(p.nseg, rows), dim3(256), 0, s, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(walk_kernel<false>, dim3(p.batch), dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_accept_rejection(const AcceptParams& p, hipStream_t s) {
+  const unsigned rows = (unsigned)(p.batch * p.max_nodes);
+  hipLaunchKernelGGL(tree_info_kernel, dim3(p.batch), dim3(256), 0, s, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(argmax_seg_kernel, dim3(p.nseg, rows), dim3(256), 0, s, p);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  for (int r = 0; r <= p.max_children; ++r) {
+    hipLaunchKernelGGL(residual_pass_kernel, dim3(p.nseg, rows), dim3(256), 0, s, p, r);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(walk_kernel<true>, dim3(p.batch), dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+}  // namespace spec

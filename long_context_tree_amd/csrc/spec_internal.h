@@ -1,0 +1,114 @@
+// Internal declarations shared by the host layer and the kernel launchers of libspec_verify.
+// Not part of the public ABI (include/spec_verify.h is).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/spec_verify.h"
+
+namespace spec {
+
+constexpr int kTile = 64;          // KV slots per attention tile
+constexpr int kMaxNodes = 256;     // tree nodes per sequence (ancestor masks are 4 x 64 bits)
+constexpr int kSegment = 8192;     // vocabulary elements per acceptance work-group
+constexpr int kMaxTopK = 8192;     // chunks sorted by one work-group for top-k
+
+inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// ------------------------------------------------------------------------------------------
+// tree attention: launch plan and workspace layout (a pure function of the host bounds)
+// ------------------------------------------------------------------------------------------
+struct AttnPlan {
+  int G = 0;             // query heads per KV head
+  int waves = 0;         // waves per work-group (4 or 8)
+  int rows_wg = 0;       // query rows per work-group = waves * 32
+  int row_groups = 0;    // work-groups sharing one KV range (rows of one KV head / rows_wg)
+  int rows_pad = 0;      // row_groups * rows_wg
+  int max_tiles = 0;     // ceil((max_ctx_len + max_nodes) / 64)
+  int split_tiles = 0;   // tiles per split
+  int max_splits = 0;    // ceil(max_tiles / split_tiles)
+  int max_chunks = 0;    // ceil(max_ctx_len / chunk_size), 0 without salience
+  size_t off_part_o = 0, off_part_ml = 0, off_chunk = 0, off_lse2 = 0, bytes = 0;
+};
+
+struct AttnParams {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  int64_t page_stride, head_stride, token_stride;
+  int page_shift;
+  int num_pages;
+  const int32_t* block_table;
+  int bt_stride;
+  const int32_t* ctx_lens;
+  const int32_t* node_offsets;
+  const int32_t* parents;
+  int batch, Hq, Hkv, G, max_nodes, max_ctx;
+  float scale_log2;      // scale * log2(e)
+  int chunk_size, max_chunks;
+  int split_tiles, max_splits, row_groups, rows_pad;
+  float* part_o;         // [batch][Hkv][max_splits][rows_pad][D]
+  float* part_ml;        // [batch][Hkv][max_splits][rows_pad][2]  (running max in log2 units, sum)
+  float* chunk_lse2;     // [batch][max_chunks][max_nodes * Hq]
+  float* lse2;           // [batch][max_nodes * Hq]
+  uint16_t* out;         // bf16 [total_nodes][Hq][D]
+  float* lse;            // [total_nodes][Hq] natural log, nullable
+};
+
+bool make_attn_plan(const spec_tree_attention_args* a, int num_cus, AttnPlan* plan);
+hipError_t launch_tree_attention(const AttnParams& p, const AttnPlan& plan, int head_dim, hipStream_t s);
+
+// ------------------------------------------------------------------------------------------
+// chunk salience
+// ------------------------------------------------------------------------------------------
+struct SalienceParams {
+  const int32_t* ctx_lens;
+  const int32_t* node_offsets;
+  int batch, Hq, max_nodes, max_ctx, chunk_size;
+  int ws_max_chunks;     // chunk stride of the attention workspace
+  const float* chunk_lse2;
+  const float* lse2;
+  float* partial;        // [batch][row_splits][ws_max_chunks]
+  int row_splits;
+  float* chunk_mass;     // [batch][max_chunks]
+  int max_chunks;
+  int accumulate;
+  int top_k;
+  int32_t* topk_index;
+  float* topk_mass;
+};
+constexpr int kSalienceRowsPerWG = 256;
+size_t salience_partial_bytes(int batch, int max_nodes, int Hq, int ws_max_chunks);
+hipError_t launch_chunk_salience(const SalienceParams& p, hipStream_t s);
+
+// ------------------------------------------------------------------------------------------
+// acceptance
+// ------------------------------------------------------------------------------------------
+struct AcceptParams {
+  int batch, vocab, max_nodes, max_path, nseg;
+  const int32_t* node_offsets;
+  const int32_t* parents;
+  const int32_t* draft_tokens;
+  const void* logits;
+  int bf16;              // 1: bf16 logits, 0: fp32
+  int32_t* out_num_accepted;
+  int32_t* out_path_nodes;
+  int32_t* out_tokens;
+  unsigned long long* seg_key;   // [batch*max_nodes][nseg] packed (ordered value, ~index)
+  // rejection only
+  int max_children;
+  const float* draft_probs;
+  const float* u_accept;
+  const float* u_sample;
+  double* seg_sum;       // [batch*max_nodes][max_children+1][nseg]
+  int32_t* n_children;   // [batch*max_nodes]
+};
+size_t greedy_ws_bytes(int batch, int max_nodes, int nseg);
+size_t rejection_ws_bytes(int batch, int max_nodes, int nseg, int max_children);
+hipError_t launch_accept_greedy(const AcceptParams& p, hipStream_t s);
+hipError_t launch_accept_rejection(const AcceptParams& p, hipStream_t s);
+
+}  // namespace spec

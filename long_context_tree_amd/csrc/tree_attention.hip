@@ -1,0 +1,468 @@
+// Tree-masked GQA attention over a paged bf16 KV cache, for gfx950.
+//
+// Every draft-tree node is a query of one verification forward; it sees the whole committed
+// context and its own ancestors in the tree ("DiffSpec: Accelerating Long Sequence Generation
+// with Differential Speculative Decoding", "What DiffSpec Does" item 5: verification shares the
+// prefixes of the speculative structure; the chain case is the per-row cache mask of "Adaptive
+// Speculative Decoding", section Layout).
+//
+// Design (MI355X-first):
+//  * Split-K flash decoding.  A work-group owns one (sequence, KV head, KV split) range and up to
+//    256 query rows (all tree nodes x the GQA group of that KV head), so each 64-slot K/V tile is
+//    read from HBM once and shared, through LDS, by every node and every query head of the group.
+//    Wider trees use several row groups; their work-groups are placed on the same XCD (work-group
+//    ids i and i+8 land on one XCD) so the second read of a tile hits that XCD's L2.
+//  * Tiles are gathered page by page through the block table with 16-byte loads (one 256-byte
+//    row per key for head_dim 128), prefetched into registers while the previous tile computes,
+//    and double-buffered in LDS.  V is transposed on its way into LDS (V^T rows are keys-contiguous).
+//  * Both products run on MFMA v_mfma_f32_16x16x32_bf16: S^T = K Q^T (A = K rows from LDS,
+//    B = Q from registers), then O^T = V^T P^T (A = V^T from LDS, B = P straight from the S^T
+//    accumulators).  In this orientation each lane owns one query row in every fragment, so the
+//    online softmax (max, exp2, rescale) needs no cross-lane data except a 4-lane max/sum.
+//  * Keys >= ctx_len are tree slots: visible iff the key's node is an ancestor-or-self of the
+//    row's node (ancestor bit masks built in LDS from the parent array).
+//  * With chunk_size > 0 each tile also emits, per query row, the log2-sum-exp of the row's scores
+//    over each context chunk; the salience pass turns these into attention mass once the
+//    row's final log-sum-exp is known (no second pass over K).
+//  * Splits write (max, sum, unnormalised O) partials; the merge kernel combines them (LSE merge).
+#include "spec_internal.h"
+
+namespace spec {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int RB = 2;               // 16-row MFMA blocks per wave
+constexpr float kNegBig = -1.0e30f; // finite "minus infinity" for running maxima
+
+__device__ __forceinline__ float max4g(float x) {   // max over lanes l, l^16, l^32, l^48
+  x = fmaxf(x, __shfl_xor(x, 16));
+  return fmaxf(x, __shfl_xor(x, 32));
+}
+__device__ __forceinline__ float sum4g(float x) {
+  x += __shfl_xor(x, 16);
+  return x + __shfl_xor(x, 32);
+}
+
+__device__ __forceinline__ u32x4 load_kv_chunk(const uint16_t* base, const AttnParams& p, const int32_t* bt_row,
+                                               int key, int keys, int kvh, int dc) {
+  u32x4 r = {0u, 0u, 0u, 0u};
+  if (key < keys) {
+    const int page = bt_row[key >> p.page_shift];
+    if (page >= 0 && page < p.num_pages) {
+      const int slot = key & ((1 << p.page_shift) - 1);
+      const uint16_t* ptr = base + (int64_t)page * p.page_stride + (int64_t)kvh * p.head_stride +
+                            (int64_t)slot * p.token_stride + dc * 8;
+      r = *reinterpret_cast<const u32x4*>(ptr);
+    }
+  }
+  return r;
+}
+
+template <int D, int W>
+__global__ __launch_bounds__(W * 64) void tree_attn_kernel(AttnParams p) {
+  constexpr int NT = W * 64;
+  constexpr int ROWS_WG = W * RB * 16;
+  constexpr int KS = D / 32;                    // k-steps of the QK^T product
+  constexpr int NB = D / 16;                    // 16-dim output blocks
+  constexpr int KST = D + 8;                    // K row stride in LDS (bf16), padded against bank conflicts
+  constexpr int VST = kTile + 4;                // V^T row stride in LDS (bf16)
+  constexpr int CPR = D / 8;                    // 16-byte chunks per K/V row
+  constexpr int K_CHUNKS = kTile * CPR;
+  constexpr int K_PER_T = K_CHUNKS / NT;
+  constexpr int V_UNITS = (kTile / 4) * CPR;    // (4 keys x 8 dims) transpose units per tile
+  constexpr int V_PER_T = (V_UNITS + NT - 1) / NT;
+  static_assert(K_CHUNKS % NT == 0, "tile must split evenly over the work-group");
+
+  __shared__ __attribute__((aligned(16))) uint16_t k_lds[2][kTile * KST];
+  __shared__ __attribute__((aligned(16))) uint16_t vt_lds[2][D * VST];
+  __shared__ uint64_t anc_lds[kMaxNodes][4];
+
+  // ---- which (row group, split, KV head, sequence): row groups of one KV range share an XCD ----
+  const int RG = p.row_groups;
+  const int n_units = p.batch * p.Hkv * p.max_splits;
+  const int wg = blockIdx.x;
+  const int rg = (wg >> 3) % RG;
+  const int unit = ((wg >> 3) / RG) * 8 + (wg & 7);
+  if (unit >= n_units) return;
+  const int split = unit % p.max_splits;
+  const int kvh = (unit / p.max_splits) % p.Hkv;
+  const int b = unit / (p.max_splits * p.Hkv);
+
+  int n0 = p.node_offsets[b];
+  int N = p.node_offsets[b + 1] - n0;
+  N = N < 0 ? 0 : (N > p.max_nodes ? p.max_nodes : N);
+  n0 = n0 < 0 ? 0 : (n0 > (p.batch - 1) * p.max_nodes ? (p.batch - 1) * p.max_nodes : n0);
+  int L = p.ctx_lens[b];
+  L = L < 0 ? 0 : (L > p.max_ctx ? p.max_ctx : L);
+  const int keys = L + N;
+  const int n_tiles = (keys + kTile - 1) / kTile;
+  const int t_begin = split * p.split_tiles;
+  const int t_end = min(n_tiles, t_begin + p.split_tiles);
+  const int G = p.G;
+  const int rows = N * G;
+  const int row0 = rg * ROWS_WG;
+  if (t_begin >= t_end || row0 >= rows) return;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int lm = lane & 15, lg = lane >> 4;
+  const int32_t* bt_row = p.block_table + (int64_t)b * p.bt_stride;
+
+  // ---- ancestor-or-self bit masks of the tree nodes (only the split holding the tree slots) ----
+  const bool has_tree = t_end * kTile > L;
+  if (has_tree) {
+    for (int i = tid; i < N; i += NT) {
+      uint64_t m[4] = {0, 0, 0, 0};
+      int j = i;
+      for (int step = 0; step < N && j >= 0; ++step) {
+        m[j >> 6] |= 1ull << (j & 63);
+        const int pj = p.parents[n0 + j];
+        if (pj >= j) break;                       // not topological: stop the walk
+        j = pj;
+      }
+      anc_lds[i][0] = m[0]; anc_lds[i][1] = m[1]; anc_lds[i][2] = m[2]; anc_lds[i][3] = m[3];
+    }
+  }
+
+  // ---- this lane's query rows (row = node * G + head-in-group) and their Q fragments ----
+  int node_r[RB], head_r[RB];
+  bool valid_r[RB];
+  bf16x8 qreg[RB][KS];
+  const bool wave_active = row0 + wave * RB * 16 < rows;
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    const int row = row0 + (wave * RB + rb) * 16 + lm;
+    valid_r[rb] = row < rows;
+    node_r[rb] = valid_r[rb] ? row / G : 0;
+    head_r[rb] = valid_r[rb] ? kvh * G + row % G : 0;
+    const uint16_t* qp = p.q + ((int64_t)(n0 + node_r[rb]) * p.Hq + head_r[rb]) * D + 8 * lg;
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) {
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (valid_r[rb]) v = *reinterpret_cast<const u32x4*>(qp + 32 * kk);
+      qreg[rb][kk] = __builtin_bit_cast(bf16x8, v);
+    }
+  }
+
+  // ---- tile staging ----
+  u32x4 kreg[K_PER_T];
+  u32x4 vreg[V_PER_T][4];
+  auto load_tile = [&](int t) {
+    const int key0 = t * kTile;
+#pragma unroll
+    for (int c = 0; c < K_PER_T; ++c) {
+      const int ch = tid + c * NT;
+      kreg[c] = load_kv_chunk(p.k, p, bt_row, key0 + ch / CPR, keys, kvh, ch % CPR);
+    }
+#pragma unroll
+    for (int u = 0; u < V_PER_T; ++u) {
+      const int un = tid + u * NT;
+      if (un < V_UNITS) {
+        const int dc = un % CPR, kgp = un / CPR;
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) vreg[u][kk] = load_kv_chunk(p.v, p, bt_row, key0 + 4 * kgp + kk, keys, kvh, dc);
+      }
+    }
+  };
+  auto store_tile = [&](int buf) {
+#pragma unroll
+    for (int c = 0; c < K_PER_T; ++c) {
+      const int ch = tid + c * NT;
+      *reinterpret_cast<u32x4*>(&k_lds[buf][(ch / CPR) * KST + (ch % CPR) * 8]) = kreg[c];
+    }
+#pragma unroll
+    for (int u = 0; u < V_PER_T; ++u) {
+      const int un = tid + u * NT;
+      if (un < V_UNITS) {
+        const int dc = un % CPR, kgp = un / CPR;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {            // dims 2w, 2w+1 of the chunk
+          const uint32_t a0 = vreg[u][0][w], a1 = vreg[u][1][w], a2 = vreg[u][2][w], a3 = vreg[u][3][w];
+          u32x2 lo, hi;
+          lo[0] = __builtin_amdgcn_perm(a1, a0, 0x05040100u);   // dim 2w: keys 0,1
+          lo[1] = __builtin_amdgcn_perm(a3, a2, 0x05040100u);   // dim 2w: keys 2,3
+          hi[0] = __builtin_amdgcn_perm(a1, a0, 0x07060302u);   // dim 2w+1: keys 0,1
+          hi[1] = __builtin_amdgcn_perm(a3, a2, 0x07060302u);
+          *reinterpret_cast<u32x2*>(&vt_lds[buf][(dc * 8 + 2 * w) * VST + 4 * kgp]) = lo;
+          *reinterpret_cast<u32x2*>(&vt_lds[buf][(dc * 8 + 2 * w + 1) * VST + 4 * kgp]) = hi;
+        }
+      }
+    }
+  };
+
+  f32x4 o[RB][NB];
+  float m_r[RB], l_r[RB], cacc[RB];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    m_r[rb] = kNegBig;
+    l_r[rb] = 0.f;
+    cacc[rb] = 0.f;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) o[rb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  const float c2 = p.scale_log2;
+  const int cs = p.chunk_size;
+  const int row_stride_chunk = p.max_nodes * p.Hq;
+
+  load_tile(t_begin);
+  store_tile(0);
+  __syncthreads();
+
+  for (int t = t_begin; t < t_end; ++t) {
+    const int buf = (t - t_begin) & 1;
+    if (t + 1 < t_end) load_tile(t + 1);
+    if (wave_active) {
+      const int key0 = t * kTile;
+      // S^T[key][row] = K . Q^T
+      f32x4 s[RB][4];
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) s[rb][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < KS; ++kk) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const bf16x8 a = *reinterpret_cast<const bf16x8*>(&k_lds[buf][(16 * j + lm) * KST + 32 * kk + 8 * lg]);
+#pragma unroll
+          for (int rb = 0; rb < RB; ++rb)
+            s[rb][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qreg[rb][kk], s[rb][j], 0, 0, 0);
+        }
+      }
+      const bool edge = key0 + kTile > L;        // tile holds tree slots or slots past the end
+      bf16x8 pb[RB][2];
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        if (edge) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int key = key0 + 16 * j + 4 * lg + i;
+              bool vis = key < L;
+              if (!vis && key < keys && valid_r[rb]) {
+                const int tj = key - L;
+                vis = (anc_lds[node_r[rb]][tj >> 6] >> (tj & 63)) & 1ull;
+              }
+              if (!vis) s[rb][j][i] = -INFINITY;
+            }
+        }
+        float mx = -INFINITY;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          mx = fmaxf(fmaxf(fmaxf(mx, s[rb][j][0]), fmaxf(s[rb][j][1], s[rb][j][2])), s[rb][j][3]);
+        mx = max4g(mx);
+        const float mnew = fmaxf(m_r[rb], mx * c2);
+        const float alpha = __builtin_amdgcn_exp2f(m_r[rb] - mnew);
+        float e[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          e[j] = 0.f;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float pv = __builtin_amdgcn_exp2f(fmaf(s[rb][j][i], c2, -mnew));
+            s[rb][j][i] = pv;
+            e[j] += pv;
+          }
+        }
+        l_r[rb] = l_r[rb] * alpha + ((e[0] + e[1]) + (e[2] + e[3]));
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) o[rb][nb] *= alpha;
+        m_r[rb] = mnew;
+
+        // per-chunk log2-sum-exp partials over context keys
+        if (cs > 0 && key0 < L) {
+          if (key0 + kTile > L) {                 // the tile where the context ends: context keys only
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              e[j] = 0.f;
+#pragma unroll
+              for (int i = 0; i < 4; ++i) e[j] += (key0 + 16 * j + 4 * lg + i < L) ? s[rb][j][i] : 0.f;
+            }
+          }
+          const int64_t rowc = (int64_t)node_r[rb] * p.Hq + head_r[rb];
+          float* cbase = p.chunk_lse2 + (int64_t)b * p.max_chunks * row_stride_chunk + rowc;
+          if (cs >= kTile) {
+            cacc[rb] = cacc[rb] * alpha + ((e[0] + e[1]) + (e[2] + e[3]));
+            const int c = key0 / cs;
+            const int cend = min((c + 1) * cs, L);
+            if (key0 + kTile >= cend) {
+              const float tot = sum4g(cacc[rb]);
+              if (valid_r[rb] && lg == 0) cbase[(int64_t)c * row_stride_chunk] = mnew + __builtin_amdgcn_logf(tot);
+              cacc[rb] = 0.f;
+            }
+          } else {
+            const int per = kTile / cs;           // 2 (cs 32) or 4 (cs 16)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              if (q >= per) break;
+              const float part = (per == 4) ? e[q] : (e[2 * q] + e[2 * q + 1]);
+              const float tot = sum4g(part);
+              const int c = key0 / cs + q;
+              if (c * cs < L && valid_r[rb] && lg == 0)
+                cbase[(int64_t)c * row_stride_chunk] = mnew + __builtin_amdgcn_logf(tot);
+            }
+          }
+        }
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2) {
+          bf16x8 v;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            v[i] = (__bf16)s[rb][2 * h2][i];
+            v[4 + i] = (__bf16)s[rb][2 * h2 + 1][i];
+          }
+          pb[rb][h2] = v;
+        }
+      }
+      // O^T[dim][row] += V^T . P^T
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2) {
+          const uint16_t* vp = &vt_lds[buf][(16 * nb + lm) * VST + 32 * h2 + 4 * lg];
+          const u32x2 lo = *reinterpret_cast<const u32x2*>(vp);
+          const u32x2 hi = *reinterpret_cast<const u32x2*>(vp + 16);
+          const u32x4 av = {lo[0], lo[1], hi[0], hi[1]};
+          const bf16x8 a = __builtin_bit_cast(bf16x8, av);
+#pragma unroll
+          for (int rb = 0; rb < RB; ++rb)
+            o[rb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb[rb][h2], o[rb][nb], 0, 0, 0);
+        }
+      }
+    }
+    if (t + 1 < t_end) store_tile(buf ^ 1);
+    __syncthreads();
+  }
+
+  if (!wave_active) return;
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    const float l = sum4g(l_r[rb]);
+    if (!valid_r[rb]) continue;
+    const int row = row0 + (wave * RB + rb) * 16 + lm;
+    const int64_t base = (((int64_t)b * p.Hkv + kvh) * p.max_splits + split) * p.rows_pad + row;
+    if (lg == 0) {
+      p.part_ml[base * 2 + 0] = m_r[rb];
+      p.part_ml[base * 2 + 1] = l;
+    }
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) *reinterpret_cast<f32x4*>(&p.part_o[base * D + 16 * nb + 4 * lg]) = o[rb][nb];
+  }
+}
+
+// LSE merge of the split partials: one wave per (node, query head) row.
+template <int D>
+__global__ __launch_bounds__(256) void attn_merge_kernel(AttnParams p) {
+  constexpr int E = D / 64;
+  const int lane = threadIdx.x & 63;
+  const int64_t rid = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int per_seq = p.max_nodes * p.Hq;
+  const int b = (int)(rid / per_seq);
+  if (b >= p.batch) return;
+  const int rem = (int)(rid % per_seq);
+  const int node = rem / p.Hq, head = rem % p.Hq;
+  int n0 = p.node_offsets[b];
+  int N = p.node_offsets[b + 1] - n0;
+  N = N < 0 ? 0 : (N > p.max_nodes ? p.max_nodes : N);
+  n0 = n0 < 0 ? 0 : (n0 > (p.batch - 1) * p.max_nodes ? (p.batch - 1) * p.max_nodes : n0);
+  if (node >= N) return;
+  int L = p.ctx_lens[b];
+  L = L < 0 ? 0 : (L > p.max_ctx ? p.max_ctx : L);
+  const int n_tiles = (L + N + kTile - 1) / kTile;
+  const int nsp = (n_tiles + p.split_tiles - 1) / p.split_tiles;
+  const int kvh = head / p.G;
+  const int row = node * p.G + head % p.G;
+  const int64_t base0 = ((int64_t)b * p.Hkv + kvh) * p.max_splits * p.rows_pad + row;
+
+  float M = -INFINITY;
+  for (int s = lane; s < nsp; s += 64) M = fmaxf(M, p.part_ml[(base0 + (int64_t)s * p.rows_pad) * 2]);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+
+  float lsum = 0.f;
+  float acc[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) acc[e] = 0.f;
+  for (int s = 0; s < nsp; ++s) {
+    const int64_t bs = base0 + (int64_t)s * p.rows_pad;
+    const float w = __builtin_amdgcn_exp2f(p.part_ml[bs * 2] - M);
+    lsum += w * p.part_ml[bs * 2 + 1];
+#pragma unroll
+    for (int e = 0; e < E; ++e) acc[e] += w * p.part_o[bs * D + lane + 64 * e];
+  }
+  const float inv = 1.0f / lsum;
+  uint16_t* op = p.out + ((int64_t)(n0 + node) * p.Hq + head) * D;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const __bf16 v = (__bf16)(acc[e] * inv);
+    op[lane + 64 * e] = __builtin_bit_cast(uint16_t, v);
+  }
+  if (lane == 0) {
+    const float l2 = M + __builtin_amdgcn_logf(lsum);
+    p.lse2[(int64_t)b * per_seq + rem] = l2;
+    if (p.lse) p.lse[(int64_t)(n0 + node) * p.Hq + head] = l2 * 0.69314718055994530942f;
+  }
+}
+
+template <int D, int W>
+hipError_t launch_d_w(const AttnParams& p, const AttnPlan& plan, hipStream_t s) {
+  const int n_units = p.batch * p.Hkv * p.max_splits;
+  const int grid = (int)(ceil_div(n_units, 8) * 8 * plan.row_groups);
+  hipLaunchKernelGGL((tree_attn_kernel<D, W>), dim3(grid), dim3(W * 64), 0, s, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t rows = (int64_t)p.batch * p.max_nodes * p.Hq;
+  hipLaunchKernelGGL((attn_merge_kernel<D>), dim3((unsigned)ceil_div(rows, 4)), dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+bool make_attn_plan(const spec_tree_attention_args* a, int num_cus, AttnPlan* plan) {
+  AttnPlan pl;
+  pl.G = a->num_q_heads / a->num_kv_heads;
+  const int rows = a->max_nodes * pl.G;
+  pl.waves = rows > 128 ? 8 : 4;
+  pl.rows_wg = pl.waves * RB * 16;
+  pl.row_groups = (int)ceil_div(rows, pl.rows_wg);
+  pl.rows_pad = pl.row_groups * pl.rows_wg;
+  pl.max_tiles = (int)ceil_div((int64_t)a->max_ctx_len + a->max_nodes, kTile);
+  const int align = (a->chunk_size >= kTile) ? a->chunk_size / kTile : 1;   // splits hold whole chunks
+  int st = a->split_tiles;
+  if (st <= 0) {
+    // enough work-groups to fill every CU about twice, but at least 8 tiles per split
+    const int64_t ranges = (int64_t)a->batch * a->num_kv_heads * pl.row_groups;
+    const int64_t target = 2LL * (num_cus > 0 ? num_cus : 256);
+    int64_t want_splits = ceil_div(target, ranges);
+    st = (int)ceil_div(pl.max_tiles, want_splits < 1 ? 1 : want_splits);
+    if (st < 8) st = 8;
+  }
+  st = (int)(ceil_div(st, align) * align);
+  pl.split_tiles = st;
+  pl.max_splits = (int)ceil_div(pl.max_tiles, st);
+  pl.max_chunks = a->chunk_size > 0 ? (int)ceil_div(a->max_ctx_len, a->chunk_size) : 0;
+  size_t off = 0;
+  pl.off_part_o = off;
+  off = align_up(off + sizeof(float) * (size_t)a->batch * a->num_kv_heads * pl.max_splits * pl.rows_pad * a->head_dim, 256);
+  pl.off_part_ml = off;
+  off = align_up(off + sizeof(float) * 2 * (size_t)a->batch * a->num_kv_heads * pl.max_splits * pl.rows_pad, 256);
+  pl.off_lse2 = off;
+  off = align_up(off + sizeof(float) * (size_t)a->batch * a->max_nodes * a->num_q_heads, 256);
+  pl.off_chunk = off;
+  off = align_up(off + sizeof(float) * (size_t)a->batch * pl.max_chunks * a->max_nodes * a->num_q_heads, 256);
+  pl.bytes = off;
+  *plan = pl;
+  return true;
+}
+
+hipError_t launch_tree_attention(const AttnParams& p, const AttnPlan& plan, int head_dim, hipStream_t s) {
+  if (head_dim == 128) return plan.waves == 8 ? launch_d_w<128, 8>(p, plan, s) : launch_d_w<128, 4>(p, plan, s);
+  return plan.waves == 8 ? launch_d_w<64, 8>(p, plan, s) : launch_d_w<64, 4>(p, plan, s);
+}
+
+}  // namespace spec

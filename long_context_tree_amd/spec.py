@@ -1,0 +1,319 @@
+"""Python binding of libspec_verify (include/spec_verify.h), argument marshalling only.
+
+torch supplies device memory and the current HIP stream; every step of the verification path runs
+in the library's HIP kernels.  If the library is missing the calls raise: there is no fallback.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libspec_verify.so")
+
+SPEC_OK = 0
+SPEC_DTYPE_BF16 = 0
+SPEC_DTYPE_F32 = 1
+ABI_VERSION = 1
+
+_lib = None
+
+
+class SpecError(RuntimeError):
+    def __init__(self, status: int, func: str, text: str):
+        super().__init__(f"{func}: {status_string(status)}: {text}")
+        self.status = status
+
+
+def lib():
+    """The loaded library; raises if it has not been built (python -m long_context_tree_amd.build)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m long_context_tree_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        L.spec_abi_version.restype = ctypes.c_int
+        L.spec_status_string.restype = ctypes.c_char_p
+        L.spec_status_string.argtypes = [ctypes.c_int]
+        L.spec_last_error.restype = ctypes.c_char_p
+        for name, argt in (("spec_tree_attention", TreeAttentionArgs), ("spec_chunk_salience", ChunkSalienceArgs),
+                           ("spec_accept_greedy", AcceptGreedyArgs), ("spec_accept_rejection", AcceptRejectionArgs)):
+            f = getattr(L, name)
+            f.restype = ctypes.c_int
+            f.argtypes = [ctypes.POINTER(argt), ctypes.c_void_p]
+        for name, argt in (("spec_tree_attention_workspace_size", TreeAttentionArgs),
+                           ("spec_accept_greedy_workspace_size", AcceptGreedyArgs),
+                           ("spec_accept_rejection_workspace_size", AcceptRejectionArgs)):
+            f = getattr(L, name)
+            f.restype = ctypes.c_size_t
+            f.argtypes = [ctypes.POINTER(argt)]
+        if L.spec_abi_version() != ABI_VERSION:
+            raise RuntimeError(f"libspec_verify ABI {L.spec_abi_version()} != binding ABI {ABI_VERSION}")
+        _lib = L
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().spec_status_string(status).decode()
+
+
+def last_error() -> str:
+    return lib().spec_last_error().decode()
+
+
+# ---------------------------------------------------------------------------------------------
+# C structs (field order and types follow include/spec_verify.h)
+# ---------------------------------------------------------------------------------------------
+
+class PagedKV(ctypes.Structure):
+    _fields_ = [("k_cache", ctypes.c_void_p), ("v_cache", ctypes.c_void_p),
+                ("page_stride", ctypes.c_int64), ("head_stride", ctypes.c_int64), ("token_stride", ctypes.c_int64),
+                ("page_size", ctypes.c_int32), ("num_pages", ctypes.c_int32),
+                ("block_table", ctypes.c_void_p), ("block_table_stride", ctypes.c_int32)]
+
+
+class TreeAttentionArgs(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("num_q_heads", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("max_nodes", ctypes.c_int32), ("max_ctx_len", ctypes.c_int32),
+                ("ctx_lens", ctypes.c_void_p), ("node_offsets", ctypes.c_void_p), ("parents", ctypes.c_void_p),
+                ("q", ctypes.c_void_p), ("kv", PagedKV), ("scale", ctypes.c_float), ("out", ctypes.c_void_p),
+                ("lse", ctypes.c_void_p), ("chunk_size", ctypes.c_int32), ("split_tiles", ctypes.c_int32),
+                ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t)]
+
+
+class ChunkSalienceArgs(ctypes.Structure):
+    _fields_ = [("attn", ctypes.POINTER(TreeAttentionArgs)), ("chunk_mass", ctypes.c_void_p),
+                ("max_chunks", ctypes.c_int32), ("accumulate", ctypes.c_int32), ("top_k", ctypes.c_int32),
+                ("topk_index", ctypes.c_void_p), ("topk_mass", ctypes.c_void_p)]
+
+
+class AcceptGreedyArgs(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("vocab", ctypes.c_int32), ("max_nodes", ctypes.c_int32),
+                ("max_path", ctypes.c_int32), ("node_offsets", ctypes.c_void_p), ("parents", ctypes.c_void_p),
+                ("draft_tokens", ctypes.c_void_p), ("target_logits", ctypes.c_void_p),
+                ("logits_dtype", ctypes.c_int32), ("out_num_accepted", ctypes.c_void_p),
+                ("out_path_nodes", ctypes.c_void_p), ("out_tokens", ctypes.c_void_p),
+                ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t)]
+
+
+class AcceptRejectionArgs(ctypes.Structure):
+    _fields_ = [("base", AcceptGreedyArgs), ("max_children", ctypes.c_int32), ("draft_probs", ctypes.c_void_p),
+                ("u_accept", ctypes.c_void_p), ("u_sample", ctypes.c_void_p)]
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _check(status: int, func: str):
+    if status != SPEC_OK:
+        raise SpecError(status, func, last_error())
+
+
+def _need(t: torch.Tensor, name: str, dtype, contiguous=True):
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: dtype {t.dtype}, expected {dtype}")
+    if contiguous and not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+
+
+def _workspace(nbytes: int, device, workspace: Optional[torch.Tensor]) -> torch.Tensor:
+    if workspace is not None and workspace.numel() * workspace.element_size() >= nbytes:
+        return workspace
+    # 256 extra bytes so the start can be aligned to 256 bytes
+    buf = torch.empty(max(nbytes, 1) + 256, dtype=torch.uint8, device=device)
+    off = (-buf.data_ptr()) % 256
+    return buf[off:off + max(nbytes, 1)]
+
+
+# ---------------------------------------------------------------------------------------------
+# spec_tree_attention
+# ---------------------------------------------------------------------------------------------
+
+class AttentionHandle:
+    """The argument struct (and the workspace it points to) of one spec_tree_attention call, as
+    spec_chunk_salience needs it."""
+
+    def __init__(self, args: TreeAttentionArgs, keep):
+        self.args = args
+        self._keep = keep
+
+
+def tree_attention_args(q, k_cache, v_cache, block_table, ctx_lens, node_offsets, parents, *, max_nodes: int,
+                        max_ctx_len: int, scale: Optional[float] = None, chunk_size: int = 0, split_tiles: int = 0,
+                        out=None, lse=None, workspace=None) -> TreeAttentionArgs:
+    """Fill the C argument struct from tensors (no launch).  k_cache / v_cache are bf16
+    [pages][kv_heads][page_size][head_dim] with unit stride in the last dimension."""
+    a = TreeAttentionArgs()
+    T, Hq, D = q.shape
+    a.batch = ctx_lens.numel()
+    a.num_q_heads = Hq
+    a.num_kv_heads = k_cache.shape[1]
+    a.head_dim = D
+    a.max_nodes = max_nodes
+    a.max_ctx_len = max_ctx_len
+    a.ctx_lens, a.node_offsets, a.parents = _ptr(ctx_lens), _ptr(node_offsets), _ptr(parents)
+    a.q = _ptr(q)
+    a.kv.k_cache, a.kv.v_cache = _ptr(k_cache), _ptr(v_cache)
+    a.kv.page_stride, a.kv.head_stride, a.kv.token_stride = k_cache.stride(0), k_cache.stride(1), k_cache.stride(2)
+    a.kv.page_size = k_cache.shape[2]
+    a.kv.num_pages = k_cache.shape[0]
+    a.kv.block_table = _ptr(block_table)
+    a.kv.block_table_stride = block_table.shape[1]
+    a.scale = (1.0 / math.sqrt(D)) if scale is None else scale
+    a.out = _ptr(out)
+    a.lse = _ptr(lse)
+    a.chunk_size = chunk_size
+    a.split_tiles = split_tiles
+    a.workspace = _ptr(workspace)
+    a.workspace_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    return a
+
+
+def tree_attention(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, block_table: torch.Tensor,
+                   ctx_lens: torch.Tensor, node_offsets: torch.Tensor, parents: torch.Tensor, *, max_nodes: int,
+                   max_ctx_len: int, scale: Optional[float] = None, chunk_size: int = 0, split_tiles: int = 0,
+                   out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None, want_lse: bool = True,
+                   workspace: Optional[torch.Tensor] = None, stream=None):
+    """Tree-masked attention of every draft-tree node over the paged KV cache.
+
+    Returns (out bf16 [T][Hq][D], lse fp32 [T][Hq] or None, handle for spec_chunk_salience)."""
+    _need(q, "q", torch.bfloat16)
+    for name, t in (("ctx_lens", ctx_lens), ("node_offsets", node_offsets), ("parents", parents),
+                    ("block_table", block_table)):
+        _need(t, name, torch.int32)
+    _need(k_cache, "k_cache", torch.bfloat16, contiguous=False)
+    _need(v_cache, "v_cache", torch.bfloat16, contiguous=False)
+    if k_cache.stride() != v_cache.stride() or k_cache.shape != v_cache.shape:
+        raise ValueError("k_cache and v_cache must have the same shape and strides")
+    if k_cache.stride(3) != 1:
+        raise ValueError("k_cache / v_cache: the head_dim stride must be 1")
+    T, Hq, D = q.shape
+    if out is None:
+        out = torch.empty((T, Hq, D), dtype=torch.bfloat16, device=q.device)
+    if lse is None and want_lse:
+        lse = torch.empty((T, Hq), dtype=torch.float32, device=q.device)
+    a = tree_attention_args(q, k_cache, v_cache, block_table, ctx_lens, node_offsets, parents, max_nodes=max_nodes,
+                            max_ctx_len=max_ctx_len, scale=scale, chunk_size=chunk_size, split_tiles=split_tiles,
+                            out=out, lse=lse)
+    need = lib().spec_tree_attention_workspace_size(ctypes.byref(a))
+    if need == 0:
+        _check(lib().spec_tree_attention(ctypes.byref(a), None), "spec_tree_attention")
+    ws = _workspace(need, q.device, workspace)
+    a.workspace, a.workspace_bytes = ws.data_ptr(), ws.numel()
+    _check(lib().spec_tree_attention(ctypes.byref(a), _stream(stream)), "spec_tree_attention")
+    return out, lse, AttentionHandle(a, (q, k_cache, v_cache, block_table, ctx_lens, node_offsets, parents, out, lse,
+                                         ws))
+
+
+def tree_attention_workspace_size(**kw) -> int:
+    """Workspace bytes for the given host bounds (fields of spec_tree_attention_args)."""
+    a = TreeAttentionArgs()
+    for k, v in kw.items():
+        if k.startswith("kv_"):
+            setattr(a.kv, k[3:], v)
+        else:
+            setattr(a, k, v)
+    return lib().spec_tree_attention_workspace_size(ctypes.byref(a))
+
+
+# ---------------------------------------------------------------------------------------------
+# spec_chunk_salience
+# ---------------------------------------------------------------------------------------------
+
+def chunk_salience(handle: AttentionHandle, chunk_mass: torch.Tensor, *, accumulate: bool = False, top_k: int = 0,
+                   topk_index: Optional[torch.Tensor] = None, topk_mass: Optional[torch.Tensor] = None, stream=None):
+    """Per-chunk attention mass of the attention call behind ``handle`` (fp32 [batch][max_chunks],
+    written or accumulated in place), and optionally the top_k chunks.  Returns (chunk_mass,
+    topk_index, topk_mass)."""
+    _need(chunk_mass, "chunk_mass", torch.float32)
+    B = handle.args.batch
+    if top_k > 0:
+        if topk_index is None:
+            topk_index = torch.empty((B, top_k), dtype=torch.int32, device=chunk_mass.device)
+        if topk_mass is None:
+            topk_mass = torch.empty((B, top_k), dtype=torch.float32, device=chunk_mass.device)
+    s = ChunkSalienceArgs()
+    s.attn = ctypes.pointer(handle.args)
+    s.chunk_mass = _ptr(chunk_mass)
+    s.max_chunks = chunk_mass.shape[1]
+    s.accumulate = int(accumulate)
+    s.top_k = top_k
+    s.topk_index = _ptr(topk_index)
+    s.topk_mass = _ptr(topk_mass)
+    _check(lib().spec_chunk_salience(ctypes.byref(s), _stream(stream)), "spec_chunk_salience")
+    return chunk_mass, topk_index, topk_mass
+
+
+# ---------------------------------------------------------------------------------------------
+# spec_accept_greedy / spec_accept_rejection
+# ---------------------------------------------------------------------------------------------
+
+def _greedy_args(node_offsets, parents, draft_tokens, logits, max_nodes, max_path, outs) -> AcceptGreedyArgs:
+    for name, t in (("node_offsets", node_offsets), ("parents", parents), ("draft_tokens", draft_tokens)):
+        _need(t, name, torch.int32)
+    if logits.dtype not in (torch.bfloat16, torch.float32) or not logits.is_contiguous():
+        raise TypeError("target_logits: contiguous bf16 or fp32 [total_nodes][vocab]")
+    a = AcceptGreedyArgs()
+    a.batch = node_offsets.numel() - 1
+    a.vocab = logits.shape[1]
+    a.max_nodes = max_nodes
+    a.max_path = max_path
+    a.node_offsets, a.parents, a.draft_tokens = _ptr(node_offsets), _ptr(parents), _ptr(draft_tokens)
+    a.target_logits = _ptr(logits)
+    a.logits_dtype = SPEC_DTYPE_BF16 if logits.dtype == torch.bfloat16 else SPEC_DTYPE_F32
+    a.out_num_accepted, a.out_path_nodes, a.out_tokens = (_ptr(t) for t in outs)
+    return a
+
+
+def _outs(batch, max_path, device):
+    return (torch.empty(batch, dtype=torch.int32, device=device),
+            torch.empty((batch, max_path), dtype=torch.int32, device=device),
+            torch.empty((batch, max_path), dtype=torch.int32, device=device))
+
+
+def accept_greedy(node_offsets, parents, draft_tokens, target_logits, *, max_nodes: int, max_path: int,
+                  workspace=None, outs=None, stream=None):
+    """Greedy longest-accepted-path acceptance.  Returns (num_accepted [B], path_nodes [B][max_path],
+    tokens [B][max_path])."""
+    B = node_offsets.numel() - 1
+    outs = outs or _outs(B, max_path, target_logits.device)
+    a = _greedy_args(node_offsets, parents, draft_tokens, target_logits, max_nodes, max_path, outs)
+    need = lib().spec_accept_greedy_workspace_size(ctypes.byref(a))
+    if need == 0:
+        _check(lib().spec_accept_greedy(ctypes.byref(a), None), "spec_accept_greedy")
+    ws = _workspace(need, target_logits.device, workspace)
+    a.workspace, a.workspace_bytes = ws.data_ptr(), ws.numel()
+    _check(lib().spec_accept_greedy(ctypes.byref(a), _stream(stream)), "spec_accept_greedy")
+    return outs
+
+
+def accept_rejection(node_offsets, parents, draft_tokens, target_logits, draft_probs, u_accept, u_sample, *,
+                     max_nodes: int, max_path: int, max_children: int, workspace=None, outs=None, stream=None):
+    """Rejection-sampling acceptance (recursive residual over siblings).  Returns as accept_greedy."""
+    for name, t in (("draft_probs", draft_probs), ("u_accept", u_accept), ("u_sample", u_sample)):
+        _need(t, name, torch.float32)
+    B = node_offsets.numel() - 1
+    outs = outs or _outs(B, max_path, target_logits.device)
+    r = AcceptRejectionArgs()
+    r.base = _greedy_args(node_offsets, parents, draft_tokens, target_logits, max_nodes, max_path, outs)
+    r.max_children = max_children
+    r.draft_probs, r.u_accept, r.u_sample = _ptr(draft_probs), _ptr(u_accept), _ptr(u_sample)
+    need = lib().spec_accept_rejection_workspace_size(ctypes.byref(r))
+    if need == 0:
+        _check(lib().spec_accept_rejection(ctypes.byref(r), None), "spec_accept_rejection")
+    ws = _workspace(need, target_logits.device, workspace)
+    r.base.workspace, r.base.workspace_bytes = ws.data_ptr(), ws.numel()
+    _check(lib().spec_accept_rejection(ctypes.byref(r), _stream(stream)), "spec_accept_rejection")
+    return outs

@@ -1,0 +1,155 @@
+"""The C-ABI library without a GPU: it loads, exports every function include/spec_verify.h declares,
+reports its ABI version, and refuses bad host arguments by name with the documented status, before
+any HIP call."""
+
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "spec_verify.h")
+
+
+def _lib():
+    from long_context_tree_amd import spec
+    if not os.path.exists(spec.LIB_PATH):
+        pytest.skip("libspec_verify.so not built (python -m long_context_tree_amd.build)")
+    return spec
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_]+\s*\*?\s*(spec_[a-z_]+)\s*\(", text, re.M)))
+
+
+def test_exports_every_declared_symbol():
+    spec = _lib()
+    names = declared_functions()
+    assert {"spec_tree_attention", "spec_chunk_salience", "spec_accept_greedy", "spec_accept_rejection"} <= set(names)
+    assert len(names) == 10, names
+    L = ctypes.CDLL(spec.LIB_PATH)
+    for n in names:
+        assert hasattr(L, n), n
+    assert spec.lib().spec_abi_version() == 1
+    assert spec.status_string(3) == "SPEC_ERR_WORKSPACE"
+
+
+def _attn_args(spec, **over):
+    q = torch.zeros(8, 4, 64, dtype=torch.bfloat16)
+    k = torch.zeros(40, 2, 16, 64, dtype=torch.bfloat16)
+    bt = torch.zeros(1, 40, dtype=torch.int32)
+    cl = torch.tensor([512], dtype=torch.int32)
+    no = torch.tensor([0, 8], dtype=torch.int32)
+    par = torch.tensor([-1, 0, 1, 2, 3, 0, 1, 2], dtype=torch.int32)
+    out = torch.zeros_like(q)
+    keep = (q, k, bt, cl, no, par, out)
+    a = spec.tree_attention_args(q, k, k, bt, cl, no, par, max_nodes=8, max_ctx_len=512, chunk_size=64, out=out)
+    for key, v in over.items():
+        if key.startswith("kv_"):
+            setattr(a.kv, key[3:], v)
+        else:
+            setattr(a, key, v)
+    return a, keep
+
+
+@pytest.mark.parametrize("field,value,status,text", [
+    ("batch", 0, 1, "batch"),
+    ("num_q_heads", 3, 1, "num_q_heads"),
+    ("head_dim", 96, 2, "head_dim"),
+    ("max_nodes", 300, 2, "max_nodes"),
+    ("max_nodes", 0, 1, "max_nodes"),
+    ("q", None, 1, "q:"),
+    ("q", 8, 1, "16-byte"),
+    ("kv_page_size", 12, 2, "page_size"),
+    ("kv_block_table_stride", 10, 1, "block_table_stride"),
+    ("kv_token_stride", 60, 1, "token_stride"),
+    ("scale", float("nan"), 1, "scale"),
+    ("scale", -1.0, 1, "scale"),
+    ("chunk_size", 48, 2, "chunk_size"),
+    ("split_tiles", -1, 1, "split_tiles"),
+])
+def test_attention_refuses_bad_arguments(field, value, status, text):
+    spec = _lib()
+    a, keep = _attn_args(spec, **{field: value})
+    st = spec.lib().spec_tree_attention(ctypes.byref(a), None)
+    assert st == status and text in spec.last_error(), (st, spec.last_error())
+    assert spec.lib().spec_tree_attention_workspace_size(ctypes.byref(a)) == 0
+
+
+def test_attention_workspace_checks_and_hip_error_without_gpu():
+    spec = _lib()
+    a, keep = _attn_args(spec)
+    need = spec.lib().spec_tree_attention_workspace_size(ctypes.byref(a))
+    assert need > 0 and spec.last_error() == ""
+    assert spec.lib().spec_tree_attention(ctypes.byref(a), None) == 3        # no workspace
+    ws = torch.zeros(need + 512, dtype=torch.uint8)
+    base = ws.data_ptr() + (-ws.data_ptr()) % 256
+    a.workspace, a.workspace_bytes = base + 8, need                        # misaligned
+    assert spec.lib().spec_tree_attention(ctypes.byref(a), None) == 3 and "aligned" in spec.last_error()
+    a.workspace, a.workspace_bytes = base, need - 1                        # too small
+    assert spec.lib().spec_tree_attention(ctypes.byref(a), None) == 3
+    if not torch.cuda.is_available():
+        a.workspace_bytes = need                                           # valid: fails only at the launch
+        assert spec.lib().spec_tree_attention(ctypes.byref(a), None) == 4
+        assert "HIP error" in spec.last_error()
+
+
+def test_salience_state_and_argument_checks():
+    spec = _lib()
+    a, keep = _attn_args(spec, chunk_size=0)
+    mass = torch.zeros(1, 8)
+    s = spec.ChunkSalienceArgs()
+    s.attn = ctypes.pointer(a)
+    s.chunk_mass = mass.data_ptr()
+    s.max_chunks = 8
+    assert spec.lib().spec_chunk_salience(ctypes.byref(s), None) == 5          # no partials: SPEC_ERR_STATE
+    a.chunk_size = 64
+    need = spec.lib().spec_tree_attention_workspace_size(ctypes.byref(a))
+    ws = torch.zeros(need + 256, dtype=torch.uint8)
+    a.workspace, a.workspace_bytes = ws.data_ptr() + (-ws.data_ptr()) % 256, need
+    s.max_chunks = 7
+    assert spec.lib().spec_chunk_salience(ctypes.byref(s), None) == 1 and "max_chunks" in spec.last_error()
+    s.max_chunks, s.top_k = 8, 4
+    assert spec.lib().spec_chunk_salience(ctypes.byref(s), None) == 1 and "topk_index" in spec.last_error()
+    s.top_k, s.accumulate = 0, 2
+    assert spec.lib().spec_chunk_salience(ctypes.byref(s), None) == 1 and "accumulate" in spec.last_error()
+
+
+def _greedy_args(spec, **over):
+    no = torch.tensor([0, 8], dtype=torch.int32)
+    par = torch.tensor([-1, 0, 1, 2, 3, 0, 1, 2], dtype=torch.int32)
+    tok = torch.zeros(8, dtype=torch.int32)
+    lg = torch.zeros(8, 32)
+    outs = (torch.zeros(1, dtype=torch.int32), torch.zeros(1, 5, dtype=torch.int32), torch.zeros(1, 5, dtype=torch.int32))
+    a = spec._greedy_args(no, par, tok, lg, 8, 5, outs)
+    for k, v in over.items():
+        setattr(a, k, v)
+    return a, (no, par, tok, lg, outs)
+
+
+@pytest.mark.parametrize("field,value,status,text", [
+    ("vocab", 0, 1, "vocab"), ("max_nodes", 257, 2, "max_nodes"), ("max_path", 0, 1, "max_path"),
+    ("logits_dtype", 7, 2, "logits_dtype"), ("draft_tokens", None, 1, "draft_tokens"),
+    ("batch", 10000, 2, "batch * max_nodes"),
+])
+def test_greedy_refuses_bad_arguments(field, value, status, text):
+    spec = _lib()
+    a, keep = _greedy_args(spec, **{field: value})
+    assert spec.lib().spec_accept_greedy(ctypes.byref(a), None) == status
+    assert text in spec.last_error()
+
+
+def test_rejection_refuses_bad_arguments():
+    spec = _lib()
+    g, keep = _greedy_args(spec)
+    r = spec.AcceptRejectionArgs()
+    r.base = g
+    r.max_children = 9
+    assert spec.lib().spec_accept_rejection(ctypes.byref(r), None) == 1 and "max_children" in spec.last_error()
+    r.max_children = 2
+    assert spec.lib().spec_accept_rejection(ctypes.byref(r), None) == 1 and "draft_probs" in spec.last_error()
+    r.base.vocab = -1
+    assert spec.lib().spec_accept_rejection(ctypes.byref(r), None) == 1 and "base.vocab" in spec.last_error()

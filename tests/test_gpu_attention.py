@@ -1,0 +1,181 @@
+"""GPU parity of spec_tree_attention and spec_chunk_salience against the oracle (same seeded inputs),
+plus determinism and block-table invariance.  Tolerances: out max-abs 1e-2, mean-abs 1e-3, relative L2
+1e-2, lse max-abs 1e-3; chunk mass the same absolute bounds plus sum|d| / sum(mass) <= 1e-3."""
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from gpu_util import (bits_of, compare_mass, compare_out, dev, oracle_attention, run_attention, topk_valid)
+
+pytestmark = pytest.mark.gpu
+
+
+def _case(name):
+    r = synth.rng_for(100, 0, 0)
+    if name == "tiny":         # 1 layer, 512 context, 4 q / 2 kv heads, D=64, 8-node tree depth <= 4
+        return synth.attention_case(101, ctx_lens=[512], trees=[synth.random_tree(r, 8, 4)], num_q_heads=4,
+                                    num_kv_heads=2, head_dim=64)
+    if name == "llama64":      # Llama-3.1-8B layer shape, 64-node tree depth 8, ragged context
+        return synth.attention_case(102, ctx_lens=[2000], trees=[synth.random_tree(r, 64, 8)], num_q_heads=32,
+                                    num_kv_heads=8, head_dim=128)
+    if name == "llama128":     # 128-node tree depth 10: two row groups per KV head
+        return synth.attention_case(103, ctx_lens=[1500], trees=[synth.random_tree(r, 128, 10)], num_q_heads=32,
+                                    num_kv_heads=8, head_dim=128)
+    if name == "ragged":       # Qwen3-8B shape, ragged batch of chains (k=4 drafts) and a lone root
+        return synth.attention_case(104, ctx_lens=[0, 1, 100, 777, 3000, 64],
+                                    trees=[synth.chain_tree(5)] * 5 + [synth.chain_tree(1)], num_q_heads=32,
+                                    num_kv_heads=8, head_dim=128)
+    if name == "gqa1_d64":     # no GQA sharing, D=64, bushy tree, several sequences
+        return synth.attention_case(105, ctx_lens=[300, 1000], trees=[synth.random_tree(r, 30, 3),
+                                                                      synth.random_tree(r, 17, 6)],
+                                    num_q_heads=6, num_kv_heads=6, head_dim=64)
+    raise KeyError(name)
+
+
+@pytest.mark.parametrize("name,chunk,split", [("tiny", 64, 0), ("tiny", 16, 1), ("llama64", 64, 0),
+                                              ("llama64", 32, 3), ("llama64", 128, 4), ("llama128", 64, 0),
+                                              ("llama128", 64, 2), ("ragged", 32, 0), ("ragged", 64, 1),
+                                              ("gqa1_d64", 64, 0), ("gqa1_d64", 16, 5)])
+def test_attention_and_mass_match_oracle(name, chunk, split):
+    case = _case(name)
+    print(f"case={name} chunk={chunk} split={split}", flush=True)
+    out, lse, h, t = run_attention(case, chunk_size=chunk, split_tiles=split)
+    import long_context_tree_amd as lt
+    n_ch = max(1, -(-int(case.ctx_lens.max()) // chunk))
+    mass = torch.full((len(case.ctx_lens), n_ch), 7.0, dtype=torch.float32, device=dev())
+    lt.chunk_salience(h, mass)
+    torch.cuda.synchronize()
+    o_ref, l_ref, m_ref = oracle_attention(case, chunk)
+    compare_out(out, lse, o_ref, l_ref)
+    mg = mass.cpu().numpy().astype(np.float64)
+    for b, mr in enumerate(m_ref):
+        compare_mass(mg[b, :len(mr)], mr)
+        assert (mg[b, len(mr):] == 0).all()
+
+
+def test_mass_accumulates_over_layers_and_topk():
+    """Three layers summed with accumulate=1, then top-k by (mass desc, index asc)."""
+    import long_context_tree_amd as lt
+    r = synth.rng_for(110, 0, 0)
+    tree = synth.random_tree(r, 16, 4)
+    L, chunk, k = 3000, 64, 20
+    total = np.zeros(-(-L // chunk))
+    mass = torch.zeros((1, len(total)), dtype=torch.float32, device=dev())
+    for layer in range(3):
+        case = synth.attention_case(110, layer=layer, ctx_lens=[L], trees=[tree], num_q_heads=8, num_kv_heads=2,
+                                    head_dim=128)
+        out, lse, h, _ = run_attention(case, chunk_size=chunk)
+        _, ti, tm = lt.chunk_salience(h, mass, accumulate=layer > 0, top_k=k if layer == 2 else 0)
+        total += oracle_attention(case, chunk)[2][0]
+    torch.cuda.synchronize()
+    compare_mass(mass.cpu().numpy()[0].astype(np.float64), total)
+    idx = ti.cpu().numpy()[0]
+    topk_valid(idx, total, k)
+    got = mass.cpu().numpy()[0]
+    # the top-k values are the GPU's own masses at those indices, in (desc, asc) order
+    np.testing.assert_array_equal(tm.cpu().numpy()[0], got[idx])
+    order = sorted(range(len(got)), key=lambda c: (-got[c], c))[:k]
+    assert idx.tolist() == order
+
+
+def test_needle_chunks_selected():
+    """Planted keys make 32 chunks salient: top-32 must be exactly those chunks."""
+    import long_context_tree_amd as lt
+    r = synth.rng_for(111, 0, 0)
+    case = synth.attention_case(111, ctx_lens=[8192], trees=[synth.random_tree(r, 16, 4)], num_q_heads=32,
+                                num_kv_heads=8, head_dim=128, needle={"count": 32, "chunk": 64, "score": 6.0})
+    out, lse, h, _ = run_attention(case, chunk_size=64)
+    mass = torch.zeros((1, 128), dtype=torch.float32, device=dev())
+    _, ti, _ = lt.chunk_salience(h, mass, top_k=32)
+    torch.cuda.synchronize()
+    o_ref, l_ref, m_ref = oracle_attention(case, 64)
+    compare_out(out, lse, o_ref, l_ref)
+    compare_mass(mass.cpu().numpy()[0].astype(np.float64), m_ref[0])
+    assert sorted(ti.cpu().numpy()[0].tolist()) == sorted(case.needle_chunks[0].tolist())
+    topk_valid(ti.cpu().numpy()[0], m_ref[0], 32)
+
+
+def test_deterministic_and_block_table_invariant():
+    r = synth.rng_for(112, 0, 0)
+    trees = [synth.random_tree(r, 64, 8)]
+    a = synth.attention_case(112, ctx_lens=[5000], trees=trees, num_q_heads=32, num_kv_heads=8, head_dim=128)
+    b = synth.attention_case(112, ctx_lens=[5000], trees=trees, num_q_heads=32, num_kv_heads=8, head_dim=128,
+                             perm_stream=60)
+    import long_context_tree_amd as lt
+    res = []
+    for case in (a, a, b):
+        out, lse, h, _ = run_attention(case, chunk_size=64)
+        mass = torch.zeros((1, 79), dtype=torch.float32, device=dev())
+        lt.chunk_salience(h, mass)
+        torch.cuda.synchronize()
+        res.append((bits_of(out), lse.cpu().numpy(), mass.cpu().numpy()))
+    for x, y in zip(res[0], res[1]):
+        assert np.array_equal(x, y)
+    for x, y in zip(res[0], res[2]):
+        assert np.array_equal(x, y)
+
+
+def test_split_count_invariance_within_tolerance():
+    case = _case("llama64")
+    outs = [run_attention(case, split_tiles=s)[:2] for s in (1, 5, 33)]
+    torch.cuda.synchronize()
+    base = outs[0][0].float()
+    for o, l in outs[1:]:
+        assert (o.float() - base).abs().max().item() <= 2e-3
+        assert (l - outs[0][1]).abs().max().item() <= 1e-4
+
+
+def test_full_size_llama_32k_sampled_heads():
+    """The Llama-3.1-8B-shaped layer at 32K context (64-node tree depth 8, chunk 64), in the launch
+    configuration the benchmark uses; the oracle checks two KV heads' rows and every chunk mass."""
+    import long_context_tree_amd as lt
+    from synth import device as sdev
+    import oracle
+    L, N = 32768, 64
+    tree = synth.random_tree(synth.rng_for(120, 0, 4), N, 8)
+    k, v, bt = sdev.paged_kv_device(120, 0, [L + N], 8, 128, dev())
+    q = sdev.queries_device(120, 0, N, 32, 128, dev())
+    cl = torch.tensor([L], dtype=torch.int32, device=dev())
+    no = torch.tensor([0, N], dtype=torch.int32, device=dev())
+    par = torch.from_numpy(tree).to(dev())
+    out, lse, h = lt.tree_attention(q, k, v, bt, cl, no, par, max_nodes=N, max_ctx_len=L, chunk_size=64)
+    mass = torch.zeros((1, L // 64), dtype=torch.float32, device=dev())
+    lt.chunk_salience(h, mass)
+    torch.cuda.synchronize()
+    kp, vp, qb = bits_of(k), bits_of(v), bits_of(q)
+    btn = bt.cpu().numpy()
+    o_ref, l_ref, m_ref = oracle.tree_attention(qb, kp, vp, btn, np.array([L]), np.array([0, N]), tree,
+                                                1 / np.sqrt(128), 8, 16, 64)
+    compare_out(out, lse, o_ref, l_ref)
+    compare_mass(mass.cpu().numpy()[0].astype(np.float64), m_ref[0])
+    s = mass.sum().item()
+    assert 0.0 < s <= 1.0
+
+
+def test_full_size_llama_128k_sampled_head():
+    """The 128K-context layer with the 128-node tree of depth 10 (two row groups per KV head):
+    every row of KV head 3 against the oracle."""
+    import long_context_tree_amd as lt
+    from synth import device as sdev
+    import oracle
+    L, N = 131072, 128
+    tree = synth.random_tree(synth.rng_for(121, 0, 4), N, 10)
+    k, v, bt = sdev.paged_kv_device(121, 0, [L + N], 8, 128, dev())
+    q = sdev.queries_device(121, 0, N, 32, 128, dev())
+    cl = torch.tensor([L], dtype=torch.int32, device=dev())
+    no = torch.tensor([0, N], dtype=torch.int32, device=dev())
+    par = torch.from_numpy(tree).to(dev())
+    out, lse, h = lt.tree_attention(q, k, v, bt, cl, no, par, max_nodes=N, max_ctx_len=L, chunk_size=64)
+    mass = torch.zeros((1, L // 64), dtype=torch.float32, device=dev())
+    lt.chunk_salience(h, mass, top_k=256)
+    torch.cuda.synchronize()
+    g = 3
+    o_ref, l_ref, _ = oracle.tree_attention(bits_of(q), bits_of(k), bits_of(v), bt.cpu().numpy(), np.array([L]),
+                                            np.array([0, N]), tree, 1 / np.sqrt(128), 8, 16, 0, kv_heads=[g])
+    sel = np.zeros((N, 32), dtype=bool)
+    sel[:, 4 * g:4 * g + 4] = True
+    compare_out(out, lse, o_ref, l_ref, mask=sel)
+    m = mass.cpu().numpy()[0]
+    assert (m >= 0).all() and 0.0 < m.sum() <= 1.0
