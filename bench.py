@@ -1,0 +1,253 @@
+#!/usr/bin/env python3
+"""Benchmark of the tree-verification step on one MI355X.
+
+One step = the verification of one 128-node draft tree (depth 10) of a Llama-3.1-8B-shaped target at
+131072 tokens of context: for each of the 32 layers, spec_tree_attention (32 q / 8 KV heads,
+head_dim 128, bf16 KV in 16-token pages through a shuffled block table) and spec_chunk_salience
+(64-token chunks, accumulated over the layers, top-256 chunks after the last layer), then
+spec_accept_greedy over a 128256-token vocabulary.  Every layer has its own seeded KV (17.2 GB of
+KV per step), so no cache level can serve a repeated layer.
+
+Prints one JSON line: KV GB/s over the whole step (the metric), steps/s, the roofline of the
+dominant call (spec_tree_attention, timed per call with HIP events on its stream inside the timed
+region) and the CPU oracle's rate on a bounded sample of the same workload.
+
+    python bench.py [--steps K] [--warmup W] [--nodes N] [--no-cpu-baseline]
+"""
+
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "tree-verify KV GB/s & % HBM roofline at 128K ctx; verify steps/sec"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--context", type=int, default=131072)
+    ap.add_argument("--nodes", type=int, default=128)
+    ap.add_argument("--depth", type=int, default=10)
+    ap.add_argument("--layers", type=int, default=32)
+    ap.add_argument("--split-tiles", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="first run a plain 1 GiB device-to-device copy 3 times (reference for HBM byte counters)")
+    return ap.parse_args()
+
+
+def cpu_baseline(k_pool, v_pool, bt, q, tree, L, N, kv_heads, head_dim, budget_s=12.0):
+    """The oracle (numpy float64) on whole KV heads of layer 0 until ~budget_s of CPU work."""
+    import numpy as np
+    import oracle
+    from threadpoolctl import threadpool_info
+    kb = k_pool.view(__import__("torch").int16).cpu().numpy().view(np.uint16)
+    vb = v_pool.view(__import__("torch").int16).cpu().numpy().view(np.uint16)
+    qb = q.view(__import__("torch").int16).cpu().numpy().view(np.uint16)
+    btn = bt.cpu().numpy()
+    done, t0 = 0, time.perf_counter()
+    for g in range(kv_heads):
+        oracle.tree_attention(qb, kb, vb, btn, np.array([L]), np.array([0, N]), tree, 1 / math.sqrt(head_dim),
+                              kv_heads, 16, 64, kv_heads=[g])
+        done += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    kv_bytes = done * (L + N) * head_dim * 2 * 2
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    return {"value": kv_bytes / dt / 1e9, "unit": "GB/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"oracle.tree_attention (numpy float64) on {done} of {kv_heads} KV heads of one layer, "
+                      f"{L} context + {N}-node tree, {dt:.1f} s; rate = KV bytes of those heads / time"}
+
+
+def traffic_record(kernel_src: str, workload: str):
+    """HBM bytes per launch from committed rocprofv3 FETCH_SIZE/WRITE_SIZE counters, if they were taken
+    on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", f"traffic_tree_attention_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    sha = hashlib.sha256(open(kernel_src, "rb").read()).hexdigest()
+    if rec.get("kernel_sha256") != sha:
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: the verification step runs on a single MI355X and this build has no "
+              "multi-GPU path; run it with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import long_context_tree_amd as lt
+    from long_context_tree_amd import spec
+    import synth
+    from synth import device as sdev
+
+    dev = torch.device("cuda:0")
+    if args.copy_calibration:
+        src = torch.ones(1 << 29, dtype=torch.int16, device=dev)      # 1 GiB
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+    L, N, depth, layers = args.context, args.nodes, args.depth, args.layers
+    Hq, Hkv, D, chunk, top_k, V = 32, 8, 128, 64, 256, 128256
+    workload = f"llama8b-{L // 1024}k-n{N}"
+    case = 4
+    tree = synth.random_tree(synth.rng_for(case, 0, synth.S_TREE), N, depth)
+    par = torch.from_numpy(tree).to(dev)
+    cl = torch.tensor([L], dtype=torch.int32, device=dev)
+    no = torch.tensor([0, N], dtype=torch.int32, device=dev)
+
+    pools, qs = [], []
+    bt = None
+    for layer in range(layers):
+        k, v, b = sdev.paged_kv_device(case, layer, [L + N], Hkv, D, dev)
+        bt = b if bt is None else bt                  # one page mapping shared by all layers
+        pools.append((k, v))
+        qs.append(sdev.queries_device(case, layer, N, Hq, D, dev))
+    outs = [torch.empty((N, Hq, D), dtype=torch.bfloat16, device=dev) for _ in range(layers)]
+    lses = [torch.empty((N, Hq), dtype=torch.float32, device=dev) for _ in range(layers)]
+
+    attn = [spec.tree_attention_args(qs[l], pools[l][0], pools[l][1], bt, cl, no, par, max_nodes=N, max_ctx_len=L,
+                                     chunk_size=chunk, split_tiles=args.split_tiles, out=outs[l], lse=lses[l])
+            for l in range(layers)]
+    need = lt.lib().spec_tree_attention_workspace_size(ctypes.byref(attn[0]))
+    ws = spec._workspace(need, dev, None)
+    for a in attn:
+        a.workspace, a.workspace_bytes = ws.data_ptr(), ws.numel()
+    n_chunks = L // chunk
+    mass = torch.zeros((1, n_chunks), dtype=torch.float32, device=dev)
+    topi = torch.empty((1, top_k), dtype=torch.int32, device=dev)
+    topm = torch.empty((1, top_k), dtype=torch.float32, device=dev)
+    sal = []
+    for l in range(layers):
+        s = spec.ChunkSalienceArgs()
+        s.attn = ctypes.pointer(attn[l])
+        s.chunk_mass, s.max_chunks, s.accumulate = mass.data_ptr(), n_chunks, int(l > 0)
+        s.top_k = top_k if l == layers - 1 else 0
+        s.topk_index, s.topk_mass = topi.data_ptr(), topm.data_ptr()
+        sal.append(s)
+    g = synth.greedy_case(case, [tree], V, dtype="bf16")
+    gt = sdev.greedy_tensors(g, dev)
+    max_path = depth + 1
+    gouts = (torch.empty(1, dtype=torch.int32, device=dev), torch.empty((1, max_path), dtype=torch.int32, device=dev),
+             torch.empty((1, max_path), dtype=torch.int32, device=dev))
+    ga = spec._greedy_args(gt["node_offsets"], gt["parents"], gt["draft_tokens"], gt["target_logits"], N, max_path,
+                           gouts)
+    gneed = lt.lib().spec_accept_greedy_workspace_size(ctypes.byref(ga))
+    gws = spec._workspace(gneed, dev, None)
+    ga.workspace, ga.workspace_bytes = gws.data_ptr(), gws.numel()
+
+    L_ = lt.lib()
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+    def events():
+        return [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(layers)]
+
+    def step(ev):
+        for l in range(layers):
+            if ev is not None:
+                ev[l][0].record(stream)
+            st = L_.spec_tree_attention(ctypes.byref(attn[l]), sh)
+            if ev is not None:
+                ev[l][1].record(stream)
+            st |= L_.spec_chunk_salience(ctypes.byref(sal[l]), sh)
+            if st:
+                raise RuntimeError(lt.last_error())
+        if L_.spec_accept_greedy(ctypes.byref(ga), sh):
+            raise RuntimeError(lt.last_error())
+
+    print(f"[bench] workload {workload}: {layers} layers, KV {layers * (L + N) * 4096 / 1e9:.2f} GB/step; "
+          f"warmup {args.warmup}", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step(None)
+    torch.cuda.synchronize()
+
+    # timed region: K whole steps between two events; every spec_tree_attention call is bracketed by
+    # its own pair of events on the same stream (read after the region ends)
+    step_events = [events() for _ in range(args.steps)]
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record(stream)
+    for k in range(args.steps):
+        step(step_events[k])
+    t1.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t0.elapsed_time(t1)
+    ms_per_step = total_ms / args.steps
+    attn_ms = [e0.elapsed_time(e1) for ev in step_events for e0, e1 in ev]
+    print(f"[bench] {ms_per_step:.3f} ms/step", file=sys.stderr, flush=True)
+
+    # correctness guard: outputs finite, greedy produced a path
+    assert torch.isfinite(outs[-1].float()).all().item() and int(gouts[0][0]) >= 0
+
+    kv_bytes_layer = (L + N) * Hkv * D * 2 * 2
+    alg_bytes = kv_bytes_layer + 2 * N * Hq * D * 2 + N * Hq * 4          # KV + Q + out + lse
+    depths = synth.tree_depths(tree)
+    alg_flops = 4.0 * D * Hq * float(np.sum(L + depths + 1))               # QK^T and PV over visible keys
+    t_attn = float(np.median(attn_ms)) * 1e-3
+    hbm_gbs = alg_bytes / t_attn / 1e9
+    tflops = alg_flops / t_attn / 1e12
+    mfma_bound = alg_flops / (MFMA_BF16_PEAK_TFLOPS * 1e12) > alg_bytes / (HBM_PEAK_GBS * 1e9)
+    kernel_src = os.path.join(ROOT, "long_context_tree_amd", "csrc", "tree_attention.hip")
+    traffic = traffic_record(kernel_src, workload)
+    if mfma_bound:
+        roof = {"bound": "mfma", "achieved": round(tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": traffic}
+    else:
+        roof = {"bound": "hbm", "achieved": round(hbm_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(hbm_gbs / HBM_PEAK_GBS, 4), "traffic": traffic}
+    roof.update({"kernel": "spec_tree_attention (tree_attn_kernel + attn_merge_kernel)",
+                 "alg_bytes_per_launch": alg_bytes, "alg_flops_per_launch": alg_flops,
+                 "launch_us_median": round(t_attn * 1e6, 2),
+                 "launch_us_p10_p90": [round(float(np.percentile(attn_ms, 10)) * 1e3, 2),
+                                       round(float(np.percentile(attn_ms, 90)) * 1e3, 2)],
+                 "hbm_gbs": round(hbm_gbs, 1), "hbm_frac": round(hbm_gbs / HBM_PEAK_GBS, 4),
+                 "mfma_tflops": round(tflops, 2), "mfma_frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4)})
+    kv_gbs_step = layers * kv_bytes_layer / (ms_per_step * 1e-3) / 1e9
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        print("[bench] cpu baseline (oracle) ...", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(pools[0][0], pools[0][1], bt, qs[0], tree, L, N, Hkv, D)
+
+    line = {
+        "metric": METRIC, "value": round(kv_gbs_step, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": workload, "context": L, "tree_nodes": N, "tree_depth": depth, "layers": layers,
+                   "q_heads": Hq, "kv_heads": Hkv, "head_dim": D, "page_size": 16, "chunk_size": chunk,
+                   "top_k": top_k, "vocab": V, "acceptance": "greedy", "kv_bytes_per_step": layers * kv_bytes_layer},
+        "verify_steps_per_s": round(1000.0 / ms_per_step, 2),
+        "hbm_frac_step": round(kv_gbs_step / HBM_PEAK_GBS, 4),
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

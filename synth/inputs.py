@@ -206,8 +206,10 @@ def attention_case(case: int, *, ctx_lens, trees, num_q_heads: int, num_kv_heads
     node_offsets[1:] = np.cumsum(sizes)
     T = int(node_offsets[-1])
     parents = np.concatenate([np.asarray(t, dtype=np.int32) for t in trees]) if T else np.zeros(0, np.int32)
+    # block-table rows sized for the batch's largest context plus its largest tree
+    max_blocks = (int(ctx_lens.max(initial=0)) + max(sizes, default=0) + page_size - 1) // page_size
     kv = paged_kv(case, layer, ctx_lens + np.asarray(sizes, np.int32), num_kv_heads, head_dim,
-                  poison=poison, perm_stream=perm_stream, kv_std=kv_std, page_size=page_size)
+                  poison=poison, perm_stream=perm_stream, kv_std=kv_std, page_size=page_size, max_blocks=max_blocks)
     rq = rng_for(case, layer, S_Q)
     G = num_q_heads // num_kv_heads
     needle_chunks = None
