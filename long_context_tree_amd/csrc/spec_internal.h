@@ -14,6 +14,7 @@ constexpr int kTile = 64;          // KV slots per attention tile
 constexpr int kMaxNodes = 256;     // tree nodes per sequence (ancestor masks are 4 x 64 bits)
 constexpr int kSegment = 8192;     // vocabulary elements per acceptance work-group
 constexpr int kMaxTopK = 8192;     // chunks sorted by one work-group for top-k
+constexpr int kMaxSplitPages = 1024;  // page ids of one attention split staged in LDS
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }

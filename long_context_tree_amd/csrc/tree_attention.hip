@@ -12,18 +12,23 @@
 //    read from HBM once and shared, through LDS, by every node and every query head of the group.
 //    Wider trees use several row groups; their work-groups are placed on the same XCD (work-group
 //    ids i and i+8 land on one XCD) so the second read of a tile hits that XCD's L2.
-//  * Tiles are gathered page by page through the block table with 16-byte loads (one 256-byte
-//    row per key for head_dim 128), prefetched into registers while the previous tile computes,
-//    and double-buffered in LDS.  V is transposed on its way into LDS (V^T rows are keys-contiguous).
+//  * The split's block-table slice is staged in LDS once; tiles are then gathered page by page
+//    with branch-free 16-byte loads (one 256-byte row per key for head_dim 128), prefetched into
+//    registers while the previous tile computes, and double-buffered in LDS.  V is transposed on
+//    its way into LDS (V^T rows are key-contiguous) with byte permutes.
 //  * Both products run on MFMA v_mfma_f32_16x16x32_bf16: S^T = K Q^T (A = K rows from LDS,
 //    B = Q from registers), then O^T = V^T P^T (A = V^T from LDS, B = P straight from the S^T
 //    accumulators).  In this orientation each lane owns one query row in every fragment, so the
-//    online softmax (max, exp2, rescale) needs no cross-lane data except a 4-lane max/sum.
+//    only cross-lane step of the online softmax is a 4-lane max (permlane swaps); the row sum is
+//    kept per lane in fp32 and reduced once at the end.  Per-chunk sums of P come from one more
+//    MFMA against a constant ones fragment (every output slot then holds the row's chunk sum).
+//  * Lazy rescaling: the running max only moves when a tile's max exceeds it by more than 2^8,
+//    so the O accumulators are rescaled on a handful of tiles per split.
 //  * Keys >= ctx_len are tree slots: visible iff the key's node is an ancestor-or-self of the
 //    row's node (ancestor bit masks built in LDS from the parent array).
 //  * With chunk_size > 0 each tile also emits, per query row, the log2-sum-exp of the row's scores
-//    over each context chunk; the salience pass turns these into attention mass once the
-//    row's final log-sum-exp is known (no second pass over K).
+//    over each context chunk; the salience pass turns these into attention mass once the row's
+//    final log-sum-exp is known (no second pass over K).
 //  * Splits write (max, sum, unnormalised O) partials; the merge kernel combines them (LSE merge).
 #include "spec_internal.h"
 
@@ -35,35 +40,25 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-constexpr int RB = 2;               // 16-row MFMA blocks per wave
-constexpr float kNegBig = -1.0e30f; // finite "minus infinity" for running maxima
+constexpr int RB = 2;                 // 16-row MFMA blocks per wave
+constexpr float kNegBig = -1.0e30f;   // finite "minus infinity" for running maxima
+constexpr float kRescale = 8.0f;      // log2 headroom before the running max must move
 
 __device__ __forceinline__ float max4g(float x) {   // max over lanes l, l^16, l^32, l^48
-  x = fmaxf(x, __shfl_xor(x, 16));
-  return fmaxf(x, __shfl_xor(x, 32));
-}
-__device__ __forceinline__ float sum4g(float x) {
-  x += __shfl_xor(x, 16);
-  return x + __shfl_xor(x, 32);
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 
-__device__ __forceinline__ u32x4 load_kv_chunk(const uint16_t* base, const AttnParams& p, const int32_t* bt_row,
-                                               int key, int keys, int kvh, int dc) {
-  u32x4 r = {0u, 0u, 0u, 0u};
-  if (key < keys) {
-    const int page = bt_row[key >> p.page_shift];
-    if (page >= 0 && page < p.num_pages) {
-      const int slot = key & ((1 << p.page_shift) - 1);
-      const uint16_t* ptr = base + (int64_t)page * p.page_stride + (int64_t)kvh * p.head_stride +
-                            (int64_t)slot * p.token_stride + dc * 8;
-      r = *reinterpret_cast<const u32x4*>(ptr);
-    }
-  }
-  return r;
+__device__ __forceinline__ bf16x8 bf16_splat8(uint32_t lo_pair, uint32_t hi_pair) {
+  const u32x4 v = {lo_pair, lo_pair, hi_pair, hi_pair};
+  return __builtin_bit_cast(bf16x8, v);
 }
 
-template <int D, int W>
-__global__ __launch_bounds__(W * 64) void tree_attn_kernel(AttnParams p) {
+// CM: 0 = chunk sums per 64-slot tile (chunk_size 0 or a multiple of 64), 1 = per 32 slots, 2 = per 16 slots
+template <int D, int W, int CM>
+__global__ __launch_bounds__(W * 64, 2) void tree_attn_kernel(AttnParams p) {
   constexpr int NT = W * 64;
   constexpr int ROWS_WG = W * RB * 16;
   constexpr int KS = D / 32;                    // k-steps of the QK^T product
@@ -75,11 +70,16 @@ __global__ __launch_bounds__(W * 64) void tree_attn_kernel(AttnParams p) {
   constexpr int K_PER_T = K_CHUNKS / NT;
   constexpr int V_UNITS = (kTile / 4) * CPR;    // (4 keys x 8 dims) transpose units per tile
   constexpr int V_PER_T = (V_UNITS + NT - 1) / NT;
+  constexpr int NS = CM == 2 ? 4 : (CM == 1 ? 2 : 1);   // row-sum fragments per row block
+  // ancestor masks: a 4-wave work-group holds <= 128 rows, hence <= 128 nodes (two 64-bit words)
+  constexpr int ANC_N = W == 8 ? kMaxNodes : 128;
+  constexpr int ANC_W = ANC_N / 64;
   static_assert(K_CHUNKS % NT == 0, "tile must split evenly over the work-group");
 
   __shared__ __attribute__((aligned(16))) uint16_t k_lds[2][kTile * KST];
   __shared__ __attribute__((aligned(16))) uint16_t vt_lds[2][D * VST];
-  __shared__ uint64_t anc_lds[kMaxNodes][4];
+  __shared__ uint64_t anc_lds[ANC_N][ANC_W];
+  __shared__ int pg_lds[kMaxSplitPages];
 
   // ---- which (row group, split, KV head, sequence): row groups of one KV range share an XCD ----
   const int RG = p.row_groups;
@@ -110,21 +110,35 @@ __global__ __launch_bounds__(W * 64) void tree_attn_kernel(AttnParams p) {
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int lm = lane & 15, lg = lane >> 4;
-  const int32_t* bt_row = p.block_table + (int64_t)b * p.bt_stride;
+  const int pshift = p.page_shift;
+
+  // ---- the split's page ids (invalid or missing pages become -1) ----
+  const int pg_first = (t_begin * kTile) >> pshift;
+  const int pg_count = (((keys < t_end * kTile ? keys : t_end * kTile) - 1) >> pshift) - pg_first + 1;
+  {
+    const int32_t* bt_row = p.block_table + (int64_t)b * p.bt_stride;
+    for (int i = tid; i < pg_count; i += NT) {
+      const int pg = bt_row[pg_first + i];
+      pg_lds[i] = (pg >= 0 && pg < p.num_pages) ? pg : -1;
+    }
+  }
 
   // ---- ancestor-or-self bit masks of the tree nodes (only the split holding the tree slots) ----
   const bool has_tree = t_end * kTile > L;
   if (has_tree) {
-    for (int i = tid; i < N; i += NT) {
-      uint64_t m[4] = {0, 0, 0, 0};
+    for (int i = tid; i < N && i < ANC_N; i += NT) {
+      uint64_t m[ANC_W];
+#pragma unroll
+      for (int w = 0; w < ANC_W; ++w) m[w] = 0;
       int j = i;
-      for (int step = 0; step < N && j >= 0; ++step) {
+      for (int step = 0; step < N && j >= 0 && j < ANC_N; ++step) {
         m[j >> 6] |= 1ull << (j & 63);
         const int pj = p.parents[n0 + j];
         if (pj >= j) break;                       // not topological: stop the walk
         j = pj;
       }
-      anc_lds[i][0] = m[0]; anc_lds[i][1] = m[1]; anc_lds[i][2] = m[2]; anc_lds[i][3] = m[3];
+#pragma unroll
+      for (int w = 0; w < ANC_W; ++w) anc_lds[i][w] = m[w];
     }
   }
 
@@ -147,8 +161,21 @@ __global__ __launch_bounds__(W * 64) void tree_attn_kernel(AttnParams p) {
       qreg[rb][kk] = __builtin_bit_cast(bf16x8, v);
     }
   }
+  __syncthreads();                                  // page ids visible before the first tile load
 
-  // ---- tile staging ----
+  // ---- tile staging: branch-free gathers (a missing key or page reads the pool start, then zero) ----
+  const uint16_t* kbase = p.k + (int64_t)kvh * p.head_stride;
+  const uint16_t* vbase = p.v + (int64_t)kvh * p.head_stride;
+  auto gather = [&](const uint16_t* base, const uint16_t* safe, int key, int dc) -> u32x4 {
+    const int pi = (key >> pshift) - pg_first;
+    const int pg = (key < keys) ? pg_lds[pi < pg_count ? pi : 0] : -1;
+    const bool ok = key < keys && pg >= 0;
+    const int64_t off = (int64_t)pg * p.page_stride + (int64_t)(key & ((1 << pshift) - 1)) * p.token_stride + dc * 8;
+    const uint16_t* ptr = ok ? base + off : safe;
+    u32x4 r = *reinterpret_cast<const u32x4*>(ptr);
+    const u32x4 z = {0u, 0u, 0u, 0u};
+    return ok ? r : z;
+  };
   u32x4 kreg[K_PER_T];
   u32x4 vreg[V_PER_T][4];
   auto load_tile = [&](int t) {
@@ -156,15 +183,15 @@ __global__ __launch_bounds__(W * 64) void tree_attn_kernel(AttnParams p) {
 #pragma unroll
     for (int c = 0; c < K_PER_T; ++c) {
       const int ch = tid + c * NT;
-      kreg[c] = load_kv_chunk(p.k, p, bt_row, key0 + ch / CPR, keys, kvh, ch % CPR);
+      kreg[c] = gather(kbase, p.k, key0 + ch / CPR, ch % CPR);
     }
 #pragma unroll
     for (int u = 0; u < V_PER_T; ++u) {
       const int un = tid + u * NT;
-      if (un < V_UNITS) {
+      if (V_UNITS % NT == 0 || un < V_UNITS) {
         const int dc = un % CPR, kgp = un / CPR;
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) vreg[u][kk] = load_kv_chunk(p.v, p, bt_row, key0 + 4 * kgp + kk, keys, kvh, dc);
+        for (int kk = 0; kk < 4; ++kk) vreg[u][kk] = gather(vbase, p.v, key0 + 4 * kgp + kk, dc);
       }
     }
   };
@@ -177,7 +204,7 @@ __global__ __launch_bounds__(W * 64) void tree_attn_kernel(AttnParams p) {
 #pragma unroll
     for (int u = 0; u < V_PER_T; ++u) {
       const int un = tid + u * NT;
-      if (un < V_UNITS) {
+      if (V_UNITS % NT == 0 || un < V_UNITS) {
         const int dc = un % CPR, kgp = un / CPR;
 #pragma unroll
         for (int w = 0; w < 4; ++w) {            // dims 2w, 2w+1 of the chunk
@@ -194,6 +221,11 @@ __global__ __launch_bounds__(W * 64) void tree_attn_kernel(AttnParams p) {
     }
   };
 
+  // constant A fragments for the row sums (bf16 1.0 = 0x3F80): all slots, or the slots of one 16-key block
+  const bf16x8 ones = bf16_splat8(0x3F803F80u, 0x3F803F80u);
+  const bf16x8 ones_lo = bf16_splat8(0x3F803F80u, 0u);
+  const bf16x8 ones_hi = bf16_splat8(0u, 0x3F803F80u);
+
   f32x4 o[RB][NB];
   float m_r[RB], l_r[RB], cacc[RB];
 #pragma unroll
@@ -207,6 +239,12 @@ __global__ __launch_bounds__(W * 64) void tree_attn_kernel(AttnParams p) {
   const float c2 = p.scale_log2;
   const int cs = p.chunk_size;
   const int row_stride_chunk = p.max_nodes * p.Hq;
+  // chunk-partial rows: lanes with lg 0 / 1 store row block 0 / 1 (32 consecutive rows, one 128-byte line)
+  const int st_rb = lg & 1;
+  const int st_row = row0 + (wave * RB + st_rb) * 16 + lm;
+  const bool st_ok = lg < 2 && st_row < rows;
+  const int64_t st_col = st_ok ? (int64_t)(st_row / G) * p.Hq + kvh * G + st_row % G : 0;
+  float* cbase = p.chunk_lse2 + (int64_t)b * p.max_chunks * row_stride_chunk + st_col;
 
   load_tile(t_begin);
   store_tile(0);
@@ -234,7 +272,9 @@ __global__ __launch_bounds__(W * 64) void tree_attn_kernel(AttnParams p) {
         }
       }
       const bool edge = key0 + kTile > L;        // tile holds tree slots or slots past the end
-      bf16x8 pb[RB][2];
+      bf16x8 pb[RB][2], pc[RB][2];
+      bool resc = false;
+      float mt[RB];
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) {
         if (edge) {
@@ -245,78 +285,59 @@ __global__ __launch_bounds__(W * 64) void tree_attn_kernel(AttnParams p) {
               const int key = key0 + 16 * j + 4 * lg + i;
               bool vis = key < L;
               if (!vis && key < keys && valid_r[rb]) {
-                const int tj = key - L;
-                vis = (anc_lds[node_r[rb]][tj >> 6] >> (tj & 63)) & 1ull;
+                const int tj = key - L;           // < N <= ANC_N, and node_r < N
+                vis = (anc_lds[node_r[rb]][(tj >> 6) & (ANC_W - 1)] >> (tj & 63)) & 1ull;
               }
               if (!vis) s[rb][j][i] = -INFINITY;
             }
         }
-        float mx = -INFINITY;
+        float mx = fmaxf(fmaxf(s[rb][0][0], s[rb][0][1]), fmaxf(s[rb][0][2], s[rb][0][3]));
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-          mx = fmaxf(fmaxf(fmaxf(mx, s[rb][j][0]), fmaxf(s[rb][j][1], s[rb][j][2])), s[rb][j][3]);
-        mx = max4g(mx);
-        const float mnew = fmaxf(m_r[rb], mx * c2);
-        const float alpha = __builtin_amdgcn_exp2f(m_r[rb] - mnew);
-        float e[4];
+        for (int j = 1; j < 4; ++j)
+          mx = fmaxf(fmaxf(mx, fmaxf(s[rb][j][0], s[rb][j][1])), fmaxf(s[rb][j][2], s[rb][j][3]));
+        mt[rb] = max4g(mx) * c2;
+        resc |= mt[rb] > m_r[rb] + kRescale;
+      }
+      if (__builtin_amdgcn_ballot_w64(resc) != 0) {  // some row's max moved: rescale (wave-uniform branch)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          e[j] = 0.f;
+        for (int rb = 0; rb < RB; ++rb) {
+          const float mnew = mt[rb] > m_r[rb] + kRescale ? mt[rb] : m_r[rb];
+          const float alpha = __builtin_amdgcn_exp2f(m_r[rb] - mnew);
+          l_r[rb] *= alpha;
+          cacc[rb] *= alpha;
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float pv = __builtin_amdgcn_exp2f(fmaf(s[rb][j][i], c2, -mnew));
-            s[rb][j][i] = pv;
-            e[j] += pv;
-          }
+          for (int nb = 0; nb < NB; ++nb) o[rb][nb] *= alpha;
+          m_r[rb] = mnew;
         }
-        l_r[rb] = l_r[rb] * alpha + ((e[0] + e[1]) + (e[2] + e[3]));
+      }
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb) o[rb][nb] *= alpha;
-        m_r[rb] = mnew;
-
-        // per-chunk log2-sum-exp partials over context keys
-        if (cs > 0 && key0 < L) {
-          if (key0 + kTile > L) {                 // the tile where the context ends: context keys only
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              e[j] = 0.f;
-#pragma unroll
-              for (int i = 0; i < 4; ++i) e[j] += (key0 + 16 * j + 4 * lg + i < L) ? s[rb][j][i] : 0.f;
-            }
-          }
-          const int64_t rowc = (int64_t)node_r[rb] * p.Hq + head_r[rb];
-          float* cbase = p.chunk_lse2 + (int64_t)b * p.max_chunks * row_stride_chunk + rowc;
-          if (cs >= kTile) {
-            cacc[rb] = cacc[rb] * alpha + ((e[0] + e[1]) + (e[2] + e[3]));
-            const int c = key0 / cs;
-            const int cend = min((c + 1) * cs, L);
-            if (key0 + kTile >= cend) {
-              const float tot = sum4g(cacc[rb]);
-              if (valid_r[rb] && lg == 0) cbase[(int64_t)c * row_stride_chunk] = mnew + __builtin_amdgcn_logf(tot);
-              cacc[rb] = 0.f;
-            }
-          } else {
-            const int per = kTile / cs;           // 2 (cs 32) or 4 (cs 16)
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              if (q >= per) break;
-              const float part = (per == 4) ? e[q] : (e[2 * q] + e[2 * q + 1]);
-              const float tot = sum4g(part);
-              const int c = key0 / cs + q;
-              if (c * cs < L && valid_r[rb] && lg == 0)
-                cbase[(int64_t)c * row_stride_chunk] = mnew + __builtin_amdgcn_logf(tot);
-            }
-          }
-        }
+      for (int rb = 0; rb < RB; ++rb) {
+        const float mneg = -m_r[rb];
+        float e0 = 0.f, e1 = 0.f;                 // fp32 row sums of this lane's 16 probabilities
 #pragma unroll
         for (int h2 = 0; h2 < 2; ++h2) {
           bf16x8 v;
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            v[i] = (__bf16)s[rb][2 * h2][i];
-            v[4 + i] = (__bf16)s[rb][2 * h2 + 1][i];
+            const float x0 = __builtin_amdgcn_exp2f(fmaf(s[rb][2 * h2][i], c2, mneg));
+            const float x1 = __builtin_amdgcn_exp2f(fmaf(s[rb][2 * h2 + 1][i], c2, mneg));
+            e0 += x0;
+            e1 += x1;
+            v[i] = (__bf16)x0;
+            v[4 + i] = (__bf16)x1;
           }
           pb[rb][h2] = v;
+          pc[rb][h2] = v;
+        }
+        l_r[rb] += e0 + e1;
+        if (edge && cs > 0) {                    // chunk sums cover context keys only
+#pragma unroll
+          for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              if (key0 + 32 * h2 + 4 * lg + i >= L) pc[rb][h2][i] = (__bf16)0.0f;
+              if (key0 + 32 * h2 + 16 + 4 * lg + i >= L) pc[rb][h2][4 + i] = (__bf16)0.0f;
+            }
         }
       }
       // O^T[dim][row] += V^T . P^T
@@ -334,6 +355,55 @@ __global__ __launch_bounds__(W * 64) void tree_attn_kernel(AttnParams p) {
             o[rb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb[rb][h2], o[rb][nb], 0, 0, 0);
         }
       }
+      // chunk sums of P (bf16 values, fp32 sums) on MFMA: every output slot of the fragment holds the
+      // row's sum, so no cross-lane reduction is needed
+      float csum[RB][NS];
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+        if (CM == 0) {
+          if (cs > 0) {
+            f32x4 c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pc[rb][0], z, 0, 0, 0);
+            c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pc[rb][1], c, 0, 0, 0);
+            csum[rb][0] = c[0];
+          } else {
+            csum[rb][0] = 0.f;
+          }
+        } else if (CM == 1) {
+#pragma unroll
+          for (int h2 = 0; h2 < 2; ++h2) csum[rb][h2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pc[rb][h2], z, 0, 0, 0)[0];
+        } else {
+#pragma unroll
+          for (int h2 = 0; h2 < 2; ++h2) {
+            csum[rb][2 * h2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones_lo, pc[rb][h2], z, 0, 0, 0)[0];
+            csum[rb][2 * h2 + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones_hi, pc[rb][h2], z, 0, 0, 0)[0];
+          }
+        }
+      }
+      // per-chunk log2-sum-exp partials over context keys (one 128-byte store per chunk and wave)
+      if (cs > 0 && key0 < L) {
+        if (CM == 0) {
+#pragma unroll
+          for (int rb = 0; rb < RB; ++rb) cacc[rb] += csum[rb][0];
+          const int c = key0 / cs;
+          const int cend = min((c + 1) * cs, L);
+          if (key0 + kTile >= cend) {
+            const float v = (st_rb == 0 ? m_r[0] + __builtin_amdgcn_logf(cacc[0])
+                                        : m_r[1] + __builtin_amdgcn_logf(cacc[1]));
+            if (st_ok) cbase[(int64_t)c * row_stride_chunk] = v;
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb) cacc[rb] = 0.f;
+          }
+        } else {
+#pragma unroll
+          for (int q = 0; q < NS; ++q) {
+            const int c = key0 / cs + q;
+            const float v = (st_rb == 0 ? m_r[0] + __builtin_amdgcn_logf(csum[0][q])
+                                        : m_r[1] + __builtin_amdgcn_logf(csum[1][q]));
+            if (st_ok && c * cs < L) cbase[(int64_t)c * row_stride_chunk] = v;
+          }
+        }
+      }
     }
     if (t + 1 < t_end) store_tile(buf ^ 1);
     __syncthreads();
@@ -342,20 +412,26 @@ __global__ __launch_bounds__(W * 64) void tree_attn_kernel(AttnParams p) {
   if (!wave_active) return;
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
-    const float l = sum4g(l_r[rb]);
+    float l = l_r[rb];                              // per-lane partial sums -> the row's sum
+    l += __shfl_xor(l, 16);
+    l += __shfl_xor(l, 32);
+    l_r[rb] = l;
+  }
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
     if (!valid_r[rb]) continue;
     const int row = row0 + (wave * RB + rb) * 16 + lm;
     const int64_t base = (((int64_t)b * p.Hkv + kvh) * p.max_splits + split) * p.rows_pad + row;
     if (lg == 0) {
       p.part_ml[base * 2 + 0] = m_r[rb];
-      p.part_ml[base * 2 + 1] = l;
+      p.part_ml[base * 2 + 1] = l_r[rb];
     }
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) *reinterpret_cast<f32x4*>(&p.part_o[base * D + 16 * nb + 4 * lg]) = o[rb][nb];
   }
 }
 
-// LSE merge of the split partials: one wave per (node, query head) row.
+// LSE merge of the split partials: one wave per (node, query head) row; each lane owns D/64 dims.
 template <int D>
 __global__ __launch_bounds__(256) void attn_merge_kernel(AttnParams p) {
   constexpr int E = D / 64;
@@ -379,6 +455,7 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnParams p) {
   const int row = node * p.G + head % p.G;
   const int64_t base0 = ((int64_t)b * p.Hkv + kvh) * p.max_splits * p.rows_pad + row;
 
+  // every lane reads the (max, sum) of up to 64 splits at once; then per-split weights by shuffle
   float M = -INFINITY;
   for (int s = lane; s < nsp; s += 64) M = fmaxf(M, p.part_ml[(base0 + (int64_t)s * p.rows_pad) * 2]);
 #pragma unroll
@@ -388,12 +465,39 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnParams p) {
   float acc[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) acc[e] = 0.f;
-  for (int s = 0; s < nsp; ++s) {
-    const int64_t bs = base0 + (int64_t)s * p.rows_pad;
-    const float w = __builtin_amdgcn_exp2f(p.part_ml[bs * 2] - M);
-    lsum += w * p.part_ml[bs * 2 + 1];
+  for (int s0 = 0; s0 < nsp; s0 += 64) {
+    const int s = s0 + lane;
+    float w = 0.f, lw = 0.f;
+    if (s < nsp) {
+      const int64_t bs = base0 + (int64_t)s * p.rows_pad;
+      w = __builtin_amdgcn_exp2f(p.part_ml[bs * 2] - M);
+      lw = w * p.part_ml[bs * 2 + 1];
+    }
 #pragma unroll
-    for (int e = 0; e < E; ++e) acc[e] += w * p.part_o[bs * D + lane + 64 * e];
+    for (int off = 32; off >= 1; off >>= 1) lw += __shfl_xor(lw, off);
+    lsum += lw;
+    const int cnt = min(64, nsp - s0);
+    int i = 0;
+    for (; i + 4 <= cnt; i += 4) {                // four splits in flight per iteration
+      float wv[4], x[4][E];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        wv[u] = __shfl(w, i + u);
+        const int64_t bs = base0 + (int64_t)(s0 + i + u) * p.rows_pad;
+#pragma unroll
+        for (int e = 0; e < E; ++e) x[u][e] = p.part_o[bs * D + lane + 64 * e];
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int e = 0; e < E; ++e) acc[e] += wv[u] * x[u][e];
+    }
+    for (; i < cnt; ++i) {
+      const float wi = __shfl(w, i);
+      const int64_t bs = base0 + (int64_t)(s0 + i) * p.rows_pad;
+#pragma unroll
+      for (int e = 0; e < E; ++e) acc[e] += wi * p.part_o[bs * D + lane + 64 * e];
+    }
   }
   const float inv = 1.0f / lsum;
   uint16_t* op = p.out + ((int64_t)(n0 + node) * p.Hq + head) * D;
@@ -409,16 +513,28 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnParams p) {
   }
 }
 
-template <int D, int W>
+template <int D, int W, int CM>
 hipError_t launch_d_w(const AttnParams& p, const AttnPlan& plan, hipStream_t s) {
   const int n_units = p.batch * p.Hkv * p.max_splits;
   const int grid = (int)(ceil_div(n_units, 8) * 8 * plan.row_groups);
-  hipLaunchKernelGGL((tree_attn_kernel<D, W>), dim3(grid), dim3(W * 64), 0, s, p);
+  hipLaunchKernelGGL((tree_attn_kernel<D, W, CM>), dim3(grid), dim3(W * 64), 0, s, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t rows = (int64_t)p.batch * p.max_nodes * p.Hq;
   hipLaunchKernelGGL((attn_merge_kernel<D>), dim3((unsigned)ceil_div(rows, 4)), dim3(256), 0, s, p);
   return hipGetLastError();
+}
+
+template <int D, int CM>
+hipError_t launch_d(const AttnParams& p, const AttnPlan& plan, hipStream_t s) {
+  return plan.waves == 8 ? launch_d_w<D, 8, CM>(p, plan, s) : launch_d_w<D, 4, CM>(p, plan, s);
+}
+
+template <int D>
+hipError_t launch_cm(const AttnParams& p, const AttnPlan& plan, hipStream_t s) {
+  if (p.chunk_size == 16) return launch_d<D, 2>(p, plan, s);
+  if (p.chunk_size == 32) return launch_d<D, 1>(p, plan, s);
+  return launch_d<D, 0>(p, plan, s);
 }
 
 }  // namespace
@@ -433,6 +549,9 @@ bool make_attn_plan(const spec_tree_attention_args* a, int num_cus, AttnPlan* pl
   pl.rows_pad = pl.row_groups * pl.rows_wg;
   pl.max_tiles = (int)ceil_div((int64_t)a->max_ctx_len + a->max_nodes, kTile);
   const int align = (a->chunk_size >= kTile) ? a->chunk_size / kTile : 1;   // splits hold whole chunks
+  // page ids of one split must fit the LDS staging array
+  const int ps = a->kv.page_size > 0 ? a->kv.page_size : 1;
+  const int64_t cap_tiles = ((int64_t)(kMaxSplitPages - 1) * ps) / kTile;
   int st = a->split_tiles;
   if (st <= 0) {
     // enough work-groups to fill every CU about twice, but at least 8 tiles per split
@@ -442,7 +561,10 @@ bool make_attn_plan(const spec_tree_attention_args* a, int num_cus, AttnPlan* pl
     st = (int)ceil_div(pl.max_tiles, want_splits < 1 ? 1 : want_splits);
     if (st < 8) st = 8;
   }
+  if (st > cap_tiles) st = (int)cap_tiles;
   st = (int)(ceil_div(st, align) * align);
+  if (st > cap_tiles) st = (int)((cap_tiles / align) * align);
+  if (st < 1) st = align;
   pl.split_tiles = st;
   pl.max_splits = (int)ceil_div(pl.max_tiles, st);
   pl.max_chunks = a->chunk_size > 0 ? (int)ceil_div(a->max_ctx_len, a->chunk_size) : 0;
@@ -461,8 +583,8 @@ bool make_attn_plan(const spec_tree_attention_args* a, int num_cus, AttnPlan* pl
 }
 
 hipError_t launch_tree_attention(const AttnParams& p, const AttnPlan& plan, int head_dim, hipStream_t s) {
-  if (head_dim == 128) return plan.waves == 8 ? launch_d_w<128, 8>(p, plan, s) : launch_d_w<128, 4>(p, plan, s);
-  return plan.waves == 8 ? launch_d_w<64, 8>(p, plan, s) : launch_d_w<64, 4>(p, plan, s);
+  if (head_dim == 128) return launch_cm<128>(p, plan, s);
+  return launch_cm<64>(p, plan, s);
 }
 
 }  // namespace spec

@@ -33,6 +33,7 @@ BF16_QNAN = np.uint16(0x7FC0)
 
 __all__ = [
     "PAGE_SIZE", "BF16_QNAN", "rng_for", "bf16_bits", "bf16_to_f32",
+    "S_Q", "S_K", "S_V", "S_BLOCKS", "S_TREE", "S_TARGET", "S_DRAFT", "S_TOKENS", "S_UNIFORM", "S_CTX",
     "chain_tree", "random_tree", "tree_depths", "children_lists",
     "PagedKV", "paged_kv", "AttentionCase", "attention_case",
     "GreedyCase", "greedy_case", "RejectionCase", "rejection_case",
