@@ -78,6 +78,7 @@ const char* spec_last_error(void);
  * (bf16 elements; V uses the same strides).  The layout [pages][kv_heads][page_size][head_dim]
  * (token_stride = head_dim, head_stride = page_size * head_dim) gives each (page, head) one
  * contiguous block and is the fastest; others work if every row is 16-byte aligned.
+ * page_stride and token_stride * page_size must stay below 2^31 elements (the pool may be larger).
  * Pages may be shared between sequences (copy-on-write prefixes): the library only reads them.
  * ------------------------------------------------------------------------------------------ */
 typedef struct spec_paged_kv {
@@ -87,7 +88,8 @@ typedef struct spec_paged_kv {
   int64_t head_stride;          /* elements; multiple of 8 */
   int64_t token_stride;         /* elements; multiple of 8, >= head_dim */
   int32_t page_size;            /* slots per page: a power of two in [1, 1024] (16 in the workloads) */
-  int32_t num_pages;            /* (host) pages in the pool; ids outside [0, num_pages) read as zeros */
+  int32_t num_pages;            /* (host) pages in the pool; an id outside [0, num_pages) is never dereferenced
+                                   (a precondition violation: that page's keys then hold unspecified finite data) */
   const int32_t* block_table;   /* int32 [batch][block_table_stride] physical page ids */
   int32_t block_table_stride;   /* >= ceil((max_ctx_len + max_nodes) / page_size) */
 } spec_paged_kv;

@@ -4,6 +4,7 @@
 // Every host-visible argument is checked before anything is enqueued, and a refusal names the
 // argument and the accepted values (the vllm.cpp "Speculative decoding" documentation, section
 // "Which keys the JSON accepts": refuse what cannot be honoured, by name, never downgrade silently).
+#include <climits>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -83,6 +84,8 @@ int check_attn(const spec_tree_attention_args* a) {
                 (long long)kv.token_stride, a->head_dim);
   if (!pow2(kv.page_size) || kv.page_size > 1024)
     return fail(SPEC_ERR_UNSUPPORTED, "kv.page_size: %d, must be a power of two in 1..1024", kv.page_size);
+  if (kv.page_stride > INT32_MAX || kv.token_stride * kv.page_size > INT32_MAX)
+    return fail(SPEC_ERR_UNSUPPORTED, "kv.page_stride and kv.token_stride * page_size must be < 2^31 elements");
   if (kv.num_pages < 1) return fail(SPEC_ERR_INVALID_ARGUMENT, "kv.num_pages: %d, must be >= 1", kv.num_pages);
   const int64_t need_blocks = spec::ceil_div((int64_t)a->max_ctx_len + a->max_nodes, kv.page_size);
   if (kv.block_table_stride < need_blocks)

@@ -63,23 +63,22 @@ __global__ __launch_bounds__(W * 64, 2) void tree_attn_kernel(AttnParams p) {
   constexpr int ROWS_WG = W * RB * 16;
   constexpr int KS = D / 32;                    // k-steps of the QK^T product
   constexpr int NB = D / 16;                    // 16-dim output blocks
-  constexpr int KST = D + 8;                    // K row stride in LDS (bf16), padded against bank conflicts
-  constexpr int VST = kTile + 4;                // V^T row stride in LDS (bf16)
   constexpr int CPR = D / 8;                    // 16-byte chunks per K/V row
-  constexpr int K_CHUNKS = kTile * CPR;
-  constexpr int K_PER_T = K_CHUNKS / NT;
-  constexpr int V_UNITS = (kTile / 4) * CPR;    // (4 keys x 8 dims) transpose units per tile
-  constexpr int V_PER_T = (V_UNITS + NT - 1) / NT;
+  constexpr int TILE_EL = kTile * D;            // bf16 elements of one K (or V) tile
+  constexpr int LOADS = 2 * kTile * CPR / NT;   // 16-byte direct-to-LDS loads per thread and tile (K and V)
   constexpr int NS = CM == 2 ? 4 : (CM == 1 ? 2 : 1);   // row-sum fragments per row block
   // ancestor masks: a 4-wave work-group holds <= 128 rows, hence <= 128 nodes (two 64-bit words)
   constexpr int ANC_N = W == 8 ? kMaxNodes : 128;
   constexpr int ANC_W = ANC_N / 64;
-  static_assert(K_CHUNKS % NT == 0, "tile must split evenly over the work-group");
+  static_assert((2 * kTile * CPR) % NT == 0 && (kTile * CPR) % 64 == 0, "tile must split evenly");
 
-  __shared__ __attribute__((aligned(16))) uint16_t k_lds[2][kTile * KST];
-  __shared__ __attribute__((aligned(16))) uint16_t vt_lds[2][D * VST];
+  // K and V tiles, double-buffered, rows of D bf16 without padding; the 16-byte chunk c of key r sits at
+  // position c ^ swz(r) of its row, which keeps both the MFMA operand reads and the transposing V reads
+  // free of bank conflicts
+  __shared__ __attribute__((aligned(16))) uint16_t kv_lds[2][2][TILE_EL];
   __shared__ uint64_t anc_lds[ANC_N][ANC_W];
   __shared__ int pg_lds[kMaxSplitPages];
+  auto swz = [](int r) -> int { return D == 128 ? (r & 15) : ((r >> 1) & 7); };
 
   // ---- which (row group, split, KV head, sequence): row groups of one KV range share an XCD ----
   const int RG = p.row_groups;
@@ -143,7 +142,7 @@ __global__ __launch_bounds__(W * 64, 2) void tree_attn_kernel(AttnParams p) {
   }
 
   // ---- this lane's query rows (row = node * G + head-in-group) and their Q fragments ----
-  int node_r[RB], head_r[RB];
+  int node_r[RB];
   bool valid_r[RB];
   bf16x8 qreg[RB][KS];
   const bool wave_active = row0 + wave * RB * 16 < rows;
@@ -152,8 +151,8 @@ __global__ __launch_bounds__(W * 64, 2) void tree_attn_kernel(AttnParams p) {
     const int row = row0 + (wave * RB + rb) * 16 + lm;
     valid_r[rb] = row < rows;
     node_r[rb] = valid_r[rb] ? row / G : 0;
-    head_r[rb] = valid_r[rb] ? kvh * G + row % G : 0;
-    const uint16_t* qp = p.q + ((int64_t)(n0 + node_r[rb]) * p.Hq + head_r[rb]) * D + 8 * lg;
+    const int head = valid_r[rb] ? kvh * G + row % G : 0;
+    const uint16_t* qp = p.q + ((int64_t)(n0 + node_r[rb]) * p.Hq + head) * D + 8 * lg;
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk) {
       u32x4 v = {0u, 0u, 0u, 0u};
@@ -163,65 +162,59 @@ __global__ __launch_bounds__(W * 64, 2) void tree_attn_kernel(AttnParams p) {
   }
   __syncthreads();                                  // page ids visible before the first tile load
 
-  // ---- tile staging: branch-free gathers (a missing key or page reads the pool start, then zero) ----
+  // ---- tile loads: straight from HBM into LDS, 16 bytes per lane, lanes in LDS order ----
+  // load i of this thread covers LDS chunk q = (wave * LOADS + i) * 64 + lane of the K (first half of
+  // the loads) or V tile; its key and source chunk are fixed across tiles.  A key past the sequence or
+  // on an invalid page reads 16 finite bytes of q instead (masked scores; zero probabilities).
   const uint16_t* kbase = p.k + (int64_t)kvh * p.head_stride;
   const uint16_t* vbase = p.v + (int64_t)kvh * p.head_stride;
-  auto gather = [&](const uint16_t* base, const uint16_t* safe, int key, int dc) -> u32x4 {
-    const int pi = (key >> pshift) - pg_first;
-    const int pg = (key < keys) ? pg_lds[pi < pg_count ? pi : 0] : -1;
-    const bool ok = key < keys && pg >= 0;
-    const int64_t off = (int64_t)pg * p.page_stride + (int64_t)(key & ((1 << pshift) - 1)) * p.token_stride + dc * 8;
-    const uint16_t* ptr = ok ? base + off : safe;
-    u32x4 r = *reinterpret_cast<const u32x4*>(ptr);
-    const u32x4 z = {0u, 0u, 0u, 0u};
-    return ok ? r : z;
-  };
-  u32x4 kreg[K_PER_T];
-  u32x4 vreg[V_PER_T][4];
-  auto load_tile = [&](int t) {
+  int ld_kt[LOADS], ld_src[LOADS];
+#pragma unroll
+  for (int i = 0; i < LOADS; ++i) {
+    const int q = ((wave * LOADS + i) * 64 + lane) % (kTile * CPR);
+    ld_kt[i] = q / CPR;
+    ld_src[i] = ((q % CPR) ^ swz(q / CPR)) * 8;
+  }
+  const uint32_t pstride = (uint32_t)p.page_stride;
+  const uint32_t tstride = (uint32_t)p.token_stride;
+  auto issue_tile = [&](int t, int buf) {
     const int key0 = t * kTile;
+    int pg[LOADS];
 #pragma unroll
-    for (int c = 0; c < K_PER_T; ++c) {
-      const int ch = tid + c * NT;
-      kreg[c] = gather(kbase, p.k, key0 + ch / CPR, ch % CPR);
+    for (int i = 0; i < LOADS; ++i) {
+      const int key = key0 + ld_kt[i];
+      const int pi = (key >> pshift) - pg_first;
+      pg[i] = pg_lds[pi < pg_count ? pi : pg_count - 1];
+      if (key >= keys) pg[i] = -1;
     }
 #pragma unroll
-    for (int u = 0; u < V_PER_T; ++u) {
-      const int un = tid + u * NT;
-      if (V_UNITS % NT == 0 || un < V_UNITS) {
-        const int dc = un % CPR, kgp = un / CPR;
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) vreg[u][kk] = gather(vbase, p.v, key0 + 4 * kgp + kk, dc);
-      }
-    }
-  };
-  auto store_tile = [&](int buf) {
-#pragma unroll
-    for (int c = 0; c < K_PER_T; ++c) {
-      const int ch = tid + c * NT;
-      *reinterpret_cast<u32x4*>(&k_lds[buf][(ch / CPR) * KST + (ch % CPR) * 8]) = kreg[c];
-    }
-#pragma unroll
-    for (int u = 0; u < V_PER_T; ++u) {
-      const int un = tid + u * NT;
-      if (V_UNITS % NT == 0 || un < V_UNITS) {
-        const int dc = un % CPR, kgp = un / CPR;
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {            // dims 2w, 2w+1 of the chunk
-          const uint32_t a0 = vreg[u][0][w], a1 = vreg[u][1][w], a2 = vreg[u][2][w], a3 = vreg[u][3][w];
-          u32x2 lo, hi;
-          lo[0] = __builtin_amdgcn_perm(a1, a0, 0x05040100u);   // dim 2w: keys 0,1
-          lo[1] = __builtin_amdgcn_perm(a3, a2, 0x05040100u);   // dim 2w: keys 2,3
-          hi[0] = __builtin_amdgcn_perm(a1, a0, 0x07060302u);   // dim 2w+1: keys 0,1
-          hi[1] = __builtin_amdgcn_perm(a3, a2, 0x07060302u);
-          *reinterpret_cast<u32x2*>(&vt_lds[buf][(dc * 8 + 2 * w) * VST + 4 * kgp]) = lo;
-          *reinterpret_cast<u32x2*>(&vt_lds[buf][(dc * 8 + 2 * w + 1) * VST + 4 * kgp]) = hi;
-        }
-      }
+    for (int i = 0; i < LOADS; ++i) {
+      const bool is_v = (wave * LOADS + i) * 64 >= kTile * CPR;
+      const int key = key0 + ld_kt[i];
+      const uint32_t in_page = (uint32_t)(key & ((1 << pshift) - 1)) * tstride + (uint32_t)ld_src[i];
+      const uint16_t* src = (is_v ? vbase : kbase) + (uint64_t)(uint32_t)pg[i] * pstride + in_page;
+      if (pg[i] < 0) src = p.q + ld_src[i];
+      uint16_t* dst = &kv_lds[buf][is_v ? 1 : 0][((wave * LOADS + i) * 64) % (kTile * CPR) * 8];
+      __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
     }
   };
 
-  // constant A fragments for the row sums (bf16 1.0 = 0x3F80): all slots, or the slots of one 16-key block
+  // per-lane LDS element offsets of the MFMA operand reads
+  int k_off[4][KS];                                 // K rows 16j + lm, chunk 4kk + lg
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) k_off[j][kk] = (16 * j + lm) * D + 8 * ((4 * kk + lg) ^ swz(16 * j + lm));
+  // transposing V reads: lane (lg, lm) points at key 32*h2 + 4*lg + lm/4 (+16), dims 16*nb + 4*(lm%4)
+  int v_row[2], v_swz[2];
+#pragma unroll
+  for (int h2 = 0; h2 < 2; ++h2) {
+    const int key = 32 * h2 + 4 * lg + (lm >> 2);
+    v_row[h2] = key * D + 4 * (lm & 1);
+    v_swz[h2] = swz(key);
+  }
+
+  // constant A fragments for the chunk sums (bf16 1.0 = 0x3F80): all slots, or the slots of one 16-key block
   const bf16x8 ones = bf16_splat8(0x3F803F80u, 0x3F803F80u);
   const bf16x8 ones_lo = bf16_splat8(0x3F803F80u, 0u);
   const bf16x8 ones_hi = bf16_splat8(0u, 0x3F803F80u);
@@ -246,14 +239,16 @@ __global__ __launch_bounds__(W * 64, 2) void tree_attn_kernel(AttnParams p) {
   const int64_t st_col = st_ok ? (int64_t)(st_row / G) * p.Hq + kvh * G + st_row % G : 0;
   float* cbase = p.chunk_lse2 + (int64_t)b * p.max_chunks * row_stride_chunk + st_col;
 
-  load_tile(t_begin);
-  store_tile(0);
+  issue_tile(t_begin, 0);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
 
   for (int t = t_begin; t < t_end; ++t) {
     const int buf = (t - t_begin) & 1;
-    if (t + 1 < t_end) load_tile(t + 1);
+    if (t + 1 < t_end) issue_tile(t + 1, buf ^ 1);
     if (wave_active) {
+      const uint16_t* kt = kv_lds[buf][0];
+      const uint16_t* vt = kv_lds[buf][1];
       const int key0 = t * kTile;
       // S^T[key][row] = K . Q^T
       f32x4 s[RB][4];
@@ -265,7 +260,7 @@ __global__ __launch_bounds__(W * 64, 2) void tree_attn_kernel(AttnParams p) {
       for (int kk = 0; kk < KS; ++kk) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(&k_lds[buf][(16 * j + lm) * KST + 32 * kk + 8 * lg]);
+          const bf16x8 a = *reinterpret_cast<const bf16x8*>(kt + k_off[j][kk]);
 #pragma unroll
           for (int rb = 0; rb < RB; ++rb)
             s[rb][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qreg[rb][kk], s[rb][j], 0, 0, 0);
@@ -340,15 +335,20 @@ __global__ __launch_bounds__(W * 64, 2) void tree_attn_kernel(AttnParams p) {
             }
         }
       }
-      // O^T[dim][row] += V^T . P^T
+      // O^T[dim][row] += V^T . P^T, with V^T fragments read transposed from the row-major V tile
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
 #pragma unroll
         for (int h2 = 0; h2 < 2; ++h2) {
-          const uint16_t* vp = &vt_lds[buf][(16 * nb + lm) * VST + 32 * h2 + 4 * lg];
-          const u32x2 lo = *reinterpret_cast<const u32x2*>(vp);
-          const u32x2 hi = *reinterpret_cast<const u32x2*>(vp + 16);
-          const u32x4 av = {lo[0], lo[1], hi[0], hi[1]};
+          const int c = 2 * nb + ((lm & 3) >> 1);
+          const int off = v_row[h2] + 8 * (c ^ v_swz[h2]);
+          typedef short i16x4 __attribute__((ext_vector_type(4)));
+          const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) i16x4*)(vt + off));
+          const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) i16x4*)(vt + off + 16 * D));
+          const u32x2 lo2 = __builtin_bit_cast(u32x2, lo), hi2 = __builtin_bit_cast(u32x2, hi);
+          const u32x4 av = {lo2[0], lo2[1], hi2[0], hi2[1]};
           const bf16x8 a = __builtin_bit_cast(bf16x8, av);
 #pragma unroll
           for (int rb = 0; rb < RB; ++rb)
@@ -357,31 +357,28 @@ __global__ __launch_bounds__(W * 64, 2) void tree_attn_kernel(AttnParams p) {
       }
       // chunk sums of P (bf16 values, fp32 sums) on MFMA: every output slot of the fragment holds the
       // row's sum, so no cross-lane reduction is needed
-      float csum[RB][NS];
+      if (cs > 0 && key0 < L) {
+        float csum[RB][NS];
 #pragma unroll
-      for (int rb = 0; rb < RB; ++rb) {
-        const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-        if (CM == 0) {
-          if (cs > 0) {
+        for (int rb = 0; rb < RB; ++rb) {
+          const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+          if (CM == 0) {
             f32x4 c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pc[rb][0], z, 0, 0, 0);
             c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pc[rb][1], c, 0, 0, 0);
             csum[rb][0] = c[0];
+          } else if (CM == 1) {
+#pragma unroll
+            for (int h2 = 0; h2 < 2; ++h2)
+              csum[rb][h2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pc[rb][h2], z, 0, 0, 0)[0];
           } else {
-            csum[rb][0] = 0.f;
-          }
-        } else if (CM == 1) {
 #pragma unroll
-          for (int h2 = 0; h2 < 2; ++h2) csum[rb][h2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pc[rb][h2], z, 0, 0, 0)[0];
-        } else {
-#pragma unroll
-          for (int h2 = 0; h2 < 2; ++h2) {
-            csum[rb][2 * h2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones_lo, pc[rb][h2], z, 0, 0, 0)[0];
-            csum[rb][2 * h2 + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones_hi, pc[rb][h2], z, 0, 0, 0)[0];
+            for (int h2 = 0; h2 < 2; ++h2) {
+              csum[rb][2 * h2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones_lo, pc[rb][h2], z, 0, 0, 0)[0];
+              csum[rb][2 * h2 + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones_hi, pc[rb][h2], z, 0, 0, 0)[0];
+            }
           }
         }
-      }
-      // per-chunk log2-sum-exp partials over context keys (one 128-byte store per chunk and wave)
-      if (cs > 0 && key0 < L) {
+        // per-chunk log2-sum-exp partials (one 128-byte store per chunk and wave)
         if (CM == 0) {
 #pragma unroll
           for (int rb = 0; rb < RB; ++rb) cacc[rb] += csum[rb][0];
@@ -405,7 +402,7 @@ __global__ __launch_bounds__(W * 64, 2) void tree_attn_kernel(AttnParams p) {
         }
       }
     }
-    if (t + 1 < t_end) store_tile(buf ^ 1);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this thread's loads of the next tile landed
     __syncthreads();
   }
 
