@@ -75,7 +75,10 @@ __global__ __launch_bounds__(W * 64, 2) void tree_attn_kernel(AttnParams p) {
   // K and V tiles, double-buffered, rows of D bf16 without padding; the 16-byte chunk c of key r sits at
   // position c ^ swz(r) of its row, which keeps both the MFMA operand reads and the transposing V reads
   // free of bank conflicts
-  __shared__ __attribute__((aligned(16))) uint16_t kv_lds[2][2][TILE_EL];
+  // two separate arrays (not one indexed by the buffer number) so that alias analysis can tell the
+  // tile being read from the tile whose direct-to-LDS loads are still in flight
+  __shared__ __attribute__((aligned(16))) uint16_t kv_a[2][TILE_EL];
+  __shared__ __attribute__((aligned(16))) uint16_t kv_b[2][TILE_EL];
   __shared__ uint64_t anc_lds[ANC_N][ANC_W];
   __shared__ int pg_lds[kMaxSplitPages];
   auto swz = [](int r) -> int { return D == 128 ? (r & 15) : ((r >> 1) & 7); };
@@ -177,7 +180,7 @@ __global__ __launch_bounds__(W * 64, 2) void tree_attn_kernel(AttnParams p) {
   }
   const uint32_t pstride = (uint32_t)p.page_stride;
   const uint32_t tstride = (uint32_t)p.token_stride;
-  auto issue_tile = [&](int t, int buf) {
+  auto issue_tile = [&](int t, uint16_t (*kv)[TILE_EL]) {
     const int key0 = t * kTile;
     int pg[LOADS];
 #pragma unroll
@@ -194,7 +197,7 @@ __global__ __launch_bounds__(W * 64, 2) void tree_attn_kernel(AttnParams p) {
       const uint32_t in_page = (uint32_t)(key & ((1 << pshift) - 1)) * tstride + (uint32_t)ld_src[i];
       const uint16_t* src = (is_v ? vbase : kbase) + (uint64_t)(uint32_t)pg[i] * pstride + in_page;
       if (pg[i] < 0) src = p.q + ld_src[i];
-      uint16_t* dst = &kv_lds[buf][is_v ? 1 : 0][((wave * LOADS + i) * 64) % (kTile * CPR) * 8];
+      uint16_t* dst = &kv[is_v ? 1 : 0][((wave * LOADS + i) * 64) % (kTile * CPR) * 8];
       __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
     }
   };
@@ -239,16 +242,16 @@ __global__ __launch_bounds__(W * 64, 2) void tree_attn_kernel(AttnParams p) {
   const int64_t st_col = st_ok ? (int64_t)(st_row / G) * p.Hq + kvh * G + st_row % G : 0;
   float* cbase = p.chunk_lse2 + (int64_t)b * p.max_chunks * row_stride_chunk + st_col;
 
-  issue_tile(t_begin, 0);
+  issue_tile(t_begin, kv_a);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
 
-  for (int t = t_begin; t < t_end; ++t) {
-    const int buf = (t - t_begin) & 1;
-    if (t + 1 < t_end) issue_tile(t + 1, buf ^ 1);
+  // one tile: prefetch t+1 into `nxt` while computing t from `cur`
+  auto step = [&](int t, const uint16_t (*cur)[TILE_EL], uint16_t (*nxt)[TILE_EL]) {
+    if (t + 1 < t_end) issue_tile(t + 1, nxt);
     if (wave_active) {
-      const uint16_t* kt = kv_lds[buf][0];
-      const uint16_t* vt = kv_lds[buf][1];
+      const uint16_t* kt = cur[0];
+      const uint16_t* vt = cur[1];
       const int key0 = t * kTile;
       // S^T[key][row] = K . Q^T
       f32x4 s[RB][4];
@@ -404,6 +407,10 @@ __global__ __launch_bounds__(W * 64, 2) void tree_attn_kernel(AttnParams p) {
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this thread's loads of the next tile landed
     __syncthreads();
+  };
+  for (int t = t_begin; t < t_end; t += 2) {
+    step(t, kv_a, kv_b);
+    if (t + 1 < t_end) step(t + 1, kv_b, kv_a);
   }
 
   if (!wave_active) return;
