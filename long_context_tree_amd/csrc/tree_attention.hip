@@ -166,39 +166,75 @@ __global__ __launch_bounds__(W * 64, 2) void tree_attn_kernel(AttnParams p) {
   __syncthreads();                                  // page ids visible before the first tile load
 
   // ---- tile loads: straight from HBM into LDS, 16 bytes per lane, lanes in LDS order ----
-  // load i of this thread covers LDS chunk q = (wave * LOADS + i) * 64 + lane of the K (first half of
-  // the loads) or V tile; its key and source chunk are fixed across tiles.  A key past the sequence or
-  // on an invalid page reads 16 finite bytes of q instead (masked scores; zero probabilities).
+  // Load i of a wave fills LDS chunks [(wave * LOADS + i) * 64, +64) of the K tile (first half of the
+  // loads) or of the V tile: 64 / CPR consecutive keys of one page (page sizes >= 4), so the page base is
+  // wave-uniform (scalar registers) and each lane only adds a fixed 32-bit offset: its key's row in the
+  // page and its (swizzled) source chunk.  Pages with an invalid id read 16 finite bytes of q instead;
+  // slots past the sequence are zeroed in LDS after the tail tile lands.
+  constexpr int KPI = 64 / CPR;                     // keys per load instruction
   const uint16_t* kbase = p.k + (int64_t)kvh * p.head_stride;
   const uint16_t* vbase = p.v + (int64_t)kvh * p.head_stride;
-  int ld_kt[LOADS], ld_src[LOADS];
+  const uint32_t tstride = (uint32_t)p.token_stride;
+  const int pmask = (1 << pshift) - 1;
+  const bool wide_pages = pshift >= 2;              // KPI (4 or 8) keys never straddle a page
+  uint32_t ld_voff[LOADS];                          // bytes, within the page (page size <= 64) or the 64-key window
+  int ld_kt[LOADS];                                 // this lane's key within the tile
 #pragma unroll
   for (int i = 0; i < LOADS; ++i) {
     const int q = ((wave * LOADS + i) * 64 + lane) % (kTile * CPR);
-    ld_kt[i] = q / CPR;
-    ld_src[i] = ((q % CPR) ^ swz(q / CPR)) * 8;
+    const int kt = q / CPR;
+    const int src = ((q % CPR) ^ swz(kt)) * 8;
+    ld_kt[i] = kt;
+    ld_voff[i] = ((uint32_t)(kt & pmask) * tstride + (uint32_t)src) * 2u;
+    if (pshift > 6) ld_voff[i] = ((uint32_t)kt * tstride + (uint32_t)src) * 2u;   // one page spans the tile
   }
-  const uint32_t pstride = (uint32_t)p.page_stride;
-  const uint32_t tstride = (uint32_t)p.token_stride;
   auto issue_tile = [&](int t, uint16_t (*kv)[TILE_EL]) {
     const int key0 = t * kTile;
-    int pg[LOADS];
-#pragma unroll
-    for (int i = 0; i < LOADS; ++i) {
-      const int key = key0 + ld_kt[i];
-      const int pi = (key >> pshift) - pg_first;
-      pg[i] = pg_lds[pi < pg_count ? pi : pg_count - 1];
-      if (key >= keys) pg[i] = -1;
-    }
 #pragma unroll
     for (int i = 0; i < LOADS; ++i) {
       const bool is_v = (wave * LOADS + i) * 64 >= kTile * CPR;
-      const int key = key0 + ld_kt[i];
-      const uint32_t in_page = (uint32_t)(key & ((1 << pshift) - 1)) * tstride + (uint32_t)ld_src[i];
-      const uint16_t* src = (is_v ? vbase : kbase) + (uint64_t)(uint32_t)pg[i] * pstride + in_page;
-      if (pg[i] < 0) src = p.q + ld_src[i];
       uint16_t* dst = &kv[is_v ? 1 : 0][((wave * LOADS + i) * 64) % (kTile * CPR) * 8];
-      __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
+      const uint16_t* base = is_v ? vbase : kbase;
+      if (wide_pages) {
+        // first key of this load: wave-uniform; its page id from LDS, made scalar
+        const int key_w = key0 + (((wave * LOADS + i) * 64) % (kTile * CPR)) / CPR;
+        int pi = (key_w >> pshift) - pg_first;
+        pi = pi < pg_count ? pi : pg_count - 1;
+        const int pg = __builtin_amdgcn_readfirstlane(pg_lds[pi]);
+        const char* sb;
+        if (pg >= 0) {
+          // page base, plus the tile's row offset inside pages larger than a tile
+          const uint32_t row0_in_page = pshift > 6 ? (uint32_t)(key0 & pmask) * tstride : 0u;
+          sb = reinterpret_cast<const char*>(base + (uint64_t)(uint32_t)pg * (uint32_t)p.page_stride + row0_in_page);
+        } else {
+          sb = reinterpret_cast<const char*>(p.q);
+        }
+        const uint32_t voff = pg >= 0 ? ld_voff[i] : (ld_voff[i] % (uint32_t)(16 * CPR));
+        __builtin_amdgcn_global_load_lds(sb + voff, (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
+      } else {
+        const int key = key0 + ld_kt[i];
+        const int pi = (key >> pshift) - pg_first;
+        const int pg = pg_lds[pi < pg_count ? pi : pg_count - 1];
+        const int src = ((((wave * LOADS + i) * 64 + lane) % CPR) ^ swz(ld_kt[i])) * 8;
+        const uint16_t* g = pg >= 0 ? base + (uint64_t)(uint32_t)pg * (uint32_t)p.page_stride +
+                                          (uint32_t)(key & pmask) * tstride + src
+                                    : p.q + src;
+        __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
+      }
+    }
+  };
+  // after the tail tile has landed: zero this thread's chunks of slots past the sequence (a stale or
+  // poisoned V row times a zero probability would otherwise still reach the output)
+  auto zero_tail = [&](int t, uint16_t (*kv)[TILE_EL]) {
+    const int key0 = t * kTile;
+    if (key0 + kTile <= keys) return;
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) {
+      if (key0 + ld_kt[i] >= keys) {
+        const bool is_v = (wave * LOADS + i) * 64 >= kTile * CPR;
+        const int q = ((wave * LOADS + i) * 64 + lane) % (kTile * CPR);
+        *reinterpret_cast<u32x4*>(&kv[is_v ? 1 : 0][q * 8]) = u32x4{0u, 0u, 0u, 0u};
+      }
     }
   };
 
@@ -244,6 +280,7 @@ __global__ __launch_bounds__(W * 64, 2) void tree_attn_kernel(AttnParams p) {
 
   issue_tile(t_begin, kv_a);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  zero_tail(t_begin, kv_a);
   __syncthreads();
 
   // one tile: prefetch t+1 into `nxt` while computing t from `cur`
@@ -270,12 +307,12 @@ __global__ __launch_bounds__(W * 64, 2) void tree_attn_kernel(AttnParams p) {
         }
       }
       const bool edge = key0 + kTile > L;        // tile holds tree slots or slots past the end
-      bf16x8 pb[RB][2], pc[RB][2];
+      bf16x8 pb[RB][2];
       bool resc = false;
       float mt[RB];
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) {
-        if (edge) {
+        if (__builtin_expect(edge, 0)) {
 #pragma unroll
           for (int j = 0; j < 4; ++j)
 #pragma unroll
@@ -325,18 +362,8 @@ __global__ __launch_bounds__(W * 64, 2) void tree_attn_kernel(AttnParams p) {
             v[4 + i] = (__bf16)x1;
           }
           pb[rb][h2] = v;
-          pc[rb][h2] = v;
         }
         l_r[rb] += e0 + e1;
-        if (edge && cs > 0) {                    // chunk sums cover context keys only
-#pragma unroll
-          for (int h2 = 0; h2 < 2; ++h2)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              if (key0 + 32 * h2 + 4 * lg + i >= L) pc[rb][h2][i] = (__bf16)0.0f;
-              if (key0 + 32 * h2 + 16 + 4 * lg + i >= L) pc[rb][h2][4 + i] = (__bf16)0.0f;
-            }
-        }
       }
       // O^T[dim][row] += V^T . P^T, with V^T fragments read transposed from the row-major V tile
 #pragma unroll
@@ -361,23 +388,35 @@ __global__ __launch_bounds__(W * 64, 2) void tree_attn_kernel(AttnParams p) {
       // chunk sums of P (bf16 values, fp32 sums) on MFMA: every output slot of the fragment holds the
       // row's sum, so no cross-lane reduction is needed
       if (cs > 0 && key0 < L) {
+        // chunk sums cover context keys only: in the tile where the context ends, the A fragments of
+        // ones are cleared at the tree slots (A is shared by the row blocks; P stays untouched)
+        bf16x8 a_all[2] = {ones, ones}, a_lo[2] = {ones_lo, ones_lo}, a_hi[2] = {ones_hi, ones_hi};
+        if (__builtin_expect(edge, 0)) {
+#pragma unroll
+          for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              if (key0 + 32 * h2 + 4 * lg + i >= L) { a_all[h2][i] = (__bf16)0.0f; a_lo[h2][i] = (__bf16)0.0f; }
+              if (key0 + 32 * h2 + 16 + 4 * lg + i >= L) { a_all[h2][4 + i] = (__bf16)0.0f; a_hi[h2][4 + i] = (__bf16)0.0f; }
+            }
+        }
         float csum[RB][NS];
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) {
           const f32x4 z = {0.f, 0.f, 0.f, 0.f};
           if (CM == 0) {
-            f32x4 c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pc[rb][0], z, 0, 0, 0);
-            c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pc[rb][1], c, 0, 0, 0);
+            f32x4 c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_all[0], pb[rb][0], z, 0, 0, 0);
+            c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_all[1], pb[rb][1], c, 0, 0, 0);
             csum[rb][0] = c[0];
           } else if (CM == 1) {
 #pragma unroll
             for (int h2 = 0; h2 < 2; ++h2)
-              csum[rb][h2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pc[rb][h2], z, 0, 0, 0)[0];
+              csum[rb][h2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_all[h2], pb[rb][h2], z, 0, 0, 0)[0];
           } else {
 #pragma unroll
             for (int h2 = 0; h2 < 2; ++h2) {
-              csum[rb][2 * h2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones_lo, pc[rb][h2], z, 0, 0, 0)[0];
-              csum[rb][2 * h2 + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones_hi, pc[rb][h2], z, 0, 0, 0)[0];
+              csum[rb][2 * h2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_lo[h2], pb[rb][h2], z, 0, 0, 0)[0];
+              csum[rb][2 * h2 + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_hi[h2], pb[rb][h2], z, 0, 0, 0)[0];
             }
           }
         }
@@ -406,6 +445,7 @@ __global__ __launch_bounds__(W * 64, 2) void tree_attn_kernel(AttnParams p) {
       }
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this thread's loads of the next tile landed
+    if (t + 1 < t_end) zero_tail(t + 1, nxt);
     __syncthreads();
   };
   for (int t = t_begin; t < t_end; t += 2) {
