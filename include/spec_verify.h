@@ -87,9 +87,9 @@ typedef struct spec_paged_kv {
   int64_t page_stride;          /* elements; multiple of 8 */
   int64_t head_stride;          /* elements; multiple of 8 */
   int64_t token_stride;         /* elements; multiple of 8, >= head_dim */
-  int32_t page_size;            /* slots per page: a power of two in [1, 1024] (16 in the workloads) */
+  int32_t page_size;            /* slots per page: a power of two in [8, 1024] (16 in the workloads) */
   int32_t num_pages;            /* (host) pages in the pool; an id outside [0, num_pages) is never dereferenced
-                                   (a precondition violation: that page's keys then hold unspecified finite data) */
+                                   (a precondition violation: that page's keys then read as zeros) */
   const int32_t* block_table;   /* int32 [batch][block_table_stride] physical page ids */
   int32_t block_table_stride;   /* >= ceil((max_ctx_len + max_nodes) / page_size) */
 } spec_paged_kv;

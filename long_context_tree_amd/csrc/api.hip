@@ -82,8 +82,8 @@ int check_attn(const spec_tree_attention_args* a) {
   if (kv.token_stride < a->head_dim || kv.token_stride % 8)
     return fail(SPEC_ERR_INVALID_ARGUMENT, "kv.token_stride: %lld, must be a multiple of 8 and >= head_dim (%d)",
                 (long long)kv.token_stride, a->head_dim);
-  if (!pow2(kv.page_size) || kv.page_size > 1024)
-    return fail(SPEC_ERR_UNSUPPORTED, "kv.page_size: %d, must be a power of two in 1..1024", kv.page_size);
+  if (!pow2(kv.page_size) || kv.page_size < 8 || kv.page_size > 1024)
+    return fail(SPEC_ERR_UNSUPPORTED, "kv.page_size: %d, must be a power of two in 8..1024", kv.page_size);
   if (kv.page_stride > INT32_MAX || kv.token_stride * kv.page_size > INT32_MAX)
     return fail(SPEC_ERR_UNSUPPORTED, "kv.page_stride and kv.token_stride * page_size must be < 2^31 elements");
   if (kv.num_pages < 1) return fail(SPEC_ERR_INVALID_ARGUMENT, "kv.num_pages: %d, must be >= 1", kv.num_pages);

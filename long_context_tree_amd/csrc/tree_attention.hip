@@ -56,6 +56,17 @@ __device__ __forceinline__ bf16x8 bf16_splat8(uint32_t lo_pair, uint32_t hi_pair
   return __builtin_bit_cast(bf16x8, v);
 }
 
+// 16 bytes per lane from global memory straight into LDS (lane i writes dst + 16 * i), through a raw
+// buffer descriptor over [base, base + num_bytes): offsets at or past num_bytes read zeros.  The buffer
+// descriptor type only exists for the device target, so the host pass sees an empty body.
+__device__ __forceinline__ void buffer_load_lds16(const void* base, uint32_t num_bytes, void* dst, uint32_t voffset) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  const __amdgpu_buffer_rsrc_t rs =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)num_bytes, 0x00020000);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)dst, 16, voffset, 0, 0, 0);
+#endif
+}
+
 // CM: 0 = chunk sums per 64-slot tile (chunk_size 0 or a multiple of 64), 1 = per 32 slots, 2 = per 16 slots
 template <int D, int W, int CM>
 __global__ __launch_bounds__(W * 64, 2) void tree_attn_kernel(AttnParams p) {
@@ -167,26 +178,22 @@ __global__ __launch_bounds__(W * 64, 2) void tree_attn_kernel(AttnParams p) {
 
   // ---- tile loads: straight from HBM into LDS, 16 bytes per lane, lanes in LDS order ----
   // Load i of a wave fills LDS chunks [(wave * LOADS + i) * 64, +64) of the K tile (first half of the
-  // loads) or of the V tile: 64 / CPR consecutive keys of one page (page sizes >= 4), so the page base is
-  // wave-uniform (scalar registers) and each lane only adds a fixed 32-bit offset: its key's row in the
-  // page and its (swizzled) source chunk.  Pages with an invalid id read 16 finite bytes of q instead;
-  // slots past the sequence are zeroed in LDS after the tail tile lands.
-  constexpr int KPI = 64 / CPR;                     // keys per load instruction
+  // loads) or of the V tile: 64 / CPR consecutive keys of one page (page sizes >= 8), so each load is a
+  // buffer load through a scalar descriptor of that page and each lane only adds a fixed offset (its
+  // key's row and its swizzled source chunk).  The descriptor's byte range ends at the sequence's last
+  // slot in the page, so slots past the sequence (and pages with an invalid id: empty range) read zeros.
   const uint16_t* kbase = p.k + (int64_t)kvh * p.head_stride;
   const uint16_t* vbase = p.v + (int64_t)kvh * p.head_stride;
   const uint32_t tstride = (uint32_t)p.token_stride;
   const int pmask = (1 << pshift) - 1;
-  const bool wide_pages = pshift >= 2;              // KPI (4 or 8) keys never straddle a page
-  uint32_t ld_voff[LOADS];                          // bytes, within the page (page size <= 64) or the 64-key window
-  int ld_kt[LOADS];                                 // this lane's key within the tile
+  uint32_t ld_voff[LOADS];                          // bytes from the page (or, for pages > 64 slots, tile) start
 #pragma unroll
   for (int i = 0; i < LOADS; ++i) {
     const int q = ((wave * LOADS + i) * 64 + lane) % (kTile * CPR);
     const int kt = q / CPR;
     const int src = ((q % CPR) ^ swz(kt)) * 8;
-    ld_kt[i] = kt;
-    ld_voff[i] = ((uint32_t)(kt & pmask) * tstride + (uint32_t)src) * 2u;
-    if (pshift > 6) ld_voff[i] = ((uint32_t)kt * tstride + (uint32_t)src) * 2u;   // one page spans the tile
+    const int row = pshift > 6 ? kt : (kt & pmask);
+    ld_voff[i] = ((uint32_t)row * tstride + (uint32_t)src) * 2u;
   }
   auto issue_tile = [&](int t, uint16_t (*kv)[TILE_EL]) {
     const int key0 = t * kTile;
@@ -194,47 +201,20 @@ __global__ __launch_bounds__(W * 64, 2) void tree_attn_kernel(AttnParams p) {
     for (int i = 0; i < LOADS; ++i) {
       const bool is_v = (wave * LOADS + i) * 64 >= kTile * CPR;
       uint16_t* dst = &kv[is_v ? 1 : 0][((wave * LOADS + i) * 64) % (kTile * CPR) * 8];
-      const uint16_t* base = is_v ? vbase : kbase;
-      if (wide_pages) {
-        // first key of this load: wave-uniform; its page id from LDS, made scalar
-        const int key_w = key0 + (((wave * LOADS + i) * 64) % (kTile * CPR)) / CPR;
-        int pi = (key_w >> pshift) - pg_first;
-        pi = pi < pg_count ? pi : pg_count - 1;
-        const int pg = __builtin_amdgcn_readfirstlane(pg_lds[pi]);
-        const char* sb;
-        if (pg >= 0) {
-          // page base, plus the tile's row offset inside pages larger than a tile
-          const uint32_t row0_in_page = pshift > 6 ? (uint32_t)(key0 & pmask) * tstride : 0u;
-          sb = reinterpret_cast<const char*>(base + (uint64_t)(uint32_t)pg * (uint32_t)p.page_stride + row0_in_page);
-        } else {
-          sb = reinterpret_cast<const char*>(p.q);
-        }
-        const uint32_t voff = pg >= 0 ? ld_voff[i] : (ld_voff[i] % (uint32_t)(16 * CPR));
-        __builtin_amdgcn_global_load_lds(sb + voff, (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
-      } else {
-        const int key = key0 + ld_kt[i];
-        const int pi = (key >> pshift) - pg_first;
-        const int pg = pg_lds[pi < pg_count ? pi : pg_count - 1];
-        const int src = ((((wave * LOADS + i) * 64 + lane) % CPR) ^ swz(ld_kt[i])) * 8;
-        const uint16_t* g = pg >= 0 ? base + (uint64_t)(uint32_t)pg * (uint32_t)p.page_stride +
-                                          (uint32_t)(key & pmask) * tstride + src
-                                    : p.q + src;
-        __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
-      }
-    }
-  };
-  // after the tail tile has landed: zero this thread's chunks of slots past the sequence (a stale or
-  // poisoned V row times a zero probability would otherwise still reach the output)
-  auto zero_tail = [&](int t, uint16_t (*kv)[TILE_EL]) {
-    const int key0 = t * kTile;
-    if (key0 + kTile <= keys) return;
-#pragma unroll
-    for (int i = 0; i < LOADS; ++i) {
-      if (key0 + ld_kt[i] >= keys) {
-        const bool is_v = (wave * LOADS + i) * 64 >= kTile * CPR;
-        const int q = ((wave * LOADS + i) * 64 + lane) % (kTile * CPR);
-        *reinterpret_cast<u32x4*>(&kv[is_v ? 1 : 0][q * 8]) = u32x4{0u, 0u, 0u, 0u};
-      }
+      // first key of this load (wave-uniform), its page id made scalar
+      const int key_w = key0 + (((wave * LOADS + i) * 64) % (kTile * CPR)) / CPR;
+      int pi = (key_w >> pshift) - pg_first;
+      pi = pi < pg_count ? pi : pg_count - 1;
+      const int pg = __builtin_amdgcn_readfirstlane(pg_lds[pi]);
+      // the descriptor starts at the page (or at the tile's first row inside a page longer than a tile)
+      const int first_key = pshift > 6 ? key0 : (key_w & ~pmask);
+      const int span = pshift > 6 ? kTile : (1 << pshift);
+      int valid = keys - first_key;
+      valid = valid < 0 ? 0 : (valid > span ? span : valid);
+      if (pg < 0) valid = 0;
+      const uint32_t row0 = pshift > 6 ? (uint32_t)(key0 & pmask) * tstride : 0u;
+      const uint16_t* b = (is_v ? vbase : kbase) + (uint64_t)(uint32_t)(pg < 0 ? 0 : pg) * (uint32_t)p.page_stride + row0;
+      buffer_load_lds16(b, (uint32_t)valid * tstride * 2u, dst, ld_voff[i]);
     }
   };
 
@@ -280,7 +260,6 @@ __global__ __launch_bounds__(W * 64, 2) void tree_attn_kernel(AttnParams p) {
 
   issue_tile(t_begin, kv_a);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  zero_tail(t_begin, kv_a);
   __syncthreads();
 
   // one tile: prefetch t+1 into `nxt` while computing t from `cur`
@@ -445,7 +424,6 @@ __global__ __launch_bounds__(W * 64, 2) void tree_attn_kernel(AttnParams p) {
       }
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this thread's loads of the next tile landed
-    if (t + 1 < t_end) zero_tail(t + 1, nxt);
     __syncthreads();
   };
   for (int t = t_begin; t < t_end; t += 2) {

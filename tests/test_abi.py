@@ -64,6 +64,7 @@ def _attn_args(spec, **over):
     ("q", None, 1, "q:"),
     ("q", 8, 1, "16-byte"),
     ("kv_page_size", 12, 2, "page_size"),
+    ("kv_page_size", 4, 2, "page_size"),
     ("kv_block_table_stride", 10, 1, "block_table_stride"),
     ("kv_token_stride", 60, 1, "token_stride"),
     ("scale", float("nan"), 1, "scale"),

@@ -179,3 +179,21 @@ def test_full_size_llama_128k_sampled_head():
     compare_out(out, lse, o_ref, l_ref, mask=sel)
     m = mass.cpu().numpy()[0]
     assert (m >= 0).all() and 0.0 < m.sum() <= 1.0
+
+
+@pytest.mark.parametrize("page_size", [8, 32, 64, 128, 256])
+def test_page_sizes(page_size):
+    """Pages smaller than, equal to and larger than a 64-slot tile (the last spans several tiles)."""
+    r = synth.rng_for(130, page_size, 0)
+    case = synth.attention_case(130 + page_size, ctx_lens=[700, 1300], trees=[synth.random_tree(r, 20, 5),
+                                                                              synth.chain_tree(4)],
+                                num_q_heads=8, num_kv_heads=2, head_dim=128, page_size=page_size)
+    out, lse, h, _ = run_attention(case, chunk_size=64, split_tiles=3)
+    import long_context_tree_amd as lt
+    mass = torch.zeros((2, 21), dtype=torch.float32, device=dev())
+    lt.chunk_salience(h, mass)
+    torch.cuda.synchronize()
+    o_ref, l_ref, m_ref = oracle_attention(case, 64)
+    compare_out(out, lse, o_ref, l_ref)
+    for b, mr in enumerate(m_ref):
+        compare_mass(mass.cpu().numpy()[b, :len(mr)].astype(np.float64), mr)
