@@ -40,7 +40,6 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-constexpr int RB = 2;                 // 16-row MFMA blocks per wave
 constexpr float kNegBig = -1.0e30f;   // finite "minus infinity" for running maxima
 constexpr float kRescale = 8.0f;      // log2 headroom before the running max must move
 
@@ -68,8 +67,8 @@ __device__ __forceinline__ void buffer_load_lds16(const void* base, uint32_t num
 }
 
 // CM: 0 = chunk sums per 64-slot tile (chunk_size 0 or a multiple of 64), 1 = per 32 slots, 2 = per 16 slots
-template <int D, int W, int CM>
-__global__ __launch_bounds__(W * 64, 2) void tree_attn_kernel(AttnParams p) {
+template <int D, int W, int RB, int CM>
+__global__ __launch_bounds__(W * 64, (RB == 2 ? 2 : 1)) void tree_attn_kernel(AttnParams p) {
   constexpr int NT = W * 64;
   constexpr int ROWS_WG = W * RB * 16;
   constexpr int KS = D / 32;                    // k-steps of the QK^T product
@@ -121,7 +120,8 @@ __global__ __launch_bounds__(W * 64, 2) void tree_attn_kernel(AttnParams p) {
   if (t_begin >= t_end || row0 >= rows) return;
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: keeps load descriptors scalar
   const int lm = lane & 15, lg = lane >> 4;
   const int pshift = p.page_shift;
 
@@ -251,10 +251,10 @@ __global__ __launch_bounds__(W * 64, 2) void tree_attn_kernel(AttnParams p) {
   const float c2 = p.scale_log2;
   const int cs = p.chunk_size;
   const int row_stride_chunk = p.max_nodes * p.Hq;
-  // chunk-partial rows: lanes with lg 0 / 1 store row block 0 / 1 (32 consecutive rows, one 128-byte line)
-  const int st_rb = lg & 1;
+  // chunk-partial rows: the lanes of group lg store row block lg (RB consecutive 16-row blocks, one store)
+  const int st_rb = lg % RB;
   const int st_row = row0 + (wave * RB + st_rb) * 16 + lm;
-  const bool st_ok = lg < 2 && st_row < rows;
+  const bool st_ok = lg < RB && st_row < rows;
   const int64_t st_col = st_ok ? (int64_t)(st_row / G) * p.Hq + kvh * G + st_row % G : 0;
   float* cbase = p.chunk_lse2 + (int64_t)b * p.max_chunks * row_stride_chunk + st_col;
 
@@ -275,15 +275,22 @@ __global__ __launch_bounds__(W * 64, 2) void tree_attn_kernel(AttnParams p) {
       for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
         for (int j = 0; j < 4; ++j) s[rb][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+      // K fragments double-buffered across k-steps: the reads for step kk+1 are in flight while the
+      // MFMAs of step kk run
+      bf16x8 kf[2][4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) kf[0][j] = *reinterpret_cast<const bf16x8*>(kt + k_off[j][0]);
 #pragma unroll
       for (int kk = 0; kk < KS; ++kk) {
+        if (kk + 1 < KS) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(kt + k_off[j][kk]);
+          for (int j = 0; j < 4; ++j) kf[(kk + 1) & 1][j] = *reinterpret_cast<const bf16x8*>(kt + k_off[j][kk + 1]);
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
 #pragma unroll
           for (int rb = 0; rb < RB; ++rb)
-            s[rb][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qreg[rb][kk], s[rb][j], 0, 0, 0);
-        }
+            s[rb][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[kk & 1][j], qreg[rb][kk], s[rb][j], 0, 0, 0);
       }
       const bool edge = key0 + kTile > L;        // tile holds tree slots or slots past the end
       bf16x8 pb[RB][2];
@@ -344,25 +351,32 @@ __global__ __launch_bounds__(W * 64, 2) void tree_attn_kernel(AttnParams p) {
         }
         l_r[rb] += e0 + e1;
       }
-      // O^T[dim][row] += V^T . P^T, with V^T fragments read transposed from the row-major V tile
+      // O^T[dim][row] += V^T . P^T, with V^T fragments read transposed from the row-major V tile;
+      // fragments are read two dim blocks ahead of their MFMAs
+      auto vfrag = [&](int nb, int h2) -> bf16x8 {
+        typedef short i16x4 __attribute__((ext_vector_type(4)));
+        const int c = 2 * nb + ((lm & 3) >> 1);
+        const int off = v_row[h2] + 8 * (c ^ v_swz[h2]);
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(vt + off));
+        const i16x4 hi =
+            __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(vt + off + 16 * D));
+        const u32x2 lo2 = __builtin_bit_cast(u32x2, lo), hi2 = __builtin_bit_cast(u32x2, hi);
+        const u32x4 av = {lo2[0], lo2[1], hi2[0], hi2[1]};
+        return __builtin_bit_cast(bf16x8, av);
+      };
+      // order (h2, nb, rb): the two MFMAs accumulating into one O fragment are 2 * NB apart, so no MFMA
+      // waits on the previous one's result
+      constexpr int NV = 2 * NB;
+      bf16x8 vf[4];
+      vf[0] = vfrag(0, 0);
+      vf[1] = vfrag(1 % NB, 1 / NB);
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
+      for (int x = 0; x < NV; ++x) {
+        if (x + 2 < NV) vf[(x + 2) & 3] = vfrag((x + 2) % NB, (x + 2) / NB);
+        const int nb = x % NB, h2 = x / NB;
 #pragma unroll
-        for (int h2 = 0; h2 < 2; ++h2) {
-          const int c = 2 * nb + ((lm & 3) >> 1);
-          const int off = v_row[h2] + 8 * (c ^ v_swz[h2]);
-          typedef short i16x4 __attribute__((ext_vector_type(4)));
-          const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (__attribute__((address_space(3))) i16x4*)(vt + off));
-          const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (__attribute__((address_space(3))) i16x4*)(vt + off + 16 * D));
-          const u32x2 lo2 = __builtin_bit_cast(u32x2, lo), hi2 = __builtin_bit_cast(u32x2, hi);
-          const u32x4 av = {lo2[0], lo2[1], hi2[0], hi2[1]};
-          const bf16x8 a = __builtin_bit_cast(bf16x8, av);
-#pragma unroll
-          for (int rb = 0; rb < RB; ++rb)
-            o[rb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb[rb][h2], o[rb][nb], 0, 0, 0);
-        }
+        for (int rb = 0; rb < RB; ++rb)
+          o[rb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[x & 3], pb[rb][h2], o[rb][nb], 0, 0, 0);
       }
       // chunk sums of P (bf16 values, fp32 sums) on MFMA: every output slot of the fragment holds the
       // row's sum, so no cross-lane reduction is needed
@@ -406,8 +420,10 @@ __global__ __launch_bounds__(W * 64, 2) void tree_attn_kernel(AttnParams p) {
           const int c = key0 / cs;
           const int cend = min((c + 1) * cs, L);
           if (key0 + kTile >= cend) {
-            const float v = (st_rb == 0 ? m_r[0] + __builtin_amdgcn_logf(cacc[0])
-                                        : m_r[1] + __builtin_amdgcn_logf(cacc[1]));
+            float v = m_r[0] + __builtin_amdgcn_logf(cacc[0]);
+#pragma unroll
+            for (int rb = 1; rb < RB; ++rb)
+              if (st_rb == rb) v = m_r[rb] + __builtin_amdgcn_logf(cacc[rb]);
             if (st_ok) cbase[(int64_t)c * row_stride_chunk] = v;
 #pragma unroll
             for (int rb = 0; rb < RB; ++rb) cacc[rb] = 0.f;
@@ -416,8 +432,10 @@ __global__ __launch_bounds__(W * 64, 2) void tree_attn_kernel(AttnParams p) {
 #pragma unroll
           for (int q = 0; q < NS; ++q) {
             const int c = key0 / cs + q;
-            const float v = (st_rb == 0 ? m_r[0] + __builtin_amdgcn_logf(csum[0][q])
-                                        : m_r[1] + __builtin_amdgcn_logf(csum[1][q]));
+            float v = m_r[0] + __builtin_amdgcn_logf(csum[0][q]);
+#pragma unroll
+            for (int rb = 1; rb < RB; ++rb)
+              if (st_rb == rb) v = m_r[rb] + __builtin_amdgcn_logf(csum[rb][q]);
             if (st_ok && c * cs < L) cbase[(int64_t)c * row_stride_chunk] = v;
           }
         }
@@ -535,11 +553,11 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnParams p) {
   }
 }
 
-template <int D, int W, int CM>
+template <int D, int W, int RB, int CM>
 hipError_t launch_d_w(const AttnParams& p, const AttnPlan& plan, hipStream_t s) {
   const int n_units = p.batch * p.Hkv * p.max_splits;
   const int grid = (int)(ceil_div(n_units, 8) * 8 * plan.row_groups);
-  hipLaunchKernelGGL((tree_attn_kernel<D, W, CM>), dim3(grid), dim3(W * 64), 0, s, p);
+  hipLaunchKernelGGL((tree_attn_kernel<D, W, RB, CM>), dim3(grid), dim3(W * 64), 0, s, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t rows = (int64_t)p.batch * p.max_nodes * p.Hq;
@@ -549,7 +567,8 @@ hipError_t launch_d_w(const AttnParams& p, const AttnPlan& plan, hipStream_t s) 
 
 template <int D, int CM>
 hipError_t launch_d(const AttnParams& p, const AttnPlan& plan, hipStream_t s) {
-  return plan.waves == 8 ? launch_d_w<D, 8, CM>(p, plan, s) : launch_d_w<D, 4, CM>(p, plan, s);
+  if (plan.rb == 4) return launch_d_w<D, 4, 4, CM>(p, plan, s);
+  return plan.waves == 8 ? launch_d_w<D, 8, 2, CM>(p, plan, s) : launch_d_w<D, 4, 2, CM>(p, plan, s);
 }
 
 template <int D>
@@ -565,8 +584,10 @@ bool make_attn_plan(const spec_tree_attention_args* a, int num_cus, AttnPlan* pl
   AttnPlan pl;
   pl.G = a->num_q_heads / a->num_kv_heads;
   const int rows = a->max_nodes * pl.G;
+  // 32 rows per wave; 8 waves (256 rows) when a KV head has more than 128 rows, else 4
   pl.waves = rows > 128 ? 8 : 4;
-  pl.rows_wg = pl.waves * RB * 16;
+  pl.rb = 2;
+  pl.rows_wg = pl.waves * pl.rb * 16;
   pl.row_groups = (int)ceil_div(rows, pl.rows_wg);
   pl.rows_pad = pl.row_groups * pl.rows_wg;
   pl.max_tiles = (int)ceil_div((int64_t)a->max_ctx_len + a->max_nodes, kTile);
