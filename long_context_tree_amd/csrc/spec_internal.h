@@ -25,7 +25,7 @@ inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 struct AttnPlan {
   int G = 0;             // query heads per KV head
   int waves = 0;         // waves per work-group (4 or 8)
-  int rb = 0;            // 16-row MFMA blocks per wave (2 or 4)
+  int rb = 0;            // 16-row MFMA blocks per wave (2)
   int rows_wg = 0;       // query rows per work-group = waves * 32
   int row_groups = 0;    // work-groups sharing one KV range (rows of one KV head / rows_wg)
   int rows_pad = 0;      // row_groups * rows_wg

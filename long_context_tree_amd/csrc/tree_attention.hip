@@ -68,7 +68,7 @@ __device__ __forceinline__ void buffer_load_lds16(const void* base, uint32_t num
 
 // CM: 0 = chunk sums per 64-slot tile (chunk_size 0 or a multiple of 64), 1 = per 32 slots, 2 = per 16 slots
 template <int D, int W, int RB, int CM>
-__global__ __launch_bounds__(W * 64, (RB == 2 ? 2 : 1)) void tree_attn_kernel(AttnParams p) {
+__global__ __launch_bounds__(W * 64, (W == 8 ? 1 : 2)) void tree_attn_kernel(AttnParams p) {
   constexpr int NT = W * 64;
   constexpr int ROWS_WG = W * RB * 16;
   constexpr int KS = D / 32;                    // k-steps of the QK^T product
@@ -145,7 +145,8 @@ __global__ __launch_bounds__(W * 64, (RB == 2 ? 2 : 1)) void tree_attn_kernel(At
       for (int w = 0; w < ANC_W; ++w) m[w] = 0;
       int j = i;
       for (int step = 0; step < N && j >= 0 && j < ANC_N; ++step) {
-        m[j >> 6] |= 1ull << (j & 63);
+#pragma unroll
+        for (int w = 0; w < ANC_W; ++w) m[w] |= (j >> 6) == w ? 1ull << (j & 63) : 0ull;   // no dynamic index
         const int pj = p.parents[n0 + j];
         if (pj >= j) break;                       // not topological: stop the walk
         j = pj;
@@ -195,7 +196,7 @@ __global__ __launch_bounds__(W * 64, (RB == 2 ? 2 : 1)) void tree_attn_kernel(At
     const int row = pshift > 6 ? kt : (kt & pmask);
     ld_voff[i] = ((uint32_t)row * tstride + (uint32_t)src) * 2u;
   }
-  auto issue_tile = [&](int t, uint16_t (*kv)[TILE_EL]) {
+  auto issue_tile = [&](int t, uint16_t (*kv)[TILE_EL]) __attribute__((always_inline)) {
     const int key0 = t * kTile;
 #pragma unroll
     for (int i = 0; i < LOADS; ++i) {
@@ -219,11 +220,11 @@ __global__ __launch_bounds__(W * 64, (RB == 2 ? 2 : 1)) void tree_attn_kernel(At
   };
 
   // per-lane LDS element offsets of the MFMA operand reads
-  int k_off[4][KS];                                 // K rows 16j + lm, chunk 4kk + lg
+  // K rows 16j + lm, chunk 4kk + lg: the swizzle of row 16j + lm does not depend on j, so the row block
+  // j only adds 16 * j * D elements (an immediate offset of the LDS read)
+  int k_off[KS];
 #pragma unroll
-  for (int j = 0; j < 4; ++j)
-#pragma unroll
-    for (int kk = 0; kk < KS; ++kk) k_off[j][kk] = (16 * j + lm) * D + 8 * ((4 * kk + lg) ^ swz(16 * j + lm));
+  for (int kk = 0; kk < KS; ++kk) k_off[kk] = lm * D + 8 * ((4 * kk + lg) ^ swz(lm));
   // transposing V reads: lane (lg, lm) points at key 32*h2 + 4*lg + lm/4 (+16), dims 16*nb + 4*(lm%4)
   int v_row[2], v_swz[2];
 #pragma unroll
@@ -258,188 +259,204 @@ __global__ __launch_bounds__(W * 64, (RB == 2 ? 2 : 1)) void tree_attn_kernel(At
   const int64_t st_col = st_ok ? (int64_t)(st_row / G) * p.Hq + kvh * G + st_row % G : 0;
   float* cbase = p.chunk_lse2 + (int64_t)b * p.max_chunks * row_stride_chunk + st_col;
 
-  issue_tile(t_begin, kv_a);
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
+  // S (scores of the current tile), P (its bf16 probabilities) live across the compute stages
+  f32x4 s[RB][4];
+  bf16x8 pb[RB][2];
 
-  // one tile: prefetch t+1 into `nxt` while computing t from `cur`
-  auto step = [&](int t, const uint16_t (*cur)[TILE_EL], uint16_t (*nxt)[TILE_EL]) {
-    if (t + 1 < t_end) issue_tile(t + 1, nxt);
-    if (wave_active) {
-      const uint16_t* kt = cur[0];
-      const uint16_t* vt = cur[1];
-      const int key0 = t * kTile;
+  // stage 1: S^T = K . Q^T for tile t from the K tile at kt
+  auto stage_qk = [&](int t, const uint16_t* kt) __attribute__((always_inline)) {
+    const int key0 = t * kTile;
+    (void)key0;
       // S^T[key][row] = K . Q^T
-      f32x4 s[RB][4];
 #pragma unroll
-      for (int rb = 0; rb < RB; ++rb)
+    for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) s[rb][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-      // K fragments double-buffered across k-steps: the reads for step kk+1 are in flight while the
-      // MFMAs of step kk run
-      bf16x8 kf[2][4];
+      for (int j = 0; j < 4; ++j) s[rb][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // K fragments double-buffered across k-steps: the reads for step kk+1 are in flight while the
+    // MFMAs of step kk run
+    bf16x8 kf[2][4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) kf[0][j] = *reinterpret_cast<const bf16x8*>(kt + k_off[j][0]);
+    for (int j = 0; j < 4; ++j) kf[0][j] = *reinterpret_cast<const bf16x8*>(kt + 16 * j * D + k_off[0]);
 #pragma unroll
-      for (int kk = 0; kk < KS; ++kk) {
-        if (kk + 1 < KS) {
+    for (int kk = 0; kk < KS; ++kk) {
+      if (kk + 1 < KS) {
 #pragma unroll
-          for (int j = 0; j < 4; ++j) kf[(kk + 1) & 1][j] = *reinterpret_cast<const bf16x8*>(kt + k_off[j][kk + 1]);
-        }
+        for (int j = 0; j < 4; ++j) kf[(kk + 1) & 1][j] = *reinterpret_cast<const bf16x8*>(kt + 16 * j * D + k_off[kk + 1]);
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb)
+          s[rb][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[kk & 1][j], qreg[rb][kk], s[rb][j], 0, 0, 0);
+    }
+  };
+  // stage 2: mask, online softmax (lazy rescale of O), bf16 probabilities
+  auto stage_softmax = [&](int t) __attribute__((always_inline)) {
+    const int key0 = t * kTile;
+      const bool edge = key0 + kTile > L;        // tile holds tree slots or slots past the end
+    bool resc = false;
+    float mt[RB];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      if (__builtin_expect(edge, 0)) {
 #pragma unroll
         for (int j = 0; j < 4; ++j)
 #pragma unroll
-          for (int rb = 0; rb < RB; ++rb)
-            s[rb][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[kk & 1][j], qreg[rb][kk], s[rb][j], 0, 0, 0);
-      }
-      const bool edge = key0 + kTile > L;        // tile holds tree slots or slots past the end
-      bf16x8 pb[RB][2];
-      bool resc = false;
-      float mt[RB];
-#pragma unroll
-      for (int rb = 0; rb < RB; ++rb) {
-        if (__builtin_expect(edge, 0)) {
-#pragma unroll
-          for (int j = 0; j < 4; ++j)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const int key = key0 + 16 * j + 4 * lg + i;
-              bool vis = key < L;
-              if (!vis && key < keys && valid_r[rb]) {
-                const int tj = key - L;           // < N <= ANC_N, and node_r < N
-                vis = (anc_lds[node_r[rb]][(tj >> 6) & (ANC_W - 1)] >> (tj & 63)) & 1ull;
-              }
-              if (!vis) s[rb][j][i] = -INFINITY;
+          for (int i = 0; i < 4; ++i) {
+            const int key = key0 + 16 * j + 4 * lg + i;
+            bool vis = key < L;
+            if (!vis && key < keys && valid_r[rb]) {
+              const int tj = key - L;           // < N <= ANC_N, and node_r < N
+              vis = (anc_lds[node_r[rb]][(tj >> 6) & (ANC_W - 1)] >> (tj & 63)) & 1ull;
             }
-        }
-        float mx = fmaxf(fmaxf(s[rb][0][0], s[rb][0][1]), fmaxf(s[rb][0][2], s[rb][0][3]));
-#pragma unroll
-        for (int j = 1; j < 4; ++j)
-          mx = fmaxf(fmaxf(mx, fmaxf(s[rb][j][0], s[rb][j][1])), fmaxf(s[rb][j][2], s[rb][j][3]));
-        mt[rb] = max4g(mx) * c2;
-        resc |= mt[rb] > m_r[rb] + kRescale;
+            if (!vis) s[rb][j][i] = -INFINITY;
+          }
       }
-      if (__builtin_amdgcn_ballot_w64(resc) != 0) {  // some row's max moved: rescale (wave-uniform branch)
+      float mx = fmaxf(fmaxf(s[rb][0][0], s[rb][0][1]), fmaxf(s[rb][0][2], s[rb][0][3]));
 #pragma unroll
-        for (int rb = 0; rb < RB; ++rb) {
-          const float mnew = mt[rb] > m_r[rb] + kRescale ? mt[rb] : m_r[rb];
-          const float alpha = __builtin_amdgcn_exp2f(m_r[rb] - mnew);
-          l_r[rb] *= alpha;
-          cacc[rb] *= alpha;
-#pragma unroll
-          for (int nb = 0; nb < NB; ++nb) o[rb][nb] *= alpha;
-          m_r[rb] = mnew;
-        }
-      }
+      for (int j = 1; j < 4; ++j)
+        mx = fmaxf(fmaxf(mx, fmaxf(s[rb][j][0], s[rb][j][1])), fmaxf(s[rb][j][2], s[rb][j][3]));
+      mt[rb] = max4g(mx) * c2;
+      resc |= mt[rb] > m_r[rb] + kRescale;
+    }
+    if (__builtin_amdgcn_ballot_w64(resc) != 0) {  // some row's max moved: rescale (wave-uniform branch)
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) {
-        const float mneg = -m_r[rb];
-        float e0 = 0.f, e1 = 0.f;                 // fp32 row sums of this lane's 16 probabilities
+        const float mnew = mt[rb] > m_r[rb] + kRescale ? mt[rb] : m_r[rb];
+        const float alpha = __builtin_amdgcn_exp2f(m_r[rb] - mnew);
+        l_r[rb] *= alpha;
+        cacc[rb] *= alpha;
 #pragma unroll
-        for (int h2 = 0; h2 < 2; ++h2) {
-          bf16x8 v;
+        for (int nb = 0; nb < NB; ++nb) o[rb][nb] *= alpha;
+        m_r[rb] = mnew;
+      }
+    }
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      const float mneg = -m_r[rb];
+      float e0 = 0.f, e1 = 0.f;                 // fp32 row sums of this lane's 16 probabilities
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2) {
+        bf16x8 v;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float x0 = __builtin_amdgcn_exp2f(fmaf(s[rb][2 * h2][i], c2, mneg));
+          const float x1 = __builtin_amdgcn_exp2f(fmaf(s[rb][2 * h2 + 1][i], c2, mneg));
+          e0 += x0;
+          e1 += x1;
+          v[i] = (__bf16)x0;
+          v[4 + i] = (__bf16)x1;
+        }
+        pb[rb][h2] = v;
+      }
+      l_r[rb] += e0 + e1;
+    }
+  };
+  // stage 3: O += V^T . P^T for tile t from the V tile at vt, chunk partials
+  auto stage_pv = [&](int t, const uint16_t* vt) __attribute__((always_inline)) {
+    const int key0 = t * kTile;
+    const bool edge = key0 + kTile > L;
+      // O^T[dim][row] += V^T . P^T, with V^T fragments read transposed from the row-major V tile;
+    // fragments are read two dim blocks ahead of their MFMAs
+    auto vfrag = [&](int nb, int h2) __attribute__((always_inline)) -> bf16x8 {
+      typedef short i16x4 __attribute__((ext_vector_type(4)));
+      const int c = 2 * nb + ((lm & 3) >> 1);
+      const int off = v_row[h2] + 8 * (c ^ v_swz[h2]);
+      const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(vt + off));
+      const i16x4 hi =
+          __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(vt + off + 16 * D));
+      const u32x2 lo2 = __builtin_bit_cast(u32x2, lo), hi2 = __builtin_bit_cast(u32x2, hi);
+      const u32x4 av = {lo2[0], lo2[1], hi2[0], hi2[1]};
+      return __builtin_bit_cast(bf16x8, av);
+    };
+    // order (h2, nb, rb): the two MFMAs accumulating into one O fragment are 2 * NB apart, so no MFMA
+    // waits on the previous one's result
+    constexpr int NV = 2 * NB;
+    bf16x8 vf[4];
+    vf[0] = vfrag(0, 0);
+    vf[1] = vfrag(1 % NB, 1 / NB);
+#pragma unroll
+    for (int x = 0; x < NV; ++x) {
+      if (x + 2 < NV) vf[(x + 2) & 3] = vfrag((x + 2) % NB, (x + 2) / NB);
+      const int nb = x % NB, h2 = x / NB;
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb)
+        o[rb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[x & 3], pb[rb][h2], o[rb][nb], 0, 0, 0);
+    }
+    // chunk sums of P (bf16 values, fp32 sums) on MFMA: every output slot of the fragment holds the
+    // row's sum, so no cross-lane reduction is needed
+    if (cs > 0 && key0 < L) {
+      // chunk sums cover context keys only: in the tile where the context ends, the A fragments of
+      // ones are cleared at the tree slots (A is shared by the row blocks; P stays untouched)
+      bf16x8 a_all[2] = {ones, ones}, a_lo[2] = {ones_lo, ones_lo}, a_hi[2] = {ones_hi, ones_hi};
+      if (__builtin_expect(edge, 0)) {
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const float x0 = __builtin_amdgcn_exp2f(fmaf(s[rb][2 * h2][i], c2, mneg));
-            const float x1 = __builtin_amdgcn_exp2f(fmaf(s[rb][2 * h2 + 1][i], c2, mneg));
-            e0 += x0;
-            e1 += x1;
-            v[i] = (__bf16)x0;
-            v[4 + i] = (__bf16)x1;
+            if (key0 + 32 * h2 + 4 * lg + i >= L) { a_all[h2][i] = (__bf16)0.0f; a_lo[h2][i] = (__bf16)0.0f; }
+            if (key0 + 32 * h2 + 16 + 4 * lg + i >= L) { a_all[h2][4 + i] = (__bf16)0.0f; a_hi[h2][4 + i] = (__bf16)0.0f; }
           }
-          pb[rb][h2] = v;
-        }
-        l_r[rb] += e0 + e1;
       }
-      // O^T[dim][row] += V^T . P^T, with V^T fragments read transposed from the row-major V tile;
-      // fragments are read two dim blocks ahead of their MFMAs
-      auto vfrag = [&](int nb, int h2) -> bf16x8 {
-        typedef short i16x4 __attribute__((ext_vector_type(4)));
-        const int c = 2 * nb + ((lm & 3) >> 1);
-        const int off = v_row[h2] + 8 * (c ^ v_swz[h2]);
-        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(vt + off));
-        const i16x4 hi =
-            __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(vt + off + 16 * D));
-        const u32x2 lo2 = __builtin_bit_cast(u32x2, lo), hi2 = __builtin_bit_cast(u32x2, hi);
-        const u32x4 av = {lo2[0], lo2[1], hi2[0], hi2[1]};
-        return __builtin_bit_cast(bf16x8, av);
-      };
-      // order (h2, nb, rb): the two MFMAs accumulating into one O fragment are 2 * NB apart, so no MFMA
-      // waits on the previous one's result
-      constexpr int NV = 2 * NB;
-      bf16x8 vf[4];
-      vf[0] = vfrag(0, 0);
-      vf[1] = vfrag(1 % NB, 1 / NB);
+      float csum[RB][NS];
 #pragma unroll
-      for (int x = 0; x < NV; ++x) {
-        if (x + 2 < NV) vf[(x + 2) & 3] = vfrag((x + 2) % NB, (x + 2) / NB);
-        const int nb = x % NB, h2 = x / NB;
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb)
-          o[rb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[x & 3], pb[rb][h2], o[rb][nb], 0, 0, 0);
-      }
-      // chunk sums of P (bf16 values, fp32 sums) on MFMA: every output slot of the fragment holds the
-      // row's sum, so no cross-lane reduction is needed
-      if (cs > 0 && key0 < L) {
-        // chunk sums cover context keys only: in the tile where the context ends, the A fragments of
-        // ones are cleared at the tree slots (A is shared by the row blocks; P stays untouched)
-        bf16x8 a_all[2] = {ones, ones}, a_lo[2] = {ones_lo, ones_lo}, a_hi[2] = {ones_hi, ones_hi};
-        if (__builtin_expect(edge, 0)) {
+      for (int rb = 0; rb < RB; ++rb) {
+        const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+        if (CM == 0) {
+          f32x4 c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_all[0], pb[rb][0], z, 0, 0, 0);
+          c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_all[1], pb[rb][1], c, 0, 0, 0);
+          csum[rb][0] = c[0];
+        } else if (CM == 1) {
 #pragma unroll
           for (int h2 = 0; h2 < 2; ++h2)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              if (key0 + 32 * h2 + 4 * lg + i >= L) { a_all[h2][i] = (__bf16)0.0f; a_lo[h2][i] = (__bf16)0.0f; }
-              if (key0 + 32 * h2 + 16 + 4 * lg + i >= L) { a_all[h2][4 + i] = (__bf16)0.0f; a_hi[h2][4 + i] = (__bf16)0.0f; }
-            }
-        }
-        float csum[RB][NS];
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb) {
-          const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-          if (CM == 0) {
-            f32x4 c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_all[0], pb[rb][0], z, 0, 0, 0);
-            c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_all[1], pb[rb][1], c, 0, 0, 0);
-            csum[rb][0] = c[0];
-          } else if (CM == 1) {
-#pragma unroll
-            for (int h2 = 0; h2 < 2; ++h2)
-              csum[rb][h2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_all[h2], pb[rb][h2], z, 0, 0, 0)[0];
-          } else {
-#pragma unroll
-            for (int h2 = 0; h2 < 2; ++h2) {
-              csum[rb][2 * h2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_lo[h2], pb[rb][h2], z, 0, 0, 0)[0];
-              csum[rb][2 * h2 + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_hi[h2], pb[rb][h2], z, 0, 0, 0)[0];
-            }
-          }
-        }
-        // per-chunk log2-sum-exp partials (one 128-byte store per chunk and wave)
-        if (CM == 0) {
-#pragma unroll
-          for (int rb = 0; rb < RB; ++rb) cacc[rb] += csum[rb][0];
-          const int c = key0 / cs;
-          const int cend = min((c + 1) * cs, L);
-          if (key0 + kTile >= cend) {
-            float v = m_r[0] + __builtin_amdgcn_logf(cacc[0]);
-#pragma unroll
-            for (int rb = 1; rb < RB; ++rb)
-              if (st_rb == rb) v = m_r[rb] + __builtin_amdgcn_logf(cacc[rb]);
-            if (st_ok) cbase[(int64_t)c * row_stride_chunk] = v;
-#pragma unroll
-            for (int rb = 0; rb < RB; ++rb) cacc[rb] = 0.f;
-          }
+            csum[rb][h2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_all[h2], pb[rb][h2], z, 0, 0, 0)[0];
         } else {
 #pragma unroll
-          for (int q = 0; q < NS; ++q) {
-            const int c = key0 / cs + q;
-            float v = m_r[0] + __builtin_amdgcn_logf(csum[0][q]);
-#pragma unroll
-            for (int rb = 1; rb < RB; ++rb)
-              if (st_rb == rb) v = m_r[rb] + __builtin_amdgcn_logf(csum[rb][q]);
-            if (st_ok && c * cs < L) cbase[(int64_t)c * row_stride_chunk] = v;
+          for (int h2 = 0; h2 < 2; ++h2) {
+            csum[rb][2 * h2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_lo[h2], pb[rb][h2], z, 0, 0, 0)[0];
+            csum[rb][2 * h2 + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_hi[h2], pb[rb][h2], z, 0, 0, 0)[0];
           }
         }
       }
+      // per-chunk log2-sum-exp partials (one 128-byte store per chunk and wave)
+      if (CM == 0) {
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) cacc[rb] += csum[rb][0];
+        const int c = key0 / cs;
+        const int cend = min((c + 1) * cs, L);
+        if (key0 + kTile >= cend) {
+          float v = m_r[0] + __builtin_amdgcn_logf(cacc[0]);
+#pragma unroll
+          for (int rb = 1; rb < RB; ++rb)
+            if (st_rb == rb) v = m_r[rb] + __builtin_amdgcn_logf(cacc[rb]);
+          if (st_ok) cbase[(int64_t)c * row_stride_chunk] = v;
+#pragma unroll
+          for (int rb = 0; rb < RB; ++rb) cacc[rb] = 0.f;
+        }
+      } else {
+#pragma unroll
+        for (int q = 0; q < NS; ++q) {
+          const int c = key0 / cs + q;
+          float v = m_r[0] + __builtin_amdgcn_logf(csum[0][q]);
+#pragma unroll
+          for (int rb = 1; rb < RB; ++rb)
+            if (st_rb == rb) v = m_r[rb] + __builtin_amdgcn_logf(csum[rb][q]);
+          if (st_ok && c * cs < L) cbase[(int64_t)c * row_stride_chunk] = v;
+        }
+      }
+    }
+      };
+
+  // one barrier per tile: tile t+1 loads straight into the other buffer while tile t is computed
+  issue_tile(t_begin, kv_a);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  auto step = [&](int t, const uint16_t (*cur)[TILE_EL], uint16_t (*nxt)[TILE_EL]) __attribute__((always_inline)) {
+    if (t + 1 < t_end) issue_tile(t + 1, nxt);
+    if (wave_active) {
+      stage_qk(t, cur[0]);
+      stage_softmax(t);
+      stage_pv(t, cur[1]);
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this thread's loads of the next tile landed
     __syncthreads();
@@ -567,7 +584,6 @@ hipError_t launch_d_w(const AttnParams& p, const AttnPlan& plan, hipStream_t s) 
 
 template <int D, int CM>
 hipError_t launch_d(const AttnParams& p, const AttnPlan& plan, hipStream_t s) {
-  if (plan.rb == 4) return launch_d_w<D, 4, 4, CM>(p, plan, s);
   return plan.waves == 8 ? launch_d_w<D, 8, 2, CM>(p, plan, s) : launch_d_w<D, 4, 2, CM>(p, plan, s);
 }
 
