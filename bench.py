@@ -44,13 +44,16 @@ def parse():
     ap.add_argument("--depth", type=int, default=10)
     ap.add_argument("--layers", type=int, default=32)
     ap.add_argument("--split-tiles", type=int, default=0)
+    ap.add_argument("--v-layout", choices=["token-rows", "dim-major"], default="token-rows",
+                    help="V cache layout inside a page (token-rows: like K; dim-major: each dim's 16 tokens "
+                         "contiguous)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run a plain 1 GiB device-to-device copy 3 times (reference for HBM byte counters)")
     return ap.parse_args()
 
 
-def cpu_baseline(pools, qs, bt, tree, L, N, kv_heads, head_dim, budget_s=12.0):
+def cpu_baseline(pools, qs, bt, tree, L, N, kv_heads, head_dim, v_layout, budget_s=12.0):
     """The oracle (numpy float64) on whole KV heads of the step's layers, in order, until ~budget_s of CPU
     work; the rate is KV bytes of the heads done per second, the unit of the benchmark's value."""
     import numpy as np
@@ -69,7 +72,7 @@ def cpu_baseline(pools, qs, bt, tree, L, N, kv_heads, head_dim, budget_s=12.0):
         for g in range(kv_heads):
             t0 = time.perf_counter()
             oracle.tree_attention(qb, kb, vb, btn, np.array([L]), np.array([0, N]), tree, 1 / math.sqrt(head_dim),
-                                  kv_heads, 16, 64, kv_heads=[g])
+                                  kv_heads, 16, 64, kv_heads=[g], v_layout=v_layout)
             dt += time.perf_counter() - t0
             done += 1
             if dt >= budget_s:
@@ -121,6 +124,7 @@ def main():
     L, N, depth, layers = args.context, args.nodes, args.depth, args.layers
     Hq, Hkv, D, chunk, top_k, V = 32, 8, 128, 64, 256, 128256
     workload = f"llama8b-{L // 1024}k-n{N}"
+    v_layout = spec.V_DIM_MAJOR if args.v_layout == "dim-major" else spec.V_TOKEN_ROWS
     case = 4
     tree = synth.random_tree(synth.rng_for(case, 0, synth.S_TREE), N, depth)
     par = torch.from_numpy(tree).to(dev)
@@ -130,7 +134,7 @@ def main():
     pools, qs = [], []
     bt = None
     for layer in range(layers):
-        k, v, b = sdev.paged_kv_device(case, layer, [L + N], Hkv, D, dev)
+        k, v, b = sdev.paged_kv_device(case, layer, [L + N], Hkv, D, dev, v_layout=v_layout)
         bt = b if bt is None else bt                  # one page mapping shared by all layers
         pools.append((k, v))
         qs.append(sdev.queries_device(case, layer, N, Hq, D, dev))
@@ -138,7 +142,8 @@ def main():
     lses = [torch.empty((N, Hq), dtype=torch.float32, device=dev) for _ in range(layers)]
 
     attn = [spec.tree_attention_args(qs[l], pools[l][0], pools[l][1], bt, cl, no, par, max_nodes=N, max_ctx_len=L,
-                                     chunk_size=chunk, split_tiles=args.split_tiles, out=outs[l], lse=lses[l])
+                                     chunk_size=chunk, split_tiles=args.split_tiles, out=outs[l], lse=lses[l],
+                                     v_layout=v_layout)
             for l in range(layers)]
     need = lt.lib().spec_tree_attention_workspace_size(ctypes.byref(attn[0]))
     ws = spec._workspace(need, dev, None)
@@ -239,14 +244,15 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle) ...", file=sys.stderr, flush=True)
-        cpu = cpu_baseline(pools, qs, bt, tree, L, N, Hkv, D)
+        cpu = cpu_baseline(pools, qs, bt, tree, L, N, Hkv, D, v_layout)
 
     line = {
         "metric": METRIC, "value": round(kv_gbs_step, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": workload, "context": L, "tree_nodes": N, "tree_depth": depth, "layers": layers,
-                   "q_heads": Hq, "kv_heads": Hkv, "head_dim": D, "page_size": 16, "chunk_size": chunk,
+                   "q_heads": Hq, "kv_heads": Hkv, "head_dim": D, "page_size": 16, "v_layout": args.v_layout,
+                   "chunk_size": chunk,
                    "top_k": top_k, "vocab": V, "acceptance": "greedy", "kv_bytes_per_step": layers * kv_bytes_layer},
         "verify_steps_per_s": round(1000.0 / ms_per_step, 2),
         "hbm_frac_step": round(kv_gbs_step / HBM_PEAK_GBS, 4),

@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define SPEC_ABI_VERSION 1
+#define SPEC_ABI_VERSION 2
 
 typedef enum spec_status {
   SPEC_OK = 0,
@@ -62,6 +62,12 @@ typedef enum spec_status {
 } spec_status;
 
 typedef enum spec_dtype { SPEC_DTYPE_BF16 = 0, SPEC_DTYPE_F32 = 1 } spec_dtype;
+
+/* Layout of the V cache inside a (page, kv_head) block; see spec_paged_kv. */
+typedef enum spec_v_layout {
+  SPEC_V_TOKEN_ROWS = 0,  /* like K: row t of the page at t * token_stride, head_dim contiguous */
+  SPEC_V_DIM_MAJOR = 1    /* dim d at d * page_size, the page's tokens of that dim contiguous */
+} spec_v_layout;
 
 /* == SPEC_ABI_VERSION of the built library. */
 int spec_abi_version(void);
@@ -75,9 +81,14 @@ const char* spec_last_error(void);
  * Logical slot t of sequence b is page block_table[b * block_table_stride + t / page_size],
  * row t % page_size.  Element (page, kv_head, row, d) of K is at
  *   k_cache + page * page_stride + kv_head * head_stride + row * token_stride + d
- * (bf16 elements; V uses the same strides).  The layout [pages][kv_heads][page_size][head_dim]
- * (token_stride = head_dim, head_stride = page_size * head_dim) gives each (page, head) one
- * contiguous block and is the fastest; others work if every row is 16-byte aligned.
+ * (bf16 elements).  V uses the same page and head strides; inside a (page, kv_head) block it is
+ *   v_layout = SPEC_V_TOKEN_ROWS:  v_cache + ... + row * token_stride + d          (like K)
+ *   v_layout = SPEC_V_DIM_MAJOR:   v_cache + ... + d * page_size + row
+ * i.e. [pages][kv_heads][page_size][head_dim] or [pages][kv_heads][head_dim][page_size] (the
+ * layout of caches that store V transposed per page).  Results of the two layouts agree to fp32
+ * rounding (the order of the key contraction differs).  With token_stride = head_dim and
+ * head_stride = page_size * head_dim each (page, head) is one contiguous block (the fastest K
+ * layout); other strides work if every row is 16-byte aligned.
  * page_stride and token_stride * page_size must stay below 2^31 elements (the pool may be larger).
  * Pages may be shared between sequences (copy-on-write prefixes): the library only reads them.
  * ------------------------------------------------------------------------------------------ */
@@ -92,6 +103,7 @@ typedef struct spec_paged_kv {
                                    (a precondition violation: that page's keys then read as zeros) */
   const int32_t* block_table;   /* int32 [batch][block_table_stride] physical page ids */
   int32_t block_table_stride;   /* >= ceil((max_ctx_len + max_nodes) / page_size) */
+  int32_t v_layout;             /* spec_v_layout */
 } spec_paged_kv;
 
 /* ------------------------------------------------------------------------------------------

@@ -87,6 +87,9 @@ int check_attn(const spec_tree_attention_args* a) {
   if (kv.page_stride > INT32_MAX || kv.token_stride * kv.page_size > INT32_MAX)
     return fail(SPEC_ERR_UNSUPPORTED, "kv.page_stride and kv.token_stride * page_size must be < 2^31 elements");
   if (kv.num_pages < 1) return fail(SPEC_ERR_INVALID_ARGUMENT, "kv.num_pages: %d, must be >= 1", kv.num_pages);
+  if (kv.v_layout != SPEC_V_TOKEN_ROWS && kv.v_layout != SPEC_V_DIM_MAJOR)
+    return fail(SPEC_ERR_INVALID_ARGUMENT, "kv.v_layout: %d, must be SPEC_V_TOKEN_ROWS (0) or SPEC_V_DIM_MAJOR (1)",
+                kv.v_layout);
   const int64_t need_blocks = spec::ceil_div((int64_t)a->max_ctx_len + a->max_nodes, kv.page_size);
   if (kv.block_table_stride < need_blocks)
     return fail(SPEC_ERR_INVALID_ARGUMENT, "kv.block_table_stride: %d, must be >= ceil((max_ctx_len + max_nodes) / "
@@ -138,6 +141,7 @@ spec::AttnParams attn_params(const spec_tree_attention_args* a, const AttnLayout
   p.token_stride = a->kv.token_stride;
   p.page_shift = log2i(a->kv.page_size);
   p.num_pages = a->kv.num_pages;
+  p.v_dim_major = a->kv.v_layout == SPEC_V_DIM_MAJOR ? 1 : 0;
   p.block_table = a->kv.block_table;
   p.bt_stride = a->kv.block_table_stride;
   p.ctx_lens = a->ctx_lens;

@@ -43,6 +43,7 @@ struct AttnParams {
   int64_t page_stride, head_stride, token_stride;
   int page_shift;
   int num_pages;
+  int v_dim_major;       // 1: V pages store each dim's page_size tokens contiguously
   const int32_t* block_table;
   int bt_stride;
   const int32_t* ctx_lens;

@@ -12,10 +12,13 @@
 //    read from HBM once and shared, through LDS, by every node and every query head of the group.
 //    Wider trees use several row groups; their work-groups are placed on the same XCD (work-group
 //    ids i and i+8 land on one XCD) so the second read of a tile hits that XCD's L2.
-//  * The split's block-table slice is staged in LDS once; tiles are then gathered page by page
-//    with branch-free 16-byte loads (one 256-byte row per key for head_dim 128), prefetched into
-//    registers while the previous tile computes, and double-buffered in LDS.  V is transposed on
-//    its way into LDS (V^T rows are key-contiguous) with byte permutes.
+//  * The split's block-table slice is staged in LDS once; each 64-slot tile is then copied straight
+//    from HBM into LDS (buffer loads with the LDS destination, 16 bytes per lane, one scalar buffer
+//    descriptor per page whose range ends at the sequence's last slot), double-buffered, the next
+//    tile in flight while the current one is computed.  Rows are XOR-swizzled in 16-byte chunks so
+//    that the MFMA operand reads hit no LDS bank conflicts.  V may be stored like K (token rows; the
+//    V^T operand then comes from transposing LDS reads) or dim-major (each dim's tokens of a page
+//    contiguous; plain 16-byte reads).
 //  * Both products run on MFMA v_mfma_f32_16x16x32_bf16: S^T = K Q^T (A = K rows from LDS,
 //    B = Q from registers), then O^T = V^T P^T (A = V^T from LDS, B = P straight from the S^T
 //    accumulators).  In this orientation each lane owns one query row in every fragment, so the
@@ -67,7 +70,8 @@ __device__ __forceinline__ void buffer_load_lds16(const void* base, uint32_t num
 }
 
 // CM: 0 = chunk sums per 64-slot tile (chunk_size 0 or a multiple of 64), 1 = per 32 slots, 2 = per 16 slots
-template <int D, int W, int RB, int CM>
+// VT: 0 = V pages hold token rows (like K), 1 = V pages are dim-major (each dim's page_size tokens contiguous)
+template <int D, int W, int RB, int CM, int VT>
 __global__ __launch_bounds__(W * 64, (W == 8 ? 1 : 2)) void tree_attn_kernel(AttnParams p) {
   constexpr int NT = W * 64;
   constexpr int ROWS_WG = W * RB * 16;
@@ -76,6 +80,7 @@ __global__ __launch_bounds__(W * 64, (W == 8 ? 1 : 2)) void tree_attn_kernel(Att
   constexpr int CPR = D / 8;                    // 16-byte chunks per K/V row
   constexpr int TILE_EL = kTile * D;            // bf16 elements of one K (or V) tile
   constexpr int LOADS = 2 * kTile * CPR / NT;   // 16-byte direct-to-LDS loads per thread and tile (K and V)
+  constexpr int KB = kTile * CPR / 64;          // 1 KiB blocks of a K (or V) tile
   constexpr int NS = CM == 2 ? 4 : (CM == 1 ? 2 : 1);   // row-sum fragments per row block
   // ancestor masks: a 4-wave work-group holds <= 128 rows, hence <= 128 nodes (two 64-bit words)
   constexpr int ANC_N = W == 8 ? kMaxNodes : 128;
@@ -91,7 +96,14 @@ __global__ __launch_bounds__(W * 64, (W == 8 ? 1 : 2)) void tree_attn_kernel(Att
   __shared__ __attribute__((aligned(16))) uint16_t kv_b[2][TILE_EL];
   __shared__ uint64_t anc_lds[ANC_N][ANC_W];
   __shared__ int pg_lds[kMaxSplitPages];
-  auto swz = [](int r) -> int { return D == 128 ? (r & 15) : ((r >> 1) & 7); };
+  // Row r of a K tile keeps its 16-byte chunk c at position c ^ swz(r), row r of a token-row V tile at
+  // c ^ swzv_rows(r).  The XOR patterns were chosen with the LDS bank-conflict counter: they leave the K
+  // operand reads (rows kmap(j, 0..15), see below) and the transposing V reads without conflicts.
+  auto swz = [](int r) -> int {
+    if (VT) return D == 128 ? ((r & 3) | ((r >> 1) & 12)) : (((r >> 1) & 1) | ((r >> 2) & 6));
+    return D == 128 ? (r & 15) : ((r >> 1) & 7);
+  };
+  auto swzv_rows = [](int r) -> int { return D == 128 ? ((2 * r) & 15) : ((r >> 1) & 7); };
 
   // ---- which (row group, split, KV head, sequence): row groups of one KV range share an XCD ----
   const int RG = p.row_groups;
@@ -187,27 +199,60 @@ __global__ __launch_bounds__(W * 64, (W == 8 ? 1 : 2)) void tree_attn_kernel(Att
   const uint16_t* vbase = p.v + (int64_t)kvh * p.head_stride;
   const uint32_t tstride = (uint32_t)p.token_stride;
   const int pmask = (1 << pshift) - 1;
+  // Dim-major V tile in LDS: one block per page of the tile ([page in tile][dim][pe keys], pe = page size
+  // capped at 64); a dim's row of pe keys holds pe / 8 chunks of 16 bytes, chunk c at c ^ vswz(dim).  An
+  // operand read takes one chunk of 16 consecutive dims; this XOR pattern keeps it free of bank conflicts
+  // for every pe (checked with the LDS bank-conflict counter).
+  const int lpe = pshift < 6 ? pshift : 6;          // log2 pe
+  const int lcr = lpe - 3;                          // log2 chunks per row
+  auto vswz = [&](int d) -> int { return (d >> 1) & ((1 << lcr) - 1); };
+  const int v_ipp_l = lpe + (D == 128 ? 7 : 6) - 9; // log2 of 1 KiB loads per page block
   uint32_t ld_voff[LOADS];                          // bytes from the page (or, for pages > 64 slots, tile) start
 #pragma unroll
   for (int i = 0; i < LOADS; ++i) {
-    const int q = ((wave * LOADS + i) * 64 + lane) % (kTile * CPR);
-    const int kt = q / CPR;
-    const int src = ((q % CPR) ^ swz(kt)) * 8;
-    const int row = pshift > 6 ? kt : (kt & pmask);
-    ld_voff[i] = ((uint32_t)row * tstride + (uint32_t)src) * 2u;
+    const int blk = wave * LOADS + i;
+    if (VT && blk >= KB) {
+      // V load u = blk - KB fills 1 KiB of page block u >> v_ipp_l: dims from (u mod loads per page) * 512 / pe
+      const int u = blk - KB;
+      const int dim = ((u & ((1 << v_ipp_l) - 1)) << (9 - lpe)) + (lane >> lcr);
+      const int c = (lane & ((1 << lcr) - 1)) ^ vswz(dim);
+      ld_voff[i] = (uint32_t)((dim << pshift) + 8 * c) * 2u;
+    } else {
+      const int q = (blk * 64 + lane) % (kTile * CPR);
+      const int kt = q / CPR;
+      const int src = ((q % CPR) ^ (blk >= KB ? swzv_rows(kt) : swz(kt))) * 8;
+      const int row = pshift > 6 ? kt : (kt & pmask);
+      ld_voff[i] = ((uint32_t)row * tstride + (uint32_t)src) * 2u;
+    }
   }
   auto issue_tile = [&](int t, uint16_t (*kv)[TILE_EL]) __attribute__((always_inline)) {
     const int key0 = t * kTile;
+    // every load reads one page: look all page ids up first (LDS reads issued together, one wait)
+    int pgv[LOADS];
 #pragma unroll
     for (int i = 0; i < LOADS; ++i) {
-      const bool is_v = (wave * LOADS + i) * 64 >= kTile * CPR;
-      uint16_t* dst = &kv[is_v ? 1 : 0][((wave * LOADS + i) * 64) % (kTile * CPR) * 8];
-      // first key of this load (wave-uniform), its page id made scalar
-      const int key_w = key0 + (((wave * LOADS + i) * 64) % (kTile * CPR)) / CPR;
+      const int blk = wave * LOADS + i;
+      const int key_w = (VT && blk >= KB) ? key0 + (((blk - KB) >> v_ipp_l) << lpe) : key0 + ((blk * 64) % (kTile * CPR)) / CPR;
       int pi = (key_w >> pshift) - pg_first;
       pi = pi < pg_count ? pi : pg_count - 1;
-      const int pg = __builtin_amdgcn_readfirstlane(pg_lds[pi]);
+      pgv[i] = pg_lds[pi];
+    }
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) {
+      const int blk = wave * LOADS + i;
+      const bool is_v = blk >= KB;
+      uint16_t* dst = &kv[is_v ? 1 : 0][(blk % KB) * 512];
+      const int pg = __builtin_amdgcn_readfirstlane(pgv[i]);
+      if (VT && is_v) {
+        // a descriptor over the page's whole dim-major block; slots past the sequence are not a byte
+        // prefix of it, so they are cleared in the V fragments instead; an invalid page id reads zeros
+        const uint32_t in_page = pshift > 6 ? (uint32_t)(key0 & pmask) * 2u : 0u;
+        const uint16_t* b = vbase + (uint64_t)(uint32_t)(pg < 0 ? 0 : pg) * (uint32_t)p.page_stride;
+        buffer_load_lds16(b, pg < 0 ? 0u : ((uint32_t)D << (pshift + 1)), dst, ld_voff[i] + in_page);
+        continue;
+      }
       // the descriptor starts at the page (or at the tile's first row inside a page longer than a tile)
+      const int key_w = key0 + ((blk * 64) % (kTile * CPR)) / CPR;
       const int first_key = pshift > 6 ? key0 : (key_w & ~pmask);
       const int span = pshift > 6 ? kTile : (1 << pshift);
       int valid = keys - first_key;
@@ -219,25 +264,47 @@ __global__ __launch_bounds__(W * 64, (W == 8 ? 1 : 2)) void tree_attn_kernel(Att
     }
   };
 
-  // per-lane LDS element offsets of the MFMA operand reads
-  // K rows 16j + lm, chunk 4kk + lg: the swizzle of row 16j + lm does not depend on j, so the row block
-  // j only adds 16 * j * D elements (an immediate offset of the LDS read)
-  int k_off[KS];
+  // per-lane LDS element offsets of the MFMA operand reads.
+  // Row r of S^T block j holds tile key kmap(j, r).  With dim-major V the keys are ordered so that the
+  // P fragment of 32-key half h2 holds keys 32 h2 + 8 lg + e in element e, the order in which a 16-byte
+  // row read of the V^T tile delivers them; with token-row V the order follows the transposing reads.
+  auto kmap = [](int j, int r) -> int { return VT ? 32 * (j >> 1) + 8 * (r >> 2) + 4 * (j & 1) + (r & 3) : 16 * j + r; };
+  // tile key of element e of this lane's P fragment for half h2
+  auto pkey = [&](int h2, int e) -> int { return VT ? 32 * h2 + 8 * lg + e : 32 * h2 + (e < 4 ? 4 * lg + e : 12 + 4 * lg + e); };
+  // K rows kmap(j, lm), chunk 4kk + lg.  Blocks j and j + 2 are 32 keys apart with the same swizzle, and
+  // with token-row V all four blocks share it, so only the offsets of blocks 0 and 1 are kept.
+  int k_off[VT ? 2 : 1][KS];
 #pragma unroll
-  for (int kk = 0; kk < KS; ++kk) k_off[kk] = lm * D + 8 * ((4 * kk + lg) ^ swz(lm));
-  // transposing V reads: lane (lg, lm) points at key 32*h2 + 4*lg + lm/4 (+16), dims 16*nb + 4*(lm%4)
+  for (int jj = 0; jj < (VT ? 2 : 1); ++jj)
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) {
+      const int r = kmap(jj, lm);
+      k_off[jj][kk] = r * D + 8 * ((4 * kk + lg) ^ swz(r));
+    }
+  auto kaddr = [&](int j, int kk) -> int {
+    return VT ? k_off[j & 1][kk] + (j >> 1) * 32 * D : k_off[0][kk] + 16 * j * D;
+  };
+  // V^T fragment reads.  Token-row V: transposing reads, lane (lg, lm) points at key 32*h2 + 4*lg + lm/4
+  // (+16), dims 16*nb + 4*(lm%4).  Dim-major V: a 16-byte read of dim 16*nb + lm, keys 32*h2 + 8*lg + 0..7.
   int v_row[2], v_swz[2];
 #pragma unroll
   for (int h2 = 0; h2 < 2; ++h2) {
-    const int key = 32 * h2 + 4 * lg + (lm >> 2);
-    v_row[h2] = key * D + 4 * (lm & 1);
-    v_swz[h2] = swz(key);
+    if (VT) {
+      const int key = 32 * h2 + 8 * lg;             // first of the lane's 8 keys
+      v_row[h2] = ((key >> lpe) << (lpe + (D == 128 ? 7 : 6))) + (lm << lpe) +
+                  8 * (((key & ((1 << lpe) - 1)) >> 3) ^ vswz(lm));
+      v_swz[h2] = 0;
+    } else {
+      const int key = 32 * h2 + 4 * lg + (lm >> 2);
+      v_row[h2] = key * D + 4 * (lm & 1);
+      v_swz[h2] = swzv_rows(key);
+    }
   }
 
   // constant A fragments for the chunk sums (bf16 1.0 = 0x3F80): all slots, or the slots of one 16-key block
   const bf16x8 ones = bf16_splat8(0x3F803F80u, 0x3F803F80u);
-  const bf16x8 ones_lo = bf16_splat8(0x3F803F80u, 0u);
-  const bf16x8 ones_hi = bf16_splat8(0u, 0x3F803F80u);
+  const bf16x8 ones_lo = VT ? (lg < 2 ? ones : bf16_splat8(0u, 0u)) : bf16_splat8(0x3F803F80u, 0u);
+  const bf16x8 ones_hi = VT ? (lg < 2 ? bf16_splat8(0u, 0u) : ones) : bf16_splat8(0u, 0x3F803F80u);
 
   f32x4 o[RB][NB];
   float m_r[RB], l_r[RB], cacc[RB];
@@ -259,7 +326,7 @@ __global__ __launch_bounds__(W * 64, (W == 8 ? 1 : 2)) void tree_attn_kernel(Att
   const int64_t st_col = st_ok ? (int64_t)(st_row / G) * p.Hq + kvh * G + st_row % G : 0;
   float* cbase = p.chunk_lse2 + (int64_t)b * p.max_chunks * row_stride_chunk + st_col;
 
-  // S (scores of the current tile), P (its bf16 probabilities) live across the compute stages
+  // S (scores of the current tile) and P (its bf16 probabilities) live across the compute stages
   f32x4 s[RB][4];
   bf16x8 pb[RB][2];
 
@@ -276,12 +343,12 @@ __global__ __launch_bounds__(W * 64, (W == 8 ? 1 : 2)) void tree_attn_kernel(Att
     // MFMAs of step kk run
     bf16x8 kf[2][4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) kf[0][j] = *reinterpret_cast<const bf16x8*>(kt + 16 * j * D + k_off[0]);
+    for (int j = 0; j < 4; ++j) kf[0][j] = *reinterpret_cast<const bf16x8*>(kt + kaddr(j, 0));
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk) {
       if (kk + 1 < KS) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) kf[(kk + 1) & 1][j] = *reinterpret_cast<const bf16x8*>(kt + 16 * j * D + k_off[kk + 1]);
+        for (int j = 0; j < 4; ++j) kf[(kk + 1) & 1][j] = *reinterpret_cast<const bf16x8*>(kt + kaddr(j, kk + 1));
       }
 #pragma unroll
       for (int j = 0; j < 4; ++j)
@@ -290,12 +357,13 @@ __global__ __launch_bounds__(W * 64, (W == 8 ? 1 : 2)) void tree_attn_kernel(Att
           s[rb][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[kk & 1][j], qreg[rb][kk], s[rb][j], 0, 0, 0);
     }
   };
-  // stage 2: mask, online softmax (lazy rescale of O), bf16 probabilities
-  auto stage_softmax = [&](int t) __attribute__((always_inline)) {
+  // stage 2a: mask the tile's scores, the row maxima; true (wave-uniform) when some row's running max
+  // must move (lazy rescaling: only when a tile's max exceeds it by more than 2^kRescale)
+  float mt[RB];
+  auto stage_max = [&](int t) __attribute__((always_inline)) -> bool {
     const int key0 = t * kTile;
-      const bool edge = key0 + kTile > L;        // tile holds tree slots or slots past the end
+    const bool edge = key0 + kTile > L;           // tile holds tree slots or slots past the end
     bool resc = false;
-    float mt[RB];
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
       if (__builtin_expect(edge, 0)) {
@@ -303,7 +371,7 @@ __global__ __launch_bounds__(W * 64, (W == 8 ? 1 : 2)) void tree_attn_kernel(Att
         for (int j = 0; j < 4; ++j)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const int key = key0 + 16 * j + 4 * lg + i;
+            const int key = key0 + kmap(j, 4 * lg + i);
             bool vis = key < L;
             if (!vis && key < keys && valid_r[rb]) {
               const int tj = key - L;           // < N <= ANC_N, and node_r < N
@@ -319,18 +387,23 @@ __global__ __launch_bounds__(W * 64, (W == 8 ? 1 : 2)) void tree_attn_kernel(Att
       mt[rb] = max4g(mx) * c2;
       resc |= mt[rb] > m_r[rb] + kRescale;
     }
-    if (__builtin_amdgcn_ballot_w64(resc) != 0) {  // some row's max moved: rescale (wave-uniform branch)
+    return __builtin_amdgcn_ballot_w64(resc) != 0;
+  };
+  // stage 2b: move the running max of the rows that need it, rescaling O, l and the chunk accumulator
+  auto stage_rescale = [&]() __attribute__((always_inline)) {
 #pragma unroll
-      for (int rb = 0; rb < RB; ++rb) {
-        const float mnew = mt[rb] > m_r[rb] + kRescale ? mt[rb] : m_r[rb];
-        const float alpha = __builtin_amdgcn_exp2f(m_r[rb] - mnew);
-        l_r[rb] *= alpha;
-        cacc[rb] *= alpha;
+    for (int rb = 0; rb < RB; ++rb) {
+      const float mnew = mt[rb] > m_r[rb] + kRescale ? mt[rb] : m_r[rb];
+      const float alpha = __builtin_amdgcn_exp2f(m_r[rb] - mnew);
+      l_r[rb] *= alpha;
+      cacc[rb] *= alpha;
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb) o[rb][nb] *= alpha;
-        m_r[rb] = mnew;
-      }
+      for (int nb = 0; nb < NB; ++nb) o[rb][nb] *= alpha;
+      m_r[rb] = mnew;
     }
+  };
+  // stage 2c: probabilities against the running max (fp32 row sums, bf16 P fragments)
+  auto stage_exp = [&](bf16x8 (&pout)[RB][2]) __attribute__((always_inline)) {
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
       const float mneg = -m_r[rb];
@@ -347,18 +420,18 @@ __global__ __launch_bounds__(W * 64, (W == 8 ? 1 : 2)) void tree_attn_kernel(Att
           v[i] = (__bf16)x0;
           v[4 + i] = (__bf16)x1;
         }
-        pb[rb][h2] = v;
+        pout[rb][h2] = v;
       }
       l_r[rb] += e0 + e1;
     }
   };
-  // stage 3: O += V^T . P^T for tile t from the V tile at vt, chunk partials
-  auto stage_pv = [&](int t, const uint16_t* vt) __attribute__((always_inline)) {
-    const int key0 = t * kTile;
-    const bool edge = key0 + kTile > L;
-      // O^T[dim][row] += V^T . P^T, with V^T fragments read transposed from the row-major V tile;
-    // fragments are read two dim blocks ahead of their MFMAs
+  // stage 3a: O^T[dim][row] += V^T . P^T for the tile at key0 (V^T fragments from vt, two dim blocks
+  // ahead of their MFMAs)
+  auto pv_mfma = [&](int key0, const uint16_t* vt, const bf16x8 (&pin)[RB][2]) __attribute__((always_inline)) {
+    (void)key0;
     auto vfrag = [&](int nb, int h2) __attribute__((always_inline)) -> bf16x8 {
+      if (VT) return *reinterpret_cast<const bf16x8*>(vt + (nb << (lpe + 4)) + v_row[h2]);
+      // token-row V: transposing reads
       typedef short i16x4 __attribute__((ext_vector_type(4)));
       const int c = 2 * nb + ((lm & 3) >> 1);
       const int off = v_row[h2] + 8 * (c ^ v_swz[h2]);
@@ -381,82 +454,109 @@ __global__ __launch_bounds__(W * 64, (W == 8 ? 1 : 2)) void tree_attn_kernel(Att
       const int nb = x % NB, h2 = x / NB;
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb)
-        o[rb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[x & 3], pb[rb][h2], o[rb][nb], 0, 0, 0);
+        o[rb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[x & 3], pin[rb][h2], o[rb][nb], 0, 0, 0);
     }
-    // chunk sums of P (bf16 values, fp32 sums) on MFMA: every output slot of the fragment holds the
-    // row's sum, so no cross-lane reduction is needed
-    if (cs > 0 && key0 < L) {
-      // chunk sums cover context keys only: in the tile where the context ends, the A fragments of
-      // ones are cleared at the tree slots (A is shared by the row blocks; P stays untouched)
-      bf16x8 a_all[2] = {ones, ones}, a_lo[2] = {ones_lo, ones_lo}, a_hi[2] = {ones_hi, ones_hi};
-      if (__builtin_expect(edge, 0)) {
+  };
+  // stage 3b: chunk sums of P (bf16 values, fp32 sums) on MFMA against constant ones: every output slot
+  // of the fragment holds the row's sum, so no cross-lane reduction is needed.  edge: the tile holds
+  // slots >= L, whose ones are cleared (chunk sums cover context keys only; P stays untouched).
+  auto chunk_mfma = [&](int key0, const bf16x8 (&pin)[RB][2], bool edge, float (&csum)[RB][NS]) __attribute__((always_inline)) {
+    bf16x8 a_all[2] = {ones, ones}, a_lo[2] = {ones_lo, ones_lo}, a_hi[2] = {ones_hi, ones_hi};
+    if (edge) {
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (key0 + pkey(h2, e) >= L) {
+            a_all[h2][e] = (__bf16)0.0f;
+            a_lo[h2][e] = (__bf16)0.0f;
+            a_hi[h2][e] = (__bf16)0.0f;
+          }
+    }
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+      if (CM == 0) {
+        f32x4 c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_all[0], pin[rb][0], z, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_all[1], pin[rb][1], c, 0, 0, 0);
+        csum[rb][0] = c[0];
+      } else if (CM == 1) {
 #pragma unroll
         for (int h2 = 0; h2 < 2; ++h2)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            if (key0 + 32 * h2 + 4 * lg + i >= L) { a_all[h2][i] = (__bf16)0.0f; a_lo[h2][i] = (__bf16)0.0f; }
-            if (key0 + 32 * h2 + 16 + 4 * lg + i >= L) { a_all[h2][4 + i] = (__bf16)0.0f; a_hi[h2][4 + i] = (__bf16)0.0f; }
-          }
-      }
-      float csum[RB][NS];
-#pragma unroll
-      for (int rb = 0; rb < RB; ++rb) {
-        const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-        if (CM == 0) {
-          f32x4 c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_all[0], pb[rb][0], z, 0, 0, 0);
-          c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_all[1], pb[rb][1], c, 0, 0, 0);
-          csum[rb][0] = c[0];
-        } else if (CM == 1) {
-#pragma unroll
-          for (int h2 = 0; h2 < 2; ++h2)
-            csum[rb][h2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_all[h2], pb[rb][h2], z, 0, 0, 0)[0];
-        } else {
-#pragma unroll
-          for (int h2 = 0; h2 < 2; ++h2) {
-            csum[rb][2 * h2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_lo[h2], pb[rb][h2], z, 0, 0, 0)[0];
-            csum[rb][2 * h2 + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_hi[h2], pb[rb][h2], z, 0, 0, 0)[0];
-          }
-        }
-      }
-      // per-chunk log2-sum-exp partials (one 128-byte store per chunk and wave)
-      if (CM == 0) {
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb) cacc[rb] += csum[rb][0];
-        const int c = key0 / cs;
-        const int cend = min((c + 1) * cs, L);
-        if (key0 + kTile >= cend) {
-          float v = m_r[0] + __builtin_amdgcn_logf(cacc[0]);
-#pragma unroll
-          for (int rb = 1; rb < RB; ++rb)
-            if (st_rb == rb) v = m_r[rb] + __builtin_amdgcn_logf(cacc[rb]);
-          if (st_ok) cbase[(int64_t)c * row_stride_chunk] = v;
-#pragma unroll
-          for (int rb = 0; rb < RB; ++rb) cacc[rb] = 0.f;
-        }
+          csum[rb][h2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_all[h2], pin[rb][h2], z, 0, 0, 0)[0];
       } else {
 #pragma unroll
-        for (int q = 0; q < NS; ++q) {
-          const int c = key0 / cs + q;
-          float v = m_r[0] + __builtin_amdgcn_logf(csum[0][q]);
-#pragma unroll
-          for (int rb = 1; rb < RB; ++rb)
-            if (st_rb == rb) v = m_r[rb] + __builtin_amdgcn_logf(csum[rb][q]);
-          if (st_ok && c * cs < L) cbase[(int64_t)c * row_stride_chunk] = v;
+        for (int h2 = 0; h2 < 2; ++h2) {
+          csum[rb][2 * h2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_lo[h2], pin[rb][h2], z, 0, 0, 0)[0];
+          csum[rb][2 * h2 + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_hi[h2], pin[rb][h2], z, 0, 0, 0)[0];
         }
       }
     }
-      };
+  };
+  // stage 3c: per-chunk log2-sum-exp partials against the running max (one 128-byte store per chunk and
+  // wave); with 64-slot (or longer) chunks the tile's sum is accumulated until the chunk ends
+  auto chunk_store = [&](int key0, const float (&csum)[RB][NS]) __attribute__((always_inline)) {
+    if (CM == 0) {
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) cacc[rb] += csum[rb][0];
+      const int c = key0 / cs;
+      const int cend = min((c + 1) * cs, L);
+      if (key0 + kTile >= cend) {
+        float v = m_r[0] + __builtin_amdgcn_logf(cacc[0]);
+#pragma unroll
+        for (int rb = 1; rb < RB; ++rb)
+          if (st_rb == rb) v = m_r[rb] + __builtin_amdgcn_logf(cacc[rb]);
+        if (st_ok) cbase[(int64_t)c * row_stride_chunk] = v;
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) cacc[rb] = 0.f;
+      }
+    } else {
+#pragma unroll
+      for (int q = 0; q < NS; ++q) {
+        const int c = key0 / cs + q;
+        float v = m_r[0] + __builtin_amdgcn_logf(csum[0][q]);
+#pragma unroll
+        for (int rb = 1; rb < RB; ++rb)
+          if (st_rb == rb) v = m_r[rb] + __builtin_amdgcn_logf(csum[rb][q]);
+        if (st_ok && c * cs < L) cbase[(int64_t)c * row_stride_chunk] = v;
+      }
+    }
+  };
+  // stage 3: P.V and the chunk partials of tile t, any tile
+  auto stage_pv = [&](int t, const uint16_t* vt, const bf16x8 (&pin)[RB][2]) __attribute__((always_inline)) {
+    const int key0 = t * kTile;
+    pv_mfma(key0, vt, pin);
+    if (cs > 0 && key0 < L) {
+      float csum[RB][NS];
+      chunk_mfma(key0, pin, key0 + kTile > L, csum);
+      chunk_store(key0, csum);
+    }
+  };
 
   // one barrier per tile: tile t+1 loads straight into the other buffer while tile t is computed
   issue_tile(t_begin, kv_a);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
-  auto step = [&](int t, const uint16_t (*cur)[TILE_EL], uint16_t (*nxt)[TILE_EL]) __attribute__((always_inline)) {
+  auto step = [&](int t, uint16_t (*cur)[TILE_EL], uint16_t (*nxt)[TILE_EL]) __attribute__((always_inline)) {
     if (t + 1 < t_end) issue_tile(t + 1, nxt);
+    if (VT && t * kTile + kTile > keys) {
+      // the sequence's last tile: its dim-major V slots past the sequence hold whatever the page held
+      // (they are not a byte prefix that the load's range check could clear), so they are zeroed in LDS
+      // before any wave multiplies them by P = 0
+      const int key0 = t * kTile;
+      for (int i = tid; i < D * kTile; i += NT) {
+        const int dim = i >> 6, key = i & 63;
+        if (key0 + key >= keys)
+          cur[1][((key >> lpe) << (lpe + (D == 128 ? 7 : 6))) + (dim << lpe) +
+                 8 * (((key & ((1 << lpe) - 1)) >> 3) ^ vswz(dim)) + (key & 7)] = 0;
+      }
+      __syncthreads();
+    }
     if (wave_active) {
       stage_qk(t, cur[0]);
-      stage_softmax(t);
-      stage_pv(t, cur[1]);
+      if (stage_max(t)) stage_rescale();
+      stage_exp(pb);
+      stage_pv(t, cur[1], pb);
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this thread's loads of the next tile landed
     __syncthreads();
@@ -570,11 +670,11 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnParams p) {
   }
 }
 
-template <int D, int W, int RB, int CM>
+template <int D, int W, int RB, int CM, int VT>
 hipError_t launch_d_w(const AttnParams& p, const AttnPlan& plan, hipStream_t s) {
   const int n_units = p.batch * p.Hkv * p.max_splits;
   const int grid = (int)(ceil_div(n_units, 8) * 8 * plan.row_groups);
-  hipLaunchKernelGGL((tree_attn_kernel<D, W, RB, CM>), dim3(grid), dim3(W * 64), 0, s, p);
+  hipLaunchKernelGGL((tree_attn_kernel<D, W, RB, CM, VT>), dim3(grid), dim3(W * 64), 0, s, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t rows = (int64_t)p.batch * p.max_nodes * p.Hq;
@@ -582,16 +682,21 @@ hipError_t launch_d_w(const AttnParams& p, const AttnPlan& plan, hipStream_t s) 
   return hipGetLastError();
 }
 
-template <int D, int CM>
+template <int D, int CM, int VT>
 hipError_t launch_d(const AttnParams& p, const AttnPlan& plan, hipStream_t s) {
-  return plan.waves == 8 ? launch_d_w<D, 8, 2, CM>(p, plan, s) : launch_d_w<D, 4, 2, CM>(p, plan, s);
+  return plan.waves == 8 ? launch_d_w<D, 8, 2, CM, VT>(p, plan, s) : launch_d_w<D, 4, 2, CM, VT>(p, plan, s);
+}
+
+template <int D, int CM>
+hipError_t launch_v(const AttnParams& p, const AttnPlan& plan, hipStream_t s) {
+  return p.v_dim_major ? launch_d<D, CM, 1>(p, plan, s) : launch_d<D, CM, 0>(p, plan, s);
 }
 
 template <int D>
 hipError_t launch_cm(const AttnParams& p, const AttnPlan& plan, hipStream_t s) {
-  if (p.chunk_size == 16) return launch_d<D, 2>(p, plan, s);
-  if (p.chunk_size == 32) return launch_d<D, 1>(p, plan, s);
-  return launch_d<D, 0>(p, plan, s);
+  if (p.chunk_size == 16) return launch_v<D, 2>(p, plan, s);
+  if (p.chunk_size == 32) return launch_v<D, 1>(p, plan, s);
+  return launch_v<D, 0>(p, plan, s);
 }
 
 }  // namespace

@@ -19,7 +19,9 @@ LIB_PATH = os.path.join(_HERE, "libspec_verify.so")
 SPEC_OK = 0
 SPEC_DTYPE_BF16 = 0
 SPEC_DTYPE_F32 = 1
-ABI_VERSION = 1
+ABI_VERSION = 2
+V_TOKEN_ROWS = 0   # spec_v_layout: V pages like K, [pages][kv_heads][page_size][head_dim]
+V_DIM_MAJOR = 1    # V pages [pages][kv_heads][head_dim][page_size]
 
 _lib = None
 
@@ -74,7 +76,8 @@ class PagedKV(ctypes.Structure):
     _fields_ = [("k_cache", ctypes.c_void_p), ("v_cache", ctypes.c_void_p),
                 ("page_stride", ctypes.c_int64), ("head_stride", ctypes.c_int64), ("token_stride", ctypes.c_int64),
                 ("page_size", ctypes.c_int32), ("num_pages", ctypes.c_int32),
-                ("block_table", ctypes.c_void_p), ("block_table_stride", ctypes.c_int32)]
+                ("block_table", ctypes.c_void_p), ("block_table_stride", ctypes.c_int32),
+                ("v_layout", ctypes.c_int32)]
 
 
 class TreeAttentionArgs(ctypes.Structure):
@@ -152,9 +155,11 @@ class AttentionHandle:
 
 def tree_attention_args(q, k_cache, v_cache, block_table, ctx_lens, node_offsets, parents, *, max_nodes: int,
                         max_ctx_len: int, scale: Optional[float] = None, chunk_size: int = 0, split_tiles: int = 0,
-                        out=None, lse=None, workspace=None) -> TreeAttentionArgs:
-    """Fill the C argument struct from tensors (no launch).  k_cache / v_cache are bf16
-    [pages][kv_heads][page_size][head_dim] with unit stride in the last dimension."""
+                        out=None, lse=None, workspace=None, v_layout: int = V_TOKEN_ROWS) -> TreeAttentionArgs:
+    """Fill the C argument struct from tensors (no launch).  k_cache is bf16 [pages][kv_heads][page_size]
+    [head_dim] with unit stride in the last dimension; v_cache has the same shape and strides
+    (V_TOKEN_ROWS) or is [pages][kv_heads][head_dim][page_size] with K's page and head strides
+    (V_DIM_MAJOR)."""
     a = TreeAttentionArgs()
     T, Hq, D = q.shape
     a.batch = ctx_lens.numel()
@@ -171,6 +176,7 @@ def tree_attention_args(q, k_cache, v_cache, block_table, ctx_lens, node_offsets
     a.kv.num_pages = k_cache.shape[0]
     a.kv.block_table = _ptr(block_table)
     a.kv.block_table_stride = block_table.shape[1]
+    a.kv.v_layout = v_layout
     a.scale = (1.0 / math.sqrt(D)) if scale is None else scale
     a.out = _ptr(out)
     a.lse = _ptr(lse)
@@ -185,7 +191,7 @@ def tree_attention(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor
                    ctx_lens: torch.Tensor, node_offsets: torch.Tensor, parents: torch.Tensor, *, max_nodes: int,
                    max_ctx_len: int, scale: Optional[float] = None, chunk_size: int = 0, split_tiles: int = 0,
                    out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None, want_lse: bool = True,
-                   workspace: Optional[torch.Tensor] = None, stream=None):
+                   workspace: Optional[torch.Tensor] = None, stream=None, v_layout: int = V_TOKEN_ROWS):
     """Tree-masked attention of every draft-tree node over the paged KV cache.
 
     Returns (out bf16 [T][Hq][D], lse fp32 [T][Hq] or None, handle for spec_chunk_salience)."""
@@ -195,10 +201,19 @@ def tree_attention(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor
         _need(t, name, torch.int32)
     _need(k_cache, "k_cache", torch.bfloat16, contiguous=False)
     _need(v_cache, "v_cache", torch.bfloat16, contiguous=False)
-    if k_cache.stride() != v_cache.stride() or k_cache.shape != v_cache.shape:
-        raise ValueError("k_cache and v_cache must have the same shape and strides")
     if k_cache.stride(3) != 1:
-        raise ValueError("k_cache / v_cache: the head_dim stride must be 1")
+        raise ValueError("k_cache: the head_dim stride must be 1")
+    if v_layout == V_TOKEN_ROWS:
+        if k_cache.stride() != v_cache.stride() or k_cache.shape != v_cache.shape:
+            raise ValueError("k_cache and v_cache must have the same shape and strides")
+    elif v_layout == V_DIM_MAJOR:
+        P, H, S, D_ = k_cache.shape
+        if tuple(v_cache.shape) != (P, H, D_, S) or v_cache.stride()[:2] != k_cache.stride()[:2] \
+                or v_cache.stride(2) != S or v_cache.stride(3) != 1:
+            raise ValueError("dim-major v_cache must be [pages][kv_heads][head_dim][page_size] with k_cache's page "
+                             "and head strides and contiguous pages")
+    else:
+        raise ValueError(f"v_layout {v_layout}: expected V_TOKEN_ROWS or V_DIM_MAJOR")
     T, Hq, D = q.shape
     if out is None:
         out = torch.empty((T, Hq, D), dtype=torch.bfloat16, device=q.device)
@@ -206,7 +221,7 @@ def tree_attention(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor
         lse = torch.empty((T, Hq), dtype=torch.float32, device=q.device)
     a = tree_attention_args(q, k_cache, v_cache, block_table, ctx_lens, node_offsets, parents, max_nodes=max_nodes,
                             max_ctx_len=max_ctx_len, scale=scale, chunk_size=chunk_size, split_tiles=split_tiles,
-                            out=out, lse=lse)
+                            out=out, lse=lse, v_layout=v_layout)
     need = lib().spec_tree_attention_workspace_size(ctypes.byref(a))
     if need == 0:
         _check(lib().spec_tree_attention(ctypes.byref(a), None), "spec_tree_attention")

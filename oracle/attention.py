@@ -21,9 +21,10 @@ Sources (the pages are cited by title and section):
 * DiffSpec README (CGCL-codes), section Features ("Chunk Arena and Paged KV"): K/V
   live in fixed-size pages addressed through a per-sequence block table.
 
-Conventions: K/V pools are bf16 bit patterns [pages][kv_heads][page_size][head_dim];
-logical slot t of sequence b lives in page block_table[b][t // page_size] at row
-t % page_size.  Node i of sequence b owns slot ctx_len[b] + i.  Query head h reads
+Conventions: K/V pools are bf16 bit patterns [pages][kv_heads][page_size][head_dim]
+(a dim-major V pool, [pages][kv_heads][head_dim][page_size], is read through the same
+indices with the last two swapped); logical slot t of sequence b lives in page
+block_table[b][t // page_size] at row t % page_size.  Node i of sequence b owns slot ctx_len[b] + i.  Query head h reads
 KV head h // (num_q_heads // num_kv_heads).  Everything is computed in float64.
 """
 
@@ -83,7 +84,8 @@ def attention_rows(q, k, v, scale: float):
 
 
 def tree_attention(q_bits, k_pool, v_pool, block_table, ctx_lens, node_offsets, parents, scale: float,
-                   num_kv_heads: int, page_size: int = 16, chunk_size: int = 0, kv_heads=None, seqs=None):
+                   num_kv_heads: int, page_size: int = 16, chunk_size: int = 0, kv_heads=None, seqs=None,
+                   v_layout: int = 0):
     """Tree verification attention (float64).
 
     For sequence b with committed context length L and tree node i, query head h with KV head g, the
@@ -95,11 +97,14 @@ def tree_attention(q_bits, k_pool, v_pool, block_table, ctx_lens, node_offsets, 
     all N nodes and all query heads of the sequence; tree keys belong to no chunk.
 
     ``kv_heads`` / ``seqs`` restrict the work to a subset (other outputs stay NaN; a mass computed
-    over a KV-head subset averages over that subset's query heads only).
+    over a KV-head subset averages over that subset's query heads only).  ``v_layout`` 1: ``v_pool`` is
+    dim-major, [pages][kv_heads][head_dim][page_size].
 
     Returns (out [T][Hq][D], lse [T][Hq], masses: list of [n_chunks] arrays or None)."""
     q = np.asarray(q_bits)
     T, Hq, D = q.shape
+    if v_layout:
+        v_pool = np.swapaxes(np.asarray(v_pool), 2, 3)     # back to [pages][kv_heads][page_size][head_dim]
     G = Hq // num_kv_heads
     out = np.full((T, Hq, D), np.nan)
     lse = np.full((T, Hq), np.nan)

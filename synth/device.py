@@ -12,18 +12,19 @@ import math
 import numpy as np
 import torch
 
-from .inputs import PAGE_SIZE, AttentionCase, GreedyCase, RejectionCase
+from .inputs import PAGE_SIZE, AttentionCase, GreedyCase, RejectionCase, dim_major
 
 
 def bf16_tensor(bits: np.ndarray, device) -> torch.Tensor:
     return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(device)
 
 
-def attention_tensors(case: AttentionCase, device) -> dict:
+def attention_tensors(case: AttentionCase, device, v_layout: int = 0) -> dict:
+    """``v_layout`` 1 hands V over dim-major ([pages][kv_heads][head_dim][page_size])."""
     return dict(
         q=bf16_tensor(case.q, device),
         k_cache=bf16_tensor(case.kv.k_pool, device),
-        v_cache=bf16_tensor(case.kv.v_pool, device),
+        v_cache=bf16_tensor(dim_major(case.kv.v_pool) if v_layout else case.kv.v_pool, device),
         block_table=torch.from_numpy(case.kv.block_table).to(device),
         ctx_lens=torch.from_numpy(case.ctx_lens).to(device),
         node_offsets=torch.from_numpy(case.node_offsets).to(device),
@@ -58,9 +59,10 @@ def _gen(device, *seed_parts) -> torch.Generator:
 
 
 def paged_kv_device(case: int, layer: int, slots, num_kv_heads: int, head_dim: int, device, *,
-                    page_size: int = PAGE_SIZE, pool_factor: float = 1.25):
+                    page_size: int = PAGE_SIZE, pool_factor: float = 1.25, v_layout: int = 0):
     """K/V pools bf16 [pool][Hkv][page_size][D] ~ N(0,1) drawn on the device, a seeded permutation block
-    table (int32 [B][max_blocks], -1 padded).  Returns (k_pool, v_pool, block_table)."""
+    table (int32 [B][max_blocks], -1 padded).  Returns (k_pool, v_pool, block_table); with ``v_layout`` 1
+    the same V values are returned dim-major, [pool][Hkv][D][page_size]."""
     slots = [int(s) for s in slots]
     npages = [(s + page_size - 1) // page_size for s in slots]
     total = sum(npages)
@@ -74,6 +76,8 @@ def paged_kv_device(case: int, layer: int, slots, num_kv_heads: int, head_dim: i
     shape = (pool, num_kv_heads, page_size, head_dim)
     k = torch.randn(shape, generator=_gen(device, case, layer, 1), device=device, dtype=torch.bfloat16)
     v = torch.randn(shape, generator=_gen(device, case, layer, 2), device=device, dtype=torch.bfloat16)
+    if v_layout:
+        v = v.transpose(2, 3).contiguous()
     return k, v, torch.from_numpy(bt).to(device)
 
 

@@ -35,7 +35,7 @@ __all__ = [
     "PAGE_SIZE", "BF16_QNAN", "rng_for", "bf16_bits", "bf16_to_f32",
     "S_Q", "S_K", "S_V", "S_BLOCKS", "S_TREE", "S_TARGET", "S_DRAFT", "S_TOKENS", "S_UNIFORM", "S_CTX",
     "chain_tree", "random_tree", "tree_depths", "children_lists",
-    "PagedKV", "paged_kv", "AttentionCase", "attention_case",
+    "PagedKV", "paged_kv", "dim_major", "AttentionCase", "attention_case",
     "GreedyCase", "greedy_case", "RejectionCase", "rejection_case",
     "uniforms24", "ragged_ctx_lens", "WORKLOADS",
 ]
@@ -165,6 +165,12 @@ def paged_kv(case: int, layer: int, slots, num_kv_heads: int, head_dim: int, *,
         v_pool[bt[b, :n]] = vl
         off += n
     return PagedKV(k_pool, v_pool, bt, slots.astype(np.int32), page_size)
+
+
+def dim_major(pool: np.ndarray) -> np.ndarray:
+    """A [pages][kv_heads][page_size][head_dim] pool rewritten as [pages][kv_heads][head_dim][page_size]
+    (each dim's page_size tokens contiguous): the dim-major V cache layout.  Only moves values."""
+    return np.ascontiguousarray(np.asarray(pool).transpose(0, 1, 3, 2))
 
 
 def ragged_ctx_lens(case: int, batch: int, lo: int, hi: int) -> np.ndarray:

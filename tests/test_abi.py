@@ -33,7 +33,7 @@ def test_exports_every_declared_symbol():
     L = ctypes.CDLL(spec.LIB_PATH)
     for n in names:
         assert hasattr(L, n), n
-    assert spec.lib().spec_abi_version() == 1
+    assert spec.lib().spec_abi_version() == 2
     assert spec.status_string(3) == "SPEC_ERR_WORKSPACE"
 
 
@@ -67,6 +67,8 @@ def _attn_args(spec, **over):
     ("kv_page_size", 4, 2, "page_size"),
     ("kv_block_table_stride", 10, 1, "block_table_stride"),
     ("kv_token_stride", 60, 1, "token_stride"),
+    ("kv_v_layout", 2, 1, "v_layout"),
+    ("kv_v_layout", -1, 1, "v_layout"),
     ("scale", float("nan"), 1, "scale"),
     ("scale", -1.0, 1, "scale"),
     ("chunk_size", 48, 2, "chunk_size"),

@@ -34,14 +34,15 @@ def _case(name):
     raise KeyError(name)
 
 
+@pytest.mark.parametrize("v_layout", [0, 1])
 @pytest.mark.parametrize("name,chunk,split", [("tiny", 64, 0), ("tiny", 16, 1), ("llama64", 64, 0),
                                               ("llama64", 32, 3), ("llama64", 128, 4), ("llama128", 64, 0),
                                               ("llama128", 64, 2), ("ragged", 32, 0), ("ragged", 64, 1),
                                               ("gqa1_d64", 64, 0), ("gqa1_d64", 16, 5)])
-def test_attention_and_mass_match_oracle(name, chunk, split):
+def test_attention_and_mass_match_oracle(name, chunk, split, v_layout):
     case = _case(name)
-    print(f"case={name} chunk={chunk} split={split}", flush=True)
-    out, lse, h, t = run_attention(case, chunk_size=chunk, split_tiles=split)
+    print(f"case={name} chunk={chunk} split={split} v_layout={v_layout}", flush=True)
+    out, lse, h, t = run_attention(case, chunk_size=chunk, split_tiles=split, v_layout=v_layout)
     import long_context_tree_amd as lt
     n_ch = max(1, -(-int(case.ctx_lens.max()) // chunk))
     mass = torch.full((len(case.ctx_lens), n_ch), 7.0, dtype=torch.float32, device=dev())
@@ -117,6 +118,31 @@ def test_deterministic_and_block_table_invariant():
         assert np.array_equal(x, y)
 
 
+@pytest.mark.parametrize("chunk", [16, 32, 64])
+def test_v_layouts_agree_to_rounding(chunk):
+    """Token-row and dim-major V give the same scores for every key; only the order in which the keys of
+    a tile are contracted (P.V, row and chunk sums) differs, so outputs, LSEs and chunk masses agree to
+    fp32 rounding (page sizes below, equal to and above a 64-slot tile)."""
+    import long_context_tree_amd as lt
+    r = synth.rng_for(113, chunk, 0)
+    for ps in (8, 16, 64, 128):
+        case = synth.attention_case(113, ctx_lens=[1000, 333], trees=[synth.random_tree(r, 40, 6),
+                                                                       synth.chain_tree(5)],
+                                    num_q_heads=32, num_kv_heads=8, head_dim=128, page_size=ps)
+        res = []
+        for vl in (0, 1):
+            print(f"chunk={chunk} page_size={ps} v_layout={vl}", flush=True)
+            out, lse, h, _ = run_attention(case, chunk_size=chunk, split_tiles=4, v_layout=vl)
+            mass = torch.zeros((2, -(-1000 // chunk)), dtype=torch.float32, device=dev())
+            lt.chunk_salience(h, mass)
+            torch.cuda.synchronize()
+            res.append((out.float().cpu().numpy(), lse.cpu().numpy(), mass.cpu().numpy()))
+        (o0, l0, m0), (o1, l1, m1) = res
+        assert np.abs(o0 - o1).max() <= 1e-3            # at most a bf16 rounding flip of |out| < 0.25
+        assert np.abs(l0 - l1).max() <= 1e-5
+        assert np.abs(m0 - m1).sum() <= 1e-5 * m0.sum()
+
+
 def test_split_count_invariance_within_tolerance():
     case = _case("llama64")
     outs = [run_attention(case, split_tiles=s)[:2] for s in (1, 5, 33)]
@@ -162,18 +188,20 @@ def test_full_size_llama_128k_sampled_head():
     import oracle
     L, N = 131072, 128
     tree = synth.random_tree(synth.rng_for(121, 0, 4), N, 10)
-    k, v, bt = sdev.paged_kv_device(121, 0, [L + N], 8, 128, dev())
+    k, v, bt = sdev.paged_kv_device(121, 0, [L + N], 8, 128, dev(), v_layout=1)
     q = sdev.queries_device(121, 0, N, 32, 128, dev())
     cl = torch.tensor([L], dtype=torch.int32, device=dev())
     no = torch.tensor([0, N], dtype=torch.int32, device=dev())
     par = torch.from_numpy(tree).to(dev())
-    out, lse, h = lt.tree_attention(q, k, v, bt, cl, no, par, max_nodes=N, max_ctx_len=L, chunk_size=64)
+    out, lse, h = lt.tree_attention(q, k, v, bt, cl, no, par, max_nodes=N, max_ctx_len=L, chunk_size=64,
+                                    v_layout=lt.V_DIM_MAJOR)
     mass = torch.zeros((1, L // 64), dtype=torch.float32, device=dev())
     lt.chunk_salience(h, mass, top_k=256)
     torch.cuda.synchronize()
     g = 3
     o_ref, l_ref, _ = oracle.tree_attention(bits_of(q), bits_of(k), bits_of(v), bt.cpu().numpy(), np.array([L]),
-                                            np.array([0, N]), tree, 1 / np.sqrt(128), 8, 16, 0, kv_heads=[g])
+                                            np.array([0, N]), tree, 1 / np.sqrt(128), 8, 16, 0, kv_heads=[g],
+                                            v_layout=1)
     sel = np.zeros((N, 32), dtype=bool)
     sel[:, 4 * g:4 * g + 4] = True
     compare_out(out, lse, o_ref, l_ref, mask=sel)
@@ -181,14 +209,16 @@ def test_full_size_llama_128k_sampled_head():
     assert (m >= 0).all() and 0.0 < m.sum() <= 1.0
 
 
+@pytest.mark.parametrize("v_layout", [0, 1])
 @pytest.mark.parametrize("page_size", [8, 32, 64, 128, 256])
-def test_page_sizes(page_size):
+def test_page_sizes(page_size, v_layout):
     """Pages smaller than, equal to and larger than a 64-slot tile (the last spans several tiles)."""
     r = synth.rng_for(130, page_size, 0)
     case = synth.attention_case(130 + page_size, ctx_lens=[700, 1300], trees=[synth.random_tree(r, 20, 5),
                                                                               synth.chain_tree(4)],
                                 num_q_heads=8, num_kv_heads=2, head_dim=128, page_size=page_size)
-    out, lse, h, _ = run_attention(case, chunk_size=64, split_tiles=3)
+    print(f"page_size={page_size} v_layout={v_layout}", flush=True)
+    out, lse, h, _ = run_attention(case, chunk_size=64, split_tiles=3, v_layout=v_layout)
     import long_context_tree_amd as lt
     mass = torch.zeros((2, 21), dtype=torch.float32, device=dev())
     lt.chunk_salience(h, mass)

@@ -190,6 +190,12 @@ def test_block_table_and_pool_invariance():
     assert np.array_equal(ra[0], rb[0]) and np.array_equal(ra[1], rb[1])
     for ma, mb in zip(ra[2], rb[2]):
         assert np.array_equal(ma, mb)
+    # the same V pool handed over dim-major reads the same values
+    vt = synth.dim_major(a.kv.v_pool)
+    assert vt.shape == (a.kv.v_pool.shape[0], 2, 64, a.kv.page_size)
+    rc = oracle.tree_attention(a.q, a.kv.k_pool, vt, a.kv.block_table, a.ctx_lens, a.node_offsets, a.parents,
+                               a.scale, a.num_kv_heads, a.kv.page_size, 64, v_layout=1)
+    assert np.array_equal(ra[0], rc[0]) and np.array_equal(ra[1], rc[1])
 
 
 def test_chunk_mass_against_torch_softmax():
