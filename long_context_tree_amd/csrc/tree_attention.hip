@@ -445,16 +445,17 @@ __global__ __launch_bounds__(W * 64, (W == 8 ? 1 : 2)) void tree_attn_kernel(Att
     // order (h2, nb, rb): the two MFMAs accumulating into one O fragment are 2 * NB apart, so no MFMA
     // waits on the previous one's result
     constexpr int NV = 2 * NB;
-    bf16x8 vf[4];
-    vf[0] = vfrag(0, 0);
-    vf[1] = vfrag(1 % NB, 1 / NB);
+    constexpr int VPF = 2;                          // fragments read ahead of their MFMAs
+    bf16x8 vf[8];
+#pragma unroll
+    for (int x = 0; x < VPF; ++x) vf[x] = vfrag(x % NB, x / NB);
 #pragma unroll
     for (int x = 0; x < NV; ++x) {
-      if (x + 2 < NV) vf[(x + 2) & 3] = vfrag((x + 2) % NB, (x + 2) / NB);
+      if (x + VPF < NV) vf[(x + VPF) & 7] = vfrag((x + VPF) % NB, (x + VPF) / NB);
       const int nb = x % NB, h2 = x / NB;
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb)
-        o[rb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[x & 3], pin[rb][h2], o[rb][nb], 0, 0, 0);
+        o[rb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[x & 7], pin[rb][h2], o[rb][nb], 0, 0, 0);
     }
   };
   // stage 3b: chunk sums of P (bf16 values, fp32 sums) on MFMA against constant ones: every output slot
@@ -718,9 +719,11 @@ bool make_attn_plan(const spec_tree_attention_args* a, int num_cus, AttnPlan* pl
   const int64_t cap_tiles = ((int64_t)(kMaxSplitPages - 1) * ps) / kTile;
   int st = a->split_tiles;
   if (st <= 0) {
-    // enough work-groups to fill every CU about twice, but at least 8 tiles per split
+    // one round of work-groups: as many as the CUs hold at once (one 8-wave or two 4-wave work-groups
+    // per CU), but at least 8 tiles per split.  A second round would add partials to write and merge
+    // and per-work-group set-up, and a partial round leaves CUs idle at the end.
     const int64_t ranges = (int64_t)a->batch * a->num_kv_heads * pl.row_groups;
-    const int64_t target = 2LL * (num_cus > 0 ? num_cus : 256);
+    const int64_t target = (int64_t)(num_cus > 0 ? num_cus : 256) * (pl.waves == 8 ? 1 : 2);
     int64_t want_splits = ceil_div(target, ranges);
     st = (int)ceil_div(pl.max_tiles, want_splits < 1 ? 1 : want_splits);
     if (st < 8) st = 8;
