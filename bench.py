@@ -241,6 +241,61 @@ def main():
                  "mfma_tflops": round(tflops, 2), "mfma_frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4)})
     kv_gbs_step = layers * kv_bytes_layer / (ms_per_step * 1e-3) / 1e9
 
+    # the other calls of the path, each timed alone with events on the same stream after the timed region
+    # (not part of the step's value): the salience reduction of one layer, greedy acceptance of the step,
+    # and rejection acceptance on a 64-node tree (depth 8) at the same vocabulary
+    def time_call(fn, reps=30):
+        for _ in range(3):
+            fn()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        for e0, e1 in ev:
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+        torch.cuda.synchronize()
+        return float(np.median([e0.elapsed_time(e1) for e0, e1 in ev])) * 1e3
+
+    def call(st):
+        if st:
+            raise RuntimeError(lt.last_error())
+
+    kernels = {}
+    rows = N * Hq
+    sal_bytes = rows * n_chunks * 4 + rows * 4 + 2 * n_chunks * 4
+    us = time_call(lambda: call(L_.spec_chunk_salience(ctypes.byref(sal[1]), sh)))
+    kernels["spec_chunk_salience"] = {"median_us": round(us, 2), "alg_bytes": sal_bytes,
+                                      "gbs": round(sal_bytes / us / 1e3, 1), "bound": "hbm",
+                                      "note": "one layer, accumulate, no top-k"}
+    us = time_call(lambda: call(L_.spec_chunk_salience(ctypes.byref(sal[-1]), sh)))
+    kernels["spec_chunk_salience_topk"] = {"median_us": round(us, 2), "alg_bytes": sal_bytes,
+                                           "gbs": round(sal_bytes / us / 1e3, 1), "bound": "hbm",
+                                           "note": f"last layer, accumulate, top-{top_k}"}
+    g_bytes = N * V * 2
+    us = time_call(lambda: call(L_.spec_accept_greedy(ctypes.byref(ga), sh)))
+    kernels["spec_accept_greedy"] = {"median_us": round(us, 2), "alg_bytes": g_bytes,
+                                     "gbs": round(g_bytes / us / 1e3, 1), "bound": "hbm",
+                                     "note": f"{N} nodes, vocab {V}, bf16 logits"}
+    rtree = synth.random_tree(synth.rng_for(3, 0, synth.S_TREE), 64, 8)
+    rc = synth.rejection_case(3, [rtree], V, dtype="bf16", draft="independent")
+    rt = sdev.rejection_tensors(rc, dev)
+    r_outs = (torch.empty(1, dtype=torch.int32, device=dev), torch.empty((1, 9), dtype=torch.int32, device=dev),
+              torch.empty((1, 9), dtype=torch.int32, device=dev))
+    ra = spec.AcceptRejectionArgs()
+    ra.base = spec._greedy_args(rt["node_offsets"], rt["parents"], rt["draft_tokens"], rt["target_logits"], 64, 9,
+                                r_outs)
+    ra.max_children = 4
+    ra.draft_probs, ra.u_accept, ra.u_sample = (rt["draft_probs"].data_ptr(), rt["u_accept"].data_ptr(),
+                                                rt["u_sample"].data_ptr())
+    rneed = lt.lib().spec_accept_rejection_workspace_size(ctypes.byref(ra))
+    rws = spec._workspace(rneed, dev, None)
+    ra.base.workspace, ra.base.workspace_bytes = rws.data_ptr(), rws.numel()
+    r_bytes = 64 * V * (2 + 4)
+    us = time_call(lambda: call(L_.spec_accept_rejection(ctypes.byref(ra), sh)))
+    kernels["spec_accept_rejection"] = {"median_us": round(us, 2), "alg_bytes": r_bytes,
+                                        "gbs": round(r_bytes / us / 1e3, 1), "bound": "hbm",
+                                        "note": f"64 nodes (depth 8, <= 4 children), vocab {V}, bf16 logits + "
+                                                "fp32 draft probabilities read once"}
+
     cpu = None
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle) ...", file=sys.stderr, flush=True)
@@ -257,6 +312,7 @@ def main():
         "verify_steps_per_s": round(1000.0 / ms_per_step, 2),
         "hbm_frac_step": round(kv_gbs_step / HBM_PEAK_GBS, 4),
         "roofline": roof,
+        "kernels": kernels,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
