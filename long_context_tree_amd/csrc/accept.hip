@@ -121,18 +121,36 @@ __global__ __launch_bounds__(256) void argmax_seg_kernel(AcceptParams p) {
   if (threadIdx.x == 0) p.seg_key[u * p.nseg + seg] = best;
 }
 
-__device__ __forceinline__ float row_max(const AcceptParams& p, int64_t u) {
-  unsigned long long k = 0;
-  for (int s = 0; s < p.nseg; ++s) k = umax64(k, p.seg_key[u * p.nseg + s]);
-  return key_value(k);
+__device__ __forceinline__ float row_max(const AcceptParams& p, int64_t u) { return key_value(p.node_key[u]); }
+
+// Normaliser k of node u: Z[0] = sum exp(l - M); Z[k] = sum max(0, res_{k-1} - q) (fixed-order totals)
+__device__ __forceinline__ double level_sum(const AcceptParams& p, int64_t u, int k) {
+  return p.zsum[u * (p.max_children + 1) + k];
 }
 
-// Normalisers of node u in a fixed order: Z[0] = sum exp(l - M); Z[k] = sum max(0, res_{k-1} - q).
-__device__ __forceinline__ double level_sum(const AcceptParams& p, int64_t u, int k) {
-  const double* s = p.seg_sum + (u * (p.max_children + 1) + k) * p.nseg;
+// ---- rejection: per node, the row-maximum key over the argmax segments (one wave per node) ----
+__global__ __launch_bounds__(64) void node_max_kernel(AcceptParams p) {
+  const int64_t u = blockIdx.x;
+  if (u >= total_nodes(p)) return;
+  unsigned long long k = 0;
+  for (int s = threadIdx.x; s < p.nseg; s += 64) k = umax64(k, p.seg_key[u * p.nseg + s]);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) k = umax64(k, shfl_xor_u64(k, off));
+  if (threadIdx.x == 0) p.node_key[u] = k;
+}
+
+// ---- rejection: per node, the total of residual level r over its segments (one wave per node,
+// fixed order: lanes stride the segments, then a butterfly) ----
+__global__ __launch_bounds__(64) void level_total_kernel(AcceptParams p, int r) {
+  const int64_t u = blockIdx.x;
+  if (u >= total_nodes(p)) return;
+  if (r > 0 && p.n_children[u] < r) return;
+  const double* s = p.seg_sum + (u * (p.max_children + 1) + r) * p.nsegr;
   double z = 0.0;
-  for (int i = 0; i < p.nseg; ++i) z += s[i];
-  return z;
+  for (int i = threadIdx.x; i < p.nsegr; i += 64) z += s[i];
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) z += __shfl_xor(z, off);
+  if (threadIdx.x == 0) p.zsum[u * (p.max_children + 1) + r] = z;
 }
 
 // ---- rejection: one residual level for every node that needs it ----
@@ -143,28 +161,32 @@ __global__ __launch_bounds__(256) void residual_pass_kernel(AcceptParams p, int 
   if (r > 0 && p.n_children[u] < r) return;
   const double M = (double)row_max(p, u);
   double Z[9];
-  const int v0 = seg * kSegment;
-  const int v1 = min(p.vocab, v0 + kSegment);
+  const int v0 = seg * kResSegment;
+  const int v1 = min(p.vocab, v0 + kResSegment);
   double acc = 0.0;
   if (r == 0) {
     for (int v = v0 + threadIdx.x; v < v1; v += 256) acc += exp((double)load_logit(p, u, v) - M);
   } else {
-    // normalisers of the earlier levels (up to 8 held in registers; deeper levels re-summed)
-    for (int k = 0; k < r && k < 9; ++k) Z[k] = level_sum(p, u, k);
+    // reciprocals of the earlier levels' normalisers (up to 9 held in registers; deeper levels re-summed);
+    // a product with the reciprocal differs from the quotient by at most one fp64 rounding
+    for (int k = 0; k < r && k < 9; ++k) {
+      const double z = level_sum(p, u, k);
+      Z[k] = z > 0.0 ? 1.0 / z : 0.0;
+    }
     const float* q = p.draft_probs + u * (int64_t)p.vocab;
     for (int v = v0 + threadIdx.x; v < v1; v += 256) {
       const double qv = (double)q[v];
-      double res = exp((double)load_logit(p, u, v) - M) / Z[0];
+      double res = exp((double)load_logit(p, u, v) - M) * Z[0];
       for (int k = 1; k < r; ++k) {
         const double d = fmax(0.0, res - qv);
-        const double zk = k < 9 ? Z[k] : level_sum(p, u, k);
-        if (zk > 0.0) res = d / zk;
+        const double zk = k < 9 ? Z[k] : (level_sum(p, u, k) > 0.0 ? 1.0 / level_sum(p, u, k) : 0.0);
+        if (zk > 0.0) res = d * zk;
       }
       acc += fmax(0.0, res - qv);
     }
   }
   acc = block_sum_f64(acc);
-  if (threadIdx.x == 0) p.seg_sum[(u * (p.max_children + 1) + r) * p.nseg + seg] = acc;
+  if (threadIdx.x == 0) p.seg_sum[(u * (p.max_children + 1) + r) * p.nsegr + seg] = acc;
 }
 
 // ---- per sequence: child counts (for the residual passes) ----
@@ -253,15 +275,18 @@ __global__ __launch_bounds__(256) void walk_kernel(AcceptParams p) {
         const int64_t gu = n0 + u;
         const int r = rank_s[c];
         double Z[9];
-        for (int k = 0; k <= r && k < 9; ++k) Z[k] = level_sum(p, gu, k);
+        for (int k = 0; k <= r && k < 9; ++k) {
+          const double z = level_sum(p, gu, k);
+          Z[k] = z > 0.0 ? 1.0 / z : 0.0;            // reciprocals, as in the residual passes
+        }
         const double M = (double)row_max(p, gu);
         const double qx = (double)p.draft_probs[gu * p.vocab + x];
         const double e = exp((double)load_logit(p, gu, x) - M);
-        double res = e / Z[0];
+        double res = e * Z[0];
         for (int k = 1; k <= r; ++k) {
           const double d = fmax(0.0, res - qx);
-          const double zk = k < 9 ? Z[k] : level_sum(p, gu, k);
-          if (zk > 0.0) res = d / zk;
+          const double zk = k < 9 ? Z[k] : (level_sum(p, gu, k) > 0.0 ? 1.0 / level_sum(p, gu, k) : 0.0);
+          if (zk > 0.0) res = d * zk;
         }
         ok = (double)p.u_accept[n0 + c] * qx < res;
       }
@@ -333,21 +358,21 @@ __global__ __launch_bounds__(256) void walk_kernel(AcceptParams p) {
         if (k < 9) zs[k] = z;
         if (z > 0.0 || k == 0) lvl = k;             // a zero residual keeps the previous level
       }
-      const double* ss = p.seg_sum + (gu * (p.max_children + 1) + lvl) * p.nseg;
+      const double* ss = p.seg_sum + (gu * (p.max_children + 1) + lvl) * p.nsegr;
       const double zl = level_sum(p, gu, lvl);
       double tot = 0.0;
-      for (int s = 0; s < p.nseg; ++s) tot += ss[s] / zl;
+      for (int s = 0; s < p.nsegr; ++s) tot += ss[s] / zl;
       const double thr = (double)p.u_sample[gu] * tot;
       double base = 0.0;
-      int seg = p.nseg - 1;
-      for (int s = 0; s < p.nseg; ++s) {
+      int seg = p.nsegr - 1;
+      for (int s = 0; s < p.nsegr; ++s) {
         const double w = ss[s] / zl;
         if (base + w > thr) { seg = s; break; }
         base += w;
       }
       if (base + ss[seg] / zl <= thr) {             // rounding left the threshold past the end:
         base = tot;                                 // fall back to the last segment with mass
-        for (int s = p.nseg - 1; s >= 0; --s) {
+        for (int s = p.nsegr - 1; s >= 0; --s) {
           base -= ss[s] / zl;
           if (ss[s] > 0.0) { seg = s; break; }
         }
@@ -359,22 +384,22 @@ __global__ __launch_bounds__(256) void walk_kernel(AcceptParams p) {
     }
     __syncthreads();
     const int seg = seg_s;
-    const int v0 = seg * kSegment;
-    const int v1 = min(p.vocab, v0 + kSegment);
-    const int per = kSegment / 256;
+    const int v0 = seg * kResSegment;
+    const int v1 = min(p.vocab, v0 + kResSegment);
+    const int per = kResSegment / 256;
     const int a0 = v0 + tid * per;
     const int a1 = min(v1, a0 + per);
     const double M = (double)row_max(p, gu);
     const float* q = p.draft_probs + gu * (int64_t)p.vocab;
     double Z[9];
-    for (int k = 0; k <= r && k < 9; ++k) Z[k] = zs[k];
+    for (int k = 0; k <= r && k < 9; ++k) Z[k] = zs[k] > 0.0 ? 1.0 / zs[k] : 0.0;
     auto res_of = [&](int v) -> double {
       const double qv = (double)q[v];
-      double res = exp((double)load_logit(p, gu, v) - M) / Z[0];
+      double res = exp((double)load_logit(p, gu, v) - M) * Z[0];
       for (int k = 1; k <= r; ++k) {
         const double dd = fmax(0.0, res - qv);
-        const double zk = k < 9 ? Z[k] : level_sum(p, gu, k);
-        if (zk > 0.0) res = dd / zk;
+        const double zk = k < 9 ? Z[k] : (level_sum(p, gu, k) > 0.0 ? 1.0 / level_sum(p, gu, k) : 0.0);
+        if (zk > 0.0) res = dd * zk;
       }
       return res;
     };
@@ -421,10 +446,11 @@ size_t greedy_ws_bytes(int batch, int max_nodes, int nseg) {
   return align_up(sizeof(unsigned long long) * (size_t)batch * max_nodes * nseg, 256);
 }
 
-size_t rejection_ws_bytes(int batch, int max_nodes, int nseg, int max_children) {
-  return greedy_ws_bytes(batch, max_nodes, nseg) +
-         align_up(sizeof(double) * (size_t)batch * max_nodes * (max_children + 1) * nseg, 256) +
-         align_up(sizeof(int32_t) * (size_t)batch * max_nodes, 256);
+size_t rejection_ws_bytes(int batch, int max_nodes, int nseg, int nsegr, int max_children) {
+  const size_t nodes = (size_t)batch * max_nodes, lv = (size_t)max_children + 1;
+  return greedy_ws_bytes(batch, max_nodes, nseg) + align_up(sizeof(unsigned long long) * nodes, 256) +
+         align_up(sizeof(double) * nodes * lv * nsegr, 256) + align_up(sizeof(double) * nodes * lv, 256) +
+         align_up(sizeof(int32_t) * nodes, 256);
 }
 
 hipError_t launch_accept_greedy(const AcceptParams& p, hipStream_t s) {
@@ -443,8 +469,12 @@ hipError_t launch_accept_rejection(const AcceptParams& p, hipStream_t s) {
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(argmax_seg_kernel, dim3(p.nseg, rows), dim3(256), 0, s, p);
   if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL(node_max_kernel, dim3(rows), dim3(64), 0, s, p);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
   for (int r = 0; r <= p.max_children; ++r) {
-    hipLaunchKernelGGL(residual_pass_kernel, dim3(p.nseg, rows), dim3(256), 0, s, p, r);
+    hipLaunchKernelGGL(residual_pass_kernel, dim3(p.nsegr, rows), dim3(256), 0, s, p, r);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL(level_total_kernel, dim3(rows), dim3(64), 0, s, p, r);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   hipLaunchKernelGGL(walk_kernel<true>, dim3(p.batch), dim3(256), 0, s, p);

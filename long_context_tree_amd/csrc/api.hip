@@ -197,6 +197,7 @@ int check_greedy(const spec_accept_greedy_args* a) {
 }
 
 int nseg_of(int vocab) { return (int)spec::ceil_div(vocab, spec::kSegment); }
+int nsegr_of(int vocab) { return (int)spec::ceil_div(vocab, spec::kResSegment); }
 
 spec::AcceptParams accept_params(const spec_accept_greedy_args* a) {
   spec::AcceptParams p{};
@@ -345,15 +346,15 @@ size_t spec_accept_rejection_workspace_size(const spec_accept_rejection_args* ar
   if (check_rejection(args) != SPEC_OK) return 0;
   g_err.clear();
   return spec::rejection_ws_bytes(args->base.batch, args->base.max_nodes, nseg_of(args->base.vocab),
-                                  args->max_children);
+                                  nsegr_of(args->base.vocab), args->max_children);
 }
 
 int spec_accept_rejection(const spec_accept_rejection_args* args, void* stream) {
   int st = check_rejection(args);
   if (st != SPEC_OK) return st;
   const spec_accept_greedy_args& g = args->base;
-  const int nseg = nseg_of(g.vocab);
-  const size_t need = spec::rejection_ws_bytes(g.batch, g.max_nodes, nseg, args->max_children);
+  const int nseg = nseg_of(g.vocab), nsegr = nsegr_of(g.vocab);
+  const size_t need = spec::rejection_ws_bytes(g.batch, g.max_nodes, nseg, nsegr, args->max_children);
   st = check_workspace(g.workspace, g.workspace_bytes, need, "spec_accept_rejection");
   if (st != SPEC_OK) return st;
   spec::AcceptParams p = accept_params(&g);
@@ -361,12 +362,17 @@ int spec_accept_rejection(const spec_accept_rejection_args* args, void* stream) 
   p.draft_probs = args->draft_probs;
   p.u_accept = args->u_accept;
   p.u_sample = args->u_sample;
+  p.nsegr = nsegr;
   char* ws = static_cast<char*>(g.workspace);
-  const size_t off_sum = spec::greedy_ws_bytes(g.batch, g.max_nodes, nseg);
-  p.seg_sum = reinterpret_cast<double*>(ws + off_sum);
-  const size_t off_nch =
-      off_sum + spec::align_up(sizeof(double) * (size_t)g.batch * g.max_nodes * (args->max_children + 1) * nseg, 256);
-  p.n_children = reinterpret_cast<int32_t*>(ws + off_nch);
+  const size_t nodes = (size_t)g.batch * g.max_nodes, lv = (size_t)args->max_children + 1;
+  size_t off = spec::greedy_ws_bytes(g.batch, g.max_nodes, nseg);
+  p.node_key = reinterpret_cast<unsigned long long*>(ws + off);
+  off += spec::align_up(sizeof(unsigned long long) * nodes, 256);
+  p.seg_sum = reinterpret_cast<double*>(ws + off);
+  off += spec::align_up(sizeof(double) * nodes * lv * nsegr, 256);
+  p.zsum = reinterpret_cast<double*>(ws + off);
+  off += spec::align_up(sizeof(double) * nodes * lv, 256);
+  p.n_children = reinterpret_cast<int32_t*>(ws + off);
   const hipError_t e = spec::launch_accept_rejection(p, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "spec_accept_rejection launch");
   return ok();

@@ -12,7 +12,8 @@ namespace spec {
 
 constexpr int kTile = 64;          // KV slots per attention tile
 constexpr int kMaxNodes = 256;     // tree nodes per sequence (ancestor masks are 4 x 64 bits)
-constexpr int kSegment = 8192;     // vocabulary elements per acceptance work-group
+constexpr int kSegment = 8192;     // vocabulary elements per argmax work-group
+constexpr int kResSegment = 2048;  // vocabulary elements per residual-sum work-group (rejection)
 constexpr int kMaxTopK = 8192;     // chunks sorted by one work-group for top-k
 constexpr int kMaxSplitPages = 1024;  // page ids of one attention split staged in LDS
 
@@ -91,7 +92,7 @@ hipError_t launch_chunk_salience(const SalienceParams& p, hipStream_t s);
 // acceptance
 // ------------------------------------------------------------------------------------------
 struct AcceptParams {
-  int batch, vocab, max_nodes, max_path, nseg;
+  int batch, vocab, max_nodes, max_path, nseg, nsegr;
   const int32_t* node_offsets;
   const int32_t* parents;
   const int32_t* draft_tokens;
@@ -106,11 +107,13 @@ struct AcceptParams {
   const float* draft_probs;
   const float* u_accept;
   const float* u_sample;
-  double* seg_sum;       // [batch*max_nodes][max_children+1][nseg]
+  unsigned long long* node_key;   // [batch*max_nodes] row maximum key
+  double* seg_sum;       // [batch*max_nodes][max_children+1][nsegr] residual sums per segment
+  double* zsum;          // [batch*max_nodes][max_children+1] residual sums per level (fixed-order totals)
   int32_t* n_children;   // [batch*max_nodes]
 };
 size_t greedy_ws_bytes(int batch, int max_nodes, int nseg);
-size_t rejection_ws_bytes(int batch, int max_nodes, int nseg, int max_children);
+size_t rejection_ws_bytes(int batch, int max_nodes, int nseg, int nsegr, int max_children);
 hipError_t launch_accept_greedy(const AcceptParams& p, hipStream_t s);
 hipError_t launch_accept_rejection(const AcceptParams& p, hipStream_t s);
 
