@@ -106,7 +106,6 @@ int check_attn(const spec_tree_attention_args* a) {
 
 struct AttnLayout {
   spec::AttnPlan plan;
-  size_t off_sal = 0;
   size_t bytes = 0;
   int ws_max_chunks = 0;
 };
@@ -115,11 +114,7 @@ AttnLayout attn_layout(const spec_tree_attention_args* a) {
   AttnLayout l;
   spec::make_attn_plan(a, kPlanCUs, &l.plan);
   l.ws_max_chunks = l.plan.max_chunks;
-  l.off_sal = l.plan.bytes;
-  size_t sal = 0;
-  if (a->chunk_size > 0)
-    sal = spec::align_up(spec::salience_partial_bytes(a->batch, a->max_nodes, a->num_q_heads, l.ws_max_chunks), 256);
-  l.bytes = l.off_sal + sal;
+  l.bytes = l.plan.bytes;
   return l;
 }
 
@@ -296,7 +291,6 @@ int spec_chunk_salience(const spec_chunk_salience_args* args, void* stream) {
   char* ws = static_cast<char*>(a->workspace);
   p.chunk_lse2 = reinterpret_cast<const float*>(ws + l.plan.off_chunk);
   p.lse2 = reinterpret_cast<const float*>(ws + l.plan.off_lse2);
-  p.partial = reinterpret_cast<float*>(ws + l.off_sal);
   p.chunk_mass = args->chunk_mass;
   p.max_chunks = args->max_chunks;
   p.accumulate = args->accumulate;

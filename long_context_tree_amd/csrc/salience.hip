@@ -10,17 +10,16 @@
 // The attention kernel leaves, per (query row, chunk), the log2-sum-exp of the row's scaled
 // scores over the chunk, and the merge leaves each row's final log2-sum-exp.  The mass of chunk c
 // is then  mean over rows of exp2(chunk_lse2[c][row] - lse2[row]).
-//   pass 1  one wave per (chunk, block of 1024 rows): lanes stride the rows (coalesced), fixed-order
-//           wave reduction -> partial[b][row block][c]
-//   pass 2  sum of the row-block partials in order, scaled, written or accumulated
-//   pass 3  (top_k > 0) one work-group per sequence: bitonic sort of (mass desc, index asc) keys in LDS
+//   salience  one work-group per (sequence, chunk): a fixed-order sum over the rows of the chunk
+//             (contiguous in the workspace), scaled, written or accumulated
+//   top-k     (top_k > 0) one work-group per sequence: bitonic sort of (mass desc, index asc) keys in LDS
 // Every reduction has a fixed order, so results are bitwise reproducible.
 #include "spec_internal.h"
 
 namespace spec {
 namespace {
 
-constexpr int kRowsPerSplit = 1024;
+constexpr int kChunksPerWG = 1;
 
 __device__ __forceinline__ void seq_bounds(const SalienceParams& p, int b, int* N, int* L) {
   int n = p.node_offsets[b + 1] - p.node_offsets[b];
@@ -29,45 +28,53 @@ __device__ __forceinline__ void seq_bounds(const SalienceParams& p, int b, int* 
   *L = l < 0 ? 0 : (l > p.max_ctx ? p.max_ctx : l);
 }
 
-__global__ __launch_bounds__(256) void salience_partial_kernel(SalienceParams p) {
-  const int lane = threadIdx.x & 63;
-  const int c = blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int rs = blockIdx.y, b = blockIdx.z;
+// One work-group per (sequence, kChunksPerWG chunks): for each chunk, every row's exp2(chunk_lse2 -
+// lse2) is summed in a fixed order (each thread a fixed set of rows, then a butterfly in each wave, then
+// the four waves in order), scaled by 1 / rows and written or accumulated.  Rows of a chunk are
+// contiguous, so the reads are 16-byte loads when the row stride allows.
+__global__ __launch_bounds__(256) void salience_kernel(SalienceParams p) {
+  __shared__ float red[4];
+  const int b = blockIdx.y;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   int N, L;
   seq_bounds(p, b, &N, &L);
   const int nch = (L + p.chunk_size - 1) / p.chunk_size;
-  if (c >= nch) return;
   const int rows = N * p.Hq;
   const int stride = p.max_nodes * p.Hq;
-  const int r0 = rs * kRowsPerSplit;
-  const int r1 = min(rows, r0 + kRowsPerSplit);
-  const float* x = p.chunk_lse2 + ((int64_t)b * p.ws_max_chunks + c) * stride;
   const float* l2 = p.lse2 + (int64_t)b * stride;
-  float acc = 0.f;
-  for (int r = r0 + lane; r < r1; r += 64) acc += __builtin_amdgcn_exp2f(x[r] - l2[r]);
+  const bool vec = (stride & 3) == 0;
+  for (int k = 0; k < kChunksPerWG; ++k) {
+    const int c = blockIdx.x * kChunksPerWG + k;
+    if (c >= p.max_chunks) return;
+    float* dst = p.chunk_mass + (int64_t)b * p.max_chunks + c;
+    if (c >= nch || N == 0) {
+      if (tid == 0 && !p.accumulate) *dst = 0.f;
+      continue;
+    }
+    const float* x = p.chunk_lse2 + ((int64_t)b * p.ws_max_chunks + c) * stride;
+    float acc = 0.f;
+    int r = 0;
+    if (vec) {
+      const int nv = rows >> 2;
+      for (int i = tid; i < nv; i += 256) {
+        const float4 a = *reinterpret_cast<const float4*>(x + 4 * i);
+        const float4 m = *reinterpret_cast<const float4*>(l2 + 4 * i);
+        acc += (__builtin_amdgcn_exp2f(a.x - m.x) + __builtin_amdgcn_exp2f(a.y - m.y)) +
+               (__builtin_amdgcn_exp2f(a.z - m.z) + __builtin_amdgcn_exp2f(a.w - m.w));
+      }
+      r = nv << 2;
+    }
+    for (int i = r + tid; i < rows; i += 256) acc += __builtin_amdgcn_exp2f(x[i] - l2[i]);
 #pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off);
-  if (lane == 0) p.partial[((int64_t)b * p.row_splits + rs) * p.ws_max_chunks + c] = acc;
-}
-
-__global__ __launch_bounds__(256) void salience_finalize_kernel(SalienceParams p) {
-  const int c = blockIdx.x * 256 + threadIdx.x;
-  const int b = blockIdx.y;
-  if (c >= p.max_chunks) return;
-  int N, L;
-  seq_bounds(p, b, &N, &L);
-  const int nch = (L + p.chunk_size - 1) / p.chunk_size;
-  float* dst = p.chunk_mass + (int64_t)b * p.max_chunks + c;
-  if (c >= nch || N == 0) {
-    if (!p.accumulate) *dst = 0.f;
-    return;
+    for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off);
+    if (lane == 0) red[w] = acc;
+    __syncthreads();
+    if (tid == 0) {
+      const float tot = ((red[0] + red[1]) + (red[2] + red[3])) * (1.0f / (float)rows);
+      *dst = p.accumulate ? *dst + tot : tot;
+    }
+    __syncthreads();
   }
-  const int rows = N * p.Hq;
-  const int nrs = (rows + kRowsPerSplit - 1) / kRowsPerSplit;
-  float tot = 0.f;
-  for (int rs = 0; rs < nrs; ++rs) tot += p.partial[((int64_t)b * p.row_splits + rs) * p.ws_max_chunks + c];
-  tot *= 1.0f / (float)rows;
-  *dst = p.accumulate ? *dst + tot : tot;
 }
 
 __global__ __launch_bounds__(1024) void topk_kernel(SalienceParams p) {
@@ -120,21 +127,10 @@ __global__ __launch_bounds__(1024) void topk_kernel(SalienceParams p) {
 
 }  // namespace
 
-size_t salience_partial_bytes(int batch, int max_nodes, int Hq, int ws_max_chunks) {
-  const int64_t row_splits = ceil_div((int64_t)max_nodes * Hq, kRowsPerSplit);
-  return sizeof(float) * (size_t)batch * row_splits * ws_max_chunks;
-}
-
-hipError_t launch_chunk_salience(const SalienceParams& pin, hipStream_t s) {
-  SalienceParams p = pin;
-  p.row_splits = (int)ceil_div((int64_t)p.max_nodes * p.Hq, kRowsPerSplit);
-  hipLaunchKernelGGL(salience_partial_kernel, dim3((unsigned)ceil_div(p.ws_max_chunks, 4), p.row_splits, p.batch),
-                     dim3(256), 0, s, p);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(salience_finalize_kernel, dim3((unsigned)ceil_div(p.max_chunks, 256), p.batch), dim3(256), 0, s,
+hipError_t launch_chunk_salience(const SalienceParams& p, hipStream_t s) {
+  hipLaunchKernelGGL(salience_kernel, dim3((unsigned)ceil_div(p.max_chunks, kChunksPerWG), p.batch), dim3(256), 0, s,
                      p);
-  e = hipGetLastError();
+  hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.top_k <= 0) return e;
   hipLaunchKernelGGL(topk_kernel, dim3(p.batch), dim3(1024), 0, s, p);
   return hipGetLastError();

@@ -75,8 +75,6 @@ struct SalienceParams {
   int ws_max_chunks;     // chunk stride of the attention workspace
   const float* chunk_lse2;
   const float* lse2;
-  float* partial;        // [batch][row_splits][ws_max_chunks]
-  int row_splits;
   float* chunk_mass;     // [batch][max_chunks]
   int max_chunks;
   int accumulate;
@@ -84,8 +82,6 @@ struct SalienceParams {
   int32_t* topk_index;
   float* topk_mass;
 };
-constexpr int kSalienceRowsPerWG = 256;
-size_t salience_partial_bytes(int batch, int max_nodes, int Hq, int ws_max_chunks);
 hipError_t launch_chunk_salience(const SalienceParams& p, hipStream_t s);
 
 // ------------------------------------------------------------------------------------------
