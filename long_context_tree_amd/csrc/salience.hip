@@ -77,6 +77,84 @@ __global__ __launch_bounds__(256) void salience_kernel(SalienceParams p) {
   }
 }
 
+__device__ __forceinline__ unsigned long long shfl_xor_u64(unsigned long long v, int m) {
+  const uint32_t lo = __shfl_xor((uint32_t)v, m), hi = __shfl_xor((uint32_t)(v >> 32), m);
+  return ((unsigned long long)hi << 32) | lo;
+}
+
+// Top-k for up to 2048 chunks: a bitonic sort of 2048 keys held in registers, two adjacent keys per
+// thread (elements 2t and 2t+1 in thread t).  Stride 1 compares within a thread, strides 2..64 exchange
+// with the partner thread t ^ (j/2) of the same wave by shuffles, and only strides >= 128 go through LDS.
+__global__ __launch_bounds__(1024) void topk2048_kernel(SalienceParams p) {
+  __shared__ unsigned long long keys[2048];
+  const int b = blockIdx.x;
+  const int t = threadIdx.x;
+  int N, L;
+  seq_bounds(p, b, &N, &L);
+  int nch = (L + p.chunk_size - 1) / p.chunk_size;
+  if (nch > p.max_chunks) nch = p.max_chunks;
+  const float* mass = p.chunk_mass + (int64_t)b * p.max_chunks;
+  unsigned long long e[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int i = 2 * t + h;
+    e[h] = ~0ull;
+    if (i < nch) {
+      const uint32_t bits = __float_as_uint(mass[i]) & 0x7FFFFFFFu;   // masses are >= 0; drop a -0 sign
+      e[h] = ((unsigned long long)(~bits) << 32) | (uint32_t)i;
+    }
+  }
+  for (int k = 2; k <= 2048; k <<= 1) {
+    const bool up = ((2 * t) & k) == 0;             // the same for both elements of the thread (k >= 2)
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      if (j == 1) {
+        const bool sw = (e[0] > e[1]) == up;
+        const unsigned long long lo = sw ? e[1] : e[0], hi = sw ? e[0] : e[1];
+        e[0] = lo;
+        e[1] = hi;
+        continue;
+      }
+      unsigned long long q[2];
+      if (j < 128) {
+        q[0] = shfl_xor_u64(e[0], j >> 1);
+        q[1] = shfl_xor_u64(e[1], j >> 1);
+      } else {
+        __syncthreads();                              // earlier LDS reads are done
+        keys[2 * t] = e[0];
+        keys[2 * t + 1] = e[1];
+        __syncthreads();
+        q[0] = keys[(2 * t) ^ j];
+        q[1] = keys[(2 * t + 1) ^ j];
+      }
+      const bool lower = (t & (j >> 1)) == 0;        // this thread holds the lower index of each pair
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const unsigned long long mn = e[h] < q[h] ? e[h] : q[h], mx = e[h] < q[h] ? q[h] : e[h];
+        e[h] = (lower == up) ? mn : mx;
+      }
+    }
+  }
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int i = 2 * t + h;
+    if (i < p.top_k) {
+      int32_t idx = -1;
+      float m = 0.f;
+      if (i < nch) {
+        idx = (int32_t)(e[h] & 0xFFFFFFFFu);
+        m = __uint_as_float(~(uint32_t)(e[h] >> 32));
+      }
+      p.topk_index[(int64_t)b * p.top_k + i] = idx;
+      p.topk_mass[(int64_t)b * p.top_k + i] = m;
+    }
+  }
+  for (int i = 2048 + t; i < p.top_k; i += 1024) {   // k above the chunk count: padding only
+    p.topk_index[(int64_t)b * p.top_k + i] = -1;
+    p.topk_mass[(int64_t)b * p.top_k + i] = 0.f;
+  }
+}
+
+// Top-k for more chunks (up to 8192): the same sort through LDS.
 __global__ __launch_bounds__(1024) void topk_kernel(SalienceParams p) {
   __shared__ unsigned long long keys[kMaxTopK];
   const int b = blockIdx.x;
@@ -96,9 +174,16 @@ __global__ __launch_bounds__(1024) void topk_kernel(SalienceParams p) {
       keys[i] = ~0ull;
     }
   }
-  __syncthreads();
+  // Element i belongs to thread i mod 1024, so for strides j < 64 both elements of a pair belong to
+  // one wave, whose LDS operations complete in order: those stages need no work-group barrier.
   for (int k = 2; k <= n; k <<= 1) {
     for (int j = k >> 1; j > 0; j >>= 1) {
+      if (j >= 64) {
+        __syncthreads();
+      } else {
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        __builtin_amdgcn_wave_barrier();
+      }
       for (int i = tid; i < n; i += 1024) {
         const int ixj = i ^ j;
         if (ixj > i) {
@@ -110,9 +195,9 @@ __global__ __launch_bounds__(1024) void topk_kernel(SalienceParams p) {
           }
         }
       }
-      __syncthreads();
     }
   }
+  __syncthreads();
   for (int i = tid; i < p.top_k; i += 1024) {
     int32_t idx = -1;
     float m = 0.f;
@@ -132,7 +217,8 @@ hipError_t launch_chunk_salience(const SalienceParams& p, hipStream_t s) {
                      p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.top_k <= 0) return e;
-  hipLaunchKernelGGL(topk_kernel, dim3(p.batch), dim3(1024), 0, s, p);
+  if (p.max_chunks <= 2048) hipLaunchKernelGGL(topk2048_kernel, dim3(p.batch), dim3(1024), 0, s, p);
+  else hipLaunchKernelGGL(topk_kernel, dim3(p.batch), dim3(1024), 0, s, p);
   return hipGetLastError();
 }
 
