@@ -275,6 +275,16 @@ def main():
     kernels["spec_accept_greedy"] = {"median_us": round(us, 2), "alg_bytes": g_bytes,
                                      "gbs": round(g_bytes / us / 1e3, 1), "bound": "hbm",
                                      "note": f"{N} nodes, vocab {V}, bf16 logits"}
+    # the commit of the step's greedy path into all 32 layers' caches (new lengths to a scratch buffer)
+    ca, ckeep = spec.kv_commit_args([pl[0] for pl in pools], [pl[1] for pl in pools], bt, cl, gouts[0], gouts[1],
+                                    max_nodes=N, new_ctx_lens=torch.empty_like(cl), v_layout=v_layout)
+    n_acc = int(gouts[0][0])
+    c_bytes = max(n_acc, 0) * layers * Hkv * D * 2 * 2 * 2
+    us = time_call(lambda: call(L_.spec_kv_commit(ctypes.byref(ca), sh)))
+    kernels["spec_kv_commit"] = {"median_us": round(us, 2), "alg_bytes": c_bytes,
+                                 "gbs": round(c_bytes / us / 1e3, 1), "bound": "latency",
+                                 "note": f"{n_acc} accepted drafts moved in {layers} layers x {Hkv} KV heads "
+                                         "(K and V, read and write)"}
     rtree = synth.random_tree(synth.rng_for(3, 0, synth.S_TREE), 64, 8)
     rc = synth.rejection_case(3, [rtree], V, dtype="bf16", draft="independent")
     rt = sdev.rejection_tensors(rc, dev)

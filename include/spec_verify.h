@@ -9,6 +9,8 @@
  *                          chunk, optionally accumulated over layers, with top-k chunk selection
  *   spec_accept_greedy     greedy longest-accepted-path acceptance
  *   spec_accept_rejection  exact rejection-sampling acceptance against the draft distribution
+ *   spec_kv_commit         moves the accepted path's K/V next to the committed context and
+ *                          advances the per-sequence lengths (the per-row rollback)
  *
  * Sources (web pages cited by title and section):
  *   [DS]  "DiffSpec: Accelerating Long Sequence Generation with Differential Speculative Decoding"
@@ -242,6 +244,53 @@ typedef struct spec_accept_rejection_args {
 
 size_t spec_accept_rejection_workspace_size(const spec_accept_rejection_args* args);
 int spec_accept_rejection(const spec_accept_rejection_args* args, void* stream);
+
+/* ------------------------------------------------------------------------------------------
+ * spec_kv_commit  [AS "Layout": a per-row length and a cache mask turn rollback into a length
+ * update; AS "The controller": k drafts yield up to k + 1 tokens]
+ *
+ * The step after acceptance.  The verification forward wrote node i's K/V at slot ctx_lens[b] + i;
+ * the accepted path (path_nodes[b][0] = root, then num_accepted[b] drafts, as returned by
+ * spec_accept_greedy / spec_accept_rejection) is moved so that the committed tokens are
+ * contiguous: for i = 1 .. num_accepted[b], in every layer and KV head, K and V of slot
+ * ctx_lens[b] + path_nodes[b][i] are copied to slot ctx_lens[b] + i (through the block table; the
+ * root already sits at ctx_lens[b]).  new_ctx_lens[b] = ctx_lens[b] + 1 + num_accepted[b].  Slots
+ * past the new length keep stale values that no later call reads (attention reads only slots
+ * below ctx_len plus the current tree's own slots).  The bonus token has no K/V yet: it is the
+ * root of the next verification, at slot new_ctx_lens[b].
+ * A sequence with num_accepted[b] < 0 (a path that did not fit max_path) is left untouched and
+ * keeps its length.  Copies are exact (bytes).
+ *
+ * Device preconditions: path_nodes[b][i] is a node of sequence b at depth i (so i <= node <
+ * max_nodes); entries that are not are skipped.  ctx_lens[b] + max_nodes slots are mapped by the
+ * block table.
+ * ------------------------------------------------------------------------------------------ */
+#define SPEC_MAX_COMMIT_LAYERS 128
+
+typedef struct spec_kv_commit_args {
+  int32_t batch;                /* >= 1 */
+  int32_t num_layers;           /* 1 .. SPEC_MAX_COMMIT_LAYERS */
+  int32_t num_kv_heads;         /* >= 1 */
+  int32_t head_dim;             /* 64 or 128 */
+  int32_t max_nodes;            /* (host) bound on tree nodes per sequence, 1..256 */
+  int32_t max_path;             /* row stride of path_nodes, >= 1 */
+  const void* const* k_caches;  /* (host) [num_layers] device pointers (bf16, 16-byte aligned) */
+  const void* const* v_caches;  /* (host) [num_layers] device pointers (bf16, 16-byte aligned) */
+  int64_t page_stride;          /* elements, shared by every layer (as in spec_paged_kv) */
+  int64_t head_stride;
+  int64_t token_stride;
+  int32_t page_size;            /* a power of two in [8, 1024] */
+  int32_t num_pages;            /* (host) pages in each layer's pool */
+  const int32_t* block_table;   /* int32 [batch][block_table_stride] */
+  int32_t block_table_stride;
+  int32_t v_layout;             /* spec_v_layout */
+  const int32_t* ctx_lens;      /* int32 [batch] */
+  const int32_t* num_accepted;  /* int32 [batch] */
+  const int32_t* path_nodes;    /* int32 [batch][max_path] */
+  int32_t* new_ctx_lens;        /* int32 [batch] out; may be ctx_lens itself */
+} spec_kv_commit_args;
+
+int spec_kv_commit(const spec_kv_commit_args* args, void* stream);
 
 #ifdef __cplusplus
 }

@@ -5,7 +5,8 @@ per-chunk attention mass with top-k selection, and greedy / rejection-sampling a
 """
 
 from .spec import (V_DIM_MAJOR, V_TOKEN_ROWS, AttentionHandle, SpecError, accept_greedy, accept_rejection,
-                   chunk_salience, last_error, lib, status_string, tree_attention, tree_attention_args)
+                   chunk_salience, kv_commit, last_error, lib, status_string, tree_attention, tree_attention_args)
 
 __all__ = ["V_DIM_MAJOR", "V_TOKEN_ROWS", "AttentionHandle", "SpecError", "accept_greedy", "accept_rejection",
-           "chunk_salience", "last_error", "lib", "status_string", "tree_attention", "tree_attention_args"]
+           "chunk_salience", "kv_commit", "last_error", "lib", "status_string", "tree_attention",
+           "tree_attention_args"]

@@ -373,3 +373,86 @@ int spec_accept_rejection(const spec_accept_rejection_args* args, void* stream) 
 }
 
 }  // extern "C"
+
+// ---------------------------------------------------------------------------------------------
+// spec_kv_commit
+// ---------------------------------------------------------------------------------------------
+namespace {
+
+int check_commit(const spec_kv_commit_args* a) {
+  if (!a) return fail(SPEC_ERR_INVALID_ARGUMENT, "args: NULL");
+  if (a->batch < 1) return fail(SPEC_ERR_INVALID_ARGUMENT, "batch: %d, must be >= 1", a->batch);
+  if (a->num_layers < 1 || a->num_layers > SPEC_MAX_COMMIT_LAYERS)
+    return fail(SPEC_ERR_UNSUPPORTED, "num_layers: %d, supported range is 1..%d", a->num_layers,
+                SPEC_MAX_COMMIT_LAYERS);
+  if (a->num_kv_heads < 1) return fail(SPEC_ERR_INVALID_ARGUMENT, "num_kv_heads: %d, must be >= 1", a->num_kv_heads);
+  if (a->head_dim != 64 && a->head_dim != 128)
+    return fail(SPEC_ERR_UNSUPPORTED, "head_dim: %d, supported values are 64 and 128", a->head_dim);
+  if (a->max_nodes < 1 || a->max_nodes > spec::kMaxNodes)
+    return fail(SPEC_ERR_UNSUPPORTED, "max_nodes: %d, supported range is 1..%d", a->max_nodes, spec::kMaxNodes);
+  if (a->max_path < 1) return fail(SPEC_ERR_INVALID_ARGUMENT, "max_path: %d, must be >= 1", a->max_path);
+  if ((int64_t)a->batch * a->max_path > (1LL << 30) || (int64_t)a->batch > 65535)
+    return fail(SPEC_ERR_UNSUPPORTED, "batch: %d, too large (limit 65535 sequences per call)", a->batch);
+  if (!a->k_caches || !a->v_caches) return fail(SPEC_ERR_INVALID_ARGUMENT, "k_caches / v_caches: NULL");
+  for (int l = 0; l < a->num_layers; ++l) {
+    if (!a->k_caches[l] || !aligned(a->k_caches[l], 16))
+      return fail(SPEC_ERR_INVALID_ARGUMENT, "k_caches[%d]: NULL or not 16-byte aligned", l);
+    if (!a->v_caches[l] || !aligned(a->v_caches[l], 16))
+      return fail(SPEC_ERR_INVALID_ARGUMENT, "v_caches[%d]: NULL or not 16-byte aligned", l);
+  }
+  if (a->page_stride <= 0 || a->page_stride % 8)
+    return fail(SPEC_ERR_INVALID_ARGUMENT, "page_stride: %lld, must be a positive multiple of 8",
+                (long long)a->page_stride);
+  if (a->head_stride < 0 || a->head_stride % 8)
+    return fail(SPEC_ERR_INVALID_ARGUMENT, "head_stride: %lld, must be a non-negative multiple of 8",
+                (long long)a->head_stride);
+  if (a->token_stride < a->head_dim || a->token_stride % 8)
+    return fail(SPEC_ERR_INVALID_ARGUMENT, "token_stride: %lld, must be a multiple of 8 and >= head_dim (%d)",
+                (long long)a->token_stride, a->head_dim);
+  if (!pow2(a->page_size) || a->page_size < 8 || a->page_size > 1024)
+    return fail(SPEC_ERR_UNSUPPORTED, "page_size: %d, must be a power of two in 8..1024", a->page_size);
+  if (a->num_pages < 1) return fail(SPEC_ERR_INVALID_ARGUMENT, "num_pages: %d, must be >= 1", a->num_pages);
+  if (!a->block_table) return fail(SPEC_ERR_INVALID_ARGUMENT, "block_table: NULL");
+  if (a->block_table_stride < 1)
+    return fail(SPEC_ERR_INVALID_ARGUMENT, "block_table_stride: %d, must be >= 1", a->block_table_stride);
+  if (a->v_layout != SPEC_V_TOKEN_ROWS && a->v_layout != SPEC_V_DIM_MAJOR)
+    return fail(SPEC_ERR_INVALID_ARGUMENT, "v_layout: %d, must be SPEC_V_TOKEN_ROWS (0) or SPEC_V_DIM_MAJOR (1)",
+                a->v_layout);
+  if (!a->ctx_lens) return fail(SPEC_ERR_INVALID_ARGUMENT, "ctx_lens: NULL");
+  if (!a->num_accepted) return fail(SPEC_ERR_INVALID_ARGUMENT, "num_accepted: NULL");
+  if (!a->path_nodes) return fail(SPEC_ERR_INVALID_ARGUMENT, "path_nodes: NULL");
+  if (!a->new_ctx_lens) return fail(SPEC_ERR_INVALID_ARGUMENT, "new_ctx_lens: NULL");
+  return SPEC_OK;
+}
+
+}  // namespace
+
+extern "C" int spec_kv_commit(const spec_kv_commit_args* a, void* stream) {
+  const int st = check_commit(a);
+  if (st != SPEC_OK) return st;
+  spec::KvCommitParams p{};
+  for (int l = 0; l < a->num_layers; ++l) {
+    p.k[l] = const_cast<void*>(a->k_caches[l]);
+    p.v[l] = const_cast<void*>(a->v_caches[l]);
+  }
+  p.batch = a->batch;
+  p.num_layers = a->num_layers;
+  p.Hkv = a->num_kv_heads;
+  p.max_nodes = a->max_nodes;
+  p.max_path = a->max_path;
+  p.page_stride = a->page_stride;
+  p.head_stride = a->head_stride;
+  p.token_stride = a->token_stride;
+  p.page_shift = log2i(a->page_size);
+  p.num_pages = a->num_pages;
+  p.v_dim_major = a->v_layout == SPEC_V_DIM_MAJOR ? 1 : 0;
+  p.block_table = a->block_table;
+  p.bt_stride = a->block_table_stride;
+  p.ctx_lens = a->ctx_lens;
+  p.num_accepted = a->num_accepted;
+  p.path_nodes = a->path_nodes;
+  p.new_ctx_lens = a->new_ctx_lens;
+  const hipError_t e = spec::launch_kv_commit(p, a->head_dim, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "spec_kv_commit launch");
+  return ok();
+}

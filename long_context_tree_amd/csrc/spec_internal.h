@@ -111,6 +111,24 @@ struct AcceptParams {
 size_t greedy_ws_bytes(int batch, int max_nodes, int nseg);
 size_t rejection_ws_bytes(int batch, int max_nodes, int nseg, int nsegr, int max_children);
 hipError_t launch_accept_greedy(const AcceptParams& p, hipStream_t s);
+
+// ------------------------------------------------------------------------------------------
+// KV commit
+// ------------------------------------------------------------------------------------------
+struct KvCommitParams {
+  void* k[SPEC_MAX_COMMIT_LAYERS];
+  void* v[SPEC_MAX_COMMIT_LAYERS];
+  int batch, num_layers, Hkv, max_nodes, max_path;
+  int64_t page_stride, head_stride, token_stride;
+  int page_shift, num_pages, v_dim_major;
+  const int32_t* block_table;
+  int bt_stride;
+  const int32_t* ctx_lens;
+  const int32_t* num_accepted;
+  const int32_t* path_nodes;
+  int32_t* new_ctx_lens;
+};
+hipError_t launch_kv_commit(const KvCommitParams& p, int head_dim, hipStream_t s);
 hipError_t launch_accept_rejection(const AcceptParams& p, hipStream_t s);
 
 }  // namespace spec

@@ -44,7 +44,8 @@ def lib():
         L.spec_status_string.argtypes = [ctypes.c_int]
         L.spec_last_error.restype = ctypes.c_char_p
         for name, argt in (("spec_tree_attention", TreeAttentionArgs), ("spec_chunk_salience", ChunkSalienceArgs),
-                           ("spec_accept_greedy", AcceptGreedyArgs), ("spec_accept_rejection", AcceptRejectionArgs)):
+                           ("spec_accept_greedy", AcceptGreedyArgs), ("spec_accept_rejection", AcceptRejectionArgs),
+                           ("spec_kv_commit", KvCommitArgs)):
             f = getattr(L, name)
             f.restype = ctypes.c_int
             f.argtypes = [ctypes.POINTER(argt), ctypes.c_void_p]
@@ -102,6 +103,18 @@ class AcceptGreedyArgs(ctypes.Structure):
                 ("logits_dtype", ctypes.c_int32), ("out_num_accepted", ctypes.c_void_p),
                 ("out_path_nodes", ctypes.c_void_p), ("out_tokens", ctypes.c_void_p),
                 ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t)]
+
+
+class KvCommitArgs(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("num_layers", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("max_nodes", ctypes.c_int32), ("max_path", ctypes.c_int32),
+                ("k_caches", ctypes.POINTER(ctypes.c_void_p)), ("v_caches", ctypes.POINTER(ctypes.c_void_p)),
+                ("page_stride", ctypes.c_int64), ("head_stride", ctypes.c_int64), ("token_stride", ctypes.c_int64),
+                ("page_size", ctypes.c_int32), ("num_pages", ctypes.c_int32),
+                ("block_table", ctypes.c_void_p), ("block_table_stride", ctypes.c_int32),
+                ("v_layout", ctypes.c_int32),
+                ("ctx_lens", ctypes.c_void_p), ("num_accepted", ctypes.c_void_p), ("path_nodes", ctypes.c_void_p),
+                ("new_ctx_lens", ctypes.c_void_p)]
 
 
 class AcceptRejectionArgs(ctypes.Structure):
@@ -332,3 +345,65 @@ def accept_rejection(node_offsets, parents, draft_tokens, target_logits, draft_p
     r.base.workspace, r.base.workspace_bytes = ws.data_ptr(), ws.numel()
     _check(lib().spec_accept_rejection(ctypes.byref(r), _stream(stream)), "spec_accept_rejection")
     return outs
+
+
+def kv_commit_args(k_caches, v_caches, block_table, ctx_lens, num_accepted, path_nodes, *, max_nodes: int,
+                   new_ctx_lens, v_layout: int = V_TOKEN_ROWS):
+    """Fill the C argument struct (no launch).  k_caches / v_caches: one tensor per layer, laid out as
+    for tree_attention (all layers share the strides).  Returns (args, objects to keep alive)."""
+    n_layers = len(k_caches)
+    kp = (ctypes.c_void_p * n_layers)(*[t.data_ptr() for t in k_caches])
+    vp = (ctypes.c_void_p * n_layers)(*[t.data_ptr() for t in v_caches])
+    k0 = k_caches[0]
+    a = KvCommitArgs()
+    a.batch = ctx_lens.numel()
+    a.num_layers = n_layers
+    a.num_kv_heads = k0.shape[1]
+    a.head_dim = k0.shape[3]
+    a.max_nodes = max_nodes
+    a.max_path = path_nodes.shape[1]
+    a.k_caches = ctypes.cast(kp, ctypes.POINTER(ctypes.c_void_p))
+    a.v_caches = ctypes.cast(vp, ctypes.POINTER(ctypes.c_void_p))
+    a.page_stride, a.head_stride, a.token_stride = k0.stride(0), k0.stride(1), k0.stride(2)
+    a.page_size = k0.shape[2]
+    a.num_pages = k0.shape[0]
+    a.block_table = _ptr(block_table)
+    a.block_table_stride = block_table.shape[1]
+    a.v_layout = v_layout
+    a.ctx_lens, a.num_accepted, a.path_nodes = _ptr(ctx_lens), _ptr(num_accepted), _ptr(path_nodes)
+    a.new_ctx_lens = _ptr(new_ctx_lens)
+    return a, (kp, vp)
+
+
+def kv_commit(k_caches, v_caches, block_table, ctx_lens, num_accepted, path_nodes, *, max_nodes: int,
+              v_layout: int = V_TOKEN_ROWS, new_ctx_lens=None, stream=None):
+    """Move each sequence's accepted path (path_nodes / num_accepted from accept_greedy or
+    accept_rejection) next to its committed context in every layer's cache, in place, and return the
+    new lengths (int32 [batch]; pass new_ctx_lens=ctx_lens to update in place)."""
+    for name, t in (("block_table", block_table), ("ctx_lens", ctx_lens), ("num_accepted", num_accepted),
+                    ("path_nodes", path_nodes)):
+        _need(t, name, torch.int32)
+    if len(k_caches) != len(v_caches) or not k_caches:
+        raise ValueError("k_caches and v_caches: one tensor per layer, the same number of each")
+    for t in list(k_caches) + list(v_caches):
+        _need(t, "k_caches / v_caches", torch.bfloat16, contiguous=False)
+    k0 = k_caches[0]
+    for t in k_caches:
+        if t.shape != k0.shape or t.stride() != k0.stride():
+            raise ValueError("every layer's k cache must have the same shape and strides")
+    for t in v_caches:
+        if v_layout == V_TOKEN_ROWS and (t.shape != k0.shape or t.stride() != k0.stride()):
+            raise ValueError("token-row v caches must have k's shape and strides")
+        if v_layout == V_DIM_MAJOR:
+            P, H, S, D_ = k0.shape
+            if tuple(t.shape) != (P, H, D_, S) or t.stride()[:2] != k0.stride()[:2] or t.stride(2) != S \
+                    or t.stride(3) != 1:
+                raise ValueError("dim-major v caches must be [pages][kv_heads][head_dim][page_size] with k's page "
+                                 "and head strides")
+    if new_ctx_lens is None:
+        new_ctx_lens = torch.empty_like(ctx_lens)
+    a, keep = kv_commit_args(k_caches, v_caches, block_table, ctx_lens, num_accepted, path_nodes,
+                             max_nodes=max_nodes, new_ctx_lens=new_ctx_lens, v_layout=v_layout)
+    _check(lib().spec_kv_commit(ctypes.byref(a), _stream(stream)), "spec_kv_commit")
+    del keep
+    return new_ctx_lens

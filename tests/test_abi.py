@@ -29,7 +29,7 @@ def test_exports_every_declared_symbol():
     spec = _lib()
     names = declared_functions()
     assert {"spec_tree_attention", "spec_chunk_salience", "spec_accept_greedy", "spec_accept_rejection"} <= set(names)
-    assert len(names) == 10, names
+    assert len(names) == 11, names
     L = ctypes.CDLL(spec.LIB_PATH)
     for n in names:
         assert hasattr(L, n), n
@@ -156,3 +156,36 @@ def test_rejection_refuses_bad_arguments():
     assert spec.lib().spec_accept_rejection(ctypes.byref(r), None) == 1 and "draft_probs" in spec.last_error()
     r.base.vocab = -1
     assert spec.lib().spec_accept_rejection(ctypes.byref(r), None) == 1 and "base.vocab" in spec.last_error()
+
+
+def _commit_args(spec, **over):
+    k = [torch.zeros(40, 2, 16, 64, dtype=torch.bfloat16) for _ in range(2)]
+    bt = torch.zeros(1, 40, dtype=torch.int32)
+    cl = torch.tensor([100], dtype=torch.int32)
+    na = torch.tensor([2], dtype=torch.int32)
+    pn = torch.tensor([[0, 1, 3, -1]], dtype=torch.int32)
+    out = torch.empty_like(cl)
+    a, keep = spec.kv_commit_args(k, k, bt, cl, na, pn, max_nodes=8, new_ctx_lens=out)
+    for key, v in over.items():
+        setattr(a, key, v)
+    return a, (keep, k, bt, cl, na, pn, out)
+
+
+@pytest.mark.parametrize("field,value,status,text", [
+    ("batch", 0, 1, "batch"),
+    ("num_layers", 0, 2, "num_layers"),
+    ("num_layers", 129, 2, "num_layers"),
+    ("head_dim", 96, 2, "head_dim"),
+    ("max_nodes", 257, 2, "max_nodes"),
+    ("max_path", 0, 1, "max_path"),
+    ("page_size", 12, 2, "page_size"),
+    ("token_stride", 60, 1, "token_stride"),
+    ("v_layout", 2, 1, "v_layout"),
+    ("ctx_lens", None, 1, "ctx_lens"),
+    ("new_ctx_lens", None, 1, "new_ctx_lens"),
+])
+def test_kv_commit_refuses_bad_arguments(field, value, status, text):
+    spec = _lib()
+    a, keep = _commit_args(spec, **{field: value})
+    st = spec.lib().spec_kv_commit(ctypes.byref(a), None)
+    assert st == status and text in spec.last_error(), (st, spec.last_error())
