@@ -11,6 +11,8 @@
  *   spec_accept_rejection  exact rejection-sampling acceptance against the draft distribution
  *   spec_kv_commit         moves the accepted path's K/V next to the committed context and
  *                          advances the per-sequence lengths (the per-row rollback)
+ *   spec_controller_*      host-side choice of the next draft depth from the online acceptance
+ *                          rate and cost ratio
  *
  * Sources (web pages cited by title and section):
  *   [DS]  "DiffSpec: Accelerating Long Sequence Generation with Differential Speculative Decoding"
@@ -291,6 +293,43 @@ typedef struct spec_kv_commit_args {
 } spec_kv_commit_args;
 
 int spec_kv_commit(const spec_kv_commit_args* args, void* stream);
+
+/* ------------------------------------------------------------------------------------------
+ * Draft-depth controller (host code, no GPU)  [AS "The controller"; DS "Configuration": long-
+ * context threshold and initial depth; DS "Architecture": adaptive verification starts long
+ * contexts shallow]
+ *
+ * With acceptance rate a per drafted token and cost ratio c = t_draft / t_target, a round that
+ * drafts k tokens yields (1 - a^(k+1)) / (1 - a) tokens (k + 1 when a = 1) and costs
+ * (k + 1) * c + 1 target forwards.  spec_controller_choose returns the k in [1, k_max] with the
+ * largest ratio (the smallest such k on ties).  a is an exponentially weighted mean decayed per
+ * observed token: in a round that drafted k and accepted n, the n accepted drafts are 1s and, if
+ * n < k, the first rejected draft is a 0 (later drafts were never tested).  c is an exponentially
+ * weighted mean per round of the measured draft/target time ratio.  A sequence whose context is
+ * at least long_ctx_threshold starts at depth long_ctx_depth (later rounds use the closed form).
+ * All functions return SPEC_OK or SPEC_ERR_INVALID_ARGUMENT (naming the argument).
+ * ------------------------------------------------------------------------------------------ */
+typedef struct spec_depth_controller {
+  double alpha;                 /* current estimate of the acceptance rate, in [0, 1] */
+  double cost_ratio;            /* current estimate of c = t_draft / t_target, > 0 */
+  double alpha_decay;           /* weight of one new token observation, in (0, 1] */
+  double cost_decay;            /* weight of one new round's cost ratio, in (0, 1] */
+  int32_t k_max;                /* >= 1 */
+  int32_t k;                    /* depth for the next round */
+  int64_t rounds;               /* rounds observed */
+} spec_depth_controller;
+
+int spec_controller_init(spec_depth_controller* ctl, int32_t k_max, double alpha0, double cost_ratio0,
+                         double alpha_decay, double cost_decay, int64_t ctx_len, int64_t long_ctx_threshold,
+                         int32_t long_ctx_depth);
+/* expected tokens per target forward for depth k: ((1 - a^(k+1)) / (1 - a)) / ((k + 1) c + 1) */
+double spec_controller_speedup(double alpha, double cost_ratio, int32_t k);
+/* (host) the k in [1, k_max] maximising spec_controller_speedup (smallest on ties); 0 on bad input */
+int32_t spec_controller_choose(double alpha, double cost_ratio, int32_t k_max);
+/* one verified round: k drafted, n accepted (0 <= n <= k), measured draft and target times
+ * (t_target > 0; t_draft >= 0, 0 keeps the cost estimate); updates alpha, cost_ratio and k */
+int spec_controller_update(spec_depth_controller* ctl, int32_t drafted, int32_t accepted, double t_draft,
+                           double t_target);
 
 #ifdef __cplusplus
 }

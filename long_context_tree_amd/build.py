@@ -2,7 +2,8 @@
 
     python -m long_context_tree_amd.build
 
-Every source under csrc/ is compiled with hipcc for gfx950 only, then linked into
+Every source under csrc/ (HIP kernels in .hip files, host-only code in .cpp files) is compiled
+with hipcc for gfx950 only, then linked into
 long_context_tree_amd/libspec_verify.so next to the Python binding.
 """
 
@@ -43,8 +44,8 @@ PER_FILE = {"tree_attention.hip": ["-fno-honor-nans"]}
 def build(verbose: bool = False) -> str:
     hipcc = _hipcc()
     os.makedirs(BUILD, exist_ok=True)
-    srcs = sorted(f for f in os.listdir(CSRC) if f.endswith(".hip"))
-    objs = [os.path.join(BUILD, s[:-4] + ".o") for s in srcs]
+    srcs = sorted(f for f in os.listdir(CSRC) if f.endswith((".hip", ".cpp")))   # .cpp: host code only
+    objs = [os.path.join(BUILD, os.path.splitext(s)[0] + ".o") for s in srcs]
 
     def compile_one(src, obj):
         extra = PER_FILE.get(src, [])

@@ -35,6 +35,22 @@ int hip_fail(hipError_t e, const char* what) {
   return fail(SPEC_ERR_HIP, "%s: HIP error %d (%s)", what, (int)e, hipGetErrorString(e));
 }
 
+}  // namespace
+
+namespace spec {
+// status and thread-local message for the controller functions (nullptr: success)
+int controller_fail(const char* what) {
+  if (!what) {
+    g_err.clear();
+    return SPEC_OK;
+  }
+  g_err = what;
+  return SPEC_ERR_INVALID_ARGUMENT;
+}
+}  // namespace spec
+
+namespace {
+
 constexpr int kPlanCUs = 256;   // MI355X compute units; the plan is a pure function of the arguments
 
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }

@@ -55,6 +55,17 @@ def lib():
             f = getattr(L, name)
             f.restype = ctypes.c_size_t
             f.argtypes = [ctypes.POINTER(argt)]
+        L.spec_controller_speedup.restype = ctypes.c_double
+        L.spec_controller_speedup.argtypes = [ctypes.c_double, ctypes.c_double, ctypes.c_int32]
+        L.spec_controller_choose.restype = ctypes.c_int32
+        L.spec_controller_choose.argtypes = [ctypes.c_double, ctypes.c_double, ctypes.c_int32]
+        L.spec_controller_init.restype = ctypes.c_int
+        L.spec_controller_init.argtypes = [ctypes.POINTER(DepthControllerState), ctypes.c_int32, ctypes.c_double,
+                                           ctypes.c_double, ctypes.c_double, ctypes.c_double, ctypes.c_int64,
+                                           ctypes.c_int64, ctypes.c_int32]
+        L.spec_controller_update.restype = ctypes.c_int
+        L.spec_controller_update.argtypes = [ctypes.POINTER(DepthControllerState), ctypes.c_int32, ctypes.c_int32,
+                                             ctypes.c_double, ctypes.c_double]
         if L.spec_abi_version() != ABI_VERSION:
             raise RuntimeError(f"libspec_verify ABI {L.spec_abi_version()} != binding ABI {ABI_VERSION}")
         _lib = L
@@ -115,6 +126,12 @@ class KvCommitArgs(ctypes.Structure):
                 ("v_layout", ctypes.c_int32),
                 ("ctx_lens", ctypes.c_void_p), ("num_accepted", ctypes.c_void_p), ("path_nodes", ctypes.c_void_p),
                 ("new_ctx_lens", ctypes.c_void_p)]
+
+
+class DepthControllerState(ctypes.Structure):
+    _fields_ = [("alpha", ctypes.c_double), ("cost_ratio", ctypes.c_double), ("alpha_decay", ctypes.c_double),
+                ("cost_decay", ctypes.c_double), ("k_max", ctypes.c_int32), ("k", ctypes.c_int32),
+                ("rounds", ctypes.c_int64)]
 
 
 class AcceptRejectionArgs(ctypes.Structure):
@@ -407,3 +424,40 @@ def kv_commit(k_caches, v_caches, block_table, ctx_lens, num_accepted, path_node
     _check(lib().spec_kv_commit(ctypes.byref(a), _stream(stream)), "spec_kv_commit")
     del keep
     return new_ctx_lens
+
+
+class DepthController:
+    """The host-side draft-depth controller of the library (spec_controller_*): keeps the online
+    acceptance rate and cost ratio and proposes the next depth ``k``."""
+
+    def __init__(self, k_max: int, alpha0: float = 0.7, cost_ratio0: float = 0.1, alpha_decay: float = 0.02,
+                 cost_decay: float = 0.1, ctx_len: int = 0, long_ctx_threshold: int = 0, long_ctx_depth: int = 2):
+        self.state = DepthControllerState()
+        _check(lib().spec_controller_init(ctypes.byref(self.state), k_max, alpha0, cost_ratio0, alpha_decay,
+                                          cost_decay, ctx_len, long_ctx_threshold, long_ctx_depth),
+               "spec_controller_init")
+
+    @property
+    def k(self) -> int:
+        return self.state.k
+
+    @property
+    def alpha(self) -> float:
+        return self.state.alpha
+
+    @property
+    def cost_ratio(self) -> float:
+        return self.state.cost_ratio
+
+    def update(self, drafted: int, accepted: int, t_draft: float, t_target: float) -> int:
+        _check(lib().spec_controller_update(ctypes.byref(self.state), drafted, accepted, t_draft, t_target),
+               "spec_controller_update")
+        return self.state.k
+
+
+def controller_speedup(alpha: float, cost_ratio: float, k: int) -> float:
+    return lib().spec_controller_speedup(alpha, cost_ratio, k)
+
+
+def controller_choose(alpha: float, cost_ratio: float, k_max: int) -> int:
+    return lib().spec_controller_choose(alpha, cost_ratio, k_max)

@@ -8,8 +8,8 @@ It is plain numpy in float64, written from the defining passages of the pages
 and kept slow and obvious on purpose: masked softmax attention of every
 draft-tree node over the paged context plus its own ancestors, the per-chunk
 attention mass, greedy longest-accepted-path acceptance, the
-recursive-residual rejection walk, and the commit of the accepted path into
-the paged cache.  Each function cites the passage it follows.
+recursive-residual rejection walk, the commit of the accepted path into
+the paged cache, and the closed-form draft-depth controller.  Each function cites the passage it follows.
 
 Every function here is pinned by tests against something other than itself
 (closed forms, library routines, brute force on tiny inputs, exact
@@ -20,6 +20,8 @@ from .attention import (bf16_to_f64, ancestor_matrix, gather_kv, tree_attention,
                         chunk_mass, topk_chunks)
 from .acceptance import argmax_lowest, accept_greedy, target_probs, accept_rejection
 from .kvcache import kv_commit
+from . import controller
 
 __all__ = ["bf16_to_f64", "ancestor_matrix", "gather_kv", "tree_attention", "attention_rows", "chunk_mass",
-           "topk_chunks", "argmax_lowest", "accept_greedy", "target_probs", "accept_rejection", "kv_commit"]
+           "topk_chunks", "argmax_lowest", "accept_greedy", "target_probs", "accept_rejection", "kv_commit",
+           "controller"]
