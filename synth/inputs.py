@@ -37,7 +37,7 @@ __all__ = [
     "chain_tree", "random_tree", "tree_depths", "children_lists",
     "PagedKV", "paged_kv", "dim_major", "AttentionCase", "attention_case",
     "GreedyCase", "greedy_case", "RejectionCase", "rejection_case",
-    "uniforms24", "ragged_ctx_lens", "WORKLOADS",
+    "uniforms24", "ragged_ctx_lens", "rope_inv_freq", "chunk_selection", "WORKLOADS",
 ]
 
 
@@ -398,6 +398,39 @@ def rejection_case(case: int, trees, vocab: int, *, dtype: str = "bf16", std: fl
     u_acc = uniforms24(ru, T)
     u_smp = uniforms24(ru, T)
     return RejectionCase(node_offsets, parents, tokens, logits, dtype, q32, u_acc, u_smp, vocab)
+
+
+# ----------------------------------------------------------------------------------------------
+# compact draft KV inputs
+# ----------------------------------------------------------------------------------------------
+
+def rope_inv_freq(head_dim: int, theta: float = 500000.0) -> np.ndarray:
+    """Rotary frequencies theta^(-2i/D), i < D/2, as float32 (a model constant; 500000 is Llama 3's base)."""
+    i = np.arange(head_dim // 2, dtype=np.float64)
+    return (theta ** (-2.0 * i / head_dim)).astype(np.float32)
+
+
+def chunk_selection(case: int, n_chunks, num_select: int, *, pad_frac: float = 0.0, dup_frac: float = 0.0,
+                    bad_frac: float = 0.0) -> np.ndarray:
+    """int32 [B][num_select] chunk ids in random order, distinct within a row, like a top-k list.  A fraction
+    of the entries is replaced by -1 (padding), by a repeat of another entry of the row, or by an id at or
+    past the row's chunk count."""
+    rng = rng_for(case, 0, S_TOKENS)
+    out = np.full((len(n_chunks), num_select), -1, dtype=np.int32)
+    for b, n in enumerate(n_chunks):
+        n = int(n)
+        k = min(num_select, n)
+        if k:
+            out[b, :k] = rng.choice(n, size=k, replace=False)
+        for j in range(num_select):
+            r = rng.random()
+            if r < pad_frac:
+                out[b, j] = -1
+            elif r < pad_frac + dup_frac and j > 0:
+                out[b, j] = out[b, rng.integers(j)]
+            elif r < pad_frac + dup_frac + bad_frac:
+                out[b, j] = n + int(rng.integers(0, 4))
+    return out
 
 
 # ----------------------------------------------------------------------------------------------
