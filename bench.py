@@ -285,6 +285,25 @@ def main():
                                  "gbs": round(c_bytes / us / 1e3, 1), "bound": "latency",
                                  "note": f"{n_acc} accepted drafts moved in {layers} layers x {Hkv} KV heads "
                                          "(K and V, read and write)"}
+    # the compact draft KV from the step's top-k list: its 24 heaviest chunks plus a 512-token window in a
+    # 2048-token budget, K rotated at local positions (layer 0's pool stands in for the draft layer's
+    # canonical cache: same shape, 8 KV heads x 128)
+    g_sel, g_win, g_cap = 24, 512, 2048
+    g_out = (torch.empty((1, g_cap, Hkv, D), dtype=torch.bfloat16, device=dev),
+             torch.empty((1, g_cap, Hkv, D), dtype=torch.bfloat16, device=dev),
+             torch.empty((1, g_cap), dtype=torch.int32, device=dev), torch.empty(1, dtype=torch.int32, device=dev))
+    inv_freq = torch.from_numpy(synth.rope_inv_freq(D)).to(dev)
+    da = spec.draft_gather_args(pools[0][0], pools[0][1], bt, cl, topi, max_ctx_len=L, chunk_size=chunk,
+                                window=g_win, capacity=g_cap, num_select=g_sel, rope=spec.ROPE_HALF,
+                                inv_freq=inv_freq, out_k=g_out[0], out_v=g_out[1], out_pos=g_out[2],
+                                out_len=g_out[3], v_layout=v_layout)
+    us = time_call(lambda: call(L_.spec_draft_gather(ctypes.byref(da), sh)))
+    g_len = int(g_out[3][0])
+    d_bytes = g_len * Hkv * D * 2 * 2 * 2 + g_cap * 4
+    kernels["spec_draft_gather"] = {"median_us": round(us, 2), "alg_bytes": d_bytes,
+                                    "gbs": round(d_bytes / us / 1e3, 1), "bound": "hbm",
+                                    "note": f"{g_len} kept tokens ({g_sel} top chunks + {g_win}-token window), "
+                                            f"{Hkv} KV heads x {D}, K rotated; K and V read and written"}
     rtree = synth.random_tree(synth.rng_for(3, 0, synth.S_TREE), 64, 8)
     rc = synth.rejection_case(3, [rtree], V, dtype="bf16", draft="independent")
     rt = sdev.rejection_tensors(rc, dev)

@@ -11,6 +11,8 @@
  *   spec_accept_rejection  exact rejection-sampling acceptance against the draft distribution
  *   spec_kv_commit         moves the accepted path's K/V next to the committed context and
  *                          advances the per-sequence lengths (the per-row rollback)
+ *   spec_draft_gather      builds the draft model's compact KV from the selected context chunks
+ *                          and the recent window, rotated at local positions
  *   spec_controller_*      host-side choice of the next draft depth from the online acceptance
  *                          rate and cost ratio
  *
@@ -54,7 +56,7 @@
 extern "C" {
 #endif
 
-#define SPEC_ABI_VERSION 2
+#define SPEC_ABI_VERSION 3
 
 typedef enum spec_status {
   SPEC_OK = 0,
@@ -293,6 +295,63 @@ typedef struct spec_kv_commit_args {
 } spec_kv_commit_args;
 
 int spec_kv_commit(const spec_kv_commit_args* args, void* stream);
+
+/* ------------------------------------------------------------------------------------------
+ * spec_draft_gather  [DS "What DiffSpec Does": item 2 (a bounded working set of important
+ * long-range context for the draft) and the paragraph after the list (chunks chosen from the
+ * target's paged KV, joined with a rolling recent window, rebuilt as a compact draft cache at
+ * local positions); DS "Architecture" (dual-view draft cache: canonical pre-RoPE KV at absolute
+ * positions, compact cache with local draft RoPE positions); DS "Configuration" (chunk size,
+ * token budget)]
+ *
+ * Builds each sequence's compact draft KV from its canonical pre-RoPE draft cache (paged like the
+ * target's).  With L = ctx_lens[b] and w0 = max(0, L - window), context token t < L is kept iff
+ * t >= w0 or chunk t / chunk_size is among chunk_index[b][0 .. num_select) (ids outside
+ * [0, ceil(L / chunk_size)), -1 padding and repeated ids select nothing more).  Kept tokens keep
+ * their order; compact slot j holds the j-th of them:
+ *   out_pos[b][j]      = t, its absolute position (-1 for j >= out_len[b], up to capacity)
+ *   out_k[b][j][h][:]  = K[t][h][:] rotated at local position j (as stored for SPEC_ROPE_NONE)
+ *   out_v[b][j][h][:]  = V[t][h][:] (bytes)
+ *   out_len[b]         = kept tokens, <= num_select * chunk_size + window <= capacity
+ * Rotation: pair i, i < head_dim / 2 (dims (i, i + head_dim/2) for SPEC_ROPE_HALF, (2i, 2i + 1)
+ * for SPEC_ROPE_PAIRS), turns by the angle j * inv_freq[i]: (x, y) -> (x cos - y sin, y cos + x sin).
+ * The angle is formed exactly and its cosine and sine evaluated in fp64; the rotation runs in
+ * fp32 and rounds to bf16 (RNE).  K/V slots j >= out_len[b] are not written.
+ * chunk_index may be the topk_index output of spec_chunk_salience (row stride top_k): its first
+ * num_select entries are the num_select heaviest chunks.
+ *
+ * Device preconditions: 0 <= ctx_lens[b] <= max_ctx_len; block-table ids < kv.num_pages (a kept
+ * row on an invalid page is written as zeros).
+ * ------------------------------------------------------------------------------------------ */
+typedef enum spec_rope {
+  SPEC_ROPE_NONE = 0,   /* copy K as stored (the compact cache stays pre-RoPE) */
+  SPEC_ROPE_HALF = 1,   /* pairs (i, i + head_dim/2): the rotate-half form of Llama and Qwen */
+  SPEC_ROPE_PAIRS = 2   /* pairs (2i, 2i + 1): the interleaved form */
+} spec_rope;
+
+typedef struct spec_draft_gather_args {
+  int32_t batch;                /* >= 1, <= 65535 */
+  int32_t num_kv_heads;         /* >= 1 */
+  int32_t head_dim;             /* 64 or 128 */
+  int32_t max_ctx_len;          /* (host) bound on ctx_lens[b]; ceil(max_ctx_len / chunk_size) <= 2^18 */
+  const int32_t* ctx_lens;      /* int32 [batch] */
+  spec_paged_kv kv;             /* canonical pre-RoPE draft K/V at absolute positions;
+                                   block_table_stride >= ceil(max_ctx_len / page_size) */
+  int32_t chunk_size;           /* 1 .. 65536 tokens per chunk */
+  int32_t window;               /* recent tokens always kept, >= 0 */
+  int32_t num_select;           /* chunk ids read per sequence, 0 .. 8192 */
+  const int32_t* chunk_index;   /* int32 [batch][chunk_index_stride]; NULL if num_select == 0 */
+  int32_t chunk_index_stride;   /* >= num_select */
+  int32_t capacity;             /* compact slots per sequence, >= num_select * chunk_size + window, <= 2^24 */
+  int32_t rope;                 /* spec_rope */
+  const float* inv_freq;        /* fp32 [head_dim / 2]; NULL for SPEC_ROPE_NONE */
+  void* out_k;                  /* bf16 [batch][capacity][num_kv_heads][head_dim], 16-byte aligned */
+  void* out_v;                  /* bf16 [batch][capacity][num_kv_heads][head_dim], 16-byte aligned */
+  int32_t* out_pos;             /* int32 [batch][capacity] */
+  int32_t* out_len;             /* int32 [batch] */
+} spec_draft_gather_args;
+
+int spec_draft_gather(const spec_draft_gather_args* args, void* stream);
 
 /* ------------------------------------------------------------------------------------------
  * Draft-depth controller (host code, no GPU)  [AS "The controller"; DS "Configuration": long-

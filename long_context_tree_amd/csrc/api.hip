@@ -61,6 +61,37 @@ int log2i(int x) {
   return s;
 }
 
+// Checks a paged KV description whose block table must map need_slots logical slots per sequence.
+int check_kv(const spec_paged_kv& kv, int head_dim, int64_t need_slots, const char* need_text) {
+  if (!kv.k_cache || !aligned(kv.k_cache, 16))
+    return fail(SPEC_ERR_INVALID_ARGUMENT, "kv.k_cache: NULL or not 16-byte aligned");
+  if (!kv.v_cache || !aligned(kv.v_cache, 16))
+    return fail(SPEC_ERR_INVALID_ARGUMENT, "kv.v_cache: NULL or not 16-byte aligned");
+  if (!kv.block_table) return fail(SPEC_ERR_INVALID_ARGUMENT, "kv.block_table: NULL");
+  if (kv.page_stride <= 0 || kv.page_stride % 8)
+    return fail(SPEC_ERR_INVALID_ARGUMENT, "kv.page_stride: %lld, must be a positive multiple of 8",
+                (long long)kv.page_stride);
+  if (kv.head_stride < 0 || kv.head_stride % 8)
+    return fail(SPEC_ERR_INVALID_ARGUMENT, "kv.head_stride: %lld, must be a non-negative multiple of 8",
+                (long long)kv.head_stride);
+  if (kv.token_stride < head_dim || kv.token_stride % 8)
+    return fail(SPEC_ERR_INVALID_ARGUMENT, "kv.token_stride: %lld, must be a multiple of 8 and >= head_dim (%d)",
+                (long long)kv.token_stride, head_dim);
+  if (!pow2(kv.page_size) || kv.page_size < 8 || kv.page_size > 1024)
+    return fail(SPEC_ERR_UNSUPPORTED, "kv.page_size: %d, must be a power of two in 8..1024", kv.page_size);
+  if (kv.page_stride > INT32_MAX || kv.token_stride * kv.page_size > INT32_MAX)
+    return fail(SPEC_ERR_UNSUPPORTED, "kv.page_stride and kv.token_stride * page_size must be < 2^31 elements");
+  if (kv.num_pages < 1) return fail(SPEC_ERR_INVALID_ARGUMENT, "kv.num_pages: %d, must be >= 1", kv.num_pages);
+  if (kv.v_layout != SPEC_V_TOKEN_ROWS && kv.v_layout != SPEC_V_DIM_MAJOR)
+    return fail(SPEC_ERR_INVALID_ARGUMENT, "kv.v_layout: %d, must be SPEC_V_TOKEN_ROWS (0) or SPEC_V_DIM_MAJOR (1)",
+                kv.v_layout);
+  const int64_t need_blocks = spec::ceil_div(need_slots, kv.page_size);
+  if (kv.block_table_stride < need_blocks)
+    return fail(SPEC_ERR_INVALID_ARGUMENT, "kv.block_table_stride: %d, must be >= %s = %lld", kv.block_table_stride,
+                need_text, (long long)need_blocks);
+  return SPEC_OK;
+}
+
 // Checks everything about the attention arguments except the workspace.
 int check_attn(const spec_tree_attention_args* a) {
   if (!a) return fail(SPEC_ERR_INVALID_ARGUMENT, "args: NULL");
@@ -83,33 +114,9 @@ int check_attn(const spec_tree_attention_args* a) {
   if (!a->parents) return fail(SPEC_ERR_INVALID_ARGUMENT, "parents: NULL");
   if (!a->q || !aligned(a->q, 16)) return fail(SPEC_ERR_INVALID_ARGUMENT, "q: NULL or not 16-byte aligned");
   if (!a->out || !aligned(a->out, 16)) return fail(SPEC_ERR_INVALID_ARGUMENT, "out: NULL or not 16-byte aligned");
-  const spec_paged_kv& kv = a->kv;
-  if (!kv.k_cache || !aligned(kv.k_cache, 16))
-    return fail(SPEC_ERR_INVALID_ARGUMENT, "kv.k_cache: NULL or not 16-byte aligned");
-  if (!kv.v_cache || !aligned(kv.v_cache, 16))
-    return fail(SPEC_ERR_INVALID_ARGUMENT, "kv.v_cache: NULL or not 16-byte aligned");
-  if (!kv.block_table) return fail(SPEC_ERR_INVALID_ARGUMENT, "kv.block_table: NULL");
-  if (kv.page_stride <= 0 || kv.page_stride % 8)
-    return fail(SPEC_ERR_INVALID_ARGUMENT, "kv.page_stride: %lld, must be a positive multiple of 8",
-                (long long)kv.page_stride);
-  if (kv.head_stride < 0 || kv.head_stride % 8)
-    return fail(SPEC_ERR_INVALID_ARGUMENT, "kv.head_stride: %lld, must be a non-negative multiple of 8",
-                (long long)kv.head_stride);
-  if (kv.token_stride < a->head_dim || kv.token_stride % 8)
-    return fail(SPEC_ERR_INVALID_ARGUMENT, "kv.token_stride: %lld, must be a multiple of 8 and >= head_dim (%d)",
-                (long long)kv.token_stride, a->head_dim);
-  if (!pow2(kv.page_size) || kv.page_size < 8 || kv.page_size > 1024)
-    return fail(SPEC_ERR_UNSUPPORTED, "kv.page_size: %d, must be a power of two in 8..1024", kv.page_size);
-  if (kv.page_stride > INT32_MAX || kv.token_stride * kv.page_size > INT32_MAX)
-    return fail(SPEC_ERR_UNSUPPORTED, "kv.page_stride and kv.token_stride * page_size must be < 2^31 elements");
-  if (kv.num_pages < 1) return fail(SPEC_ERR_INVALID_ARGUMENT, "kv.num_pages: %d, must be >= 1", kv.num_pages);
-  if (kv.v_layout != SPEC_V_TOKEN_ROWS && kv.v_layout != SPEC_V_DIM_MAJOR)
-    return fail(SPEC_ERR_INVALID_ARGUMENT, "kv.v_layout: %d, must be SPEC_V_TOKEN_ROWS (0) or SPEC_V_DIM_MAJOR (1)",
-                kv.v_layout);
-  const int64_t need_blocks = spec::ceil_div((int64_t)a->max_ctx_len + a->max_nodes, kv.page_size);
-  if (kv.block_table_stride < need_blocks)
-    return fail(SPEC_ERR_INVALID_ARGUMENT, "kv.block_table_stride: %d, must be >= ceil((max_ctx_len + max_nodes) / "
-                "page_size) = %lld", kv.block_table_stride, (long long)need_blocks);
+  const int kst = check_kv(a->kv, a->head_dim, (int64_t)a->max_ctx_len + a->max_nodes,
+                           "ceil((max_ctx_len + max_nodes) / page_size)");
+  if (kst != SPEC_OK) return kst;
   if (!std::isfinite(a->scale) || !(a->scale > 0.f))
     return fail(SPEC_ERR_INVALID_ARGUMENT, "scale: %g, must be finite and > 0", (double)a->scale);
   if (a->chunk_size < 0) return fail(SPEC_ERR_INVALID_ARGUMENT, "chunk_size: %d, must be >= 0", a->chunk_size);
@@ -470,5 +477,87 @@ extern "C" int spec_kv_commit(const spec_kv_commit_args* a, void* stream) {
   p.new_ctx_lens = a->new_ctx_lens;
   const hipError_t e = spec::launch_kv_commit(p, a->head_dim, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "spec_kv_commit launch");
+  return ok();
+}
+
+namespace {
+
+int check_gather(const spec_draft_gather_args* a) {
+  if (!a) return fail(SPEC_ERR_INVALID_ARGUMENT, "args: NULL");
+  if (a->batch < 1 || a->batch > 65535)
+    return fail(SPEC_ERR_INVALID_ARGUMENT, "batch: %d, must be in 1..65535", a->batch);
+  if (a->num_kv_heads < 1) return fail(SPEC_ERR_INVALID_ARGUMENT, "num_kv_heads: %d, must be >= 1", a->num_kv_heads);
+  if (a->head_dim != 64 && a->head_dim != 128)
+    return fail(SPEC_ERR_UNSUPPORTED, "head_dim: %d, supported values are 64 and 128", a->head_dim);
+  if (a->max_ctx_len < 0 || a->max_ctx_len > (1 << 30))
+    return fail(SPEC_ERR_INVALID_ARGUMENT, "max_ctx_len: %d, must be in 0..2^30", a->max_ctx_len);
+  if (a->chunk_size < 1 || a->chunk_size > 65536)
+    return fail(SPEC_ERR_INVALID_ARGUMENT, "chunk_size: %d, must be in 1..65536", a->chunk_size);
+  if (spec::ceil_div(a->max_ctx_len, a->chunk_size) > spec::kMaxGatherChunks)
+    return fail(SPEC_ERR_UNSUPPORTED, "max_ctx_len / chunk_size: %lld chunks, supported up to %d",
+                (long long)spec::ceil_div(a->max_ctx_len, a->chunk_size), spec::kMaxGatherChunks);
+  if (!a->ctx_lens) return fail(SPEC_ERR_INVALID_ARGUMENT, "ctx_lens: NULL");
+  const int kst = check_kv(a->kv, a->head_dim, a->max_ctx_len, "ceil(max_ctx_len / page_size)");
+  if (kst != SPEC_OK) return kst;
+  if (a->window < 0) return fail(SPEC_ERR_INVALID_ARGUMENT, "window: %d, must be >= 0", a->window);
+  if (a->num_select < 0 || a->num_select > spec::kMaxSelect)
+    return fail(SPEC_ERR_INVALID_ARGUMENT, "num_select: %d, must be in 0..%d", a->num_select, spec::kMaxSelect);
+  if (a->num_select > 0 && !a->chunk_index)
+    return fail(SPEC_ERR_INVALID_ARGUMENT, "chunk_index: NULL with num_select = %d", a->num_select);
+  if (a->num_select > 0 && a->chunk_index_stride < a->num_select)
+    return fail(SPEC_ERR_INVALID_ARGUMENT, "chunk_index_stride: %d, must be >= num_select (%d)",
+                a->chunk_index_stride, a->num_select);
+  const int64_t need = (int64_t)a->num_select * a->chunk_size + a->window;
+  if (a->capacity < 1 || a->capacity > (1 << 24) || a->capacity < need)
+    return fail(SPEC_ERR_INVALID_ARGUMENT, "capacity: %d, must be in 1..2^24 and >= num_select * chunk_size + "
+                "window = %lld", a->capacity, (long long)need);
+  if ((int64_t)a->batch * a->capacity * a->num_kv_heads * a->head_dim > (1LL << 40))
+    return fail(SPEC_ERR_UNSUPPORTED, "batch * capacity * num_kv_heads * head_dim: too large");
+  if (a->rope != SPEC_ROPE_NONE && a->rope != SPEC_ROPE_HALF && a->rope != SPEC_ROPE_PAIRS)
+    return fail(SPEC_ERR_INVALID_ARGUMENT, "rope: %d, must be SPEC_ROPE_NONE (0), SPEC_ROPE_HALF (1) or "
+                "SPEC_ROPE_PAIRS (2)", a->rope);
+  if (a->rope != SPEC_ROPE_NONE && !a->inv_freq)
+    return fail(SPEC_ERR_INVALID_ARGUMENT, "inv_freq: NULL with rope = %d", a->rope);
+  if (!a->out_k || !aligned(a->out_k, 16)) return fail(SPEC_ERR_INVALID_ARGUMENT, "out_k: NULL or not 16-byte aligned");
+  if (!a->out_v || !aligned(a->out_v, 16)) return fail(SPEC_ERR_INVALID_ARGUMENT, "out_v: NULL or not 16-byte aligned");
+  if (!a->out_pos) return fail(SPEC_ERR_INVALID_ARGUMENT, "out_pos: NULL");
+  if (!a->out_len) return fail(SPEC_ERR_INVALID_ARGUMENT, "out_len: NULL");
+  return SPEC_OK;
+}
+
+}  // namespace
+
+extern "C" int spec_draft_gather(const spec_draft_gather_args* a, void* stream) {
+  const int st = check_gather(a);
+  if (st != SPEC_OK) return st;
+  spec::DraftGatherParams p{};
+  p.k = static_cast<const uint16_t*>(a->kv.k_cache);
+  p.v = static_cast<const uint16_t*>(a->kv.v_cache);
+  p.page_stride = a->kv.page_stride;
+  p.head_stride = a->kv.head_stride;
+  p.token_stride = a->kv.token_stride;
+  p.page_shift = log2i(a->kv.page_size);
+  p.num_pages = a->kv.num_pages;
+  p.v_dim_major = a->kv.v_layout == SPEC_V_DIM_MAJOR ? 1 : 0;
+  p.block_table = a->kv.block_table;
+  p.bt_stride = a->kv.block_table_stride;
+  p.ctx_lens = a->ctx_lens;
+  p.batch = a->batch;
+  p.Hkv = a->num_kv_heads;
+  p.max_ctx = a->max_ctx_len;
+  p.chunk_size = a->chunk_size;
+  p.window = a->window;
+  p.num_select = a->num_select;
+  p.chunk_index = a->chunk_index;
+  p.ci_stride = a->chunk_index_stride;
+  p.capacity = a->capacity;
+  p.nwords = (int)((spec::ceil_div(a->max_ctx_len, a->chunk_size) + 31) / 32);
+  p.inv_freq = a->inv_freq;
+  p.out_k = static_cast<uint16_t*>(a->out_k);
+  p.out_v = static_cast<uint16_t*>(a->out_v);
+  p.out_pos = a->out_pos;
+  p.out_len = a->out_len;
+  const hipError_t e = spec::launch_draft_gather(p, a->head_dim, a->rope, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "spec_draft_gather launch");
   return ok();
 }

@@ -131,4 +131,30 @@ struct KvCommitParams {
 hipError_t launch_kv_commit(const KvCommitParams& p, int head_dim, hipStream_t s);
 hipError_t launch_accept_rejection(const AcceptParams& p, hipStream_t s);
 
+// ------------------------------------------------------------------------------------------
+// compact draft KV gather
+// ------------------------------------------------------------------------------------------
+constexpr int kMaxSelect = 8192;          // chunk ids read per sequence
+constexpr int kMaxGatherChunks = 1 << 18; // chunks per sequence (the selection bitmap is 32 KB of LDS)
+struct DraftGatherParams {
+  const uint16_t* k;
+  const uint16_t* v;
+  int64_t page_stride, head_stride, token_stride;
+  int page_shift, num_pages, v_dim_major;
+  const int32_t* block_table;
+  int bt_stride;
+  const int32_t* ctx_lens;
+  int batch, Hkv, max_ctx, chunk_size, window, num_select;
+  const int32_t* chunk_index;
+  int ci_stride;
+  int capacity;
+  int nwords;            // 32-bit words of the selection bitmap: ceil(ceil(max_ctx / chunk_size) / 32)
+  const float* inv_freq;
+  uint16_t* out_k;       // bf16 [batch][capacity][Hkv][D]
+  uint16_t* out_v;
+  int32_t* out_pos;      // [batch][capacity]
+  int32_t* out_len;      // [batch]
+};
+hipError_t launch_draft_gather(const DraftGatherParams& p, int head_dim, int rope, hipStream_t s);
+
 }  // namespace spec

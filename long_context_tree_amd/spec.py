@@ -19,9 +19,12 @@ LIB_PATH = os.path.join(_HERE, "libspec_verify.so")
 SPEC_OK = 0
 SPEC_DTYPE_BF16 = 0
 SPEC_DTYPE_F32 = 1
-ABI_VERSION = 2
+ABI_VERSION = 3
 V_TOKEN_ROWS = 0   # spec_v_layout: V pages like K, [pages][kv_heads][page_size][head_dim]
 V_DIM_MAJOR = 1    # V pages [pages][kv_heads][head_dim][page_size]
+ROPE_NONE = 0      # spec_rope: K copied as stored
+ROPE_HALF = 1      # pairs (i, i + head_dim/2)
+ROPE_PAIRS = 2     # pairs (2i, 2i + 1)
 
 _lib = None
 
@@ -45,7 +48,7 @@ def lib():
         L.spec_last_error.restype = ctypes.c_char_p
         for name, argt in (("spec_tree_attention", TreeAttentionArgs), ("spec_chunk_salience", ChunkSalienceArgs),
                            ("spec_accept_greedy", AcceptGreedyArgs), ("spec_accept_rejection", AcceptRejectionArgs),
-                           ("spec_kv_commit", KvCommitArgs)):
+                           ("spec_kv_commit", KvCommitArgs), ("spec_draft_gather", DraftGatherArgs)):
             f = getattr(L, name)
             f.restype = ctypes.c_int
             f.argtypes = [ctypes.POINTER(argt), ctypes.c_void_p]
@@ -128,6 +131,16 @@ class KvCommitArgs(ctypes.Structure):
                 ("new_ctx_lens", ctypes.c_void_p)]
 
 
+class DraftGatherArgs(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("max_ctx_len", ctypes.c_int32), ("ctx_lens", ctypes.c_void_p), ("kv", PagedKV),
+                ("chunk_size", ctypes.c_int32), ("window", ctypes.c_int32), ("num_select", ctypes.c_int32),
+                ("chunk_index", ctypes.c_void_p), ("chunk_index_stride", ctypes.c_int32),
+                ("capacity", ctypes.c_int32), ("rope", ctypes.c_int32), ("inv_freq", ctypes.c_void_p),
+                ("out_k", ctypes.c_void_p), ("out_v", ctypes.c_void_p), ("out_pos", ctypes.c_void_p),
+                ("out_len", ctypes.c_void_p)]
+
+
 class DepthControllerState(ctypes.Structure):
     _fields_ = [("alpha", ctypes.c_double), ("cost_ratio", ctypes.c_double), ("alpha_decay", ctypes.c_double),
                 ("cost_decay", ctypes.c_double), ("k_max", ctypes.c_int32), ("k", ctypes.c_int32),
@@ -183,6 +196,34 @@ class AttentionHandle:
         self._keep = keep
 
 
+def _check_kv_layout(k_cache, v_cache, v_layout):
+    _need(k_cache, "k_cache", torch.bfloat16, contiguous=False)
+    _need(v_cache, "v_cache", torch.bfloat16, contiguous=False)
+    if k_cache.stride(3) != 1:
+        raise ValueError("k_cache: the head_dim stride must be 1")
+    if v_layout == V_TOKEN_ROWS:
+        if k_cache.stride() != v_cache.stride() or k_cache.shape != v_cache.shape:
+            raise ValueError("k_cache and v_cache must have the same shape and strides")
+    elif v_layout == V_DIM_MAJOR:
+        P, H, S, D_ = k_cache.shape
+        if tuple(v_cache.shape) != (P, H, D_, S) or v_cache.stride()[:2] != k_cache.stride()[:2] \
+                or v_cache.stride(2) != S or v_cache.stride(3) != 1:
+            raise ValueError("dim-major v_cache must be [pages][kv_heads][head_dim][page_size] with k_cache's page "
+                             "and head strides and contiguous pages")
+    else:
+        raise ValueError(f"v_layout {v_layout}: expected V_TOKEN_ROWS or V_DIM_MAJOR")
+
+
+def _fill_kv(kv: PagedKV, k_cache, v_cache, block_table, v_layout):
+    kv.k_cache, kv.v_cache = _ptr(k_cache), _ptr(v_cache)
+    kv.page_stride, kv.head_stride, kv.token_stride = k_cache.stride(0), k_cache.stride(1), k_cache.stride(2)
+    kv.page_size = k_cache.shape[2]
+    kv.num_pages = k_cache.shape[0]
+    kv.block_table = _ptr(block_table)
+    kv.block_table_stride = block_table.shape[1]
+    kv.v_layout = v_layout
+
+
 def tree_attention_args(q, k_cache, v_cache, block_table, ctx_lens, node_offsets, parents, *, max_nodes: int,
                         max_ctx_len: int, scale: Optional[float] = None, chunk_size: int = 0, split_tiles: int = 0,
                         out=None, lse=None, workspace=None, v_layout: int = V_TOKEN_ROWS) -> TreeAttentionArgs:
@@ -200,13 +241,7 @@ def tree_attention_args(q, k_cache, v_cache, block_table, ctx_lens, node_offsets
     a.max_ctx_len = max_ctx_len
     a.ctx_lens, a.node_offsets, a.parents = _ptr(ctx_lens), _ptr(node_offsets), _ptr(parents)
     a.q = _ptr(q)
-    a.kv.k_cache, a.kv.v_cache = _ptr(k_cache), _ptr(v_cache)
-    a.kv.page_stride, a.kv.head_stride, a.kv.token_stride = k_cache.stride(0), k_cache.stride(1), k_cache.stride(2)
-    a.kv.page_size = k_cache.shape[2]
-    a.kv.num_pages = k_cache.shape[0]
-    a.kv.block_table = _ptr(block_table)
-    a.kv.block_table_stride = block_table.shape[1]
-    a.kv.v_layout = v_layout
+    _fill_kv(a.kv, k_cache, v_cache, block_table, v_layout)
     a.scale = (1.0 / math.sqrt(D)) if scale is None else scale
     a.out = _ptr(out)
     a.lse = _ptr(lse)
@@ -229,21 +264,7 @@ def tree_attention(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor
     for name, t in (("ctx_lens", ctx_lens), ("node_offsets", node_offsets), ("parents", parents),
                     ("block_table", block_table)):
         _need(t, name, torch.int32)
-    _need(k_cache, "k_cache", torch.bfloat16, contiguous=False)
-    _need(v_cache, "v_cache", torch.bfloat16, contiguous=False)
-    if k_cache.stride(3) != 1:
-        raise ValueError("k_cache: the head_dim stride must be 1")
-    if v_layout == V_TOKEN_ROWS:
-        if k_cache.stride() != v_cache.stride() or k_cache.shape != v_cache.shape:
-            raise ValueError("k_cache and v_cache must have the same shape and strides")
-    elif v_layout == V_DIM_MAJOR:
-        P, H, S, D_ = k_cache.shape
-        if tuple(v_cache.shape) != (P, H, D_, S) or v_cache.stride()[:2] != k_cache.stride()[:2] \
-                or v_cache.stride(2) != S or v_cache.stride(3) != 1:
-            raise ValueError("dim-major v_cache must be [pages][kv_heads][head_dim][page_size] with k_cache's page "
-                             "and head strides and contiguous pages")
-    else:
-        raise ValueError(f"v_layout {v_layout}: expected V_TOKEN_ROWS or V_DIM_MAJOR")
+    _check_kv_layout(k_cache, v_cache, v_layout)
     T, Hq, D = q.shape
     if out is None:
         out = torch.empty((T, Hq, D), dtype=torch.bfloat16, device=q.device)
@@ -461,3 +482,70 @@ def controller_speedup(alpha: float, cost_ratio: float, k: int) -> float:
 
 def controller_choose(alpha: float, cost_ratio: float, k_max: int) -> int:
     return lib().spec_controller_choose(alpha, cost_ratio, k_max)
+
+
+def draft_gather_args(k_cache, v_cache, block_table, ctx_lens, chunk_index, *, max_ctx_len: int, chunk_size: int,
+                      window: int, capacity: int, num_select: Optional[int] = None, rope: int = ROPE_HALF,
+                      inv_freq=None, out_k=None, out_v=None, out_pos=None, out_len=None,
+                      v_layout: int = V_TOKEN_ROWS) -> DraftGatherArgs:
+    """Fill the C argument struct (no launch).  chunk_index: int32 [batch][stride] (or None); its first
+    num_select columns are read (all of them by default)."""
+    a = DraftGatherArgs()
+    a.batch = ctx_lens.numel()
+    a.num_kv_heads = k_cache.shape[1]
+    a.head_dim = k_cache.shape[3]
+    a.max_ctx_len = max_ctx_len
+    a.ctx_lens = _ptr(ctx_lens)
+    _fill_kv(a.kv, k_cache, v_cache, block_table, v_layout)
+    a.chunk_size, a.window, a.capacity, a.rope = chunk_size, window, capacity, rope
+    if chunk_index is None:
+        a.num_select, a.chunk_index, a.chunk_index_stride = 0, None, 0
+    else:
+        a.num_select = chunk_index.shape[1] if num_select is None else num_select
+        a.chunk_index, a.chunk_index_stride = _ptr(chunk_index), chunk_index.stride(0)
+    a.inv_freq = _ptr(inv_freq)
+    a.out_k, a.out_v, a.out_pos, a.out_len = _ptr(out_k), _ptr(out_v), _ptr(out_pos), _ptr(out_len)
+    return a
+
+
+def draft_gather(k_cache: torch.Tensor, v_cache: torch.Tensor, block_table: torch.Tensor, ctx_lens: torch.Tensor,
+                 chunk_index: Optional[torch.Tensor], *, max_ctx_len: int, chunk_size: int, window: int,
+                 capacity: int, num_select: Optional[int] = None, rope: int = ROPE_HALF,
+                 inv_freq: Optional[torch.Tensor] = None, out_k=None, out_v=None, out_pos=None, out_len=None,
+                 v_layout: int = V_TOKEN_ROWS, stream=None):
+    """The compact draft KV of each sequence: its selected chunks (chunk_index rows, e.g. the top-k
+    output of chunk_salience) and its last ``window`` tokens, in context order, K rotated at local
+    positions.  k_cache / v_cache: the canonical pre-RoPE draft cache, laid out as for tree_attention.
+
+    Returns (out_k, out_v bf16 [batch][capacity][kv_heads][head_dim], out_pos int32 [batch][capacity],
+    out_len int32 [batch]); K/V slots at or past out_len are not written."""
+    _check_kv_layout(k_cache, v_cache, v_layout)
+    _need(block_table, "block_table", torch.int32)
+    _need(ctx_lens, "ctx_lens", torch.int32)
+    if chunk_index is not None:
+        _need(chunk_index, "chunk_index", torch.int32, contiguous=False)
+        if chunk_index.dim() != 2 or chunk_index.stride(1) != 1:
+            raise ValueError("chunk_index: int32 [batch][stride] with unit column stride")
+    if inv_freq is not None:
+        _need(inv_freq, "inv_freq", torch.float32)
+    B, H, D = ctx_lens.numel(), k_cache.shape[1], k_cache.shape[3]
+    dev = k_cache.device
+    if out_k is None:
+        out_k = torch.empty((B, capacity, H, D), dtype=torch.bfloat16, device=dev)
+    if out_v is None:
+        out_v = torch.empty((B, capacity, H, D), dtype=torch.bfloat16, device=dev)
+    if out_pos is None:
+        out_pos = torch.empty((B, capacity), dtype=torch.int32, device=dev)
+    if out_len is None:
+        out_len = torch.empty((B,), dtype=torch.int32, device=dev)
+    for name, t, dt in (("out_k", out_k, torch.bfloat16), ("out_v", out_v, torch.bfloat16),
+                        ("out_pos", out_pos, torch.int32), ("out_len", out_len, torch.int32)):
+        _need(t, name, dt)
+    if tuple(out_k.shape) != (B, capacity, H, D) or tuple(out_v.shape) != (B, capacity, H, D):
+        raise ValueError("out_k / out_v: bf16 [batch][capacity][kv_heads][head_dim]")
+    a = draft_gather_args(k_cache, v_cache, block_table, ctx_lens, chunk_index, max_ctx_len=max_ctx_len,
+                          chunk_size=chunk_size, window=window, capacity=capacity, num_select=num_select, rope=rope,
+                          inv_freq=inv_freq, out_k=out_k, out_v=out_v, out_pos=out_pos, out_len=out_len,
+                          v_layout=v_layout)
+    _check(lib().spec_draft_gather(ctypes.byref(a), _stream(stream)), "spec_draft_gather")
+    return out_k, out_v, out_pos, out_len

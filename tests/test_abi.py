@@ -29,11 +29,11 @@ def test_exports_every_declared_symbol():
     spec = _lib()
     names = declared_functions()
     assert {"spec_tree_attention", "spec_chunk_salience", "spec_accept_greedy", "spec_accept_rejection"} <= set(names)
-    assert len(names) == 15, names
+    assert len(names) == 16, names
     L = ctypes.CDLL(spec.LIB_PATH)
     for n in names:
         assert hasattr(L, n), n
-    assert spec.lib().spec_abi_version() == 2
+    assert spec.lib().spec_abi_version() == 3
     assert spec.status_string(3) == "SPEC_ERR_WORKSPACE"
 
 
@@ -189,3 +189,61 @@ def test_kv_commit_refuses_bad_arguments(field, value, status, text):
     a, keep = _commit_args(spec, **{field: value})
     st = spec.lib().spec_kv_commit(ctypes.byref(a), None)
     assert st == status and text in spec.last_error(), (st, spec.last_error())
+
+
+def _gather_args(spec, **over):
+    k = torch.zeros(40, 2, 16, 64, dtype=torch.bfloat16)
+    bt = torch.zeros(1, 40, dtype=torch.int32)
+    cl = torch.tensor([600], dtype=torch.int32)
+    ids = torch.zeros(1, 8, dtype=torch.int32)
+    inv = torch.ones(32)
+    ok = torch.zeros(1, 8 * 64 + 32, 2, 64, dtype=torch.bfloat16)
+    pos = torch.zeros(1, 8 * 64 + 32, dtype=torch.int32)
+    ln = torch.zeros(1, dtype=torch.int32)
+    a = spec.draft_gather_args(k, k, bt, cl, ids, max_ctx_len=640, chunk_size=64, window=32, capacity=8 * 64 + 32,
+                               inv_freq=inv, out_k=ok, out_v=ok, out_pos=pos, out_len=ln)
+    for key, v in over.items():
+        if key.startswith("kv_"):
+            setattr(a.kv, key[3:], v)
+        else:
+            setattr(a, key, v)
+    return a, (k, bt, cl, ids, inv, ok, pos, ln)
+
+
+@pytest.mark.parametrize("field,value,status,text", [
+    ("batch", 0, 1, "batch"),
+    ("num_kv_heads", 0, 1, "num_kv_heads"),
+    ("head_dim", 96, 2, "head_dim"),
+    ("max_ctx_len", -1, 1, "max_ctx_len"),
+    ("chunk_size", 0, 1, "chunk_size"),
+    ("chunk_size", 70000, 1, "chunk_size"),
+    ("max_ctx_len", 1 << 25, 2, "chunks"),
+    ("kv_page_size", 12, 2, "page_size"),
+    ("kv_block_table_stride", 39, 1, "block_table_stride"),
+    ("kv_v_layout", 3, 1, "v_layout"),
+    ("window", -1, 1, "window"),
+    ("num_select", 8193, 1, "num_select"),
+    ("chunk_index", None, 1, "chunk_index"),
+    ("chunk_index_stride", 7, 1, "chunk_index_stride"),
+    ("capacity", 8 * 64 + 31, 1, "capacity"),
+    ("rope", 3, 1, "rope"),
+    ("inv_freq", None, 1, "inv_freq"),
+    ("out_k", None, 1, "out_k"),
+    ("out_v", 8, 1, "out_v"),
+    ("out_pos", None, 1, "out_pos"),
+    ("out_len", None, 1, "out_len"),
+])
+def test_draft_gather_refuses_bad_arguments(field, value, status, text):
+    spec = _lib()
+    a, keep = _gather_args(spec, **{field: value})
+    st = spec.lib().spec_draft_gather(ctypes.byref(a), None)
+    assert st == status and text in spec.last_error(), (st, spec.last_error())
+
+
+def test_draft_gather_accepts_valid_arguments_until_the_launch():
+    spec = _lib()
+    a, keep = _gather_args(spec)
+    a.rope, a.inv_freq = 0, None                       # no frequencies needed without rotation
+    a.num_select, a.chunk_index = 0, None              # no selection: the window alone
+    if not torch.cuda.is_available():
+        assert spec.lib().spec_draft_gather(ctypes.byref(a), None) == 4 and "HIP error" in spec.last_error()
