@@ -10,7 +10,8 @@ draft-tree node over the paged context plus its own ancestors, the per-chunk
 attention mass, greedy longest-accepted-path acceptance, the
 recursive-residual rejection walk, the commit of the accepted path into
 the paged cache, the compact draft KV built from the selected chunks and the
-recent window, and the closed-form draft-depth controller.  Each function cites the passage it follows.
+recent window, the bundle (preorder) order of a draft tree, and the
+closed-form draft-depth controller.  Each function cites the passage it follows.
 
 Every function here is pinned by tests against something other than itself
 (closed forms, library routines, brute force on tiny inputs, exact
@@ -22,8 +23,9 @@ from .attention import (bf16_to_f64, ancestor_matrix, gather_kv, tree_attention,
 from .acceptance import argmax_lowest, accept_greedy, target_probs, accept_rejection
 from .kvcache import kv_commit
 from .draft_kv import draft_gather
+from .bundle import bundle_order
 from . import controller, draft_kv
 
 __all__ = ["bf16_to_f64", "ancestor_matrix", "gather_kv", "tree_attention", "attention_rows", "chunk_mass",
            "topk_chunks", "argmax_lowest", "accept_greedy", "target_probs", "accept_rejection", "kv_commit",
-           "draft_gather", "draft_kv", "controller"]
+           "draft_gather", "draft_kv", "bundle_order", "controller"]
