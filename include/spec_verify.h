@@ -13,6 +13,8 @@
  *                          advances the per-sequence lengths (the per-row rollback)
  *   spec_draft_gather      builds the draft model's compact KV from the selected context chunks
  *                          and the recent window, rotated at local positions
+ *   spec_tree_bundle_order host-side preorder renumbering of a draft tree (bundles of leaves
+ *                          under one branching node adjacent; subtrees as index ranges)
  *   spec_controller_*      host-side choice of the next draft depth from the online acceptance
  *                          rate and cost ratio
  *
@@ -21,7 +23,8 @@
  *         (vllm-diffspec README): "What DiffSpec Does" items 2 and 5, "Architecture"
  *         (target-guided retrieval from paged target KV), "Configuration" (chunk size 64,
  *         up to 50 verifier tree nodes).
- *   [DSC] DiffSpec README (CGCL-codes), "Features": salience-aware chunk encoding, paged KV.
+ *   [DSC] DiffSpec README (CGCL-codes), "Features": salience-aware chunk encoding, paged KV,
+ *         the bundle scheduler.
  *   [AS]  "Adaptive Speculative Decoding": "Correctness first" (exact rejection sampling,
  *         greedy as its temperature-0 case), "The controller" (acceptance probability
  *         min(1, p/q); k drafts give up to k+1 tokens), "Layout" (per-row cache mask
@@ -56,7 +59,11 @@
 extern "C" {
 #endif
 
-#define SPEC_ABI_VERSION 3
+#define SPEC_ABI_VERSION 4
+
+/* Largest draft tree (nodes per sequence) any call accepts.  spec_tree_attention takes up to 256
+ * nodes in index order, and up to this many when the tree is in preorder with subtree ends. */
+#define SPEC_MAX_TREE_NODES 2048
 
 typedef enum spec_status {
   SPEC_OK = 0,
@@ -117,7 +124,11 @@ typedef struct spec_paged_kv {
  *
  * Every node of each sequence's draft tree is a query.  Node i of sequence b (L = ctx_lens[b]
  * committed tokens) sees the keys {0 .. L-1} and {L + j : j is i or an ancestor of i}; its own
- * K/V must already be written at logical slot L + i.  Query head h reads KV head
+ * K/V must already be written at logical slot L + i.  The ancestor relation comes from parents
+ * (up to 256 nodes), or, when subtree_end is given, from index ranges: the tree is then in
+ * preorder (every subtree a contiguous range of nodes, as spec_tree_bundle_order returns it) and
+ * j is i or an ancestor of i iff j <= i < subtree_end[j] (up to SPEC_MAX_TREE_NODES nodes; parents
+ * is not read).  Query head h reads KV head
  * h / (num_q_heads / num_kv_heads).  For a chain of drafts this is ordinary causal decode.
  *   out[n][h][:] = softmax(scale * q[n][h] . K^T) V  over the visible keys   (bf16, RNE)
  *   lse[n][h]    = natural log of the softmax denominator                     (fp32)
@@ -129,18 +140,23 @@ typedef struct spec_paged_kv {
  *
  * Device preconditions: 0 <= ctx_lens[b] <= max_ctx_len; node_offsets non-decreasing with
  * node_offsets[0] = 0 and at most max_nodes nodes per sequence; parents sequence-local with
- * parents[first node] = -1 and 0 <= parents[i] < i otherwise; block-table ids < num_pages.
+ * parents[first node] = -1 and 0 <= parents[i] < i otherwise; with subtree_end, i < subtree_end[i]
+ * <= the sequence's node count (values outside are clamped into that range); block-table ids <
+ * num_pages.
  * ------------------------------------------------------------------------------------------ */
 typedef struct spec_tree_attention_args {
   int32_t batch;                /* >= 1 */
   int32_t num_q_heads;          /* >= 1, multiple of num_kv_heads */
   int32_t num_kv_heads;         /* >= 1 */
   int32_t head_dim;             /* 64 or 128 */
-  int32_t max_nodes;            /* (host) bound on tree nodes per sequence, 1..256 */
+  int32_t max_nodes;            /* (host) bound on tree nodes per sequence: 1..256, or
+                                   1..SPEC_MAX_TREE_NODES with subtree_end */
   int32_t max_ctx_len;          /* (host) bound on ctx_lens[b], >= 0 */
   const int32_t* ctx_lens;      /* int32 [batch] committed tokens before the root */
   const int32_t* node_offsets;  /* int32 [batch + 1] packed node ranges; the first node of a range is the root */
-  const int32_t* parents;       /* int32 [total_nodes] sequence-local parent ids */
+  const int32_t* parents;       /* int32 [total_nodes] sequence-local parent ids (may be NULL with subtree_end) */
+  const int32_t* subtree_end;   /* int32 [total_nodes] sequence-local, one past each node's subtree
+                                   (preorder trees), or NULL to take the ancestors from parents */
   const void* q;                /* bf16 [total_nodes][num_q_heads][head_dim], 16-byte aligned (post-RoPE) */
   spec_paged_kv kv;
   float scale;                  /* finite; usually 1/sqrt(head_dim) */
@@ -203,7 +219,7 @@ int spec_chunk_salience(const spec_chunk_salience_args* args, void* stream);
 typedef struct spec_accept_greedy_args {
   int32_t batch;                /* >= 1 */
   int32_t vocab;                /* 1 .. 2^24 */
-  int32_t max_nodes;            /* (host) bound on nodes per sequence, 1..256 */
+  int32_t max_nodes;            /* (host) bound on nodes per sequence, 1..SPEC_MAX_TREE_NODES */
   int32_t max_path;             /* (host) row length of the path/token outputs, >= 1 (max depth + 1) */
   const int32_t* node_offsets;  /* int32 [batch + 1] */
   const int32_t* parents;       /* int32 [total_nodes] sequence-local */
@@ -276,7 +292,7 @@ typedef struct spec_kv_commit_args {
   int32_t num_layers;           /* 1 .. SPEC_MAX_COMMIT_LAYERS */
   int32_t num_kv_heads;         /* >= 1 */
   int32_t head_dim;             /* 64 or 128 */
-  int32_t max_nodes;            /* (host) bound on tree nodes per sequence, 1..256 */
+  int32_t max_nodes;            /* (host) bound on tree nodes per sequence, 1..SPEC_MAX_TREE_NODES */
   int32_t max_path;             /* row stride of path_nodes, >= 1 */
   const void* const* k_caches;  /* (host) [num_layers] device pointers (bf16, 16-byte aligned) */
   const void* const* v_caches;  /* (host) [num_layers] device pointers (bf16, 16-byte aligned) */
@@ -352,6 +368,27 @@ typedef struct spec_draft_gather_args {
 } spec_draft_gather_args;
 
 int spec_draft_gather(const spec_draft_gather_args* args, void* stream);
+
+/* ------------------------------------------------------------------------------------------
+ * spec_tree_bundle_order (host code, no GPU)  [DSC "Features": the bundle scheduler groups
+ * draft-tree leaves by their branching ancestor for prefix-coherent target verification]
+ *
+ * Renumbers one draft tree (parents[0] = -1, 0 <= parents[i] < i, host memory) in depth-first
+ * preorder from the root, the children of a node in increasing index.  Every subtree becomes one
+ * contiguous range, and the leaves under one branching node become adjacent, so consecutive
+ * verification rows share their prefix.  Outputs, in the new numbering (host arrays of num_nodes):
+ *   order[i]        original index of the node placed at i (the permutation to apply to the
+ *                   tree's queries, draft tokens and tree K/V slots)
+ *   new_parents[i]  parent position (-1 for the root)                       (may be NULL)
+ *   subtree_end[i]  one past the last position of i's subtree: j is an ancestor-or-self of i
+ *                   iff j <= i < subtree_end[j] (the subtree_end of spec_tree_attention_args)
+ *   bundle[i]       position of i's nearest proper ancestor with >= 2 children, 0 if none
+ *                   (0 for the root)                                        (may be NULL)
+ * Returns SPEC_OK, or SPEC_ERR_INVALID_ARGUMENT naming the first bad parent, or
+ * SPEC_ERR_UNSUPPORTED above SPEC_MAX_TREE_NODES nodes.  Allocates nothing.
+ * ------------------------------------------------------------------------------------------ */
+int spec_tree_bundle_order(const int32_t* parents, int32_t num_nodes, int32_t* order, int32_t* new_parents,
+                           int32_t* subtree_end, int32_t* bundle);
 
 /* ------------------------------------------------------------------------------------------
  * Draft-depth controller (host code, no GPU)  [AS "The controller"; DS "Configuration": long-

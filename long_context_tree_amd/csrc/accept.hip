@@ -191,7 +191,7 @@ __global__ __launch_bounds__(256) void residual_pass_kernel(AcceptParams p, int 
 
 // ---- per sequence: child counts (for the residual passes) ----
 __global__ __launch_bounds__(256) void tree_info_kernel(AcceptParams p) {
-  __shared__ int cnt[kMaxNodes];
+  __shared__ int cnt[kMaxTreeNodes];
   const int b = blockIdx.x;
   int n0 = p.node_offsets[b];
   int N = p.node_offsets[b + 1] - n0;
@@ -207,12 +207,46 @@ __global__ __launch_bounds__(256) void tree_info_kernel(AcceptParams p) {
   for (int i = threadIdx.x; i < N; i += 256) p.n_children[n0 + i] = cnt[i];
 }
 
+// Child count and sibling rank (earlier siblings) of the nodes tid + 256 q, q < PER; flags a parent
+// array that is not topological or a node with more than max_children children.
+template <int PER>
+__device__ __forceinline__ void child_ranks(const int* par_s, int N, int tid, int max_children, int* rank_s,
+                                            int* nch_s, int& bad_s) {
+  int own_p[PER], rank[PER], nch[PER];
+#pragma unroll
+  for (int q = 0; q < PER; ++q) {
+    const int i = tid + 256 * q;
+    own_p[q] = i < N ? par_s[i] : -2;
+    rank[q] = 0;
+    nch[q] = 0;
+    if (i < N && i > 0 && !(own_p[q] >= 0 && own_p[q] < i)) bad_s = 1;
+    if (i == 0 && own_p[q] != -1) bad_s = 1;
+  }
+  for (int j = 1; j < N; ++j) {
+    const int pj = par_s[j];
+#pragma unroll
+    for (int q = 0; q < PER; ++q) {
+      const int i = tid + 256 * q;
+      rank[q] += (j < i && pj == own_p[q]) ? 1 : 0;
+      nch[q] += (pj == i) ? 1 : 0;
+    }
+  }
+#pragma unroll
+  for (int q = 0; q < PER; ++q) {
+    const int i = tid + 256 * q;
+    if (i < N) {
+      rank_s[i] = rank[q];
+      nch_s[i] = nch[q];
+      if (nch[q] > max_children) bad_s = 1;
+    }
+  }
+}
+
 // ---- per sequence: the walk and the bonus token ----
 template <bool REJECT>
 __global__ __launch_bounds__(256) void walk_kernel(AcceptParams p) {
-  __shared__ int par_s[kMaxNodes], tok_s[kMaxNodes], first_s[kMaxNodes], nch_s[kMaxNodes], rank_s[kMaxNodes];
-  __shared__ int amax_s[kMaxNodes];
-  __shared__ int path_s[kMaxNodes];
+  __shared__ int par_s[kMaxTreeNodes], tok_s[kMaxTreeNodes], first_s[kMaxTreeNodes], nch_s[kMaxTreeNodes];
+  __shared__ int rank_s[kMaxTreeNodes], amax_s[kMaxTreeNodes], path_s[kMaxTreeNodes];
   __shared__ int stop_s, depth_s, bad_s, seg_s, bonus_s;
   __shared__ double base_s, thr_s;
   __shared__ double zs[9];
@@ -244,19 +278,12 @@ __global__ __launch_bounds__(256) void walk_kernel(AcceptParams p) {
     }
   }
   __syncthreads();
-  for (int i = tid; i < N; i += 256) {
-    const int pi = par_s[i];
-    if (i > 0 && !(pi >= 0 && pi < i)) bad_s = 1;
-    if (i == 0 && pi != -1) bad_s = 1;
-    int rank = 0, nch = 0;
-    for (int j = 1; j < N; ++j) {
-      rank += (j < i && par_s[j] == pi) ? 1 : 0;
-      nch += (par_s[j] == i) ? 1 : 0;
-    }
-    rank_s[i] = rank;
-    nch_s[i] = nch;
-    if (REJECT && nch > p.max_children) bad_s = 1;
-  }
+  // child counts and sibling ranks: each parent entry is read once and compared with the nodes this
+  // thread owns (tid, tid + 256, ...): one node per thread for trees of <= 256 nodes, else up to 8
+  if (N <= 256)
+    child_ranks<1>(par_s, N, tid, REJECT ? p.max_children : 0x7FFFFFFF, rank_s, nch_s, bad_s);
+  else
+    child_ranks<kMaxTreeNodes / 256>(par_s, N, tid, REJECT ? p.max_children : 0x7FFFFFFF, rank_s, nch_s, bad_s);
   __syncthreads();
   if (bad_s) {
     for (int i = tid; i < p.max_path; i += 256) { o_path[i] = -1; o_tok[i] = -1; }
@@ -303,7 +330,7 @@ __global__ __launch_bounds__(256) void walk_kernel(AcceptParams p) {
     if (tid == 0) {
       int u = 0, d = 0;
       path_s[0] = 0;
-      while (first_s[u] != 0x7FFFFFFF && d + 1 < kMaxNodes) {
+      while (first_s[u] != 0x7FFFFFFF && d + 1 < kMaxTreeNodes) {
         u = first_s[u];
         path_s[++d] = u;
       }

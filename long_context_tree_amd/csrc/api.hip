@@ -38,14 +38,14 @@ int hip_fail(hipError_t e, const char* what) {
 }  // namespace
 
 namespace spec {
-// status and thread-local message for the controller functions (nullptr: success)
-int controller_fail(const char* what) {
+// status and thread-local message for the host-only functions (what == nullptr: success)
+int host_fail(int status, const char* what) {
   if (!what) {
     g_err.clear();
     return SPEC_OK;
   }
   g_err = what;
-  return SPEC_ERR_INVALID_ARGUMENT;
+  return status;
 }
 }  // namespace spec
 
@@ -103,15 +103,18 @@ int check_attn(const spec_tree_attention_args* a) {
   if (a->head_dim != 64 && a->head_dim != 128)
     return fail(SPEC_ERR_UNSUPPORTED, "head_dim: %d, supported values are 64 and 128", a->head_dim);
   if (a->max_nodes < 1) return fail(SPEC_ERR_INVALID_ARGUMENT, "max_nodes: %d, must be >= 1", a->max_nodes);
-  if (a->max_nodes > spec::kMaxNodes)
-    return fail(SPEC_ERR_UNSUPPORTED, "max_nodes: %d, supported range is 1..%d", a->max_nodes, spec::kMaxNodes);
+  const int node_cap = a->subtree_end ? spec::kMaxTreeNodes : spec::kMaxNodes;
+  if (a->max_nodes > node_cap)
+    return fail(SPEC_ERR_UNSUPPORTED, "max_nodes: %d, supported range is 1..%d%s", a->max_nodes, node_cap,
+                a->subtree_end ? "" : " (up to 2048 for trees in preorder, with subtree_end)");
   if (a->max_ctx_len < 0 || a->max_ctx_len > (1 << 30))
     return fail(SPEC_ERR_INVALID_ARGUMENT, "max_ctx_len: %d, must be in 0..2^30", a->max_ctx_len);
   if ((int64_t)a->batch * a->max_nodes * a->num_q_heads > (1LL << 30))
     return fail(SPEC_ERR_UNSUPPORTED, "batch * max_nodes * num_q_heads: too large (limit 2^30)");
   if (!a->ctx_lens) return fail(SPEC_ERR_INVALID_ARGUMENT, "ctx_lens: NULL");
   if (!a->node_offsets) return fail(SPEC_ERR_INVALID_ARGUMENT, "node_offsets: NULL");
-  if (!a->parents) return fail(SPEC_ERR_INVALID_ARGUMENT, "parents: NULL");
+  if (!a->parents && !a->subtree_end)
+    return fail(SPEC_ERR_INVALID_ARGUMENT, "parents: NULL (needed unless subtree_end is given)");
   if (!a->q || !aligned(a->q, 16)) return fail(SPEC_ERR_INVALID_ARGUMENT, "q: NULL or not 16-byte aligned");
   if (!a->out || !aligned(a->out, 16)) return fail(SPEC_ERR_INVALID_ARGUMENT, "out: NULL or not 16-byte aligned");
   const int kst = check_kv(a->kv, a->head_dim, (int64_t)a->max_ctx_len + a->max_nodes,
@@ -165,6 +168,7 @@ spec::AttnParams attn_params(const spec_tree_attention_args* a, const AttnLayout
   p.ctx_lens = a->ctx_lens;
   p.node_offsets = a->node_offsets;
   p.parents = a->parents;
+  p.subtree_end = a->subtree_end;
   p.batch = a->batch;
   p.Hq = a->num_q_heads;
   p.Hkv = a->num_kv_heads;
@@ -194,8 +198,8 @@ int check_greedy(const spec_accept_greedy_args* a) {
   if (a->vocab < 1 || a->vocab > (1 << 24))
     return fail(SPEC_ERR_INVALID_ARGUMENT, "vocab: %d, must be in 1..2^24", a->vocab);
   if (a->max_nodes < 1) return fail(SPEC_ERR_INVALID_ARGUMENT, "max_nodes: %d, must be >= 1", a->max_nodes);
-  if (a->max_nodes > spec::kMaxNodes)
-    return fail(SPEC_ERR_UNSUPPORTED, "max_nodes: %d, supported range is 1..%d", a->max_nodes, spec::kMaxNodes);
+  if (a->max_nodes > spec::kMaxTreeNodes)
+    return fail(SPEC_ERR_UNSUPPORTED, "max_nodes: %d, supported range is 1..%d", a->max_nodes, spec::kMaxTreeNodes);
   if ((int64_t)a->batch * a->max_nodes > 65535)
     return fail(SPEC_ERR_UNSUPPORTED, "batch * max_nodes: %lld, limit 65535", (long long)a->batch * a->max_nodes);
   if (a->max_path < 1) return fail(SPEC_ERR_INVALID_ARGUMENT, "max_path: %d, must be >= 1", a->max_path);
@@ -411,8 +415,8 @@ int check_commit(const spec_kv_commit_args* a) {
   if (a->num_kv_heads < 1) return fail(SPEC_ERR_INVALID_ARGUMENT, "num_kv_heads: %d, must be >= 1", a->num_kv_heads);
   if (a->head_dim != 64 && a->head_dim != 128)
     return fail(SPEC_ERR_UNSUPPORTED, "head_dim: %d, supported values are 64 and 128", a->head_dim);
-  if (a->max_nodes < 1 || a->max_nodes > spec::kMaxNodes)
-    return fail(SPEC_ERR_UNSUPPORTED, "max_nodes: %d, supported range is 1..%d", a->max_nodes, spec::kMaxNodes);
+  if (a->max_nodes < 1 || a->max_nodes > spec::kMaxTreeNodes)
+    return fail(SPEC_ERR_UNSUPPORTED, "max_nodes: %d, supported range is 1..%d", a->max_nodes, spec::kMaxTreeNodes);
   if (a->max_path < 1) return fail(SPEC_ERR_INVALID_ARGUMENT, "max_path: %d, must be >= 1", a->max_path);
   if ((int64_t)a->batch * a->max_path > (1LL << 30) || (int64_t)a->batch > 65535)
     return fail(SPEC_ERR_UNSUPPORTED, "batch: %d, too large (limit 65535 sequences per call)", a->batch);

@@ -10,7 +10,7 @@
 #include "spec_internal.h"
 
 namespace spec {
-int controller_fail(const char* what);
+int host_fail(int status, const char* what);
 }
 
 namespace {
@@ -49,13 +49,13 @@ int32_t spec_controller_choose(double alpha, double cost_ratio, int32_t k_max) {
 int spec_controller_init(spec_depth_controller* ctl, int32_t k_max, double alpha0, double cost_ratio0,
                          double alpha_decay, double cost_decay, int64_t ctx_len, int64_t long_ctx_threshold,
                          int32_t long_ctx_depth) {
-  if (!ctl) return spec::controller_fail("ctl: NULL");
-  if (k_max < 1) return spec::controller_fail("k_max: must be >= 1");
-  if (!finite_in(alpha0, 0.0, 1.0)) return spec::controller_fail("alpha0: must be in [0, 1]");
-  if (!(cost_ratio0 > 0.0) || !std::isfinite(cost_ratio0)) return spec::controller_fail("cost_ratio0: must be > 0");
-  if (!(alpha_decay > 0.0) || !(alpha_decay <= 1.0)) return spec::controller_fail("alpha_decay: must be in (0, 1]");
-  if (!(cost_decay > 0.0) || !(cost_decay <= 1.0)) return spec::controller_fail("cost_decay: must be in (0, 1]");
-  if (long_ctx_depth < 1) return spec::controller_fail("long_ctx_depth: must be >= 1");
+  if (!ctl) return spec::host_fail(SPEC_ERR_INVALID_ARGUMENT, "ctl: NULL");
+  if (k_max < 1) return spec::host_fail(SPEC_ERR_INVALID_ARGUMENT, "k_max: must be >= 1");
+  if (!finite_in(alpha0, 0.0, 1.0)) return spec::host_fail(SPEC_ERR_INVALID_ARGUMENT, "alpha0: must be in [0, 1]");
+  if (!(cost_ratio0 > 0.0) || !std::isfinite(cost_ratio0)) return spec::host_fail(SPEC_ERR_INVALID_ARGUMENT, "cost_ratio0: must be > 0");
+  if (!(alpha_decay > 0.0) || !(alpha_decay <= 1.0)) return spec::host_fail(SPEC_ERR_INVALID_ARGUMENT, "alpha_decay: must be in (0, 1]");
+  if (!(cost_decay > 0.0) || !(cost_decay <= 1.0)) return spec::host_fail(SPEC_ERR_INVALID_ARGUMENT, "cost_decay: must be in (0, 1]");
+  if (long_ctx_depth < 1) return spec::host_fail(SPEC_ERR_INVALID_ARGUMENT, "long_ctx_depth: must be >= 1");
   ctl->alpha = alpha0;
   ctl->cost_ratio = cost_ratio0;
   ctl->alpha_decay = alpha_decay;
@@ -65,16 +65,16 @@ int spec_controller_init(spec_depth_controller* ctl, int32_t k_max, double alpha
   ctl->k = (long_ctx_threshold > 0 && ctx_len >= long_ctx_threshold)
                ? (long_ctx_depth < k_max ? long_ctx_depth : k_max)
                : spec_controller_choose(alpha0, cost_ratio0, k_max);
-  return spec::controller_fail(nullptr);
+  return spec::host_fail(SPEC_OK, nullptr);
 }
 
 int spec_controller_update(spec_depth_controller* ctl, int32_t drafted, int32_t accepted, double t_draft,
                            double t_target) {
-  if (!ctl) return spec::controller_fail("ctl: NULL");
+  if (!ctl) return spec::host_fail(SPEC_ERR_INVALID_ARGUMENT, "ctl: NULL");
   if (drafted < 0 || accepted < 0 || accepted > drafted)
-    return spec::controller_fail("drafted / accepted: need 0 <= accepted <= drafted");
-  if (!(t_target > 0.0) || !std::isfinite(t_target)) return spec::controller_fail("t_target: must be > 0");
-  if (!(t_draft >= 0.0) || !std::isfinite(t_draft)) return spec::controller_fail("t_draft: must be >= 0");
+    return spec::host_fail(SPEC_ERR_INVALID_ARGUMENT, "drafted / accepted: need 0 <= accepted <= drafted");
+  if (!(t_target > 0.0) || !std::isfinite(t_target)) return spec::host_fail(SPEC_ERR_INVALID_ARGUMENT, "t_target: must be > 0");
+  if (!(t_draft >= 0.0) || !std::isfinite(t_draft)) return spec::host_fail(SPEC_ERR_INVALID_ARGUMENT, "t_draft: must be >= 0");
   double a = ctl->alpha;
   const double w = ctl->alpha_decay;
   for (int32_t i = 0; i < accepted; ++i) a = (1.0 - w) * a + w * 1.0;
@@ -83,7 +83,7 @@ int spec_controller_update(spec_depth_controller* ctl, int32_t drafted, int32_t 
   if (t_draft > 0.0) ctl->cost_ratio = (1.0 - ctl->cost_decay) * ctl->cost_ratio + ctl->cost_decay * (t_draft / t_target);
   ctl->rounds += 1;
   ctl->k = spec_controller_choose(ctl->alpha, ctl->cost_ratio, ctl->k_max);
-  return spec::controller_fail(nullptr);
+  return spec::host_fail(SPEC_OK, nullptr);
 }
 
 }  // extern "C"

@@ -11,7 +11,8 @@
 namespace spec {
 
 constexpr int kTile = 64;          // KV slots per attention tile
-constexpr int kMaxNodes = 256;     // tree nodes per sequence (ancestor masks are 4 x 64 bits)
+constexpr int kMaxNodes = 256;     // tree nodes per sequence with ancestor bit masks (4 x 64 bits)
+constexpr int kMaxTreeNodes = SPEC_MAX_TREE_NODES;   // tree nodes per sequence otherwise
 constexpr int kSegment = 8192;     // vocabulary elements per argmax work-group
 constexpr int kResSegment = 2048;  // vocabulary elements per residual-sum work-group (rejection)
 constexpr int kMaxTopK = 8192;     // chunks sorted by one work-group for top-k
@@ -50,6 +51,7 @@ struct AttnParams {
   const int32_t* ctx_lens;
   const int32_t* node_offsets;
   const int32_t* parents;
+  const int32_t* subtree_end;   // preorder trees: ancestors as index ranges (NULL: bit masks from parents)
   int batch, Hq, Hkv, G, max_nodes, max_ctx;
   float scale_log2;      // scale * log2(e)
   int chunk_size, max_chunks;

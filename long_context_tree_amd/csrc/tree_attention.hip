@@ -28,7 +28,12 @@
 //  * Lazy rescaling: the running max only moves when a tile's max exceeds it by more than 2^8,
 //    so the O accumulators are rescaled on a handful of tiles per split.
 //  * Keys >= ctx_len are tree slots: visible iff the key's node is an ancestor-or-self of the
-//    row's node (ancestor bit masks built in LDS from the parent array).
+//    row's node.  The relation comes from ancestor bit masks built in LDS from the parent array
+//    (up to 256 nodes), or, for trees in preorder (the bundle order of the DiffSpec README,
+//    "Features": leaves grouped by branching ancestor), from index ranges: j is an ancestor-or-self
+//    of i iff j <= i < subtree_end[j] (up to 2048 nodes, one int per node in LDS).
+//  * A work-group's split stops after the tree slot of its last row's node: an ancestor's index is
+//    below its descendant's, so later tree tiles are masked for all of its rows.
 //  * With chunk_size > 0 each tile also emits, per query row, the log2-sum-exp of the row's scores
 //    over each context chunk; the salience pass turns these into attention mass once the row's
 //    final log-sum-exp is known (no second pass over K).
@@ -71,7 +76,11 @@ __device__ __forceinline__ void buffer_load_lds16(const void* base, uint32_t num
 
 // CM: 0 = chunk sums per 64-slot tile (chunk_size 0 or a multiple of 64), 1 = per 32 slots, 2 = per 16 slots
 // VT: 0 = V pages hold token rows (like K), 1 = V pages are dim-major (each dim's page_size tokens contiguous)
-template <int D, int W, int RB, int CM, int VT>
+// PRE: the tree is in preorder and p.subtree_end gives the ancestor relation as index ranges.  It is a
+// compile-time switch: with a run-time flag the compiler versioned the tile loop on it, and that
+// build gave wrong results on the bit-mask path as well (cause not found), so the two mask sources are
+// separate instantiations.
+template <int D, int W, int RB, int CM, int VT, int PRE>
 __global__ __launch_bounds__(W * 64, (W == 8 ? 1 : 2)) void tree_attn_kernel(AttnParams p) {
   constexpr int NT = W * 64;
   constexpr int ROWS_WG = W * RB * 16;
@@ -95,6 +104,10 @@ __global__ __launch_bounds__(W * 64, (W == 8 ? 1 : 2)) void tree_attn_kernel(Att
   __shared__ __attribute__((aligned(16))) uint16_t kv_a[2][TILE_EL];
   __shared__ __attribute__((aligned(16))) uint16_t kv_b[2][TILE_EL];
   __shared__ uint64_t anc_lds[ANC_N][ANC_W];
+  // preorder trees: the same memory holds each node's subtree end (2 ints per 64-bit word)
+  int* const end_lds = reinterpret_cast<int*>(&anc_lds[0][0]);
+  constexpr int END_N = ANC_N * ANC_W * 2;
+  static_assert(W != 8 || END_N >= kMaxTreeNodes, "subtree ends of the largest tree must fit");
   __shared__ int pg_lds[kMaxSplitPages];
   // Row r of a K tile keeps its 16-byte chunk c at position c ^ swz(r), row r of a token-row V tile at
   // c ^ swzv_rows(r).  The XOR patterns were chosen with the LDS bank-conflict counter: they leave the K
@@ -125,11 +138,19 @@ __global__ __launch_bounds__(W * 64, (W == 8 ? 1 : 2)) void tree_attn_kernel(Att
   const int keys = L + N;
   const int n_tiles = (keys + kTile - 1) / kTile;
   const int t_begin = split * p.split_tiles;
-  const int t_end = min(n_tiles, t_begin + p.split_tiles);
+  int t_end = min(n_tiles, t_begin + p.split_tiles);
   const int G = p.G;
   const int rows = N * G;
   const int row0 = rg * ROWS_WG;
   if (t_begin >= t_end || row0 >= rows) return;
+  // an ancestor's index is below its descendant's, so tree slots past the work-group's last node are
+  // masked for all of its rows: the split ends there (at least one tile stays, so that every split
+  // the merge reads writes its partial; a fully masked tile leaves the neutral one)
+  {
+    const int last_node = (min(row0 + ROWS_WG, rows) - 1) / G;
+    const int t_need = (L + last_node + 1 + kTile - 1) / kTile;
+    t_end = max(t_begin + 1, min(t_end, t_need));
+  }
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -150,7 +171,13 @@ __global__ __launch_bounds__(W * 64, (W == 8 ? 1 : 2)) void tree_attn_kernel(Att
 
   // ---- ancestor-or-self bit masks of the tree nodes (only the split holding the tree slots) ----
   const bool has_tree = t_end * kTile > L;
-  if (has_tree) {
+  if (PRE && has_tree) {
+    // a 4-wave work-group serves <= 128 rows, hence <= 128 nodes (< END_N)
+    for (int i = tid; i < N && i < END_N; i += NT) {
+      int e = p.subtree_end[n0 + i];
+      end_lds[i] = e <= i ? i + 1 : (e > N ? N : e);
+    }
+  } else if (has_tree) {
     for (int i = tid; i < N && i < ANC_N; i += NT) {
       uint64_t m[ANC_W];
 #pragma unroll
@@ -374,8 +401,11 @@ __global__ __launch_bounds__(W * 64, (W == 8 ? 1 : 2)) void tree_attn_kernel(Att
             const int key = key0 + kmap(j, 4 * lg + i);
             bool vis = key < L;
             if (!vis && key < keys && valid_r[rb]) {
-              const int tj = key - L;           // < N <= ANC_N, and node_r < N
-              vis = (anc_lds[node_r[rb]][(tj >> 6) & (ANC_W - 1)] >> (tj & 63)) & 1ull;
+              const int tj = key - L;           // < N (<= ANC_N, or <= END_N in preorder), and node_r < N
+              if constexpr (PRE != 0)
+                vis = tj <= node_r[rb] && node_r[rb] < end_lds[tj];
+              else
+                vis = (anc_lds[node_r[rb]][(tj >> 6) & (ANC_W - 1)] >> (tj & 63)) & 1ull;
             }
             if (!vis) s[rb][j][i] = -INFINITY;
           }
@@ -675,7 +705,10 @@ template <int D, int W, int RB, int CM, int VT>
 hipError_t launch_d_w(const AttnParams& p, const AttnPlan& plan, hipStream_t s) {
   const int n_units = p.batch * p.Hkv * p.max_splits;
   const int grid = (int)(ceil_div(n_units, 8) * 8 * plan.row_groups);
-  hipLaunchKernelGGL((tree_attn_kernel<D, W, RB, CM, VT>), dim3(grid), dim3(W * 64), 0, s, p);
+  if (p.subtree_end)
+    hipLaunchKernelGGL((tree_attn_kernel<D, W, RB, CM, VT, 1>), dim3(grid), dim3(W * 64), 0, s, p);
+  else
+    hipLaunchKernelGGL((tree_attn_kernel<D, W, RB, CM, VT, 0>), dim3(grid), dim3(W * 64), 0, s, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t rows = (int64_t)p.batch * p.max_nodes * p.Hq;

@@ -19,7 +19,8 @@ LIB_PATH = os.path.join(_HERE, "libspec_verify.so")
 SPEC_OK = 0
 SPEC_DTYPE_BF16 = 0
 SPEC_DTYPE_F32 = 1
-ABI_VERSION = 3
+ABI_VERSION = 4
+MAX_TREE_NODES = 2048
 V_TOKEN_ROWS = 0   # spec_v_layout: V pages like K, [pages][kv_heads][page_size][head_dim]
 V_DIM_MAJOR = 1    # V pages [pages][kv_heads][head_dim][page_size]
 ROPE_NONE = 0      # spec_rope: K copied as stored
@@ -58,6 +59,8 @@ def lib():
             f = getattr(L, name)
             f.restype = ctypes.c_size_t
             f.argtypes = [ctypes.POINTER(argt)]
+        L.spec_tree_bundle_order.restype = ctypes.c_int
+        L.spec_tree_bundle_order.argtypes = [ctypes.c_void_p, ctypes.c_int32] + [ctypes.c_void_p] * 4
         L.spec_controller_speedup.restype = ctypes.c_double
         L.spec_controller_speedup.argtypes = [ctypes.c_double, ctypes.c_double, ctypes.c_int32]
         L.spec_controller_choose.restype = ctypes.c_int32
@@ -99,6 +102,7 @@ class TreeAttentionArgs(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int32), ("num_q_heads", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
                 ("head_dim", ctypes.c_int32), ("max_nodes", ctypes.c_int32), ("max_ctx_len", ctypes.c_int32),
                 ("ctx_lens", ctypes.c_void_p), ("node_offsets", ctypes.c_void_p), ("parents", ctypes.c_void_p),
+                ("subtree_end", ctypes.c_void_p),
                 ("q", ctypes.c_void_p), ("kv", PagedKV), ("scale", ctypes.c_float), ("out", ctypes.c_void_p),
                 ("lse", ctypes.c_void_p), ("chunk_size", ctypes.c_int32), ("split_tiles", ctypes.c_int32),
                 ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t)]
@@ -226,7 +230,8 @@ def _fill_kv(kv: PagedKV, k_cache, v_cache, block_table, v_layout):
 
 def tree_attention_args(q, k_cache, v_cache, block_table, ctx_lens, node_offsets, parents, *, max_nodes: int,
                         max_ctx_len: int, scale: Optional[float] = None, chunk_size: int = 0, split_tiles: int = 0,
-                        out=None, lse=None, workspace=None, v_layout: int = V_TOKEN_ROWS) -> TreeAttentionArgs:
+                        out=None, lse=None, workspace=None, v_layout: int = V_TOKEN_ROWS,
+                        subtree_end=None) -> TreeAttentionArgs:
     """Fill the C argument struct from tensors (no launch).  k_cache is bf16 [pages][kv_heads][page_size]
     [head_dim] with unit stride in the last dimension; v_cache has the same shape and strides
     (V_TOKEN_ROWS) or is [pages][kv_heads][head_dim][page_size] with K's page and head strides
@@ -240,6 +245,7 @@ def tree_attention_args(q, k_cache, v_cache, block_table, ctx_lens, node_offsets
     a.max_nodes = max_nodes
     a.max_ctx_len = max_ctx_len
     a.ctx_lens, a.node_offsets, a.parents = _ptr(ctx_lens), _ptr(node_offsets), _ptr(parents)
+    a.subtree_end = _ptr(subtree_end)
     a.q = _ptr(q)
     _fill_kv(a.kv, k_cache, v_cache, block_table, v_layout)
     a.scale = (1.0 / math.sqrt(D)) if scale is None else scale
@@ -256,14 +262,18 @@ def tree_attention(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor
                    ctx_lens: torch.Tensor, node_offsets: torch.Tensor, parents: torch.Tensor, *, max_nodes: int,
                    max_ctx_len: int, scale: Optional[float] = None, chunk_size: int = 0, split_tiles: int = 0,
                    out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None, want_lse: bool = True,
-                   workspace: Optional[torch.Tensor] = None, stream=None, v_layout: int = V_TOKEN_ROWS):
-    """Tree-masked attention of every draft-tree node over the paged KV cache.
+                   workspace: Optional[torch.Tensor] = None, stream=None, v_layout: int = V_TOKEN_ROWS,
+                   subtree_end: Optional[torch.Tensor] = None):
+    """Tree-masked attention of every draft-tree node over the paged KV cache.  With subtree_end
+    (int32 [T], sequence-local; trees in preorder, e.g. from tree_bundle_order) the ancestors come
+    from index ranges and trees may have up to MAX_TREE_NODES nodes; parents may then be None.
 
     Returns (out bf16 [T][Hq][D], lse fp32 [T][Hq] or None, handle for spec_chunk_salience)."""
     _need(q, "q", torch.bfloat16)
     for name, t in (("ctx_lens", ctx_lens), ("node_offsets", node_offsets), ("parents", parents),
-                    ("block_table", block_table)):
-        _need(t, name, torch.int32)
+                    ("block_table", block_table), ("subtree_end", subtree_end)):
+        if t is not None or name not in ("parents", "subtree_end"):
+            _need(t, name, torch.int32)
     _check_kv_layout(k_cache, v_cache, v_layout)
     T, Hq, D = q.shape
     if out is None:
@@ -272,7 +282,7 @@ def tree_attention(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor
         lse = torch.empty((T, Hq), dtype=torch.float32, device=q.device)
     a = tree_attention_args(q, k_cache, v_cache, block_table, ctx_lens, node_offsets, parents, max_nodes=max_nodes,
                             max_ctx_len=max_ctx_len, scale=scale, chunk_size=chunk_size, split_tiles=split_tiles,
-                            out=out, lse=lse, v_layout=v_layout)
+                            out=out, lse=lse, v_layout=v_layout, subtree_end=subtree_end)
     need = lib().spec_tree_attention_workspace_size(ctypes.byref(a))
     if need == 0:
         _check(lib().spec_tree_attention(ctypes.byref(a), None), "spec_tree_attention")
@@ -280,7 +290,7 @@ def tree_attention(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor
     a.workspace, a.workspace_bytes = ws.data_ptr(), ws.numel()
     _check(lib().spec_tree_attention(ctypes.byref(a), _stream(stream)), "spec_tree_attention")
     return out, lse, AttentionHandle(a, (q, k_cache, v_cache, block_table, ctx_lens, node_offsets, parents, out, lse,
-                                         ws))
+                                         ws, subtree_end))
 
 
 def tree_attention_workspace_size(**kw) -> int:
@@ -549,3 +559,17 @@ def draft_gather(k_cache: torch.Tensor, v_cache: torch.Tensor, block_table: torc
                           v_layout=v_layout)
     _check(lib().spec_draft_gather(ctypes.byref(a), _stream(stream)), "spec_draft_gather")
     return out_k, out_v, out_pos, out_len
+
+
+def tree_bundle_order(parents):
+    """Bundle (preorder) order of one draft tree, computed by the library on the host.
+
+    parents: sequence-local int array (parents[0] = -1, 0 <= parents[i] < i).  Returns numpy int32
+    arrays (order, new_parents, subtree_end, bundle) in the new numbering; see spec_tree_bundle_order."""
+    import numpy as np
+    par = np.ascontiguousarray(np.asarray(parents, dtype=np.int32))
+    n = len(par)
+    outs = [np.empty(n, dtype=np.int32) for _ in range(4)]
+    st = lib().spec_tree_bundle_order(par.ctypes.data, n, *[o.ctypes.data for o in outs])
+    _check(st, "spec_tree_bundle_order")
+    return tuple(outs)

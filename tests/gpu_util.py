@@ -25,16 +25,19 @@ def bits_of(t: torch.Tensor) -> np.ndarray:
     return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
 
 
-def run_attention(case: synth.AttentionCase, chunk_size=0, split_tiles=0, max_nodes=None, max_ctx=None, v_layout=0):
+def run_attention(case: synth.AttentionCase, chunk_size=0, split_tiles=0, max_nodes=None, max_ctx=None, v_layout=0,
+                  subtree_end=None):
+    """subtree_end: sequence-local int32 [T] (trees in preorder) to take the ancestors from index ranges."""
     import long_context_tree_amd as lt
     t = sdev.attention_tensors(case, dev(), v_layout)
     sizes = np.diff(case.node_offsets)
     mn = int(max_nodes or max(1, sizes.max(initial=1)))
     mc = int(max_ctx if max_ctx is not None else case.ctx_lens.max(initial=0))
+    se = None if subtree_end is None else torch.from_numpy(np.asarray(subtree_end, dtype=np.int32)).to(dev())
     out, lse, h = lt.tree_attention(t["q"], t["k_cache"], t["v_cache"], t["block_table"], t["ctx_lens"],
                                     t["node_offsets"], t["parents"], max_nodes=mn, max_ctx_len=mc,
                                     scale=case.scale, chunk_size=chunk_size, split_tiles=split_tiles,
-                                    v_layout=v_layout)
+                                    v_layout=v_layout, subtree_end=se)
     return out, lse, h, t
 
 

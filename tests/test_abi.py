@@ -29,11 +29,11 @@ def test_exports_every_declared_symbol():
     spec = _lib()
     names = declared_functions()
     assert {"spec_tree_attention", "spec_chunk_salience", "spec_accept_greedy", "spec_accept_rejection"} <= set(names)
-    assert len(names) == 16, names
+    assert len(names) == 17, names
     L = ctypes.CDLL(spec.LIB_PATH)
     for n in names:
         assert hasattr(L, n), n
-    assert spec.lib().spec_abi_version() == 3
+    assert spec.lib().spec_abi_version() == 4
     assert spec.status_string(3) == "SPEC_ERR_WORKSPACE"
 
 
@@ -69,6 +69,7 @@ def _attn_args(spec, **over):
     ("kv_token_stride", 60, 1, "token_stride"),
     ("kv_v_layout", 2, 1, "v_layout"),
     ("kv_v_layout", -1, 1, "v_layout"),
+    ("parents", None, 1, "parents"),
     ("scale", float("nan"), 1, "scale"),
     ("scale", -1.0, 1, "scale"),
     ("chunk_size", 48, 2, "chunk_size"),
@@ -134,7 +135,7 @@ def _greedy_args(spec, **over):
 
 
 @pytest.mark.parametrize("field,value,status,text", [
-    ("vocab", 0, 1, "vocab"), ("max_nodes", 257, 2, "max_nodes"), ("max_path", 0, 1, "max_path"),
+    ("vocab", 0, 1, "vocab"), ("max_nodes", 2049, 2, "max_nodes"), ("max_path", 0, 1, "max_path"),
     ("logits_dtype", 7, 2, "logits_dtype"), ("draft_tokens", None, 1, "draft_tokens"),
     ("batch", 10000, 2, "batch * max_nodes"),
 ])
@@ -176,7 +177,7 @@ def _commit_args(spec, **over):
     ("num_layers", 0, 2, "num_layers"),
     ("num_layers", 129, 2, "num_layers"),
     ("head_dim", 96, 2, "head_dim"),
-    ("max_nodes", 257, 2, "max_nodes"),
+    ("max_nodes", 2049, 2, "max_nodes"),
     ("max_path", 0, 1, "max_path"),
     ("page_size", 12, 2, "page_size"),
     ("token_stride", 60, 1, "token_stride"),
@@ -247,3 +248,18 @@ def test_draft_gather_accepts_valid_arguments_until_the_launch():
     a.num_select, a.chunk_index = 0, None              # no selection: the window alone
     if not torch.cuda.is_available():
         assert spec.lib().spec_draft_gather(ctypes.byref(a), None) == 4 and "HIP error" in spec.last_error()
+
+
+def test_attention_node_limits_depend_on_the_mask():
+    """Up to 256 nodes with ancestor bit masks; up to SPEC_MAX_TREE_NODES with subtree ends."""
+    spec = _lib()
+    se = torch.arange(1, 9, dtype=torch.int32)
+    for mn, with_end, status in ((256, False, None), (257, False, 2), (2048, True, None), (2049, True, 2)):
+        a, keep = _attn_args(spec, max_nodes=mn, kv_block_table_stride=200)
+        if with_end:
+            a.subtree_end, a.parents = se.data_ptr(), None
+        need = spec.lib().spec_tree_attention_workspace_size(ctypes.byref(a))
+        if status is None:
+            assert need > 0, spec.last_error()
+        else:
+            assert need == 0 and "max_nodes" in spec.last_error()
