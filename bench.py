@@ -10,7 +10,8 @@ KV per step), so no cache level can serve a repeated layer.
 
 Prints one JSON line: KV GB/s over the whole step (the metric), steps/s, the roofline of the
 dominant call (spec_tree_attention, timed per call with HIP events on its stream inside the timed
-region) and the CPU oracle's rate on a bounded sample of the same workload.
+region), the step's KV rate against a measured streaming-read rate (spec_read_probe over 4 GiB) beside
+the 8 TB/s spec, and the CPU oracle's rate on a bounded sample of the same workload.
 
     python bench.py [--steps K] [--warmup W] [--nodes N] [--no-cpu-baseline]
 """
@@ -97,6 +98,25 @@ def traffic_record(kernel_src: str, workload: str):
     return rec.get("bytes_per_launch")
 
 
+def read_ceiling(torch, lt, dev, gib: int = 4, reps: int = 5) -> float:
+    """Measured streaming-read rate of this GPU in GB/s: the median time of spec_read_probe (every byte read
+    once with 16-byte loads) over a gib-GiB buffer, the practical ceiling beside the 8 TB/s spec."""
+    import numpy as np
+    x = torch.zeros((gib << 30,), dtype=torch.uint8, device=dev)
+    sink = lt.read_probe(x)
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        lt.read_probe(x, sink)
+        e1.record()
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1) * 1e-3)
+    del x
+    return (gib << 30) / float(np.median(ts)) / 1e9
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -121,6 +141,8 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+    ceiling = read_ceiling(torch, lt, dev)
+    print(f"[bench] measured streaming read: {ceiling:.0f} GB/s", file=sys.stderr, flush=True)
     L, N, depth, layers = args.context, args.nodes, args.depth, args.layers
     Hq, Hkv, D, chunk, top_k, V = 32, 8, 128, 64, 256, 128256
     workload = f"llama8b-{L // 1024}k-n{N}"
@@ -340,6 +362,8 @@ def main():
                    "top_k": top_k, "vocab": V, "acceptance": "greedy", "kv_bytes_per_step": layers * kv_bytes_layer},
         "verify_steps_per_s": round(1000.0 / ms_per_step, 2),
         "hbm_frac_step": round(kv_gbs_step / HBM_PEAK_GBS, 4),
+        "hbm_read_ceiling_gbs": round(ceiling, 1),
+        "hbm_frac_step_of_read_ceiling": round(kv_gbs_step / ceiling, 4),
         "roofline": roof,
         "kernels": kernels,
         "cpu_baseline": cpu,

@@ -370,6 +370,19 @@ typedef struct spec_draft_gather_args {
 int spec_draft_gather(const spec_draft_gather_args* args, void* stream);
 
 /* ------------------------------------------------------------------------------------------
+ * spec_read_probe  (a measurement helper, not a step of the method)
+ *
+ * Reads every byte of data once with 16-byte loads and writes the XOR of all its 32-bit words to
+ * sink[0], so that no load is elided; sink[1 .. SPEC_READ_PROBE_SINK_WORDS) is scratch for the
+ * per-work-group partials.  Timing it over a buffer much larger than the caches gives the streaming-read
+ * rate that bounds the library's HBM-bound calls, a measured ceiling beside the HBM peak of the spec
+ * sheet.  bytes must be a positive multiple of 16 and data 16-byte aligned.
+ * ------------------------------------------------------------------------------------------ */
+#define SPEC_READ_PROBE_SINK_WORDS 2049
+
+int spec_read_probe(const void* data, size_t bytes, uint32_t* sink, void* stream);
+
+/* ------------------------------------------------------------------------------------------
  * spec_tree_bundle_order (host code, no GPU)  [DSC "Features": the bundle scheduler groups
  * draft-tree leaves by their branching ancestor for prefix-coherent target verification]
  *

@@ -565,3 +565,13 @@ extern "C" int spec_draft_gather(const spec_draft_gather_args* a, void* stream) 
   if (e != hipSuccess) return hip_fail(e, "spec_draft_gather launch");
   return ok();
 }
+
+extern "C" int spec_read_probe(const void* data, size_t bytes, uint32_t* sink, void* stream) {
+  if (!data || !aligned(data, 16)) return fail(SPEC_ERR_INVALID_ARGUMENT, "data: NULL or not 16-byte aligned");
+  if (bytes == 0 || bytes % 16) return fail(SPEC_ERR_INVALID_ARGUMENT, "bytes: %zu, must be a positive multiple of 16", bytes);
+  if (!sink || !aligned(sink, 4)) return fail(SPEC_ERR_INVALID_ARGUMENT, "sink: NULL or not 4-byte aligned");
+  static_assert(SPEC_READ_PROBE_SINK_WORDS == spec::kProbeGrid + 1, "sink size");
+  const hipError_t e = spec::launch_read_probe(data, (int64_t)bytes, sink, spec::kProbeGrid, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "spec_read_probe launch");
+  return ok();
+}

@@ -159,4 +159,10 @@ struct DraftGatherParams {
 };
 hipError_t launch_draft_gather(const DraftGatherParams& p, int head_dim, int rope, hipStream_t s);
 
+// ------------------------------------------------------------------------------------------
+// streaming-read probe
+// ------------------------------------------------------------------------------------------
+constexpr int kProbeGrid = 2048;  // work-groups of the probe (8 per CU); the sink holds 1 + this many words
+hipError_t launch_read_probe(const void* data, int64_t bytes, uint32_t* sink, int grid, hipStream_t s);
+
 }  // namespace spec

@@ -59,6 +59,8 @@ def lib():
             f = getattr(L, name)
             f.restype = ctypes.c_size_t
             f.argtypes = [ctypes.POINTER(argt)]
+        L.spec_read_probe.restype = ctypes.c_int
+        L.spec_read_probe.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p]
         L.spec_tree_bundle_order.restype = ctypes.c_int
         L.spec_tree_bundle_order.argtypes = [ctypes.c_void_p, ctypes.c_int32] + [ctypes.c_void_p] * 4
         L.spec_controller_speedup.restype = ctypes.c_double
@@ -573,3 +575,19 @@ def tree_bundle_order(parents):
     st = lib().spec_tree_bundle_order(par.ctypes.data, n, *[o.ctypes.data for o in outs])
     _check(st, "spec_tree_bundle_order")
     return tuple(outs)
+
+
+READ_PROBE_SINK_WORDS = 2049
+
+
+def read_probe(data: torch.Tensor, sink: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Streaming-read probe (a measurement helper): reads every byte of ``data`` (contiguous, 16-byte aligned,
+    a multiple of 16 bytes) with 16-byte loads; returns the int32 sink whose element 0 is the XOR of all the
+    buffer's 32-bit words."""
+    if not data.is_contiguous():
+        raise ValueError("data: must be contiguous")
+    if sink is None:
+        sink = torch.empty(READ_PROBE_SINK_WORDS, dtype=torch.int32, device=data.device)
+    _check(lib().spec_read_probe(data.data_ptr(), data.numel() * data.element_size(), sink.data_ptr(),
+                                 _stream(stream)), "spec_read_probe")
+    return sink

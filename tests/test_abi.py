@@ -29,7 +29,7 @@ def test_exports_every_declared_symbol():
     spec = _lib()
     names = declared_functions()
     assert {"spec_tree_attention", "spec_chunk_salience", "spec_accept_greedy", "spec_accept_rejection"} <= set(names)
-    assert len(names) == 17, names
+    assert len(names) == 18, names
     L = ctypes.CDLL(spec.LIB_PATH)
     for n in names:
         assert hasattr(L, n), n
@@ -263,3 +263,14 @@ def test_attention_node_limits_depend_on_the_mask():
             assert need > 0, spec.last_error()
         else:
             assert need == 0 and "max_nodes" in spec.last_error()
+
+
+def test_read_probe_refuses_bad_arguments():
+    spec = _lib()
+    buf = torch.zeros(64, dtype=torch.uint8)
+    sink = torch.zeros(spec.READ_PROBE_SINK_WORDS, dtype=torch.int32)
+    L = spec.lib()
+    assert L.spec_read_probe(None, 64, sink.data_ptr(), None) == 1 and "data" in spec.last_error()
+    base = buf.data_ptr() + (-buf.data_ptr()) % 16
+    assert L.spec_read_probe(base, 40, sink.data_ptr(), None) == 1 and "bytes" in spec.last_error()
+    assert L.spec_read_probe(base, 32, None, None) == 1 and "sink" in spec.last_error()

@@ -227,3 +227,45 @@ def test_page_sizes(page_size, v_layout):
     compare_out(out, lse, o_ref, l_ref)
     for b, mr in enumerate(m_ref):
         compare_mass(mass.cpu().numpy()[b, :len(mr)].astype(np.float64), mr)
+
+
+def test_batch_invariance():
+    """Ragged batch of chains (the Qwen3-8B shape, 4 drafts): each sequence's outputs and LSE are the same
+    bytes whether it runs alone or inside the batch (with the split size fixed, the plan is the same)."""
+    ctx = [4096, 9001, 6000, 12345]
+    trees = [synth.chain_tree(5) for _ in ctx]
+    case = synth.attention_case(140, ctx_lens=ctx, trees=trees, num_q_heads=32, num_kv_heads=8, head_dim=128)
+    out, lse, _, _ = run_attention(case, chunk_size=64, split_tiles=16, max_ctx=12345)
+    for b in range(len(ctx)):
+        one = synth.attention_case(140, ctx_lens=ctx, trees=trees, num_q_heads=32, num_kv_heads=8, head_dim=128)
+        sel = slice(int(one.node_offsets[b]), int(one.node_offsets[b + 1]))
+        one.ctx_lens = one.ctx_lens[b:b + 1].copy()
+        one.q = one.q[sel].copy()
+        one.parents = one.parents[sel].copy()
+        one.node_offsets = np.array([0, 5], dtype=np.int32)
+        one.kv.block_table = one.kv.block_table[b:b + 1].copy()
+        o1, l1, _, _ = run_attention(one, chunk_size=64, split_tiles=16, max_ctx=12345, max_nodes=5)
+        torch.cuda.synchronize()
+        assert torch.equal(o1.view(torch.int16), out[sel].view(torch.int16)), b
+        assert torch.equal(l1, lse[sel]), b
+
+
+def test_chain_equals_causal_decode():
+    """A chain of drafts is ordinary causal decode: node i's output equals a one-token decode of its query
+    over the L + i committed slots plus its own (the same cache, the same physical pages)."""
+    L, n = 3000, 6
+    case = synth.attention_case(141, ctx_lens=[L], trees=[synth.chain_tree(n)], num_q_heads=32, num_kv_heads=8,
+                                head_dim=128)
+    out, lse, _, _ = run_attention(case)
+    for i in range(n):
+        dec = synth.attention_case(141, ctx_lens=[L], trees=[synth.chain_tree(n)], num_q_heads=32, num_kv_heads=8,
+                                   head_dim=128)
+        dec.ctx_lens = np.array([L + i], dtype=np.int32)
+        dec.q = dec.q[i:i + 1].copy()
+        dec.parents = np.array([-1], dtype=np.int32)
+        dec.node_offsets = np.array([0, 1], dtype=np.int32)
+        o1, l1, _, _ = run_attention(dec, max_ctx=L + n, max_nodes=1)
+        torch.cuda.synchronize()
+        d = (o1.float() - out[i:i + 1].float()).abs().max().item()
+        assert d <= 2 ** -8 * max(out[i].float().abs().max().item(), 1e-3) + 1e-3, (i, d)
+        assert (l1 - lse[i:i + 1]).abs().max().item() <= 1e-4

@@ -86,3 +86,16 @@ def test_commit_of_the_greedy_path_in_place():
     k_ref, v_ref, lens_ref = oracle.kv_commit([kv.k_pool], [kv.v_pool], kv.block_table, ctx, na, pa, 16)
     assert cl.cpu().numpy().tolist() == lens_ref.tolist()
     assert np.array_equal(_bits(kd[0]), k_ref[0]) and np.array_equal(_bits(vd[0]), v_ref[0])
+
+
+def test_read_probe_xor_of_the_buffer():
+    """The streaming-read probe reads every byte: its result is the XOR of all 32-bit words (checked on a
+    ragged size that leaves a tail for the non-unrolled loop)."""
+    import long_context_tree_amd as lt
+    rng = np.random.default_rng(7)
+    for n_words in (4, 4 * 1000003, 4 * (1 << 22)):
+        host = rng.integers(0, 1 << 32, size=n_words, dtype=np.uint64).astype(np.uint32)
+        dev_buf = torch.from_numpy(host.view(np.int32)).to(dev())
+        sink = lt.read_probe(dev_buf)
+        torch.cuda.synchronize()
+        assert int(sink[0].item()) & 0xFFFFFFFF == int(np.bitwise_xor.reduce(host)), n_words
