@@ -524,8 +524,27 @@ __global__ __launch_bounds__(W * 64, (W == 8 ? 1 : 2)) void tree_attn_kernel(Att
       }
     }
   };
+  // Chunk partials computed in one step are stored at the start of the next one, after that step's tile
+  // loads are issued: the wait that closes a step (for the next tile) then does not also wait for a store
+  // issued just before it, which would add a store round trip to every tile.  pend_c: the first chunk of
+  // the pending values, -1 when none (wave-uniform).  16-slot chunks (four values per tile) store at once:
+  // holding four values more would spill registers.
+  constexpr bool DEFER = CM != 2;
+  float pend_v[NS];
+  int pend_c = -1;
+  auto flush_chunks = [&]() __attribute__((always_inline)) {
+    if (pend_c >= 0) {
+#pragma unroll
+      for (int q = 0; q < NS; ++q) {
+        const int c = pend_c + q;
+        if (st_ok && (CM == 0 || c * cs < L)) cbase[(int64_t)c * row_stride_chunk] = pend_v[q];
+      }
+      pend_c = -1;
+    }
+  };
   // stage 3c: per-chunk log2-sum-exp partials against the running max (one 128-byte store per chunk and
-  // wave); with 64-slot (or longer) chunks the tile's sum is accumulated until the chunk ends
+  // wave, deferred as above); with 64-slot (or longer) chunks the tile's sum is accumulated until the
+  // chunk ends
   auto chunk_store = [&](int key0, const float (&csum)[RB][NS]) __attribute__((always_inline)) {
     if (CM == 0) {
 #pragma unroll
@@ -537,7 +556,9 @@ __global__ __launch_bounds__(W * 64, (W == 8 ? 1 : 2)) void tree_attn_kernel(Att
 #pragma unroll
         for (int rb = 1; rb < RB; ++rb)
           if (st_rb == rb) v = m_r[rb] + __builtin_amdgcn_logf(cacc[rb]);
-        if (st_ok) cbase[(int64_t)c * row_stride_chunk] = v;
+        pend_v[0] = v;
+        pend_c = c;
+        if (!DEFER) flush_chunks();
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) cacc[rb] = 0.f;
       }
@@ -549,8 +570,10 @@ __global__ __launch_bounds__(W * 64, (W == 8 ? 1 : 2)) void tree_attn_kernel(Att
 #pragma unroll
         for (int rb = 1; rb < RB; ++rb)
           if (st_rb == rb) v = m_r[rb] + __builtin_amdgcn_logf(csum[rb][q]);
-        if (st_ok && c * cs < L) cbase[(int64_t)c * row_stride_chunk] = v;
+        pend_v[q] = v;
       }
+      pend_c = key0 / cs;
+      if (!DEFER) flush_chunks();
     }
   };
   // stage 3: P.V and the chunk partials of tile t, any tile
@@ -570,6 +593,7 @@ __global__ __launch_bounds__(W * 64, (W == 8 ? 1 : 2)) void tree_attn_kernel(Att
   __syncthreads();
   auto step = [&](int t, uint16_t (*cur)[TILE_EL], uint16_t (*nxt)[TILE_EL]) __attribute__((always_inline)) {
     if (t + 1 < t_end) issue_tile(t + 1, nxt);
+    flush_chunks();
     if (VT && t * kTile + kTile > keys) {
       // the sequence's last tile: its dim-major V slots past the sequence hold whatever the page held
       // (they are not a byte prefix that the load's range check could clear), so they are zeroed in LDS
@@ -597,6 +621,7 @@ __global__ __launch_bounds__(W * 64, (W == 8 ? 1 : 2)) void tree_attn_kernel(Att
     if (t + 1 < t_end) step(t + 1, kv_b, kv_a);
   }
 
+  flush_chunks();
   if (!wave_active) return;
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
