@@ -272,9 +272,18 @@ __global__ __launch_bounds__(256) void walk_kernel(AcceptParams p) {
     tok_s[i] = t;
     first_s[i] = 0x7FFFFFFF;
     if (!REJECT) {
-      unsigned long long k = 0;
-      for (int s = 0; s < p.nseg; ++s) k = umax64(k, p.seg_key[(int64_t)(n0 + i) * p.nseg + s]);
-      amax_s[i] = key_index(k);
+      // four independent accumulators, so that the segment loads are in flight together
+      const unsigned long long* sk = p.seg_key + (int64_t)(n0 + i) * p.nseg;
+      unsigned long long k0 = 0, k1 = 0, k2 = 0, k3 = 0;
+      int s = 0;
+      for (; s + 4 <= p.nseg; s += 4) {
+        k0 = umax64(k0, sk[s]);
+        k1 = umax64(k1, sk[s + 1]);
+        k2 = umax64(k2, sk[s + 2]);
+        k3 = umax64(k3, sk[s + 3]);
+      }
+      for (; s < p.nseg; ++s) k0 = umax64(k0, sk[s]);
+      amax_s[i] = key_index(umax64(umax64(k0, k1), umax64(k2, k3)));
     }
   }
   __syncthreads();
