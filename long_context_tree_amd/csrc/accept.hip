@@ -85,6 +85,31 @@ __device__ double block_sum_f64(double v) {
   return v;
 }
 
+// Block-wide (256 threads) exclusive prefix sum in fp64, in a fixed order (inclusive wave scan by
+// shuffles, then the wave totals in order); every thread gets the sum of the values of lower threads,
+// and *total the sum of all.
+__device__ double block_scan_excl_f64(double v, double* total) {
+  __shared__ double wsum[4];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  double incl = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const double y = __shfl_up(incl, off, 64);
+    if (lane >= off) incl += y;
+  }
+  if (lane == 63) wsum[wave] = incl;
+  __syncthreads();
+  double before = 0.0, all = 0.0;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    if (w < wave) before += wsum[w];
+    all += wsum[w];
+  }
+  __syncthreads();
+  *total = all;
+  return before + incl - v;
+}
+
 // ---- per (segment, node): maximum logit with the lowest index among exact ties ----
 __global__ __launch_bounds__(256) void argmax_seg_kernel(AcceptParams p) {
   const int seg = blockIdx.x;
@@ -250,7 +275,6 @@ __global__ __launch_bounds__(256) void walk_kernel(AcceptParams p) {
   __shared__ int stop_s, depth_s, bad_s, seg_s, bonus_s;
   __shared__ double base_s, thr_s;
   __shared__ double zs[9];
-  __shared__ double scan_s[256];
   const int b = blockIdx.x;
   const int tid = threadIdx.x;
   int n0 = p.node_offsets[b];
@@ -394,29 +418,68 @@ __global__ __launch_bounds__(256) void walk_kernel(AcceptParams p) {
         if (k < 9) zs[k] = z;
         if (z > 0.0 || k == 0) lvl = k;             // a zero residual keeps the previous level
       }
+      seg_s = lvl;                                  // the level, handed to the block below
+    }
+    __syncthreads();
+    {
+      // the segment where the cumulative residual passes u * total: each thread owns a run of consecutive
+      // segments; a fixed-order block scan of the run totals gives every run its starting point
+      const int lvl = seg_s;
       const double* ss = p.seg_sum + (gu * (p.max_children + 1) + lvl) * p.nsegr;
-      const double zl = level_sum(p, gu, lvl);
-      double tot = 0.0;
-      for (int s = 0; s < p.nsegr; ++s) tot += ss[s] / zl;
+      const double rz = 1.0 / level_sum(p, gu, lvl);
+      const int per_s = (p.nsegr + 255) / 256;
+      const int s0 = min(tid * per_s, p.nsegr), s1 = min(s0 + per_s, p.nsegr);
+      double run_tot = 0.0;
+      for (int q = s0; q < s1; ++q) run_tot += ss[q] * rz;
+      double tot;
+      const double start = block_scan_excl_f64(run_tot, &tot);
       const double thr = (double)p.u_sample[gu] * tot;
-      double base = 0.0;
-      int seg = p.nsegr - 1;
-      for (int s = 0; s < p.nsegr; ++s) {
-        const double w = ss[s] / zl;
-        if (base + w > thr) { seg = s; break; }
-        base += w;
+      if (tid == 0) {
+        seg_s = 0x7FFFFFFF;
+        base_s = 0.0;
+        thr_s = thr;
+        bonus_s = 0x7FFFFFFF;
       }
-      if (base + ss[seg] / zl <= thr) {             // rounding left the threshold past the end:
-        base = tot;                                 // fall back to the last segment with mass
-        for (int s = p.nsegr - 1; s >= 0; --s) {
-          base -= ss[s] / zl;
-          if (ss[s] > 0.0) { seg = s; break; }
+      __syncthreads();
+      int my_q = -1;
+      double my_base = 0.0;
+      if (start <= thr && start + run_tot > thr) {
+        double base = start;
+        for (int q = s0; q < s1; ++q) {
+          const double w = ss[q] * rz;
+          if (base + w > thr) {
+            my_q = q;
+            my_base = base;
+            break;
+          }
+          base += w;
         }
+        if (my_q < 0) {                             // rounding inside the run: its last segment with mass
+          for (int q = s1 - 1; q >= s0; --q)
+            if (ss[q] > 0.0) {
+              my_q = q;
+              break;
+            }
+          my_base = start;
+          for (int q = s0; q < my_q; ++q) my_base += ss[q] * rz;
+        }
+        if (my_q >= 0) atomicMin(&seg_s, my_q);     // rounding may let two runs claim: lowest wins
       }
-      seg_s = seg;
-      base_s = base;
-      thr_s = thr;
-      bonus_s = 0x7FFFFFFF;
+      __syncthreads();
+      if (my_q >= 0 && my_q == seg_s) base_s = my_base;
+      if (tid == 0 && seg_s == 0x7FFFFFFF) {        // rounding left the threshold past the end: the last
+        double base = tot;                          // segment with mass
+        int seg = p.nsegr - 1;
+        for (int q = p.nsegr - 1; q >= 0; --q) {
+          base -= ss[q] * rz;
+          if (ss[q] > 0.0) {
+            seg = q;
+            break;
+          }
+        }
+        seg_s = seg;
+        base_s = base;
+      }
     }
     __syncthreads();
     const int seg = seg_s;
@@ -441,14 +504,8 @@ __global__ __launch_bounds__(256) void walk_kernel(AcceptParams p) {
     };
     double mine = 0.0;
     for (int v = a0; v < a1; ++v) mine += res_of(v);
-    scan_s[tid] = mine;
-    __syncthreads();
-    if (tid == 0) {                                 // exclusive scan in thread order
-      double run = 0.0;
-      for (int i = 0; i < 256; ++i) { const double t = scan_s[i]; scan_s[i] = run; run += t; }
-    }
-    __syncthreads();
-    const double lo = base_s + scan_s[tid];
+    double seg_tot;
+    const double lo = base_s + block_scan_excl_f64(mine, &seg_tot);
     const double thr = thr_s;
     if (a0 < a1 && lo + mine > thr && lo <= thr) {
       double run = lo;

@@ -565,7 +565,6 @@ __global__ __launch_bounds__(W * 64, (W == 8 ? 1 : 2)) void tree_attn_kernel(Att
     } else {
 #pragma unroll
       for (int q = 0; q < NS; ++q) {
-        const int c = key0 / cs + q;
         float v = m_r[0] + __builtin_amdgcn_logf(csum[0][q]);
 #pragma unroll
         for (int rb = 1; rb < RB; ++rb)
