@@ -164,17 +164,24 @@ __global__ __launch_bounds__(64) void node_max_kernel(AcceptParams p) {
   if (threadIdx.x == 0) p.node_key[u] = k;
 }
 
-// ---- rejection: per node, the total of residual level r over its segments (one wave per node,
-// fixed order: lanes stride the segments, then a butterfly) ----
-__global__ __launch_bounds__(64) void level_total_kernel(AcceptParams p, int r) {
-  const int64_t u = blockIdx.x;
-  if (u >= total_nodes(p)) return;
-  if (r > 0 && p.n_children[u] < r) return;
+// Total of residual level r of node u over its segments, summed by one wave in a fixed order (lanes
+// stride the segments, then a butterfly): every caller gets the same bits.  Valid in every lane.
+__device__ __forceinline__ double level_total_wave(const AcceptParams& p, int64_t u, int r) {
   const double* s = p.seg_sum + (u * (p.max_children + 1) + r) * p.nsegr;
   double z = 0.0;
-  for (int i = threadIdx.x; i < p.nsegr; i += 64) z += s[i];
+  for (int i = threadIdx.x & 63; i < p.nsegr; i += 64) z += s[i];
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) z += __shfl_xor(z, off);
+  return z;
+}
+
+// ---- rejection: per (node, level), the level's total over its segments, for the walk ----
+__global__ __launch_bounds__(64) void level_total_kernel(AcceptParams p) {
+  const int64_t u = blockIdx.x;
+  const int r = blockIdx.y;
+  if (u >= total_nodes(p)) return;
+  if (r > 0 && p.n_children[u] < r) return;
+  const double z = level_total_wave(p, u, r);
   if (threadIdx.x == 0) p.zsum[u * (p.max_children + 1) + r] = z;
 }
 
@@ -186,25 +193,29 @@ __global__ __launch_bounds__(256) void residual_pass_kernel(AcceptParams p, int 
   if (r > 0 && p.n_children[u] < r) return;
   const double M = (double)row_max(p, u);
   double Z[9];
+  extern __shared__ double rz_s[];                // [max_children + 1] reciprocals of the earlier levels' totals
   const int v0 = seg * kResSegment;
   const int v1 = min(p.vocab, v0 + kResSegment);
   double acc = 0.0;
   if (r == 0) {
     for (int v = v0 + threadIdx.x; v < v1; v += 256) acc += exp((double)load_logit(p, u, v) - M);
   } else {
-    // reciprocals of the earlier levels' normalisers (up to 9 held in registers; deeper levels re-summed);
-    // a product with the reciprocal differs from the quotient by at most one fp64 rounding
-    for (int k = 0; k < r && k < 9; ++k) {
-      const double z = level_sum(p, u, k);
-      Z[k] = z > 0.0 ? 1.0 / z : 0.0;
+    // the earlier levels' totals, summed here (wave w takes levels w, w + 4, ...; each in the order the
+    // walk's totals use), kept as reciprocals: a product with the reciprocal differs from the quotient
+    // by at most one fp64 rounding.  The first 9 are held in registers.
+    for (int k = threadIdx.x >> 6; k < r; k += 4) {
+      const double z = level_total_wave(p, u, k);
+      if ((threadIdx.x & 63) == 0) rz_s[k] = z > 0.0 ? 1.0 / z : 0.0;
     }
+    __syncthreads();
+    for (int k = 0; k < r && k < 9; ++k) Z[k] = rz_s[k];
     const float* q = p.draft_probs + u * (int64_t)p.vocab;
     for (int v = v0 + threadIdx.x; v < v1; v += 256) {
       const double qv = (double)q[v];
       double res = exp((double)load_logit(p, u, v) - M) * Z[0];
       for (int k = 1; k < r; ++k) {
         const double d = fmax(0.0, res - qv);
-        const double zk = k < 9 ? Z[k] : (level_sum(p, u, k) > 0.0 ? 1.0 / level_sum(p, u, k) : 0.0);
+        const double zk = k < 9 ? Z[k] : rz_s[k];
         if (zk > 0.0) res = d * zk;
       }
       acc += fmax(0.0, res - qv);
@@ -565,11 +576,12 @@ hipError_t launch_accept_rejection(const AcceptParams& p, hipStream_t s) {
   hipLaunchKernelGGL(node_max_kernel, dim3(rows), dim3(64), 0, s, p);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   for (int r = 0; r <= p.max_children; ++r) {
-    hipLaunchKernelGGL(residual_pass_kernel, dim3(p.nsegr, rows), dim3(256), 0, s, p, r);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL(level_total_kernel, dim3(rows), dim3(64), 0, s, p, r);
+    hipLaunchKernelGGL(residual_pass_kernel, dim3(p.nsegr, rows), dim3(256),
+                       sizeof(double) * (size_t)(p.max_children + 1), s, p, r);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
+  hipLaunchKernelGGL(level_total_kernel, dim3(rows, p.max_children + 1), dim3(64), 0, s, p);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL(walk_kernel<true>, dim3(p.batch), dim3(256), 0, s, p);
   return hipGetLastError();
 }

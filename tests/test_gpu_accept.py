@@ -153,3 +153,17 @@ def test_rejection_gpu_g1_gate():
     floor = math.sqrt(V / (2 * math.pi * trials))
     print(f"TV={tv:.4f} floor={floor:.4f}")
     assert tv < gold["tv_gate"] and tv < 2.5 * floor
+
+
+@pytest.mark.parametrize("K", [12, 20])
+def test_rejection_many_siblings(K):
+    """A root with K i.i.d. children (plus one grandchild) where every child is rejected: the bonus token is
+    drawn from the root's residual after K levels, past the 9 levels held in registers; bit-exact with the
+    oracle, and the case is outside the tie band."""
+    t = np.array([-1] + [0] * K + [1], dtype=np.int32)
+    case = synth.rejection_case(263, [t], 64, dtype="bf16", draft="independent")
+    ref = oracle.accept_rejection(case.node_offsets, case.parents, case.draft_tokens, case.logits, case.draft_probs,
+                                  case.u_accept, case.u_sample, "bf16", return_margins=True)
+    assert ref[0][0] == 0 and ref[0][3] > 1e-6
+    outs = _rejection(case, 3, K)
+    _check(outs, _expected([x[:3] for x in ref], 1, 3))
