@@ -25,16 +25,17 @@ def _preorder_tree(seed, n, depth, kids=4):
     return new_parents, end
 
 
+@pytest.mark.parametrize("chunk", [16, 32, 64])
 @pytest.mark.parametrize("v_layout", [0, 1])
-def test_interval_mask_equals_bit_masks(v_layout):
+def test_interval_mask_equals_bit_masks(v_layout, chunk):
     trees, ends = zip(*[_preorder_tree(500 + i, n, d) for i, (n, d) in enumerate([(100, 8), (37, 5), (1, 0)])])
     case = synth.attention_case(500, ctx_lens=[700, 64, 5], trees=list(trees), num_q_heads=8, num_kv_heads=2,
                                 head_dim=128)
     se = np.concatenate(ends)
-    a = run_attention(case, chunk_size=64, v_layout=v_layout)
-    b = run_attention(case, chunk_size=64, v_layout=v_layout, subtree_end=se)
+    a = run_attention(case, chunk_size=chunk, v_layout=v_layout)
+    b = run_attention(case, chunk_size=chunk, v_layout=v_layout, subtree_end=se)
     import long_context_tree_amd as lt
-    ma = torch.zeros((3, 11), dtype=torch.float32, device=dev())
+    ma = torch.zeros((3, -(-700 // chunk)), dtype=torch.float32, device=dev())
     mb = torch.zeros_like(ma)
     lt.chunk_salience(a[2], ma)
     lt.chunk_salience(b[2], mb)
@@ -122,3 +123,18 @@ def test_wide_tree_rejection_matches_oracle():
                                   case.u_accept, case.u_sample, "bf16", return_margins=True)
     assert ref[0][3] >= 1e-9, "decision within the tie band"
     _check(outs, _expected([x[:3] for x in ref], 1, depth + 1))
+
+
+@pytest.mark.parametrize("chunk", [16, 32])
+def test_wide_tree_small_chunks_dim_major(chunk):
+    """A 300-node preorder tree with 16- and 32-slot chunk partials and dim-major V, against the oracle."""
+    tree, end = _preorder_tree(525, 300, 10)
+    case = synth.attention_case(525, ctx_lens=[900], trees=[tree], num_q_heads=8, num_kv_heads=2, head_dim=128)
+    out, lse, h, _ = run_attention(case, chunk_size=chunk, subtree_end=end, v_layout=1)
+    import long_context_tree_amd as lt
+    mass = torch.zeros((1, -(-900 // chunk)), dtype=torch.float32, device=dev())
+    lt.chunk_salience(h, mass)
+    torch.cuda.synchronize()
+    o_ref, l_ref, m_ref = oracle_attention(case, chunk)
+    compare_out(out, lse, o_ref, l_ref)
+    compare_mass(mass.cpu().numpy()[0].astype(np.float64), m_ref[0])
