@@ -347,6 +347,83 @@ def main():
                                         "note": f"64 nodes (depth 8, <= 4 children), vocab {V}, bf16 logits + "
                                                 "fp32 draft probabilities read once"}
 
+    # spec_tree_attention alone for narrower trees at the same context, and for the ragged Qwen3-8B-shaped
+    # batch of 4-draft chains: these are HBM-bound (<= 256 query rows per KV head), so the KV rate against
+    # 8 TB/s is their roofline.  Calls rotate over layers with independent KV, so no cache level serves a
+    # repeated layer; medians of 64 calls after 8 warm-up calls.
+    def attention_widths():
+        out = {}
+
+        def timed(arg_list, reps=64):
+            for i in range(8):
+                call(L_.spec_tree_attention(ctypes.byref(arg_list[i % len(arg_list)]), sh))
+            ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+            for i, (e0, e1) in enumerate(ev):
+                e0.record(stream)
+                call(L_.spec_tree_attention(ctypes.byref(arg_list[i % len(arg_list)]), sh))
+                e1.record(stream)
+            torch.cuda.synchronize()
+            return float(np.median([e0.elapsed_time(e1) for e0, e1 in ev])) * 1e3
+
+        def entry(us, kv_bytes, flops, note):
+            gbs = kv_bytes / us / 1e3
+            tf = flops / us / 1e6
+            bound = "mfma" if flops / (MFMA_BF16_PEAK_TFLOPS * 1e12) > kv_bytes / (HBM_PEAK_GBS * 1e9) else "hbm"
+            return {"median_us": round(us, 2), "kv_bytes": kv_bytes, "kv_gbs": round(gbs, 1),
+                    "hbm_frac": round(gbs / HBM_PEAK_GBS, 4), "hbm_frac_of_read_ceiling": round(gbs / ceiling, 4),
+                    "mfma_frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4), "bound": bound, "note": note}
+
+        for name, wn, wd in (("n64-depth8", 64, 8), ("chain-k4", 5, 4)):
+            wtree = (synth.chain_tree(wn) if name.startswith("chain") else
+                     synth.random_tree(synth.rng_for(case, 1, synth.S_TREE), wn, wd))
+            wpar = torch.from_numpy(wtree).to(dev)
+            wno = torch.tensor([0, wn], dtype=torch.int32, device=dev)
+            wq = [sdev.queries_device(case, 100 + l, wn, Hq, D, dev) for l in range(layers)]
+            wo = [torch.empty((wn, Hq, D), dtype=torch.bfloat16, device=dev) for _ in range(layers)]
+            wl = [torch.empty((wn, Hq), dtype=torch.float32, device=dev) for _ in range(layers)]
+            wa = [spec.tree_attention_args(wq[l], pools[l][0], pools[l][1], bt, cl, wno, wpar, max_nodes=wn,
+                                           max_ctx_len=L, chunk_size=chunk, split_tiles=0, out=wo[l], lse=wl[l],
+                                           v_layout=v_layout) for l in range(layers)]
+            wws = spec._workspace(lt.lib().spec_tree_attention_workspace_size(ctypes.byref(wa[0])), dev, None)
+            for x in wa:
+                x.workspace, x.workspace_bytes = wws.data_ptr(), wws.numel()
+            kvb = (L + wn) * Hkv * D * 2 * 2
+            fl = 4.0 * D * Hq * float(np.sum(L + synth.tree_depths(wtree) + 1))
+            out[f"llama8b-{L // 1024}k-{name}"] = entry(timed(wa), kvb, fl,
+                                                      f"{wn}-node tree, chunk partials ({chunk}-token chunks)")
+            del wa, wws, wq, wo, wl
+        # ragged batch: 16 sequences, contexts uniform in [4096, 65536], 4-draft chains, Qwen3-8B layer shape
+        rb_case, rb_n, rb_layers = 5, 5, 4
+        rlens = synth.ragged_ctx_lens(rb_case, 16, 4096, 65536)
+        rpools = [sdev.paged_kv_device(rb_case, l, [int(x) + rb_n for x in rlens], Hkv, D, dev, v_layout=v_layout)
+                  for l in range(rb_layers)]
+        rpar = torch.from_numpy(np.concatenate([synth.chain_tree(rb_n)] * 16).astype(np.int32)).to(dev)
+        rno = torch.arange(0, 16 * rb_n + 1, rb_n, dtype=torch.int32, device=dev)
+        rcl = torch.from_numpy(rlens).to(dev)
+        rq = [sdev.queries_device(rb_case, l, 16 * rb_n, Hq, D, dev) for l in range(rb_layers)]
+        ro = [torch.empty((16 * rb_n, Hq, D), dtype=torch.bfloat16, device=dev) for _ in range(rb_layers)]
+        rlse = [torch.empty((16 * rb_n, Hq), dtype=torch.float32, device=dev) for _ in range(rb_layers)]
+        kvb = int(np.sum(rlens.astype(np.int64) + rb_n)) * Hkv * D * 2 * 2
+        fl = 4.0 * D * Hq * float(np.sum([np.sum(int(x) + np.arange(rb_n) + 1) for x in rlens]))
+        for cs in (chunk, 0):
+            ra_ = [spec.tree_attention_args(rq[l], rpools[l][0], rpools[l][1], rpools[l][2], rcl, rno, rpar,
+                                            max_nodes=rb_n, max_ctx_len=int(rlens.max()), chunk_size=cs,
+                                            split_tiles=0, out=ro[l], lse=rlse[l], v_layout=v_layout)
+                   for l in range(rb_layers)]
+            rws = spec._workspace(lt.lib().spec_tree_attention_workspace_size(ctypes.byref(ra_[0])), dev, None)
+            for x in ra_:
+                x.workspace, x.workspace_bytes = rws.data_ptr(), rws.numel()
+            tag = "with chunk partials" if cs else "without chunk partials"
+            out[f"qwen3-8b-ragged16-chain-k4-{'chunks' if cs else 'nochunks'}"] = entry(
+                timed(ra_), kvb, fl, f"16 sequences, contexts {int(rlens.min())}..{int(rlens.max())} "
+                                     f"(sum {int(rlens.sum())}), {tag}")
+            del ra_, rws
+        del rpools
+        return out
+
+    widths = attention_widths()
+    torch.cuda.synchronize()
+
     cpu = None
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle) ...", file=sys.stderr, flush=True)
@@ -366,6 +443,7 @@ def main():
         "hbm_frac_step_of_read_ceiling": round(kv_gbs_step / ceiling, 4),
         "roofline": roof,
         "kernels": kernels,
+        "attention_widths": widths,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
