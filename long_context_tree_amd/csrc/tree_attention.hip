@@ -25,8 +25,9 @@
 //    only cross-lane step of the online softmax is a 4-lane max (permlane swaps); the row sum is
 //    kept per lane in fp32 and reduced once at the end.  Per-chunk sums of P come from one more
 //    MFMA against a constant ones fragment (every output slot then holds the row's chunk sum).
-//  * Lazy rescaling: the running max only moves when a tile's max exceeds it by more than 2^8,
-//    so the O accumulators are rescaled on a handful of tiles per split.
+//  * Lazy rescaling: the running max only moves when a tile's max exceeds it by more than 2^8, so the
+//    O accumulators are rescaled on a handful of tiles per split.  The exps are taken against the
+//    running max first; only a tile whose probabilities exceed 2^8 computes its max and redoes them.
 //  * Keys >= ctx_len are tree slots: visible iff the key's node is an ancestor-or-self of the
 //    row's node.  The relation comes from ancestor bit masks built in LDS from the parent array
 //    (up to 256 nodes), or, for trees in preorder (the bundle order of the DiffSpec README,
@@ -384,16 +385,13 @@ __global__ __launch_bounds__(W * 64, (W == 8 ? 1 : 2)) void tree_attn_kernel(Att
           s[rb][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[kk & 1][j], qreg[rb][kk], s[rb][j], 0, 0, 0);
     }
   };
-  // stage 2a: mask the tile's scores, the row maxima; true (wave-uniform) when some row's running max
-  // must move (lazy rescaling: only when a tile's max exceeds it by more than 2^kRescale)
+  // stage 2a: in a tile that reaches past the context, mask the scores of slots a row may not see
   float mt[RB];
-  auto stage_max = [&](int t) __attribute__((always_inline)) -> bool {
+  auto stage_mask = [&](int t) __attribute__((always_inline)) {
     const int key0 = t * kTile;
-    const bool edge = key0 + kTile > L;           // tile holds tree slots or slots past the end
-    bool resc = false;
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
-      if (__builtin_expect(edge, 0)) {
+      {
 #pragma unroll
         for (int j = 0; j < 4; ++j)
 #pragma unroll
@@ -410,6 +408,15 @@ __global__ __launch_bounds__(W * 64, (W == 8 ? 1 : 2)) void tree_attn_kernel(Att
             if (!vis) s[rb][j][i] = -INFINITY;
           }
       }
+    }
+  };
+  // stage 2b (only when stage 2c found a probability above 2^kRescale): the rows' tile maxima; true
+  // (wave-uniform) when some row's running max must move (lazy rescaling: only when a tile's max exceeds
+  // it by more than 2^kRescale)
+  auto stage_max = [&]() __attribute__((always_inline)) -> bool {
+    bool resc = false;
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
       float mx = fmaxf(fmaxf(s[rb][0][0], s[rb][0][1]), fmaxf(s[rb][0][2], s[rb][0][3]));
 #pragma unroll
       for (int j = 1; j < 4; ++j)
@@ -419,7 +426,7 @@ __global__ __launch_bounds__(W * 64, (W == 8 ? 1 : 2)) void tree_attn_kernel(Att
     }
     return __builtin_amdgcn_ballot_w64(resc) != 0;
   };
-  // stage 2b: move the running max of the rows that need it, rescaling O, l and the chunk accumulator
+  // stage 2b': move the running max of the rows that need it, rescaling O, l and the chunk accumulator
   auto stage_rescale = [&]() __attribute__((always_inline)) {
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
@@ -432,7 +439,8 @@ __global__ __launch_bounds__(W * 64, (W == 8 ? 1 : 2)) void tree_attn_kernel(Att
       m_r[rb] = mnew;
     }
   };
-  // stage 2c: probabilities against the running max (fp32 row sums, bf16 P fragments)
+  // stage 2c: probabilities against the running max (bf16 P fragments; esum: this lane's fp32 sum of them)
+  float esum[RB];
   auto stage_exp = [&](bf16x8 (&pout)[RB][2]) __attribute__((always_inline)) {
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
@@ -452,7 +460,7 @@ __global__ __launch_bounds__(W * 64, (W == 8 ? 1 : 2)) void tree_attn_kernel(Att
         }
         pout[rb][h2] = v;
       }
-      l_r[rb] += e0 + e1;
+      esum[rb] = e0 + e1;
     }
   };
   // stage 3a: O^T[dim][row] += V^T . P^T for the tile at key0 (V^T fragments from vt, two dim blocks
@@ -608,8 +616,23 @@ __global__ __launch_bounds__(W * 64, (W == 8 ? 1 : 2)) void tree_attn_kernel(Att
     }
     if (wave_active) {
       stage_qk(t, cur[0]);
-      if (stage_max(t)) stage_rescale();
+      if (__builtin_expect(t * kTile + kTile > L, 0)) stage_mask(t);
+      // The exps run against the running max with no tile max first.  A probability above 2^kRescale
+      // makes its lane's sum exceed 2^kRescale (on a split's first tile, where the max is still -1e30,
+      // every sum is infinite); only then are the tile maxima taken, the running max moved and the exps
+      // redone.  That is the same decision the max would give, on a handful of tiles per split, and saves
+      // the max reduction and its cross-lane steps on all the others.
       stage_exp(pb);
+      bool big = false;
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) big |= esum[rb] > 0x1p8f;
+      static_assert(kRescale == 8.0f, "the sum test above is 2^kRescale");
+      if (__builtin_expect(__builtin_amdgcn_ballot_w64(big) != 0, 0)) {
+        if (stage_max()) stage_rescale();
+        stage_exp(pb);
+      }
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) l_r[rb] += esum[rb];
       stage_pv(t, cur[1], pb);
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this thread's loads of the next tile landed
