@@ -502,11 +502,15 @@ __global__ __launch_bounds__(W * 64, (W == 8 ? 1 : 2)) void tree_attn_kernel(Att
   auto chunk_mfma = [&](int key0, const bf16x8 (&pin)[RB][2], bool edge, float (&csum)[RB][NS]) __attribute__((always_inline)) {
     bf16x8 a_all[2] = {ones, ones}, a_lo[2] = {ones_lo, ones_lo}, a_hi[2] = {ones_hi, ones_hi};
     if (edge) {
+      // nv comes out of an opaque (volatile) statement, so the compares and selects below cannot be hoisted
+      // out of this branch: hoisted, they would run on every tile (16 per half), not only in the edge tile
+      int nv = L - key0;                              // context slots left in this tile
+      asm volatile("" : "+s"(nv));
 #pragma unroll
       for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
         for (int e = 0; e < 8; ++e)
-          if (key0 + pkey(h2, e) >= L) {
+          if (pkey(h2, e) >= nv) {
             a_all[h2][e] = (__bf16)0.0f;
             a_lo[h2][e] = (__bf16)0.0f;
             a_hi[h2][e] = (__bf16)0.0f;
