@@ -253,8 +253,33 @@ __global__ __launch_bounds__(W * 64, (W == 8 ? 1 : 2)) void tree_attn_kernel(Att
       ld_voff[i] = ((uint32_t)row * tstride + (uint32_t)src) * 2u;
     }
   }
+  // A wave's loads are all K or all V (KB is a multiple of LOADS), LOADS * 64 / CPR consecutive keys.  When
+  // they sit in one page (pages of >= that many keys, or any tile inside a page longer than a tile), one
+  // page-id lookup and one buffer descriptor serve them all.
+  constexpr int WAVE_KEYS = LOADS * 64 / CPR;
+  static_assert(KB % LOADS == 0, "a wave's loads must be all K or all V");
+  const bool wave_is_v = wave * LOADS >= KB;
+  const bool one_page = !(VT && wave_is_v) && (pshift > 6 || WAVE_KEYS <= (1 << pshift));
   auto issue_tile = [&](int t, uint16_t (*kv)[TILE_EL]) __attribute__((always_inline)) {
     const int key0 = t * kTile;
+    if (one_page) {
+      const int key_w = key0 + ((wave * LOADS * 64) % (kTile * CPR)) / CPR;
+      int pi = (key_w >> pshift) - pg_first;
+      pi = pi < pg_count ? pi : pg_count - 1;
+      const int pg = __builtin_amdgcn_readfirstlane(pg_lds[pi]);
+      const int first_key = pshift > 6 ? key0 : (key_w & ~pmask);
+      const int span = pshift > 6 ? kTile : (1 << pshift);
+      int valid = keys - first_key;
+      valid = valid < 0 ? 0 : (valid > span ? span : valid);
+      if (pg < 0) valid = 0;
+      const uint32_t row0 = pshift > 6 ? (uint32_t)(key0 & pmask) * tstride : 0u;
+      const uint16_t* b = (wave_is_v ? vbase : kbase) + (uint64_t)(uint32_t)(pg < 0 ? 0 : pg) * (uint32_t)p.page_stride + row0;
+#pragma unroll
+      for (int i = 0; i < LOADS; ++i)
+        buffer_load_lds16(b, (uint32_t)valid * tstride * 2u, &kv[wave_is_v ? 1 : 0][((wave * LOADS + i) % KB) * 512],
+                          ld_voff[i]);
+      return;
+    }
     // every load reads one page: look all page ids up first (LDS reads issued together, one wait)
     int pgv[LOADS];
 #pragma unroll
@@ -346,6 +371,9 @@ __global__ __launch_bounds__(W * 64, (W == 8 ? 1 : 2)) void tree_attn_kernel(Att
   }
   const float c2 = p.scale_log2;
   const int cs = p.chunk_size;
+  // chunk of a context slot: a shift for power-of-two chunk sizes (no per-tile scalar division)
+  const int cs_shift = (cs > 0 && (cs & (cs - 1)) == 0) ? __builtin_ctz((unsigned)cs) : -1;
+  auto chunk_of = [&](int key) __attribute__((always_inline)) -> int { return cs_shift >= 0 ? key >> cs_shift : key / cs; };
   const int row_stride_chunk = p.max_nodes * p.Hq;
   // chunk-partial rows: the lanes of group lg store row block lg (RB consecutive 16-row blocks, one store)
   const int st_rb = lg % RB;
@@ -561,7 +589,7 @@ __global__ __launch_bounds__(W * 64, (W == 8 ? 1 : 2)) void tree_attn_kernel(Att
     if (CM == 0) {
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) cacc[rb] += csum[rb][0];
-      const int c = key0 / cs;
+      const int c = chunk_of(key0);
       const int cend = min((c + 1) * cs, L);
       if (key0 + kTile >= cend) {
         float v = m_r[0] + __builtin_amdgcn_logf(cacc[0]);
@@ -583,7 +611,7 @@ __global__ __launch_bounds__(W * 64, (W == 8 ? 1 : 2)) void tree_attn_kernel(Att
           if (st_rb == rb) v = m_r[rb] + __builtin_amdgcn_logf(csum[rb][q]);
         pend_v[q] = v;
       }
-      pend_c = key0 / cs;
+      pend_c = chunk_of(key0);
       if (!DEFER) flush_chunks();
     }
   };
