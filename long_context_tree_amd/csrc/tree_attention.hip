@@ -253,31 +253,42 @@ __global__ __launch_bounds__(W * 64, (W == 8 ? 1 : 2)) void tree_attn_kernel(Att
       ld_voff[i] = ((uint32_t)row * tstride + (uint32_t)src) * 2u;
     }
   }
-  // A wave's loads are all K or all V (KB is a multiple of LOADS), LOADS * 64 / CPR consecutive keys.  When
-  // they sit in one page (pages of >= that many keys, or any tile inside a page longer than a tile), one
-  // page-id lookup and one buffer descriptor serve them all.
-  constexpr int WAVE_KEYS = LOADS * 64 / CPR;
-  static_assert(KB % LOADS == 0, "a wave's loads must be all K or all V");
+  // A wave's loads are all K or all V (KB is a multiple of LOADS), LOADS * 64 / CPR consecutive keys, in
+  // groups of 16 keys (GL loads) that never straddle a page when pages hold >= 16 tokens.  Then one page-id
+  // lookup and one buffer descriptor serve each group: one per tile step for an 8-wave work-group at
+  // D = 128, two for a 4-wave one.
+  constexpr int KPL = 64 / CPR;                     // keys per load
+  constexpr int GL = 16 / KPL < LOADS ? 16 / KPL : LOADS;   // loads per 16-key group
+  static_assert(KB % LOADS == 0 && LOADS % GL == 0, "a wave's loads must be all K or all V, in whole groups");
   const bool wave_is_v = wave * LOADS >= KB;
-  const bool one_page = !(VT && wave_is_v) && (pshift > 6 || WAVE_KEYS <= (1 << pshift));
+  const bool grouped = !(VT && wave_is_v) && pshift >= 4;
   auto issue_tile = [&](int t, uint16_t (*kv)[TILE_EL]) __attribute__((always_inline)) {
     const int key0 = t * kTile;
-    if (one_page) {
-      const int key_w = key0 + ((wave * LOADS * 64) % (kTile * CPR)) / CPR;
-      int pi = (key_w >> pshift) - pg_first;
-      pi = pi < pg_count ? pi : pg_count - 1;
-      const int pg = __builtin_amdgcn_readfirstlane(pg_lds[pi]);
-      const int first_key = pshift > 6 ? key0 : (key_w & ~pmask);
-      const int span = pshift > 6 ? kTile : (1 << pshift);
-      int valid = keys - first_key;
-      valid = valid < 0 ? 0 : (valid > span ? span : valid);
-      if (pg < 0) valid = 0;
-      const uint32_t row0 = pshift > 6 ? (uint32_t)(key0 & pmask) * tstride : 0u;
-      const uint16_t* b = (wave_is_v ? vbase : kbase) + (uint64_t)(uint32_t)(pg < 0 ? 0 : pg) * (uint32_t)p.page_stride + row0;
+    if (grouped) {
+      int pgs[LOADS / GL];
 #pragma unroll
-      for (int i = 0; i < LOADS; ++i)
-        buffer_load_lds16(b, (uint32_t)valid * tstride * 2u, &kv[wave_is_v ? 1 : 0][((wave * LOADS + i) % KB) * 512],
-                          ld_voff[i]);
+      for (int g = 0; g < LOADS / GL; ++g) {      // page ids of the groups (LDS reads issued together)
+        const int key_w = key0 + (((wave * LOADS + g * GL) * 64) % (kTile * CPR)) / CPR;
+        int pi = (key_w >> pshift) - pg_first;
+        pi = pi < pg_count ? pi : pg_count - 1;
+        pgs[g] = pg_lds[pi];
+      }
+#pragma unroll
+      for (int g = 0; g < LOADS / GL; ++g) {
+        const int key_w = key0 + (((wave * LOADS + g * GL) * 64) % (kTile * CPR)) / CPR;
+        const int pg = __builtin_amdgcn_readfirstlane(pgs[g]);
+        const int first_key = pshift > 6 ? key0 : (key_w & ~pmask);
+        const int span = pshift > 6 ? kTile : (1 << pshift);
+        int valid = keys - first_key;
+        valid = valid < 0 ? 0 : (valid > span ? span : valid);
+        if (pg < 0) valid = 0;
+        const uint32_t row0 = pshift > 6 ? (uint32_t)(key0 & pmask) * tstride : 0u;
+        const uint16_t* b = (wave_is_v ? vbase : kbase) + (uint64_t)(uint32_t)(pg < 0 ? 0 : pg) * (uint32_t)p.page_stride + row0;
+#pragma unroll
+        for (int i = g * GL; i < (g + 1) * GL; ++i)
+          buffer_load_lds16(b, (uint32_t)valid * tstride * 2u, &kv[wave_is_v ? 1 : 0][((wave * LOADS + i) % KB) * 512],
+                            ld_voff[i]);
+      }
       return;
     }
     // every load reads one page: look all page ids up first (LDS reads issued together, one wait)
