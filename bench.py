@@ -373,25 +373,30 @@ def main():
                     "hbm_frac": round(gbs / HBM_PEAK_GBS, 4), "hbm_frac_of_read_ceiling": round(gbs / ceiling, 4),
                     "mfma_frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4), "bound": bound, "note": note}
 
-        for name, wn, wd in (("n64-depth8", 64, 8), ("chain-k4", 5, 4)):
+        # (the 32K and 64K contexts use the first slots of the same pools: a shorter committed length)
+        for name, wn, wd, wl in (("n64-depth8", 64, 8, L), ("chain-k4", 5, 4, L), ("n64-depth8", 64, 8, 32768),
+                                 ("n64-depth8", 64, 8, 65536)):
+            if wl > L:
+                continue
             wtree = (synth.chain_tree(wn) if name.startswith("chain") else
                      synth.random_tree(synth.rng_for(case, 1, synth.S_TREE), wn, wd))
             wpar = torch.from_numpy(wtree).to(dev)
             wno = torch.tensor([0, wn], dtype=torch.int32, device=dev)
+            wcl = torch.tensor([wl], dtype=torch.int32, device=dev)
             wq = [sdev.queries_device(case, 100 + l, wn, Hq, D, dev) for l in range(layers)]
             wo = [torch.empty((wn, Hq, D), dtype=torch.bfloat16, device=dev) for _ in range(layers)]
-            wl = [torch.empty((wn, Hq), dtype=torch.float32, device=dev) for _ in range(layers)]
-            wa = [spec.tree_attention_args(wq[l], pools[l][0], pools[l][1], bt, cl, wno, wpar, max_nodes=wn,
-                                           max_ctx_len=L, chunk_size=chunk, split_tiles=0, out=wo[l], lse=wl[l],
+            wlse = [torch.empty((wn, Hq), dtype=torch.float32, device=dev) for _ in range(layers)]
+            wa = [spec.tree_attention_args(wq[l], pools[l][0], pools[l][1], bt, wcl, wno, wpar, max_nodes=wn,
+                                           max_ctx_len=wl, chunk_size=chunk, split_tiles=0, out=wo[l], lse=wlse[l],
                                            v_layout=v_layout) for l in range(layers)]
             wws = spec._workspace(lt.lib().spec_tree_attention_workspace_size(ctypes.byref(wa[0])), dev, None)
             for x in wa:
                 x.workspace, x.workspace_bytes = wws.data_ptr(), wws.numel()
-            kvb = (L + wn) * Hkv * D * 2 * 2
-            fl = 4.0 * D * Hq * float(np.sum(L + synth.tree_depths(wtree) + 1))
-            out[f"llama8b-{L // 1024}k-{name}"] = entry(timed(wa), kvb, fl,
-                                                      f"{wn}-node tree, chunk partials ({chunk}-token chunks)")
-            del wa, wws, wq, wo, wl
+            kvb = (wl + wn) * Hkv * D * 2 * 2
+            fl = 4.0 * D * Hq * float(np.sum(wl + synth.tree_depths(wtree) + 1))
+            out[f"llama8b-{wl // 1024}k-{name}"] = entry(timed(wa), kvb, fl,
+                                                       f"{wn}-node tree, chunk partials ({chunk}-token chunks)")
+            del wa, wws, wq, wo, wlse
         # ragged batch: 16 sequences, contexts uniform in [4096, 65536], 4-draft chains, Qwen3-8B layer shape
         rb_case, rb_n, rb_layers = 5, 5, 4
         rlens = synth.ragged_ctx_lens(rb_case, 16, 4096, 65536)
