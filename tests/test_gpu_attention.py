@@ -269,3 +269,34 @@ def test_chain_equals_causal_decode():
         d = (o1.float() - out[i:i + 1].float()).abs().max().item()
         assert d <= 2 ** -8 * max(out[i].float().abs().max().item(), 1e-3) + 1e-3, (i, d)
         assert (l1 - lse[i:i + 1]).abs().max().item() <= 1e-4
+
+
+@pytest.mark.parametrize("v_layout", [0, 1])
+@pytest.mark.parametrize("chunk,split", [(64, 4), (128, 4), (32, 3), (16, 5)])
+def test_rising_scores_rescale_mid_split(chunk, split, v_layout):
+    """Keys whose magnitude grows along the context make later tiles' score maxima jump past the running
+    max by far more than the lazy-rescale headroom, several times inside each split: the exps are redone
+    against a moved max, and O, the row sums and the chunk accumulators are rescaled mid-split (with
+    128-slot chunks, between the two tiles of one chunk)."""
+    r = synth.rng_for(106, 0, 0)
+    case = synth.attention_case(106, ctx_lens=[1000], trees=[synth.random_tree(r, 16, 4)], num_q_heads=8,
+                                num_kv_heads=2, head_dim=128)
+    kv = case.kv
+    k = synth.bf16_to_f32(kv.k_pool).astype(np.float64)
+    for tkn in range(int(kv.slots[0])):
+        pg, slot = kv.block_table[0, tkn // kv.page_size], tkn % kv.page_size
+        k[pg, :, slot, :] *= 1.0 + 0.02 * tkn             # many rows see their tile max jump by > 8 (log2) inside a split
+    kv.k_pool[...] = synth.bf16_bits(k.astype(np.float32))
+    # the softmax is now nearly one-hot, so the outputs are V-sized; V / 8 (exact in bf16) keeps them in the
+    # range the output tolerance is set for, and leaves the scores (the rescale path) unchanged
+    kv.v_pool[...] = synth.bf16_bits((synth.bf16_to_f32(kv.v_pool) * 0.125).astype(np.float32))
+    print(f"case=rising chunk={chunk} split={split} v_layout={v_layout}", flush=True)
+    out, lse, h, t = run_attention(case, chunk_size=chunk, split_tiles=split, v_layout=v_layout)
+    import long_context_tree_amd as lt
+    n_ch = -(-int(case.ctx_lens.max()) // chunk)
+    mass = torch.full((1, n_ch), 7.0, dtype=torch.float32, device=dev())
+    lt.chunk_salience(h, mass)
+    torch.cuda.synchronize()
+    o_ref, l_ref, m_ref = oracle_attention(case, chunk)
+    compare_out(out, lse, o_ref, l_ref)
+    compare_mass(mass.cpu().numpy().astype(np.float64)[0, :len(m_ref[0])], m_ref[0])
