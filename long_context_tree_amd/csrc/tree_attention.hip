@@ -663,8 +663,10 @@ __global__ __launch_bounds__(W * 64, (W == 8 ? 1 : 2)) void tree_attn_kernel(Att
       // The exps run against the running max with no tile max first.  A probability above 2^kRescale
       // makes its lane's sum exceed 2^kRescale (on a split's first tile, where the max is still -1e30,
       // every sum is infinite); only then are the tile maxima taken, the running max moved and the exps
-      // redone.  That is the same decision the max would give, on a handful of tiles per split, and saves
-      // the max reduction and its cross-lane steps on all the others.
+      // redone.  That is the decision the tile max would give (they can differ only for a probability
+      // that rounds to exactly 2^kRescale, where either is valid: the headroom only bounds how large a
+      // probability may grow), on a handful of tiles per split, and it saves the max reduction and its
+      // cross-lane steps on all the others.
       stage_exp(pb);
       bool big = false;
 #pragma unroll
