@@ -300,3 +300,44 @@ def test_rising_scores_rescale_mid_split(chunk, split, v_layout):
     o_ref, l_ref, m_ref = oracle_attention(case, chunk)
     compare_out(out, lse, o_ref, l_ref)
     compare_mass(mass.cpu().numpy().astype(np.float64)[0, :len(m_ref[0])], m_ref[0])
+
+
+@pytest.mark.parametrize("ctx,k,kind", [(32768, 256, "ties"), (32768, 1, "ties"), (32768, 256, "equal"),
+                                        (1600, 256, "ties"), (32768, 256, "zeros"), (32768, 200, "distinct")])
+def test_topk_order_ties_and_padding(ctx, k, kind):
+    """Exact top-k: (mass desc, index asc) with planted ties, equal and zero masses, and -1 / 0 padding
+    when there are fewer chunks than k.  The masses are planted as large fp32 values in the accumulator,
+    so one layer's attention mass (~1e-4 per chunk) leaves them unchanged when it is accumulated."""
+    import long_context_tree_amd as lt
+    import oracle
+    r = synth.rng_for(107, 0, 0)
+    case = synth.attention_case(107, ctx_lens=[ctx], trees=[synth.random_tree(r, 4, 2)], num_q_heads=4,
+                                num_kv_heads=1, head_dim=64)
+    chunk = 16
+    n_ch = -(-ctx // chunk)
+    rng = np.random.default_rng(ctx + k)
+    base = np.float32(1 << 27)                      # fp32 spacing 16 here: the added mass rounds away
+    if kind == "ties":
+        planted = base + 16 * rng.integers(0, 64, n_ch)
+    elif kind == "equal":
+        planted = np.full(n_ch, base)
+    elif kind == "zeros":
+        planted = np.where(rng.random(n_ch) < 0.95, 0.0, base + 16 * rng.integers(0, 8, n_ch))
+    else:
+        planted = base + 16 * rng.permutation(n_ch)
+    planted = planted.astype(np.float32)
+    print(f"topk ctx={ctx} k={k} kind={kind}", flush=True)
+    out, lse, h, t = run_attention(case, chunk_size=chunk)
+    width = max(n_ch, k)                            # the row may be wider than the sequence's chunks (top_k <= width)
+    row = np.zeros(width, dtype=np.float32)
+    row[:n_ch] = planted
+    mass = torch.from_numpy(row[None, :].copy()).to(dev())
+    before = mass.clone()
+    _, ti, tm = lt.chunk_salience(h, mass, accumulate=True, top_k=k)
+    torch.cuda.synchronize()
+    m = mass.cpu().numpy()[0, :n_ch].astype(np.float64)
+    if kind != "zeros":
+        assert np.array_equal(m, before.cpu().numpy()[0, :n_ch].astype(np.float64)), "the planted masses moved"
+    idx_ref, val_ref = oracle.topk_chunks(m, k)
+    assert np.array_equal(ti.cpu().numpy()[0].astype(np.int64), idx_ref)
+    assert np.array_equal(tm.cpu().numpy()[0].astype(np.float64), val_ref.astype(np.float32).astype(np.float64))
