@@ -11,7 +11,10 @@ KV per step), so no cache level can serve a repeated layer.
 Prints one JSON line: KV GB/s over the whole step (the metric), steps/s, the roofline of the
 dominant call (spec_tree_attention, timed per call with HIP events on its stream inside the timed
 region), the step's KV rate against a measured streaming-read rate (spec_read_probe over 4 GiB) beside
-the 8 TB/s spec, and the CPU oracle's rate on a bounded sample of the same workload.
+the 8 TB/s spec, and the CPU oracle's rate on a bounded sample of the same workload.  After the timed
+region, the other calls of the path are timed alone ("kernels"), and spec_tree_attention alone for the
+HBM-bound shapes ("attention_widths": 64-node trees at 32K, 64K and 128K, a 4-draft chain at 128K, and
+a ragged batch of 16 Qwen3-8B-shaped chains).
 
     python bench.py [--steps K] [--warmup W] [--nodes N] [--no-cpu-baseline]
 """
