@@ -9,11 +9,16 @@
 // Both are HBM streams over the [nodes][vocab] logits (16-33 MB at vocab 128K), so the work is
 // spread over (vocab segment x node) work-groups with fixed-order reductions, and only the tree
 // walk itself runs in one work-group per sequence:
-//   argmax_seg     per (node, 8192-token segment): the packed key (ordered value, ~index) maximum,
-//                  i.e. the largest logit with the lowest index among exact ties
-//   residual_pass  (rejection) level r = 0: sum exp(l - M); level r >= 1, for nodes with >= r
-//                  children: sum max(0, res_{r-1} - q), with res_{r-1} rebuilt per element from the
-//                  earlier levels' normalisers (all fp64, exp evaluated in fp64)
+//   argmax_seg     (greedy) per (node, 8192-token segment): the packed key (ordered value, ~index)
+//                  maximum, i.e. the largest logit with the lowest index among exact ties
+//   max_sum_seg    (rejection) per (node, 2048-token segment): the same key, and level 0's
+//                  sum exp(l - m_s) against the segment maximum m_s, from one read of the logits;
+//                  node_max then takes the row maximum M and scales each sum by exp(m_s - M)
+//   residual_pass  (rejection) level r >= 1, for nodes with >= r children: sum max(0, res_{r-1} - q),
+//                  with res_{r-1} rebuilt per element from the earlier levels' normalisers
+//                  (all fp64, exp evaluated in fp64)
+// Each thread of the rejection passes loads its run of 8 consecutive entries before using any of them,
+// so a pass costs one round trip to memory.
 //   walk           per sequence: accept tests of every child in parallel (a child is tested only
 //                  after all earlier siblings were rejected, so its residual level is its sibling
 //                  rank), first accepted child per node by LDS atomic-min, walk from the root,
@@ -125,18 +130,29 @@ __global__ __launch_bounds__(256) void argmax_seg_kernel(AcceptParams p) {
   int v = v0;
   if (vec) {
     const int nvec = (v1 - v0) / per;
-    for (int i = threadIdx.x; i < nvec; i += 256) {
-      const u32x4 w = *reinterpret_cast<const u32x4*>(row + (int64_t)(v0 + i * per) * esz);
-      const int base = v0 + i * per;
-      if (p.bf16) {
+    // four loads in flight per round trip; an index past the end repeats the last load, whose keys
+    // (value, index) are then seen twice, which leaves the maximum unchanged
+    for (int i0 = threadIdx.x; i0 < nvec; i0 += 4 * 256) {
+      u32x4 w[4];
+      int base[4];
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          best = umax64(best, pack_key(__uint_as_float(w[k] << 16), base + 2 * k));
-          best = umax64(best, pack_key(__uint_as_float(w[k] & 0xFFFF0000u), base + 2 * k + 1));
+      for (int j = 0; j < 4; ++j) {
+        const int i = min(i0 + 256 * j, nvec - 1);
+        base[j] = v0 + i * per;
+        w[j] = *reinterpret_cast<const u32x4*>(row + (int64_t)base[j] * esz);
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if (p.bf16) {
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            best = umax64(best, pack_key(__uint_as_float(w[j][k] << 16), base[j] + 2 * k));
+            best = umax64(best, pack_key(__uint_as_float(w[j][k] & 0xFFFF0000u), base[j] + 2 * k + 1));
+          }
+        } else {
+#pragma unroll
+          for (int k = 0; k < 4; ++k) best = umax64(best, pack_key(__uint_as_float(w[j][k]), base[j] + k));
         }
-      } else {
-#pragma unroll
-        for (int k = 0; k < 4; ++k) best = umax64(best, pack_key(__uint_as_float(w[k]), base + k));
       }
     }
     v = v0 + nvec * per;
@@ -153,15 +169,30 @@ __device__ __forceinline__ double level_sum(const AcceptParams& p, int64_t u, in
   return p.zsum[u * (p.max_children + 1) + k];
 }
 
-// ---- rejection: per node, the row-maximum key over the argmax segments (one wave per node) ----
+// ---- rejection: per node, the row-maximum key over the segments (one wave per node); then the
+// level-0 segment sums, taken against each segment's own maximum m_s, are brought to the row maximum M:
+// sum exp(l - m_s) * exp(m_s - M) ----
 __global__ __launch_bounds__(64) void node_max_kernel(AcceptParams p) {
   const int64_t u = blockIdx.x;
-  if (u >= total_nodes(p)) return;
-  unsigned long long k = 0;
-  for (int s = threadIdx.x; s < p.nseg; s += 64) k = umax64(k, p.seg_key[u * p.nseg + s]);
+  // seg_key has a row for every row of the grid: its reads go out together with the row-count read
+  const int tn = total_nodes(p);
+  // the first key and level-0 sum of each lane stay in registers for the rescale below
+  const int s_first = threadIdx.x;
+  double* s0 = p.seg_sum + u * (p.max_children + 1) * p.nsegr;
+  const unsigned long long k_first = s_first < p.nseg ? p.seg_key[u * p.nseg + s_first] : 0ull;
+  const double sum_first = s_first < p.nsegr ? s0[s_first] : 0.0;
+  unsigned long long k = k_first;
+  for (int s = s_first + 64; s < p.nseg; s += 64) k = umax64(k, p.seg_key[u * p.nseg + s]);
+  if (u >= tn) return;
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) k = umax64(k, shfl_xor_u64(k, off));
   if (threadIdx.x == 0) p.node_key[u] = k;
+  const double M = (double)key_value(k);
+  for (int s = s_first; s < p.nsegr; s += 64) {
+    const double ms = (double)key_value(s == s_first ? k_first : p.seg_key[u * p.nseg + s]);
+    const double sum = s == s_first ? sum_first : s0[s];
+    s0[s] = ms > -INFINITY ? sum * exp(ms - M) : 0.0;
+  }
 }
 
 // Total of residual level r of node u over its segments, summed by one wave in a fixed order (lanes
@@ -179,27 +210,117 @@ __device__ __forceinline__ double level_total_wave(const AcceptParams& p, int64_
 __global__ __launch_bounds__(64) void level_total_kernel(AcceptParams p) {
   const int64_t u = blockIdx.x;
   const int r = blockIdx.y;
-  if (u >= total_nodes(p)) return;
-  if (r > 0 && p.n_children[u] < r) return;
+  // the workspace has an entry for every row of the grid: all reads go out before the tests
+  const int tn = total_nodes(p);
+  const int nc = p.n_children[u];
   const double z = level_total_wave(p, u, r);
+  if ((u >= tn) | ((r > 0) & (nc < r))) return;
   if (threadIdx.x == 0) p.zsum[u * (p.max_children + 1) + r] = z;
 }
 
-// ---- rejection: one residual level for every node that needs it ----
-__global__ __launch_bounds__(256) void residual_pass_kernel(AcceptParams p, int r) {
+// A thread's run of kResPer consecutive vocabulary entries [a0, a1) of row u (a1 - a0 <= kResPer): the
+// logits as fp32 and, if want_q, the draft probabilities.  Every load is issued before any value is
+// used (one round trip to memory instead of one per entry); 16-byte loads where the run is whole and
+// aligned.  Entries at and past a1 are left 0.
+constexpr int kResPer = kResSegment / 256;
+static_assert(kResPer == 8, "a run is one 16-byte load of bf16 logits and two of fp32 probabilities");
+
+__device__ __forceinline__ void load_run(const AcceptParams& p, int64_t u, int a0, int a1, bool want_q,
+                                         float (&lg)[kResPer], float (&qv)[kResPer]) {
+  const bool whole = a1 - a0 == kResPer;
+  if (p.bf16) {
+    const uint16_t* row = reinterpret_cast<const uint16_t*>(p.logits) + u * p.vocab + a0;
+    if (whole && ((uintptr_t)row & 15) == 0) {
+      const u32x4 w = *reinterpret_cast<const u32x4*>(row);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        lg[2 * k] = __uint_as_float(w[k] << 16);
+        lg[2 * k + 1] = __uint_as_float(w[k] & 0xFFFF0000u);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < kResPer; ++i) lg[i] = a0 + i < a1 ? __uint_as_float((uint32_t)row[i] << 16) : 0.f;
+    }
+  } else {
+    const float* row = reinterpret_cast<const float*>(p.logits) + u * p.vocab + a0;
+    if (whole && ((uintptr_t)row & 15) == 0) {
+      const u32x4 w0 = *reinterpret_cast<const u32x4*>(row), w1 = *reinterpret_cast<const u32x4*>(row + 4);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        lg[k] = __uint_as_float(w0[k]);
+        lg[4 + k] = __uint_as_float(w1[k]);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < kResPer; ++i) lg[i] = a0 + i < a1 ? row[i] : 0.f;
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < kResPer; ++i) qv[i] = 0.f;
+  if (want_q) {
+    const float* row = p.draft_probs + u * p.vocab + a0;
+    if (whole && ((uintptr_t)row & 15) == 0) {
+      const u32x4 w0 = *reinterpret_cast<const u32x4*>(row), w1 = *reinterpret_cast<const u32x4*>(row + 4);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        qv[k] = __uint_as_float(w0[k]);
+        qv[4 + k] = __uint_as_float(w1[k]);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < kResPer; ++i) qv[i] = a0 + i < a1 ? row[i] : 0.f;
+    }
+  }
+}
+
+// ---- rejection: per (node, residual segment) the maximum key and the level-0 sum sum exp(l - m_s)
+// against the segment's own maximum m_s, from one read of the logits (the row maximum is not known
+// yet; node_max_kernel rescales the sums to it) ----
+__global__ __launch_bounds__(256) void max_sum_seg_kernel(AcceptParams p) {
   const int seg = blockIdx.x;
   const int64_t u = blockIdx.y;
   if (u >= total_nodes(p)) return;
-  if (r > 0 && p.n_children[u] < r) return;
-  const double M = (double)row_max(p, u);
-  double Z[9];
+  const int v0 = seg * kResSegment;
+  const int v1 = min(p.vocab, v0 + kResSegment);
+  const int a0 = min(v1, v0 + (int)threadIdx.x * kResPer), a1 = min(v1, a0 + kResPer);
+  float lg[kResPer], qv[kResPer];
+  load_run(p, u, a0, a1, false, lg, qv);
+  unsigned long long best = 0;
+#pragma unroll
+  for (int i = 0; i < kResPer; ++i)
+    if (a0 + i < a1) best = umax64(best, pack_key(lg[i], a0 + i));
+  best = block_max_u64(best);
+  const double m = (double)key_value(best);
+  double acc = 0.0;                               // this thread's run, summed in order
+  if (m > -INFINITY) {                            // a segment of -inf logits has no mass
+#pragma unroll
+    for (int i = 0; i < kResPer; ++i)
+      if (a0 + i < a1) acc += exp((double)lg[i] - m);
+  }
+  acc = block_sum_f64(acc);
+  if (threadIdx.x == 0) {
+    p.seg_key[u * p.nseg + seg] = best;
+    p.seg_sum[u * (p.max_children + 1) * p.nsegr + seg] = acc;
+  }
+}
+
+// ---- rejection: one residual level r >= 1 for every node that needs it ----
+__global__ __launch_bounds__(256) void residual_pass_kernel(AcceptParams p, int r) {
+  const int seg = blockIdx.x;
+  const int64_t u = blockIdx.y;
+  // both reads are issued before either test (n_children has an entry for every row of the grid)
+  const int tn = total_nodes(p);
+  const int nc = p.n_children[u];
+  if ((u >= tn) | (nc < r)) return;
   extern __shared__ double rz_s[];                // [max_children + 1] reciprocals of the earlier levels' totals
   const int v0 = seg * kResSegment;
   const int v1 = min(p.vocab, v0 + kResSegment);
-  double acc = 0.0;
-  if (r == 0) {
-    for (int v = v0 + threadIdx.x; v < v1; v += 256) acc += exp((double)load_logit(p, u, v) - M);
-  } else {
+  const int a0 = min(v1, v0 + (int)threadIdx.x * kResPer), a1 = min(v1, a0 + kResPer);
+  float lg[kResPer], qv[kResPer];
+  load_run(p, u, a0, a1, true, lg, qv);
+  const double M = (double)row_max(p, u);
+  double acc = 0.0;                               // this thread's run, summed in order
+  {
     // the earlier levels' totals, summed here (wave w takes levels w, w + 4, ...; each in the order the
     // walk's totals use), kept as reciprocals: a product with the reciprocal differs from the quotient
     // by at most one fp64 rounding.  The first 9 are held in registers.
@@ -208,17 +329,28 @@ __global__ __launch_bounds__(256) void residual_pass_kernel(AcceptParams p, int 
       if ((threadIdx.x & 63) == 0) rz_s[k] = z > 0.0 ? 1.0 / z : 0.0;
     }
     __syncthreads();
-    for (int k = 0; k < r && k < 9; ++k) Z[k] = rz_s[k];
-    const float* q = p.draft_probs + u * (int64_t)p.vocab;
-    for (int v = v0 + threadIdx.x; v < v1; v += 256) {
-      const double qv = (double)q[v];
-      double res = exp((double)load_logit(p, u, v) - M) * Z[0];
-      for (int k = 1; k < r; ++k) {
-        const double d = fmax(0.0, res - qv);
-        const double zk = k < 9 ? Z[k] : rz_s[k];
+    // the first 9 in registers: every index below is a constant after unrolling (an array indexed by a
+    // loop variable would live in scratch memory, one read per entry and level)
+    double Z[9];
+#pragma unroll
+    for (int k = 0; k < 9; ++k) Z[k] = k < r ? rz_s[k] : 0.0;
+#pragma unroll
+    for (int i = 0; i < kResPer; ++i) {
+      if (a0 + i >= a1) continue;
+      const double q = (double)qv[i];
+      double res = exp((double)lg[i] - M) * Z[0];
+#pragma unroll
+      for (int k = 1; k < 9; ++k) {
+        if (k >= r) break;
+        const double d = fmax(0.0, res - q);
+        if (Z[k] > 0.0) res = d * Z[k];
+      }
+      for (int k = 9; k < r; ++k) {
+        const double d = fmax(0.0, res - q);
+        const double zk = rz_s[k];
         if (zk > 0.0) res = d * zk;
       }
-      acc += fmax(0.0, res - qv);
+      acc += fmax(0.0, res - q);
     }
   }
   acc = block_sum_f64(acc);
@@ -345,14 +477,17 @@ __global__ __launch_bounds__(256) void walk_kernel(AcceptParams p) {
       } else {
         const int64_t gu = n0 + u;
         const int r = rank_s[c];
+        // every read of the test is issued before any is used: the first 9 level totals (entries past r
+        // repeat level r, which exists, and are not used), the row maximum, q(x) and the logit
         double Z[9];
-        for (int k = 0; k <= r && k < 9; ++k) {
-          const double z = level_sum(p, gu, k);
-          Z[k] = z > 0.0 ? 1.0 / z : 0.0;            // reciprocals, as in the residual passes
-        }
+#pragma unroll
+        for (int k = 0; k < 9; ++k) Z[k] = level_sum(p, gu, k < r ? k : r);
         const double M = (double)row_max(p, gu);
         const double qx = (double)p.draft_probs[gu * p.vocab + x];
-        const double e = exp((double)load_logit(p, gu, x) - M);
+        const float lx = load_logit(p, gu, x);
+#pragma unroll
+        for (int k = 0; k < 9; ++k) Z[k] = Z[k] > 0.0 ? 1.0 / Z[k] : 0.0;   // reciprocals, as in the residual passes
+        const double e = exp((double)lx - M);
         double res = e * Z[0];
         for (int k = 1; k <= r; ++k) {
           const double d = fmax(0.0, res - qx);
@@ -422,11 +557,12 @@ __global__ __launch_bounds__(256) void walk_kernel(AcceptParams p) {
     // inverse CDF of the residual left at u after all its children were rejected
     const int64_t gu = n0 + u;
     const int r = nch_s[u];
+    if (tid <= r && tid < 9) zs[tid] = level_sum(p, gu, tid);   // read in parallel
+    __syncthreads();
     if (tid == 0) {
       int lvl = 0;
       for (int k = 0; k <= r; ++k) {
-        const double z = level_sum(p, gu, k);
-        if (k < 9) zs[k] = z;
+        const double z = k < 9 ? zs[k] : level_sum(p, gu, k);
         if (z > 0.0 || k == 0) lvl = k;             // a zero residual keeps the previous level
       }
       seg_s = lvl;                                  // the level, handed to the block below
@@ -496,16 +632,17 @@ __global__ __launch_bounds__(256) void walk_kernel(AcceptParams p) {
     const int seg = seg_s;
     const int v0 = seg * kResSegment;
     const int v1 = min(p.vocab, v0 + kResSegment);
-    const int per = kResSegment / 256;
-    const int a0 = v0 + tid * per;
-    const int a1 = min(v1, a0 + per);
+    const int a0 = min(v1, v0 + tid * kResPer);
+    const int a1 = min(v1, a0 + kResPer);
+    float lg[kResPer], qr[kResPer];
+    load_run(p, gu, a0, a1, true, lg, qr);
     const double M = (double)row_max(p, gu);
     const float* q = p.draft_probs + gu * (int64_t)p.vocab;
     double Z[9];
     for (int k = 0; k <= r && k < 9; ++k) Z[k] = zs[k] > 0.0 ? 1.0 / zs[k] : 0.0;
-    auto res_of = [&](int v) -> double {
-      const double qv = (double)q[v];
-      double res = exp((double)load_logit(p, gu, v) - M) * Z[0];
+    auto res_from = [&](float l, float qf) -> double {
+      const double qv = (double)qf;
+      double res = exp((double)l - M) * Z[0];
       for (int k = 1; k <= r; ++k) {
         const double dd = fmax(0.0, res - qv);
         const double zk = k < 9 ? Z[k] : (level_sum(p, gu, k) > 0.0 ? 1.0 / level_sum(p, gu, k) : 0.0);
@@ -513,17 +650,30 @@ __global__ __launch_bounds__(256) void walk_kernel(AcceptParams p) {
       }
       return res;
     };
+    auto res_of = [&](int v) -> double { return res_from(load_logit(p, gu, v), q[v]); };
+    // this thread's run of the residual, evaluated once and kept for the claim below
+    double rv[kResPer];
     double mine = 0.0;
-    for (int v = a0; v < a1; ++v) mine += res_of(v);
+#pragma unroll
+    for (int i = 0; i < kResPer; ++i) {
+      rv[i] = a0 + i < a1 ? res_from(lg[i], qr[i]) : 0.0;
+      mine += rv[i];
+    }
     double seg_tot;
     const double lo = base_s + block_scan_excl_f64(mine, &seg_tot);
     const double thr = thr_s;
     if (a0 < a1 && lo + mine > thr && lo <= thr) {
       double run = lo;
       int pick = a1 - 1;
-      for (int v = a0; v < a1; ++v) {
-        run += res_of(v);
-        if (run > thr) { pick = v; break; }
+      bool found = false;
+#pragma unroll
+      for (int i = 0; i < kResPer; ++i) {         // the first entry whose running sum passes thr
+        if (found || a0 + i >= a1) continue;
+        run += rv[i];
+        if (run > thr) {
+          pick = a0 + i;
+          found = true;
+        }
       }
       atomicMin(&bonus_s, pick);                    // rounding may let two threads claim: lowest wins
     }
@@ -550,9 +700,9 @@ size_t greedy_ws_bytes(int batch, int max_nodes, int nseg) {
   return align_up(sizeof(unsigned long long) * (size_t)batch * max_nodes * nseg, 256);
 }
 
-size_t rejection_ws_bytes(int batch, int max_nodes, int nseg, int nsegr, int max_children) {
+size_t rejection_ws_bytes(int batch, int max_nodes, int nsegr, int max_children) {
   const size_t nodes = (size_t)batch * max_nodes, lv = (size_t)max_children + 1;
-  return greedy_ws_bytes(batch, max_nodes, nseg) + align_up(sizeof(unsigned long long) * nodes, 256) +
+  return greedy_ws_bytes(batch, max_nodes, nsegr) + align_up(sizeof(unsigned long long) * nodes, 256) +
          align_up(sizeof(double) * nodes * lv * nsegr, 256) + align_up(sizeof(double) * nodes * lv, 256) +
          align_up(sizeof(int32_t) * nodes, 256);
 }
@@ -571,11 +721,11 @@ hipError_t launch_accept_rejection(const AcceptParams& p, hipStream_t s) {
   hipLaunchKernelGGL(tree_info_kernel, dim3(p.batch), dim3(256), 0, s, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(argmax_seg_kernel, dim3(p.nseg, rows), dim3(256), 0, s, p);
+  hipLaunchKernelGGL(max_sum_seg_kernel, dim3(p.nsegr, rows), dim3(256), 0, s, p);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL(node_max_kernel, dim3(rows), dim3(64), 0, s, p);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  for (int r = 0; r <= p.max_children; ++r) {
+  for (int r = 1; r <= p.max_children; ++r) {
     hipLaunchKernelGGL(residual_pass_kernel, dim3(p.nsegr, rows), dim3(256),
                        sizeof(double) * (size_t)(p.max_children + 1), s, p, r);
     if ((e = hipGetLastError()) != hipSuccess) return e;

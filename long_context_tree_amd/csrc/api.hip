@@ -366,16 +366,16 @@ static int check_rejection(const spec_accept_rejection_args* a) {
 size_t spec_accept_rejection_workspace_size(const spec_accept_rejection_args* args) {
   if (check_rejection(args) != SPEC_OK) return 0;
   g_err.clear();
-  return spec::rejection_ws_bytes(args->base.batch, args->base.max_nodes, nseg_of(args->base.vocab),
-                                  nsegr_of(args->base.vocab), args->max_children);
+  return spec::rejection_ws_bytes(args->base.batch, args->base.max_nodes, nsegr_of(args->base.vocab),
+                                  args->max_children);
 }
 
 int spec_accept_rejection(const spec_accept_rejection_args* args, void* stream) {
   int st = check_rejection(args);
   if (st != SPEC_OK) return st;
   const spec_accept_greedy_args& g = args->base;
-  const int nseg = nseg_of(g.vocab), nsegr = nsegr_of(g.vocab);
-  const size_t need = spec::rejection_ws_bytes(g.batch, g.max_nodes, nseg, nsegr, args->max_children);
+  const int nsegr = nsegr_of(g.vocab);
+  const size_t need = spec::rejection_ws_bytes(g.batch, g.max_nodes, nsegr, args->max_children);
   st = check_workspace(g.workspace, g.workspace_bytes, need, "spec_accept_rejection");
   if (st != SPEC_OK) return st;
   spec::AcceptParams p = accept_params(&g);
@@ -384,9 +384,10 @@ int spec_accept_rejection(const spec_accept_rejection_args* args, void* stream) 
   p.u_accept = args->u_accept;
   p.u_sample = args->u_sample;
   p.nsegr = nsegr;
+  p.nseg = nsegr;                                 // rejection keeps its segment maxima per residual segment
   char* ws = static_cast<char*>(g.workspace);
   const size_t nodes = (size_t)g.batch * g.max_nodes, lv = (size_t)args->max_children + 1;
-  size_t off = spec::greedy_ws_bytes(g.batch, g.max_nodes, nseg);
+  size_t off = spec::greedy_ws_bytes(g.batch, g.max_nodes, nsegr);
   p.node_key = reinterpret_cast<unsigned long long*>(ws + off);
   off += spec::align_up(sizeof(unsigned long long) * nodes, 256);
   p.seg_sum = reinterpret_cast<double*>(ws + off);

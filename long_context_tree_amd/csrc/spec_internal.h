@@ -99,7 +99,8 @@ struct AcceptParams {
   int32_t* out_num_accepted;
   int32_t* out_path_nodes;
   int32_t* out_tokens;
-  unsigned long long* seg_key;   // [batch*max_nodes][nseg] packed (ordered value, ~index)
+  unsigned long long* seg_key;   // [batch*max_nodes][nseg] packed (ordered value, ~index); rejection:
+                                 // one per residual segment (nseg == nsegr)
   // rejection only
   int max_children;
   const float* draft_probs;
@@ -111,7 +112,7 @@ struct AcceptParams {
   int32_t* n_children;   // [batch*max_nodes]
 };
 size_t greedy_ws_bytes(int batch, int max_nodes, int nseg);
-size_t rejection_ws_bytes(int batch, int max_nodes, int nseg, int nsegr, int max_children);
+size_t rejection_ws_bytes(int batch, int max_nodes, int nsegr, int max_children);
 hipError_t launch_accept_greedy(const AcceptParams& p, hipStream_t s);
 
 // ------------------------------------------------------------------------------------------
