@@ -223,7 +223,7 @@ __global__ __launch_bounds__(64) void level_total_kernel(AcceptParams p) {
 // used (one round trip to memory instead of one per entry); 16-byte loads where the run is whole and
 // aligned.  Entries at and past a1 are left 0.
 constexpr int kResPer = kResSegment / 256;
-static_assert(kResPer == 8, "a run is one 16-byte load of bf16 logits and two of fp32 probabilities");
+static_assert(kResPer % 8 == 0, "a run is whole 16-byte loads of bf16 logits and of fp32 probabilities");
 
 __device__ __forceinline__ void load_run(const AcceptParams& p, int64_t u, int a0, int a1, bool want_q,
                                          float (&lg)[kResPer], float (&qv)[kResPer]) {
@@ -231,12 +231,16 @@ __device__ __forceinline__ void load_run(const AcceptParams& p, int64_t u, int a
   if (p.bf16) {
     const uint16_t* row = reinterpret_cast<const uint16_t*>(p.logits) + u * p.vocab + a0;
     if (whole && ((uintptr_t)row & 15) == 0) {
-      const u32x4 w = *reinterpret_cast<const u32x4*>(row);
+      u32x4 w[kResPer / 8];
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        lg[2 * k] = __uint_as_float(w[k] << 16);
-        lg[2 * k + 1] = __uint_as_float(w[k] & 0xFFFF0000u);
-      }
+      for (int j = 0; j < kResPer / 8; ++j) w[j] = *reinterpret_cast<const u32x4*>(row + 8 * j);
+#pragma unroll
+      for (int j = 0; j < kResPer / 8; ++j)
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          lg[8 * j + 2 * k] = __uint_as_float(w[j][k] << 16);
+          lg[8 * j + 2 * k + 1] = __uint_as_float(w[j][k] & 0xFFFF0000u);
+        }
     } else {
 #pragma unroll
       for (int i = 0; i < kResPer; ++i) lg[i] = a0 + i < a1 ? __uint_as_float((uint32_t)row[i] << 16) : 0.f;
@@ -244,12 +248,13 @@ __device__ __forceinline__ void load_run(const AcceptParams& p, int64_t u, int a
   } else {
     const float* row = reinterpret_cast<const float*>(p.logits) + u * p.vocab + a0;
     if (whole && ((uintptr_t)row & 15) == 0) {
-      const u32x4 w0 = *reinterpret_cast<const u32x4*>(row), w1 = *reinterpret_cast<const u32x4*>(row + 4);
+      u32x4 w[kResPer / 4];
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        lg[k] = __uint_as_float(w0[k]);
-        lg[4 + k] = __uint_as_float(w1[k]);
-      }
+      for (int j = 0; j < kResPer / 4; ++j) w[j] = *reinterpret_cast<const u32x4*>(row + 4 * j);
+#pragma unroll
+      for (int j = 0; j < kResPer / 4; ++j)
+#pragma unroll
+        for (int k = 0; k < 4; ++k) lg[4 * j + k] = __uint_as_float(w[j][k]);
     } else {
 #pragma unroll
       for (int i = 0; i < kResPer; ++i) lg[i] = a0 + i < a1 ? row[i] : 0.f;
@@ -260,12 +265,13 @@ __device__ __forceinline__ void load_run(const AcceptParams& p, int64_t u, int a
   if (want_q) {
     const float* row = p.draft_probs + u * p.vocab + a0;
     if (whole && ((uintptr_t)row & 15) == 0) {
-      const u32x4 w0 = *reinterpret_cast<const u32x4*>(row), w1 = *reinterpret_cast<const u32x4*>(row + 4);
+      u32x4 w[kResPer / 4];
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        qv[k] = __uint_as_float(w0[k]);
-        qv[4 + k] = __uint_as_float(w1[k]);
-      }
+      for (int j = 0; j < kResPer / 4; ++j) w[j] = *reinterpret_cast<const u32x4*>(row + 4 * j);
+#pragma unroll
+      for (int j = 0; j < kResPer / 4; ++j)
+#pragma unroll
+        for (int k = 0; k < 4; ++k) qv[4 * j + k] = __uint_as_float(w[j][k]);
     } else {
 #pragma unroll
       for (int i = 0; i < kResPer; ++i) qv[i] = a0 + i < a1 ? row[i] : 0.f;
@@ -293,9 +299,10 @@ __global__ __launch_bounds__(256) void max_sum_seg_kernel(AcceptParams p) {
   const double m = (double)key_value(best);
   double acc = 0.0;                               // this thread's run, summed in order
   if (m > -INFINITY) {                            // a segment of -inf logits has no mass
+    // branch-free: an entry past the end takes exp(-inf) = +0, which leaves the sum's bits unchanged,
+    // and the eight exps share their constants and interleave
 #pragma unroll
-    for (int i = 0; i < kResPer; ++i)
-      if (a0 + i < a1) acc += exp((double)lg[i] - m);
+    for (int i = 0; i < kResPer; ++i) acc += exp(a0 + i < a1 ? (double)lg[i] - m : -INFINITY);
   }
   acc = block_sum_f64(acc);
   if (threadIdx.x == 0) {
@@ -334,11 +341,11 @@ __global__ __launch_bounds__(256) void residual_pass_kernel(AcceptParams p, int 
     double Z[9];
 #pragma unroll
     for (int k = 0; k < 9; ++k) Z[k] = k < r ? rz_s[k] : 0.0;
+    // branch-free over the run: an entry past the end has q = 0 and exp(-inf) = +0, so it adds +0
 #pragma unroll
     for (int i = 0; i < kResPer; ++i) {
-      if (a0 + i >= a1) continue;
       const double q = (double)qv[i];
-      double res = exp((double)lg[i] - M) * Z[0];
+      double res = exp(a0 + i < a1 ? (double)lg[i] - M : -INFINITY) * Z[0];
 #pragma unroll
       for (int k = 1; k < 9; ++k) {
         if (k >= r) break;
@@ -655,8 +662,8 @@ __global__ __launch_bounds__(256) void walk_kernel(AcceptParams p) {
     double rv[kResPer];
     double mine = 0.0;
 #pragma unroll
-    for (int i = 0; i < kResPer; ++i) {
-      rv[i] = a0 + i < a1 ? res_from(lg[i], qr[i]) : 0.0;
+    for (int i = 0; i < kResPer; ++i) {             // an entry past the end gives +0 (q = 0, exp(-inf) = +0)
+      rv[i] = res_from(a0 + i < a1 ? lg[i] : -INFINITY, qr[i]);
       mine += rv[i];
     }
     double seg_tot;
