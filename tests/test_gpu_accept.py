@@ -49,7 +49,8 @@ def _greedy(case, max_path):
     return outs
 
 
-@pytest.mark.parametrize("name", ["tiny", "tiny_batch", "llama_v128k", "qwen_chains", "ties", "single_nodes"])
+@pytest.mark.parametrize("name", ["tiny", "tiny_batch", "llama_v128k", "qwen_chains", "ties", "single_nodes",
+                                  "odd_vocab"])
 def test_greedy_matches_oracle(name):
     r = synth.rng_for(200, 0, 0)
     if name == "tiny":
@@ -62,6 +63,8 @@ def test_greedy_matches_oracle(name):
         trees, V, dt = [synth.chain_tree(5) for _ in range(16)], 151936, "bf16"
     elif name == "ties":
         trees, V, dt = [synth.random_tree(r, 128, 10) for _ in range(2)], 128256, "bf16"
+    elif name == "odd_vocab":                  # rows off 16-byte boundaries: the entry-by-entry loads
+        trees, V, dt = [synth.random_tree(r, 24, 5), synth.random_tree(r, 9, 3)], 20011, "bf16"
     else:
         trees, V, dt = [synth.chain_tree(1), synth.random_tree(r, 3, 2), synth.chain_tree(1)], 1000, "bf16"
     case = synth.greedy_case(200 + len(name), trees, V, dtype=dt, tie_frac=0.5 if name == "ties" else 0.25)
@@ -167,3 +170,30 @@ def test_rejection_many_siblings(K):
     assert ref[0][0] == 0 and ref[0][3] > 1e-6
     outs = _rejection(case, 3, K)
     _check(outs, _expected([x[:3] for x in ref], 1, 3))
+
+
+@pytest.mark.parametrize("dt,V", [("bf16", 5003), ("f32", 5003), ("bf16", 128256)])
+def test_rejection_odd_vocab_and_masked_segments(dt, V):
+    """Rows whose length is not a multiple of 8 (most rows then start off a 16-byte boundary, so their
+    runs take the entry-by-entry loads, and the last segment is ragged), and target logits of -inf over
+    the whole second 2048-entry segment plus 5% of the other entries (p = 0 there; a segment with no
+    finite logit has no mass at any level): bit-exact with the oracle, every decision outside the tie
+    band."""
+    r = synth.rng_for(270, 0, 0)
+    trees = [synth.random_tree(r, 24, 5), synth.random_tree(r, 9, 3)]
+    case = synth.rejection_case(270 + V % 97, trees, V, dtype=dt, draft="independent")
+    neg = np.uint16(0xFF80) if dt == "bf16" else np.float32(-np.inf)
+    lg = case.logits.copy()
+    lg[:, 2048:4096] = neg
+    hit = synth.rng_for(271, 0, 0).random(lg.shape) < 0.05
+    lg[hit] = neg
+    case.logits = lg
+    rows = oracle.acceptance._rows_f64(lg, dt)
+    assert np.isfinite(rows.max(axis=1)).all()
+    print(f"case={dt} V={V}", flush=True)
+    max_children = max(max(len(c) for c in synth.children_lists(t)) for t in trees)
+    ref = oracle.accept_rejection(case.node_offsets, case.parents, case.draft_tokens, case.logits, case.draft_probs,
+                                  case.u_accept, case.u_sample, dt, return_margins=True)
+    assert all(x[3] > 1e-9 for x in ref)
+    outs = _rejection(case, 12, max(1, max_children))
+    _check(outs, _expected([x[:3] for x in ref], len(trees), 12))
