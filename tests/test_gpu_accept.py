@@ -197,3 +197,15 @@ def test_rejection_odd_vocab_and_masked_segments(dt, V):
     assert all(x[3] > 1e-9 for x in ref)
     outs = _rejection(case, 12, max(1, max_children))
     _check(outs, _expected([x[:3] for x in ref], len(trees), 12))
+
+
+def test_rejection_single_node_trees():
+    """Every tree is its root alone (max_nodes = 1, so max_children = 0: no residual level beyond p): each
+    sequence accepts nothing and draws its bonus token from p, bit-exact with the oracle."""
+    trees = [synth.chain_tree(1) for _ in range(5)]
+    case = synth.rejection_case(275, trees, 3001, dtype="bf16", draft="independent")
+    ref = oracle.accept_rejection(case.node_offsets, case.parents, case.draft_tokens, case.logits, case.draft_probs,
+                                  case.u_accept, case.u_sample, "bf16", return_margins=True)
+    assert all(x[0] == 0 and x[3] > 1e-9 for x in ref)
+    outs = _rejection(case, 2, 0)
+    _check(outs, _expected([x[:3] for x in ref], len(trees), 2))
