@@ -13,10 +13,12 @@
 //                  maximum, i.e. the largest logit with the lowest index among exact ties
 //   max_sum_seg    (rejection) per (node, 2048-token segment): the same key, and level 0's
 //                  sum exp(l - m_s) against the segment maximum m_s, from one read of the logits;
-//                  node_max then takes the row maximum M and scales each sum by exp(m_s - M)
+//                  segment 0 also counts the node's children.  node_max then takes the row maximum
+//                  M and scales each sum by exp(m_s - M)
 //   residual_pass  (rejection) level r >= 1, for nodes with >= r children: sum max(0, res_{r-1} - q),
 //                  with res_{r-1} rebuilt per element from the earlier levels' normalisers
-//                  (all fp64, exp evaluated in fp64)
+//                  (all fp64, exp evaluated in fp64), whose totals every work-group sums in one fixed
+//                  order and segment 0 stores for the walk
 // Each thread of the rejection passes loads its run of 8 consecutive entries before using any of them,
 // so a pass costs one round trip to memory.
 //   walk           per sequence: accept tests of every child in parallel (a child is tested only
@@ -206,18 +208,6 @@ __device__ __forceinline__ double level_total_wave(const AcceptParams& p, int64_
   return z;
 }
 
-// ---- rejection: per (node, level), the level's total over its segments, for the walk ----
-__global__ __launch_bounds__(64) void level_total_kernel(AcceptParams p) {
-  const int64_t u = blockIdx.x;
-  const int r = blockIdx.y;
-  // the workspace has an entry for every row of the grid: all reads go out before the tests
-  const int tn = total_nodes(p);
-  const int nc = p.n_children[u];
-  const double z = level_total_wave(p, u, r);
-  if ((u >= tn) | ((r > 0) & (nc < r))) return;
-  if (threadIdx.x == 0) p.zsum[u * (p.max_children + 1) + r] = z;
-}
-
 // A thread's run of kResPer consecutive vocabulary entries [a0, a1) of row u (a1 - a0 <= kResPer): the
 // logits as fp32 and, if want_q, the draft probabilities.  Every load is issued before any value is
 // used (one round trip to memory instead of one per entry); 16-byte loads where the run is whole and
@@ -284,8 +274,20 @@ __device__ __forceinline__ void load_run(const AcceptParams& p, int64_t u, int a
 // yet; node_max_kernel rescales the sums to it) ----
 __global__ __launch_bounds__(256) void max_sum_seg_kernel(AcceptParams p) {
   const int seg = blockIdx.x;
-  const int64_t u = blockIdx.y;
-  if (u >= total_nodes(p)) return;
+  const int i = blockIdx.y;                       // the node within its sequence
+  const int b = blockIdx.z;
+  const int tn = total_nodes(p);
+  int n0 = p.node_offsets[b];
+  int N = p.node_offsets[b + 1] - n0;
+  N = N < 0 ? 0 : (N > p.max_nodes ? p.max_nodes : N);
+  n0 = n0 < 0 ? 0 : (n0 > (p.batch - 1) * p.max_nodes ? (p.batch - 1) * p.max_nodes : n0);
+  const int64_t u = (int64_t)n0 + i;
+  if (i >= N || u >= tn) return;
+  // segment 0 also counts the node's children (the later ones among the sequence's nodes whose parent
+  // is i), for the residual passes; its parent reads go out with the logit reads
+  int kids = 0;
+  if (seg == 0)
+    for (int j = 1 + (int)threadIdx.x; j < N && n0 + j < tn; j += 256) kids += (p.parents[n0 + j] == i && i < j) ? 1 : 0;
   const int v0 = seg * kResSegment;
   const int v1 = min(p.vocab, v0 + kResSegment);
   const int a0 = min(v1, v0 + (int)threadIdx.x * kResPer), a1 = min(v1, a0 + kResPer);
@@ -308,6 +310,10 @@ __global__ __launch_bounds__(256) void max_sum_seg_kernel(AcceptParams p) {
   if (threadIdx.x == 0) {
     p.seg_key[u * p.nseg + seg] = best;
     p.seg_sum[u * (p.max_children + 1) * p.nsegr + seg] = acc;
+  }
+  if (seg == 0) {                                 // uniform in the work-group
+    const double k = block_sum_f64((double)kids); // exact: at most max_nodes
+    if (threadIdx.x == 0) p.n_children[u] = (int)k;
   }
 }
 
@@ -333,7 +339,10 @@ __global__ __launch_bounds__(256) void residual_pass_kernel(AcceptParams p, int 
     // by at most one fp64 rounding.  The first 9 are held in registers.
     for (int k = threadIdx.x >> 6; k < r; k += 4) {
       const double z = level_total_wave(p, u, k);
-      if ((threadIdx.x & 63) == 0) rz_s[k] = z > 0.0 ? 1.0 / z : 0.0;
+      if ((threadIdx.x & 63) == 0) {
+        rz_s[k] = z > 0.0 ? 1.0 / z : 0.0;
+        if (seg == 0) p.zsum[u * (p.max_children + 1) + k] = z;   // for the walk (the same bits in every pass)
+      }
     }
     __syncthreads();
     // the first 9 in registers: every index below is a constant after unrolling (an array indexed by a
@@ -362,24 +371,6 @@ __global__ __launch_bounds__(256) void residual_pass_kernel(AcceptParams p, int 
   }
   acc = block_sum_f64(acc);
   if (threadIdx.x == 0) p.seg_sum[(u * (p.max_children + 1) + r) * p.nsegr + seg] = acc;
-}
-
-// ---- per sequence: child counts (for the residual passes) ----
-__global__ __launch_bounds__(256) void tree_info_kernel(AcceptParams p) {
-  __shared__ int cnt[kMaxTreeNodes];
-  const int b = blockIdx.x;
-  int n0 = p.node_offsets[b];
-  int N = p.node_offsets[b + 1] - n0;
-  N = N < 0 ? 0 : (N > p.max_nodes ? p.max_nodes : N);
-  n0 = n0 < 0 ? 0 : (n0 > (p.batch - 1) * p.max_nodes ? (p.batch - 1) * p.max_nodes : n0);
-  for (int i = threadIdx.x; i < N; i += 256) cnt[i] = 0;
-  __syncthreads();
-  for (int i = threadIdx.x + 1; i < N; i += 256) {
-    const int pi = p.parents[n0 + i];
-    if (pi >= 0 && pi < i) atomicAdd(&cnt[pi], 1);
-  }
-  __syncthreads();
-  for (int i = threadIdx.x; i < N; i += 256) p.n_children[n0 + i] = cnt[i];
 }
 
 // Child count and sibling rank (earlier siblings) of the nodes tid + 256 q, q < PER; flags a parent
@@ -423,7 +414,7 @@ __global__ __launch_bounds__(256) void walk_kernel(AcceptParams p) {
   __shared__ int par_s[kMaxTreeNodes], tok_s[kMaxTreeNodes], first_s[kMaxTreeNodes], nch_s[kMaxTreeNodes];
   __shared__ int rank_s[kMaxTreeNodes], amax_s[kMaxTreeNodes], path_s[kMaxTreeNodes];
   __shared__ int stop_s, depth_s, bad_s, seg_s, bonus_s;
-  __shared__ double base_s, thr_s;
+  __shared__ double base_s, thr_s, zlast_s;
   __shared__ double zs[9];
   const int b = blockIdx.x;
   const int tid = threadIdx.x;
@@ -564,12 +555,22 @@ __global__ __launch_bounds__(256) void walk_kernel(AcceptParams p) {
     // inverse CDF of the residual left at u after all its children were rejected
     const int64_t gu = n0 + u;
     const int r = nch_s[u];
-    if (tid <= r && tid < 9) zs[tid] = level_sum(p, gu, tid);   // read in parallel
+    // the totals of levels < r were stored by the residual passes; level r's (no pass follows it for this
+    // node) is summed here by wave 0 in the passes' order, so it has the bits they would give it
+    if (tid < 64) {
+      const double z = level_total_wave(p, gu, r);
+      if (tid == 0) {
+        zlast_s = z;
+        if (r < 9) zs[r] = z;
+      }
+    }
+    if (tid < r && tid < 9) zs[tid] = level_sum(p, gu, tid);    // read in parallel
     __syncthreads();
+    auto zsum_of = [&](int k) -> double { return k == r ? zlast_s : level_sum(p, gu, k); };
     if (tid == 0) {
       int lvl = 0;
       for (int k = 0; k <= r; ++k) {
-        const double z = k < 9 ? zs[k] : level_sum(p, gu, k);
+        const double z = k < 9 ? zs[k] : zsum_of(k);
         if (z > 0.0 || k == 0) lvl = k;             // a zero residual keeps the previous level
       }
       seg_s = lvl;                                  // the level, handed to the block below
@@ -580,7 +581,7 @@ __global__ __launch_bounds__(256) void walk_kernel(AcceptParams p) {
       // segments; a fixed-order block scan of the run totals gives every run its starting point
       const int lvl = seg_s;
       const double* ss = p.seg_sum + (gu * (p.max_children + 1) + lvl) * p.nsegr;
-      const double rz = 1.0 / level_sum(p, gu, lvl);
+      const double rz = 1.0 / zsum_of(lvl);
       const int per_s = (p.nsegr + 255) / 256;
       const int s0 = min(tid * per_s, p.nsegr), s1 = min(s0 + per_s, p.nsegr);
       double run_tot = 0.0;
@@ -652,7 +653,7 @@ __global__ __launch_bounds__(256) void walk_kernel(AcceptParams p) {
       double res = exp((double)l - M) * Z[0];
       for (int k = 1; k <= r; ++k) {
         const double dd = fmax(0.0, res - qv);
-        const double zk = k < 9 ? Z[k] : (level_sum(p, gu, k) > 0.0 ? 1.0 / level_sum(p, gu, k) : 0.0);
+        const double zk = k < 9 ? Z[k] : (zsum_of(k) > 0.0 ? 1.0 / zsum_of(k) : 0.0);
         if (zk > 0.0) res = dd * zk;
       }
       return res;
@@ -725,11 +726,9 @@ hipError_t launch_accept_greedy(const AcceptParams& p, hipStream_t s) {
 
 hipError_t launch_accept_rejection(const AcceptParams& p, hipStream_t s) {
   const unsigned rows = (unsigned)(p.batch * p.max_nodes);
-  hipLaunchKernelGGL(tree_info_kernel, dim3(p.batch), dim3(256), 0, s, p);
+  hipLaunchKernelGGL(max_sum_seg_kernel, dim3(p.nsegr, p.max_nodes, p.batch), dim3(256), 0, s, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(max_sum_seg_kernel, dim3(p.nsegr, rows), dim3(256), 0, s, p);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL(node_max_kernel, dim3(rows), dim3(64), 0, s, p);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   for (int r = 1; r <= p.max_children; ++r) {
@@ -737,8 +736,6 @@ hipError_t launch_accept_rejection(const AcceptParams& p, hipStream_t s) {
                        sizeof(double) * (size_t)(p.max_children + 1), s, p, r);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(level_total_kernel, dim3(rows, p.max_children + 1), dim3(64), 0, s, p);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL(walk_kernel<true>, dim3(p.batch), dim3(256), 0, s, p);
   return hipGetLastError();
 }
