@@ -437,10 +437,12 @@ __global__ __launch_bounds__(256) void walk_kernel(AcceptParams p) {
     tok_s[i] = t;
     first_s[i] = 0x7FFFFFFF;
     if (!REJECT) {
-      // four independent accumulators, so that the segment loads are in flight together
+      // four independent accumulators, unrolled so that 16 segment loads (the whole row at V = 128K) are
+      // in flight together
       const unsigned long long* sk = p.seg_key + (int64_t)(n0 + i) * p.nseg;
       unsigned long long k0 = 0, k1 = 0, k2 = 0, k3 = 0;
       int s = 0;
+#pragma unroll 4
       for (; s + 4 <= p.nseg; s += 4) {
         k0 = umax64(k0, sk[s]);
         k1 = umax64(k1, sk[s + 1]);
