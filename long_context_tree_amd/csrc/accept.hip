@@ -374,8 +374,9 @@ __global__ __launch_bounds__(256) void residual_pass_kernel(AcceptParams p, int 
 }
 
 // Child count and sibling rank (earlier siblings) of the nodes tid + 256 q, q < PER; flags a parent
-// array that is not topological or a node with more than max_children children.
-template <int PER>
+// array that is not topological or a node with more than max_children children.  Without COUNT (greedy)
+// only the parent-order checks run.
+template <int PER, bool COUNT>
 __device__ __forceinline__ void child_ranks(const int* par_s, int N, int tid, int max_children, int* rank_s,
                                             int* nch_s, int& bad_s) {
   int own_p[PER], rank[PER], nch[PER];
@@ -388,7 +389,8 @@ __device__ __forceinline__ void child_ranks(const int* par_s, int N, int tid, in
     if (i < N && i > 0 && !(own_p[q] >= 0 && own_p[q] < i)) bad_s = 1;
     if (i == 0 && own_p[q] != -1) bad_s = 1;
   }
-  for (int j = 1; j < N; ++j) {
+  // the counts (rejection only; greedy needs just the parent-order checks above)
+  for (int j = 1; COUNT && j < N; ++j) {
     const int pj = par_s[j];
 #pragma unroll
     for (int q = 0; q < PER; ++q) {
@@ -457,9 +459,10 @@ __global__ __launch_bounds__(256) void walk_kernel(AcceptParams p) {
   // child counts and sibling ranks: each parent entry is read once and compared with the nodes this
   // thread owns (tid, tid + 256, ...): one node per thread for trees of <= 256 nodes, else up to 8
   if (N <= 256)
-    child_ranks<1>(par_s, N, tid, REJECT ? p.max_children : 0x7FFFFFFF, rank_s, nch_s, bad_s);
+    child_ranks<1, REJECT>(par_s, N, tid, REJECT ? p.max_children : 0x7FFFFFFF, rank_s, nch_s, bad_s);
   else
-    child_ranks<kMaxTreeNodes / 256>(par_s, N, tid, REJECT ? p.max_children : 0x7FFFFFFF, rank_s, nch_s, bad_s);
+    child_ranks<kMaxTreeNodes / 256, REJECT>(par_s, N, tid, REJECT ? p.max_children : 0x7FFFFFFF, rank_s, nch_s,
+                                             bad_s);
   __syncthreads();
   if (bad_s) {
     for (int i = tid; i < p.max_path; i += 256) { o_path[i] = -1; o_tok[i] = -1; }
