@@ -26,6 +26,8 @@
 //                  rank), first accepted child per node by LDS atomic-min, walk from the root,
 //                  then the bonus token (greedy: argmax; rejection: inverse CDF of the residual,
 //                  segment found from the segment sums, then an in-segment scan)
+#include <type_traits>
+
 #include "spec_internal.h"
 
 namespace spec {
@@ -143,19 +145,31 @@ __global__ __launch_bounds__(256) void argmax_seg_kernel(AcceptParams p) {
         base[j] = v0 + i * per;
         w[j] = *reinterpret_cast<const u32x4*>(row + (int64_t)base[j] * esz);
       }
+      // the largest value of this round first (one max per entry), then the lowest index holding it
+      // (entries visited from the highest index down, so the last match is the lowest), and one packed key:
+      // the same key as the per-entry maximum, since -0 == +0 here as in ordered()
+      auto round_key = [&](auto ne_c, auto val) -> unsigned long long {
+        constexpr int NE = decltype(ne_c)::value;   // entries per 16-byte load
+        float mv = -INFINITY;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        if (p.bf16) {
+        for (int j = 0; j < 4; ++j)
 #pragma unroll
-          for (int k = 0; k < 4; ++k) {
-            best = umax64(best, pack_key(__uint_as_float(w[j][k] << 16), base[j] + 2 * k));
-            best = umax64(best, pack_key(__uint_as_float(w[j][k] & 0xFFFF0000u), base[j] + 2 * k + 1));
-          }
-        } else {
+          for (int e = 0; e < NE; ++e) mv = fmaxf(mv, val(j, e));
+        int idx = 0x7FFFFFFF;
 #pragma unroll
-          for (int k = 0; k < 4; ++k) best = umax64(best, pack_key(__uint_as_float(w[j][k]), base[j] + k));
-        }
-      }
+        for (int j = 3; j >= 0; --j)
+#pragma unroll
+          for (int e = NE - 1; e >= 0; --e)
+            if (val(j, e) == mv) idx = base[j] + e;
+        return pack_key(mv, idx);
+      };
+      if (p.bf16)
+        best = umax64(best, round_key(std::integral_constant<int, 8>{}, [&](int j, int e) {
+          return __uint_as_float((e & 1) ? (w[j][e >> 1] & 0xFFFF0000u) : (w[j][e >> 1] << 16));
+        }));
+      else
+        best = umax64(best, round_key(std::integral_constant<int, 4>{},
+                                      [&](int j, int e) { return __uint_as_float(w[j][e]); }));
     }
     v = v0 + nvec * per;
   }
