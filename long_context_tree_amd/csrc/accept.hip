@@ -307,10 +307,16 @@ __global__ __launch_bounds__(256) void max_sum_seg_kernel(AcceptParams p) {
   const int a0 = min(v1, v0 + (int)threadIdx.x * kResPer), a1 = min(v1, a0 + kResPer);
   float lg[kResPer], qv[kResPer];
   load_run(p, u, a0, a1, false, lg, qv);
-  unsigned long long best = 0;
+  // this thread's largest logit, then the lowest index holding it (visited from the top down), packed once
+  float mv = -INFINITY;
 #pragma unroll
   for (int i = 0; i < kResPer; ++i)
-    if (a0 + i < a1) best = umax64(best, pack_key(lg[i], a0 + i));
+    if (a0 + i < a1) mv = fmaxf(mv, lg[i]);
+  int idx = a0;
+#pragma unroll
+  for (int i = kResPer - 1; i >= 0; --i)
+    if (a0 + i < a1 && lg[i] == mv) idx = a0 + i;
+  unsigned long long best = a0 < a1 ? pack_key(mv, idx) : 0ull;
   best = block_max_u64(best);
   const double m = (double)key_value(best);
   double acc = 0.0;                               // this thread's run, summed in order
