@@ -52,16 +52,29 @@ __global__ __launch_bounds__(256) void salience_kernel(SalienceParams p) {
       continue;
     }
     const float* x = p.chunk_lse2 + ((int64_t)b * p.ws_max_chunks + c) * stride;
+    const float prev = (p.accumulate && tid == 0) ? *dst : 0.f;   // read now, used after the reduction
     float acc = 0.f;
     int r = 0;
     if (vec) {
       const int nv = rows >> 2;
-      for (int i = tid; i < nv; i += 256) {
-        const float4 a = *reinterpret_cast<const float4*>(x + 4 * i);
-        const float4 m = *reinterpret_cast<const float4*>(l2 + 4 * i);
+      auto add4 = [&](const float4& a, const float4& m) {
         acc += (__builtin_amdgcn_exp2f(a.x - m.x) + __builtin_amdgcn_exp2f(a.y - m.y)) +
                (__builtin_amdgcn_exp2f(a.z - m.z) + __builtin_amdgcn_exp2f(a.w - m.w));
+      };
+      int i = tid;
+      // four pairs of 16-byte loads in flight per round trip; the sum keeps the order i, i + 256, ...
+      for (; i + 3 * 256 < nv; i += 4 * 256) {
+        float4 a[4], m[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          a[j] = *reinterpret_cast<const float4*>(x + 4 * (i + 256 * j));
+          m[j] = *reinterpret_cast<const float4*>(l2 + 4 * (i + 256 * j));
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) add4(a[j], m[j]);
       }
+      for (; i < nv; i += 256)
+        add4(*reinterpret_cast<const float4*>(x + 4 * i), *reinterpret_cast<const float4*>(l2 + 4 * i));
       r = nv << 2;
     }
     for (int i = r + tid; i < rows; i += 256) acc += __builtin_amdgcn_exp2f(x[i] - l2[i]);
@@ -71,7 +84,7 @@ __global__ __launch_bounds__(256) void salience_kernel(SalienceParams p) {
     __syncthreads();
     if (tid == 0) {
       const float tot = ((red[0] + red[1]) + (red[2] + red[3])) * (1.0f / (float)rows);
-      *dst = p.accumulate ? *dst + tot : tot;
+      *dst = p.accumulate ? prev + tot : tot;
     }
     __syncthreads();
   }
