@@ -6,8 +6,9 @@
 // One work-group per (sequence, layer, KV head).  Row i (depth i) moves from slot L + path[i] to
 // slot L + i.  Since path[i] >= i, no move's source is the destination of an earlier or equal row,
 // so rows are moved in increasing order, a batch of rows at a time: the whole batch is read into
-// registers, then written (a source inside the batch may be another row's destination).  A second
-// launch writes the new lengths, after every work-group has read the old ones.
+// registers, then written (a source inside the batch may be another row's destination).  The new
+// lengths are written by work-group (b, 0, 0) when they go to a buffer of their own; when they replace
+// ctx_lens in place, a second launch writes them after every work-group has read the old ones.
 #include "spec_internal.h"
 
 namespace spec {
@@ -24,9 +25,12 @@ __global__ __launch_bounds__(kCommitThreads) void kv_commit_kernel(KvCommitParam
   constexpr int VI = kCommitRows * D / kCommitThreads;        // dim-major V elements per thread and batch
   const int b = blockIdx.x, layer = blockIdx.y, kvh = blockIdx.z;
   const int tid = threadIdx.x;
-  int L = p.ctx_lens[b];
+  const int L_in = p.ctx_lens[b], n_in = p.num_accepted[b];
+  if (p.lengths_in_commit && layer == 0 && kvh == 0 && tid == 0)
+    p.new_ctx_lens[b] = n_in >= 0 ? L_in + 1 + n_in : L_in;   // as kv_lengths_kernel
+  int L = L_in;
   L = L < 0 ? 0 : L;
-  int n = p.num_accepted[b];
+  int n = n_in;
   n = n < p.max_path - 1 ? n : p.max_path - 1;
   n = n < p.max_nodes - 1 ? n : p.max_nodes - 1;
   if (n <= 0) return;
@@ -127,9 +131,14 @@ hipError_t launch_d(const KvCommitParams& p, hipStream_t s) {
 
 }  // namespace
 
-hipError_t launch_kv_commit(const KvCommitParams& p, int head_dim, hipStream_t s) {
+hipError_t launch_kv_commit(const KvCommitParams& p_in, int head_dim, hipStream_t s) {
+  KvCommitParams p = p_in;
+  // separate buffers (no shared element): the move kernel writes the lengths, no second launch
+  const int32_t *a0 = p.ctx_lens, *a1 = p.ctx_lens + p.batch;
+  const int32_t *c0 = p.new_ctx_lens, *c1 = p.new_ctx_lens + p.batch;
+  p.lengths_in_commit = (c1 <= a0 || a1 <= c0) ? 1 : 0;
   hipError_t e = head_dim == 128 ? launch_d<128>(p, s) : launch_d<64>(p, s);
-  if (e != hipSuccess) return e;
+  if (e != hipSuccess || p.lengths_in_commit) return e;
   hipLaunchKernelGGL(kv_lengths_kernel, dim3((unsigned)ceil_div(p.batch, 256)), dim3(256), 0, s, p);
   return hipGetLastError();
 }
