@@ -307,7 +307,8 @@ typedef struct spec_kv_commit_args {
   const int32_t* ctx_lens;      /* int32 [batch] */
   const int32_t* num_accepted;  /* int32 [batch] */
   const int32_t* path_nodes;    /* int32 [batch][max_path] */
-  int32_t* new_ctx_lens;        /* int32 [batch] out; may be ctx_lens itself */
+  int32_t* new_ctx_lens;        /* int32 [batch] out; may be ctx_lens itself, and may overlap num_accepted
+                                   or path_nodes (then the lengths are written by a second launch) */
 } spec_kv_commit_args;
 
 int spec_kv_commit(const spec_kv_commit_args* args, void* stream);

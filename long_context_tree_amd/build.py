@@ -36,9 +36,8 @@ FLAGS = [
 ]
 
 
-# The attention kernel never produces NaN on purpose (masked scores are -inf, never NaN), so its
-# max reductions need no NaN canonicalisation.
-PER_FILE = {"tree_attention.hip": ["-fno-honor-nans"]}
+# extra flags per source file (none at present)
+PER_FILE: dict = {}
 
 
 def build(verbose: bool = False) -> str:

@@ -133,10 +133,17 @@ hipError_t launch_d(const KvCommitParams& p, hipStream_t s) {
 
 hipError_t launch_kv_commit(const KvCommitParams& p_in, int head_dim, hipStream_t s) {
   KvCommitParams p = p_in;
-  // separate buffers (no shared element): the move kernel writes the lengths, no second launch
-  const int32_t *a0 = p.ctx_lens, *a1 = p.ctx_lens + p.batch;
-  const int32_t *c0 = p.new_ctx_lens, *c1 = p.new_ctx_lens + p.batch;
-  p.lengths_in_commit = (c1 <= a0 || a1 <= c0) ? 1 : 0;
+  // The move kernel's work-groups read ctx_lens, num_accepted and path_nodes of their sequence while
+  // work-group (b, 0, 0) writes new_ctx_lens[b].  When new_ctx_lens shares no byte with any of the three,
+  // that write can happen in the move kernel (no second launch); otherwise a second launch writes the
+  // lengths after every work-group has read its inputs.
+  auto disjoint = [&](const void* x, size_t xb) {
+    const char *a = reinterpret_cast<const char*>(p.new_ctx_lens), *c = reinterpret_cast<const char*>(x);
+    return a + sizeof(int32_t) * (size_t)p.batch <= c || c + xb <= a;
+  };
+  p.lengths_in_commit = (disjoint(p.ctx_lens, sizeof(int32_t) * (size_t)p.batch) &&
+                         disjoint(p.num_accepted, sizeof(int32_t) * (size_t)p.batch) &&
+                         disjoint(p.path_nodes, sizeof(int32_t) * (size_t)p.batch * p.max_path)) ? 1 : 0;
   hipError_t e = head_dim == 128 ? launch_d<128>(p, s) : launch_d<64>(p, s);
   if (e != hipSuccess || p.lengths_in_commit) return e;
   hipLaunchKernelGGL(kv_lengths_kernel, dim3((unsigned)ceil_div(p.batch, 256)), dim3(256), 0, s, p);

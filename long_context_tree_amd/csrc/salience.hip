@@ -188,10 +188,13 @@ __global__ __launch_bounds__(1024) void topk_kernel(SalienceParams p) {
     }
   }
   // Element i belongs to thread i mod 1024, so for strides j < 64 both elements of a pair belong to
-  // one wave, whose LDS operations complete in order: those stages need no work-group barrier.
+  // one wave.  A stage reads what the previous stage wrote: after a stage of stride >= 64 (whose swaps
+  // write elements owned by another wave) that needs a work-group barrier, so every stage of stride
+  // >= 32 starts with one; a stage of stride < 32 follows one of stride < 64, whose writes all came
+  // from its own wave, and the wave's LDS operations complete in order.
   for (int k = 2; k <= n; k <<= 1) {
     for (int j = k >> 1; j > 0; j >>= 1) {
-      if (j >= 64) {
+      if (j >= 32) {
         __syncthreads();
       } else {
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");

@@ -130,7 +130,8 @@ struct KvCommitParams {
   const int32_t* num_accepted;
   const int32_t* path_nodes;
   int32_t* new_ctx_lens;
-  int lengths_in_commit;  // 1: new_ctx_lens shares no element with ctx_lens, so the move kernel writes it
+  int lengths_in_commit;  // 1: new_ctx_lens shares no byte with ctx_lens, num_accepted or path_nodes, so the
+                          //    move kernel writes it
 };
 hipError_t launch_kv_commit(const KvCommitParams& p, int head_dim, hipStream_t s);
 hipError_t launch_accept_rejection(const AcceptParams& p, hipStream_t s);

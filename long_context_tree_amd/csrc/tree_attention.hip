@@ -104,11 +104,17 @@ __global__ __launch_bounds__(W * 64, (W == 8 ? 1 : 2)) void tree_attn_kernel(Att
   // tile being read from the tile whose direct-to-LDS loads are still in flight
   __shared__ __attribute__((aligned(16))) uint16_t kv_a[2][TILE_EL];
   __shared__ __attribute__((aligned(16))) uint16_t kv_b[2][TILE_EL];
-  __shared__ uint64_t anc_lds[ANC_N][ANC_W];
-  // preorder trees: the same memory holds each node's subtree end (2 ints per 64-bit word)
-  int* const end_lds = reinterpret_cast<int*>(&anc_lds[0][0]);
+  // The tree relation: ancestor bit masks (PRE = 0) or, for preorder trees, each node's subtree end
+  // (PRE = 1).  One instantiation only ever touches one of the two members.
   constexpr int END_N = ANC_N * ANC_W * 2;
   static_assert(W != 8 || END_N >= kMaxTreeNodes, "subtree ends of the largest tree must fit");
+  union TreeRel {
+    uint64_t anc[ANC_N][ANC_W];
+    int end[END_N];
+  };
+  __shared__ TreeRel rel_lds;
+  auto& anc_lds = rel_lds.anc;
+  auto& end_lds = rel_lds.end;
   __shared__ int pg_lds[kMaxSplitPages];
   // Row r of a K tile keeps its 16-byte chunk c at position c ^ swz(r), row r of a token-row V tile at
   // c ^ swzv_rows(r).  The XOR patterns were chosen with the LDS bank-conflict counter: they leave the K

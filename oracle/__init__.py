@@ -18,14 +18,13 @@ Every function here is pinned by tests against something other than itself
 enumeration of the sampler's output law).  None is "parity unpinned".
 """
 
-from .attention import (bf16_to_f64, ancestor_matrix, gather_kv, tree_attention, attention_rows,
-                        chunk_mass, topk_chunks)
+from .attention import bf16_to_f64, ancestor_matrix, gather_kv, tree_attention, topk_chunks
 from .acceptance import argmax_lowest, accept_greedy, target_probs, accept_rejection
 from .kvcache import kv_commit
 from .draft_kv import draft_gather
 from .bundle import bundle_order
 from . import controller, draft_kv
 
-__all__ = ["bf16_to_f64", "ancestor_matrix", "gather_kv", "tree_attention", "attention_rows", "chunk_mass",
-           "topk_chunks", "argmax_lowest", "accept_greedy", "target_probs", "accept_rejection", "kv_commit",
-           "draft_gather", "draft_kv", "bundle_order", "controller"]
+__all__ = ["bf16_to_f64", "ancestor_matrix", "gather_kv", "tree_attention", "topk_chunks", "argmax_lowest",
+           "accept_greedy", "target_probs", "accept_rejection", "kv_commit", "draft_gather", "draft_kv",
+           "bundle_order", "controller"]

@@ -72,17 +72,6 @@ def gather_kv(pool, block_table_row, n_slots: int, page_size: int, kv_head=None)
     return bf16_to_f64(pool[pages, kv_head, t % page_size, :])
 
 
-def attention_rows(q, k, v, scale: float):
-    """Softmax attention of query rows q [R][D] over keys k [n][D] / values v [n][D], all visible.
-    Returns (out [R][D], lse [R] natural log, probs [R][n])."""
-    s = scale * (q @ k.T)
-    m = s.max(axis=1, keepdims=True)
-    e = np.exp(s - m)
-    z = e.sum(axis=1, keepdims=True)
-    probs = e / z
-    return probs @ v, (m + np.log(z))[:, 0], probs
-
-
 def tree_attention(q_bits, k_pool, v_pool, block_table, ctx_lens, node_offsets, parents, scale: float,
                    num_kv_heads: int, page_size: int = 16, chunk_size: int = 0, kv_heads=None, seqs=None,
                    v_layout: int = 0):
@@ -143,13 +132,6 @@ def tree_attention(q_bits, k_pool, v_pool, block_table, ctx_lens, node_offsets, 
         if chunk_size:
             masses.append(mass / (N * G * len(kv_heads)))
     return out, lse, masses
-
-
-def chunk_mass(q_bits, k_pool, v_pool, block_table, ctx_lens, node_offsets, parents, scale: float,
-               num_kv_heads: int, chunk_size: int, page_size: int = 16):
-    """Per-sequence chunk attention mass (see ``tree_attention``)."""
-    return tree_attention(q_bits, k_pool, v_pool, block_table, ctx_lens, node_offsets, parents, scale,
-                          num_kv_heads, page_size, chunk_size)[2]
 
 
 def topk_chunks(mass, k: int):

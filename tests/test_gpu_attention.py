@@ -180,35 +180,6 @@ def test_full_size_llama_32k_sampled_heads():
     assert 0.0 < s <= 1.0
 
 
-def test_full_size_llama_128k_sampled_head():
-    """The 128K-context layer with the 128-node tree of depth 10 (two row groups per KV head):
-    every row of KV head 3 against the oracle."""
-    import long_context_tree_amd as lt
-    from synth import device as sdev
-    import oracle
-    L, N = 131072, 128
-    tree = synth.random_tree(synth.rng_for(121, 0, 4), N, 10)
-    k, v, bt = sdev.paged_kv_device(121, 0, [L + N], 8, 128, dev(), v_layout=1)
-    q = sdev.queries_device(121, 0, N, 32, 128, dev())
-    cl = torch.tensor([L], dtype=torch.int32, device=dev())
-    no = torch.tensor([0, N], dtype=torch.int32, device=dev())
-    par = torch.from_numpy(tree).to(dev())
-    out, lse, h = lt.tree_attention(q, k, v, bt, cl, no, par, max_nodes=N, max_ctx_len=L, chunk_size=64,
-                                    v_layout=lt.V_DIM_MAJOR)
-    mass = torch.zeros((1, L // 64), dtype=torch.float32, device=dev())
-    lt.chunk_salience(h, mass, top_k=256)
-    torch.cuda.synchronize()
-    g = 3
-    o_ref, l_ref, _ = oracle.tree_attention(bits_of(q), bits_of(k), bits_of(v), bt.cpu().numpy(), np.array([L]),
-                                            np.array([0, N]), tree, 1 / np.sqrt(128), 8, 16, 0, kv_heads=[g],
-                                            v_layout=1)
-    sel = np.zeros((N, 32), dtype=bool)
-    sel[:, 4 * g:4 * g + 4] = True
-    compare_out(out, lse, o_ref, l_ref, mask=sel)
-    m = mass.cpu().numpy()[0]
-    assert (m >= 0).all() and 0.0 < m.sum() <= 1.0
-
-
 @pytest.mark.parametrize("v_layout", [0, 1])
 @pytest.mark.parametrize("page_size", [8, 32, 64, 128, 256])
 def test_page_sizes(page_size, v_layout):
@@ -302,12 +273,19 @@ def test_rising_scores_rescale_mid_split(chunk, split, v_layout):
     compare_mass(mass.cpu().numpy().astype(np.float64)[0, :len(m_ref[0])], m_ref[0])
 
 
-@pytest.mark.parametrize("ctx,k,kind", [(32768, 256, "ties"), (32768, 1, "ties"), (32768, 256, "equal"),
-                                        (1600, 256, "ties"), (32768, 256, "zeros"), (32768, 200, "distinct")])
-def test_topk_order_ties_and_padding(ctx, k, kind):
+@pytest.mark.parametrize("ctx,k,kind,width", [
+    (32768, 256, "ties", 0), (32768, 1, "ties", 0), (32768, 256, "equal", 0), (1600, 256, "ties", 0),
+    (32768, 256, "zeros", 0), (32768, 200, "distinct", 0),
+    # more than 2048 chunks (the sort through LDS, strides of 64 and more cross waves)
+    (65536, 256, "ties", 0), (131072, 256, "ties", 0), (131072, 300, "distinct", 0), (131072, 256, "equal", 0),
+    (98304, 1000, "ties", 0),
+    # a mass row wider than 2048 while the sequence has fewer chunks
+    (20000, 256, "ties", 3000), (40000, 64, "distinct", 8192)])
+def test_topk_order_ties_and_padding(ctx, k, kind, width):
     """Exact top-k: (mass desc, index asc) with planted ties, equal and zero masses, and -1 / 0 padding
-    when there are fewer chunks than k.  The masses are planted as large fp32 values in the accumulator,
-    so one layer's attention mass (~1e-4 per chunk) leaves them unchanged when it is accumulated."""
+    when there are fewer chunks than k, up to 8192 chunks, and mass rows wider than the sequence's
+    chunks.  The masses are planted as large fp32 values in the accumulator, so one layer's attention
+    mass (~1e-4 per chunk) leaves them unchanged when it is accumulated."""
     import long_context_tree_amd as lt
     import oracle
     r = synth.rng_for(107, 0, 0)
@@ -326,9 +304,9 @@ def test_topk_order_ties_and_padding(ctx, k, kind):
     else:
         planted = base + 16 * rng.permutation(n_ch)
     planted = planted.astype(np.float32)
-    print(f"topk ctx={ctx} k={k} kind={kind}", flush=True)
+    print(f"topk ctx={ctx} k={k} kind={kind} width={width}", flush=True)
     out, lse, h, t = run_attention(case, chunk_size=chunk)
-    width = max(n_ch, k)                            # the row may be wider than the sequence's chunks (top_k <= width)
+    width = max(n_ch, k, width)                     # the row may be wider than the sequence's chunks (top_k <= width)
     row = np.zeros(width, dtype=np.float32)
     row[:n_ch] = planted
     mass = torch.from_numpy(row[None, :].copy()).to(dev())

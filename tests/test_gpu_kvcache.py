@@ -88,6 +88,41 @@ def test_commit_of_the_greedy_path_in_place():
     assert np.array_equal(_bits(kd[0]), k_ref[0]) and np.array_equal(_bits(vd[0]), v_ref[0])
 
 
+def test_commit_with_new_lengths_over_num_accepted():
+    """new_ctx_lens written over num_accepted (the same buffer): every layer and KV head still moves the
+    accepted count it was given, and the buffer ends up holding the new lengths."""
+    import long_context_tree_amd as lt
+    r = synth.rng_for(231, 0, 0)
+    trees = [synth.random_tree(r, 40, 9), synth.chain_tree(5), synth.random_tree(r, 12, 4)]
+    ctx = np.array([900, 33, 70], dtype=np.int32)
+    slots = ctx + np.array([len(t) for t in trees], dtype=np.int32)
+    layers = 4
+    ks, vs, bt = [], [], None
+    for layer in range(layers):
+        kv = synth.paged_kv(231, layer, slots, 8, 128)
+        bt = kv.block_table if bt is None else bt
+        ks.append(kv.k_pool)
+        vs.append(kv.v_pool)
+    max_path = 12
+    paths = np.full((3, max_path), -1, dtype=np.int32)
+    nacc = np.zeros(3, dtype=np.int32)
+    for b, t in enumerate(trees):
+        p = _root_path(t, int(np.argmax(synth.tree_depths(t))))
+        paths[b, :len(p)] = p
+        nacc[b] = len(p) - 1
+    k_ref, v_ref, lens_ref = oracle.kv_commit(ks, vs, bt, ctx, nacc, paths, 16, 0, max_nodes=40)
+    kd = [sdev.bf16_tensor(k, dev()) for k in ks]
+    vd = [sdev.bf16_tensor(v, dev()) for v in vs]
+    na = torch.from_numpy(nacc).to(dev())
+    lt.kv_commit(kd, vd, torch.from_numpy(bt).to(dev()), torch.from_numpy(ctx).to(dev()), na,
+                 torch.from_numpy(paths).to(dev()), max_nodes=40, new_ctx_lens=na)
+    torch.cuda.synchronize()
+    assert na.cpu().numpy().tolist() == lens_ref.tolist()
+    for layer in range(layers):
+        assert np.array_equal(_bits(kd[layer]), k_ref[layer])
+        assert np.array_equal(_bits(vd[layer]), v_ref[layer])
+
+
 def test_read_probe_xor_of_the_buffer():
     """The streaming-read probe reads every byte: its result is the XOR of all 32-bit words (checked on a
     ragged size that leaves a tail for the non-unrolled loop)."""

@@ -236,3 +236,59 @@ def test_topk_chunks_order_and_padding():
         m = np.round(r.random(50), 1)
         idx, _ = oracle.topk_chunks(m, 17)
         assert idx.tolist() == np.argsort(-m, kind="stable")[:17].tolist()
+
+
+def test_bf16_to_f64_known_bit_patterns():
+    """bf16 decoding against values fixed by the format: sign, 8-bit exponent (bias 127), 7-bit fraction."""
+    bits = np.array([0x0000, 0x8000, 0x3F80, 0xC000, 0x4049, 0x7F80, 0xFF80, 0x0001, 0x7F7F, 0x3E80],
+                    dtype=np.uint16)
+    want = [0.0, -0.0, 1.0, -2.0, 3.140625, math.inf, -math.inf, 2.0 ** -133, (2 - 2 ** -7) * 2.0 ** 127, 0.25]
+    got = oracle.bf16_to_f64(bits)
+    assert got.dtype == np.float64
+    for g, w in zip(got, want):
+        assert g == w and math.copysign(1.0, g) == math.copysign(1.0, w)
+    assert np.isnan(oracle.bf16_to_f64(np.array([0x7FC0], dtype=np.uint16)))[0]
+
+
+def test_gather_kv_reads_each_slot_from_its_page():
+    """Every logical slot t comes from page block_table[t // page_size], row t % page_size: the pool is
+    filled with a code of (page, head, row, dim) so each gathered value names where it was read."""
+    pages, H, ps, D = 7, 3, 4, 2
+    pool = np.zeros((pages, H, ps, D), dtype=np.uint16)
+    for p in range(pages):
+        for h in range(H):
+            for r in range(ps):
+                for d in range(D):
+                    val = np.float32(((p * H + h) * ps + r) * D + d)   # integers < 2^8: exact in bf16
+                    pool[p, h, r, d] = np.frombuffer(val.tobytes(), dtype=np.uint32)[0] >> 16
+    table = np.array([5, 0, 3, 6])
+    n = 13
+    allh = oracle.gather_kv(pool, table, n, ps)
+    assert allh.shape == (n, H, D)
+    for t in range(n):
+        for h in range(H):
+            for d in range(D):
+                assert allh[t, h, d] == ((table[t // ps] * H + h) * ps + t % ps) * D + d
+    np.testing.assert_array_equal(oracle.gather_kv(pool, table, n, ps, kv_head=2), allh[:, 2])
+    with pytest.raises(ValueError):
+        oracle.gather_kv(pool, np.array([1, -1]), 6, ps)
+
+
+def test_argmax_lowest_and_target_probs():
+    """argmax with exact ties goes to the lowest index (numpy's argmax has the same rule); softmax equals
+    scipy's, -inf logits get probability 0, and a row without a finite maximum is refused."""
+    rng = np.random.default_rng(5)
+    for _ in range(50):
+        row = rng.integers(-3, 4, 40).astype(np.float64)
+        assert oracle.argmax_lowest(row) == int(np.argmax(row))
+    assert oracle.argmax_lowest([1.0, 3.0, -0.0, 3.0]) == 1
+    assert oracle.argmax_lowest([-0.0, 0.0]) == 0
+    with pytest.raises(ValueError):
+        oracle.argmax_lowest([1.0, float("nan")])
+    lg = rng.normal(0, 2, 1000)
+    lg[::7] = -np.inf
+    p = oracle.target_probs(lg)
+    np.testing.assert_allclose(p, scipy.special.softmax(lg), rtol=1e-12, atol=1e-300)
+    assert (p[::7] == 0).all() and abs(p.sum() - 1.0) < 1e-14
+    with pytest.raises(ValueError):
+        oracle.target_probs(np.full(4, -np.inf))
