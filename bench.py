@@ -57,35 +57,60 @@ def parse():
     return ap.parse_args()
 
 
-def cpu_baseline(pools, qs, bt, tree, L, N, kv_heads, head_dim, v_layout, budget_s=12.0):
-    """The oracle (numpy float64) on whole KV heads of the step's layers, in order, until ~budget_s of CPU
-    work; the rate is KV bytes of the heads done per second, the unit of the benchmark's value."""
+def host_cores() -> int:
+    return len(os.sched_getaffinity(0))
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def oracle_heads(qb, kb, vb, btn, ctx, offs, tree, head_dim, kv_heads, heads, v_layout, chunk=64):
+    """oracle.tree_attention over the listed KV heads, one head per worker thread (numpy releases the GIL in
+    its array and BLAS work); returns the seconds taken."""
+    import concurrent.futures as cf
+    import numpy as np
+    import oracle
+    t0 = time.perf_counter()
+    with cf.ThreadPoolExecutor(max(1, min(len(heads), host_cores()))) as ex:
+        list(ex.map(lambda g: oracle.tree_attention(qb, kb, vb, btn, ctx, offs, tree, 1 / math.sqrt(head_dim),
+                                                    kv_heads, 16, chunk, kv_heads=[g], v_layout=v_layout), heads))
+    return time.perf_counter() - t0
+
+
+def host_bits(t):
     import numpy as np
     import torch
-    import oracle
-    from threadpoolctl import threadpool_info
+    return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def cpu_baseline(pools, qs, bt, tree, L, N, kv_heads, head_dim, v_layout, budget_s=12.0):
+    """The oracle (numpy float64) on whole layers of the step (all KV heads of a layer in parallel, one per
+    host thread), layer after layer until ~budget_s of oracle time; the rate is KV bytes of the heads done
+    per second, the unit of the benchmark's value."""
+    import numpy as np
     btn = bt.cpu().numpy()
     done, layers_used, dt = 0, 0, 0.0               # dt: oracle time only (device-to-host copies excluded)
     for (k_pool, v_pool), q in zip(pools, qs):
         if dt >= budget_s:
             break
-        kb = k_pool.view(torch.int16).cpu().numpy().view(np.uint16)
-        vb = v_pool.view(torch.int16).cpu().numpy().view(np.uint16)
-        qb = q.view(torch.int16).cpu().numpy().view(np.uint16)
+        kb, vb, qb = host_bits(k_pool), host_bits(v_pool), host_bits(q)
+        dt += oracle_heads(qb, kb, vb, btn, np.array([L]), np.array([0, N]), tree, head_dim, kv_heads,
+                           list(range(kv_heads)), v_layout)
+        done += kv_heads
         layers_used += 1
-        for g in range(kv_heads):
-            t0 = time.perf_counter()
-            oracle.tree_attention(qb, kb, vb, btn, np.array([L]), np.array([0, N]), tree, 1 / math.sqrt(head_dim),
-                                  kv_heads, 16, 64, kv_heads=[g], v_layout=v_layout)
-            dt += time.perf_counter() - t0
-            done += 1
-            if dt >= budget_s:
-                break
     kv_bytes = done * (L + N) * head_dim * 2 * 2
-    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    return {"value": kv_bytes / dt / 1e9, "unit": "GB/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"oracle.tree_attention (numpy float64) on {done} KV heads ({layers_used} layers of {kv_heads} "
-                      f"heads), {L} context + {N}-node tree each, {dt:.1f} s; rate = KV bytes of those heads / time"}
+    return {"value": kv_bytes / dt / 1e9, "unit": "GB/s", "cores": host_cores(), "cpu_model": cpu_model(),
+            "kind": "oracle", "seconds": round(dt, 2),
+            "sample": f"oracle.tree_attention (numpy float64) on {layers_used} whole layers of the step "
+                      f"({done} KV heads, one per worker thread on {host_cores()} host cores), {L} context + "
+                      f"{N}-node tree each, chunk masses included, {dt:.1f} s; rate = KV bytes of those heads / time"}
 
 
 def traffic_record(kernel_src: str, workload: str):
@@ -222,21 +247,33 @@ def main():
         step(None)
     torch.cuda.synchronize()
 
-    # timed region: K whole steps between two events; every spec_tree_attention call is bracketed by
-    # its own pair of events on the same stream (read after the region ends)
-    step_events = [events() for _ in range(args.steps)]
+    # timed region 1 (the value): K whole steps between two events on the stream, nothing else inside
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0.record(stream)
-    for k in range(args.steps):
-        step(step_events[k])
+    for _ in range(args.steps):
+        step(None)
     t1.record(stream)
     torch.cuda.synchronize()
     total_ms = t0.elapsed_time(t1)
     ms_per_step = total_ms / args.steps
-    attn_ms = [e0.elapsed_time(e1) for ev in step_events for e0, e1 in ev]
     print(f"[bench] {ms_per_step:.3f} ms/step", file=sys.stderr, flush=True)
+
+    # timed region 2 (the roofline): the same K steps again, every spec_tree_attention call bracketed by its
+    # own pair of events on the stream it is launched on (read after the region ends).  The events add
+    # their own gaps, so this region's step time is reported beside the value, not as it.
+    step_events = [events() for _ in range(args.steps)]
+    t2 = torch.cuda.Event(enable_timing=True)
+    t3 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t2.record(stream)
+    for k in range(args.steps):
+        step(step_events[k])
+    t3.record(stream)
+    torch.cuda.synchronize()
+    ms_per_step_events = t2.elapsed_time(t3) / args.steps
+    attn_ms = [e0.elapsed_time(e1) for ev in step_events for e0, e1 in ev]
 
     # correctness guard: outputs finite, greedy produced a path
     assert torch.isfinite(outs[-1].float()).all().item() and int(gouts[0][0]) >= 0
@@ -284,6 +321,14 @@ def main():
         if st:
             raise RuntimeError(lt.last_error())
 
+    do_cpu = not args.no_cpu_baseline
+
+    def oracle_time(fn):
+        """Seconds of one oracle call on the host (the oracle as it stands, numpy float64)."""
+        t = time.perf_counter()
+        fn()
+        return time.perf_counter() - t
+
     kernels = {}
     rows = N * Hq
     sal_bytes = rows * n_chunks * 4 + rows * 4 + 2 * n_chunks * 4
@@ -295,11 +340,24 @@ def main():
     kernels["spec_chunk_salience_topk"] = {"median_us": round(us, 2), "alg_bytes": sal_bytes,
                                            "gbs": round(sal_bytes / us / 1e3, 1), "bound": "hbm",
                                            "note": f"last layer, accumulate, top-{top_k}"}
+    if do_cpu:
+        import oracle
+        m_host = mass.cpu().numpy()[0].astype(np.float64)
+        kernels["spec_chunk_salience_topk"].update(
+            oracle_ms=round(oracle_time(lambda: oracle.topk_chunks(m_host, top_k)) * 1e3, 2),
+            oracle_sample=f"oracle.topk_chunks over the step's {n_chunks} masses (one host thread); the masses "
+                          "themselves come out of oracle.tree_attention, timed in cpu_baseline")
     g_bytes = N * V * 2
     us = time_call(lambda: call(L_.spec_accept_greedy(ctypes.byref(ga), sh)))
     kernels["spec_accept_greedy"] = {"median_us": round(us, 2), "alg_bytes": g_bytes,
                                      "gbs": round(g_bytes / us / 1e3, 1), "bound": "hbm",
                                      "note": f"{N} nodes, vocab {V}, bf16 logits"}
+    if do_cpu:
+        import oracle
+        kernels["spec_accept_greedy"].update(
+            oracle_ms=round(oracle_time(lambda: oracle.accept_greedy(g.node_offsets, g.parents, g.draft_tokens,
+                                                                      g.logits, "bf16")) * 1e3, 2),
+            oracle_sample="oracle.accept_greedy on the same inputs (one host thread)")
     # the commit of the step's greedy path into all 32 layers' caches (new lengths to a scratch buffer)
     ca, ckeep = spec.kv_commit_args([pl[0] for pl in pools], [pl[1] for pl in pools], bt, cl, gouts[0], gouts[1],
                                     max_nodes=N, new_ctx_lens=torch.empty_like(cl), v_layout=v_layout)
@@ -349,6 +407,13 @@ def main():
                                         "gbs": round(r_bytes / us / 1e3, 1), "bound": "hbm",
                                         "note": f"64 nodes (depth 8, <= 4 children), vocab {V}, bf16 logits + "
                                                 "fp32 draft probabilities read once"}
+    if do_cpu:
+        import oracle
+        kernels["spec_accept_rejection"].update(
+            oracle_ms=round(oracle_time(lambda: oracle.accept_rejection(
+                rc.node_offsets, rc.parents, rc.draft_tokens, rc.logits, rc.draft_probs, rc.u_accept, rc.u_sample,
+                "bf16")) * 1e3, 2),
+            oracle_sample="oracle.accept_rejection on the same inputs (one host thread)")
 
     # spec_tree_attention alone for narrower trees at the same context, and for the ragged Qwen3-8B-shaped
     # batch of 4-draft chains: these are HBM-bound (<= 256 query rows per KV head), so the KV rate against
@@ -368,13 +433,55 @@ def main():
             torch.cuda.synchronize()
             return float(np.median([e0.elapsed_time(e1) for e0, e1 in ev])) * 1e3
 
-        def entry(us, kv_bytes, flops, note):
+        def entry(us, kv_bytes, flops, note, oracle_s=None, oracle_note=None):
             gbs = kv_bytes / us / 1e3
             tf = flops / us / 1e6
             bound = "mfma" if flops / (MFMA_BF16_PEAK_TFLOPS * 1e12) > kv_bytes / (HBM_PEAK_GBS * 1e9) else "hbm"
-            return {"median_us": round(us, 2), "kv_bytes": kv_bytes, "kv_gbs": round(gbs, 1),
-                    "hbm_frac": round(gbs / HBM_PEAK_GBS, 4), "hbm_frac_of_read_ceiling": round(gbs / ceiling, 4),
-                    "mfma_frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4), "bound": bound, "note": note}
+            e = {"median_us": round(us, 2), "kv_bytes": kv_bytes, "kv_gbs": round(gbs, 1),
+                 "hbm_frac": round(gbs / HBM_PEAK_GBS, 4), "hbm_frac_of_read_ceiling": round(gbs / ceiling, 4),
+                 "mfma_frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4), "bound": bound, "note": note}
+            if oracle_s is not None:
+                e.update(oracle_s=round(oracle_s, 3), oracle_kv_gbs=round(kv_bytes / oracle_s / 1e9, 4),
+                         oracle_cores=host_cores(), oracle_note=oracle_note)
+            return e
+
+        def oracle_one_layer(q, k_pool, v_pool, btab, ctx, offs, par, hkv, hd, seqs=None):
+            """The oracle on the same call (first layer): KV heads (one sequence) or sequences (a batch) in
+            parallel, one per host thread."""
+            if not do_cpu:
+                return None, None
+            import concurrent.futures as cf
+            import oracle
+            qb, kb, vb, btn = host_bits(q), host_bits(k_pool), host_bits(v_pool), btab.cpu().numpy()
+            if seqs is None:
+                return oracle_heads(qb, kb, vb, btn, ctx, offs, par, hd, hkv, list(range(hkv)), v_layout, chunk), \
+                    f"oracle.tree_attention on the first layer, {hkv} KV heads in parallel"
+            t = time.perf_counter()
+            with cf.ThreadPoolExecutor(max(1, min(seqs, host_cores()))) as ex:
+                list(ex.map(lambda b: oracle.tree_attention(qb, kb, vb, btn, ctx, offs, par, 1 / math.sqrt(hd), hkv,
+                                                            16, chunk, seqs=[b], v_layout=v_layout), range(seqs)))
+            return time.perf_counter() - t, f"oracle.tree_attention on the first layer, {seqs} sequences in parallel"
+
+        # the tiny parity workload: 512 committed tokens, 4 q / 2 KV heads, head_dim 64, an 8-node tree of
+        # depth <= 4 (launch-latency bound; timed like the others)
+        tiny = synth.attention_case(1, ctx_lens=[512], trees=[synth.random_tree(synth.rng_for(1, 0, synth.S_TREE),
+                                                                                  8, 4)],
+                                    num_q_heads=4, num_kv_heads=2, head_dim=64)
+        tt = sdev.attention_tensors(tiny, dev, v_layout)
+        to = torch.empty((8, 4, 64), dtype=torch.bfloat16, device=dev)
+        tl = torch.empty((8, 4), dtype=torch.float32, device=dev)
+        ta = [spec.tree_attention_args(tt["q"], tt["k_cache"], tt["v_cache"], tt["block_table"], tt["ctx_lens"],
+                                       tt["node_offsets"], tt["parents"], max_nodes=8, max_ctx_len=512,
+                                       chunk_size=chunk, out=to, lse=tl, v_layout=v_layout)]
+        tws = spec._workspace(lt.lib().spec_tree_attention_workspace_size(ctypes.byref(ta[0])), dev, None)
+        ta[0].workspace, ta[0].workspace_bytes = tws.data_ptr(), tws.numel()
+        t_kvb = (512 + 8) * 2 * 64 * 2 * 2
+        t_fl = 4.0 * 64 * 4 * float(np.sum(512 + synth.tree_depths(tiny.parents) + 1))
+        os_, on_ = oracle_one_layer(tt["q"], tt["k_cache"], tt["v_cache"], tt["block_table"], tiny.ctx_lens,
+                                    tiny.node_offsets, tiny.parents, 2, 64)
+        out["tiny-512-n8"] = entry(timed(ta), t_kvb, t_fl, "512 context, 8-node tree, 4 q / 2 KV heads, head_dim 64",
+                                   os_, on_)
+        del ta, tws
 
         # (the 32K and 64K contexts use the first slots of the same pools: a shorter committed length)
         for name, wn, wd, wl in (("n64-depth8", 64, 8, L), ("chain-k4", 5, 4, L), ("n64-depth8", 64, 8, 32768),
@@ -397,8 +504,13 @@ def main():
                 x.workspace, x.workspace_bytes = wws.data_ptr(), wws.numel()
             kvb = (wl + wn) * Hkv * D * 2 * 2
             fl = 4.0 * D * Hq * float(np.sum(wl + synth.tree_depths(wtree) + 1))
-            out[f"llama8b-{wl // 1024}k-{name}"] = entry(timed(wa), kvb, fl,
-                                                       f"{wn}-node tree, chunk partials ({chunk}-token chunks)")
+            us_w = timed(wa)
+            # the oracle reads the same slots: a shorter context is the first wl slots of the same pages
+            os_, on_ = oracle_one_layer(wq[0], pools[0][0], pools[0][1], bt, np.array([wl]), np.array([0, wn]), wtree,
+                                        Hkv, D)
+            out[f"llama8b-{wl // 1024}k-{name}"] = entry(us_w, kvb, fl,
+                                                       f"{wn}-node tree, chunk partials ({chunk}-token chunks)",
+                                                       os_, on_)
             del wa, wws, wq, wo, wlse
         # ragged batch: 16 sequences, contexts uniform in [4096, 65536], 4-draft chains, Qwen3-8B layer shape
         rb_case, rb_n, rb_layers = 5, 5, 4
@@ -422,9 +534,13 @@ def main():
             for x in ra_:
                 x.workspace, x.workspace_bytes = rws.data_ptr(), rws.numel()
             tag = "with chunk partials" if cs else "without chunk partials"
+            us_r = timed(ra_)
+            os_, on_ = (oracle_one_layer(rq[0], rpools[0][0], rpools[0][1], rpools[0][2], rlens,
+                                         np.arange(0, 16 * rb_n + 1, rb_n), rpar.cpu().numpy(), Hkv, D, seqs=16)
+                        if cs else (None, None))
             out[f"qwen3-8b-ragged16-chain-k4-{'chunks' if cs else 'nochunks'}"] = entry(
-                timed(ra_), kvb, fl, f"16 sequences, contexts {int(rlens.min())}..{int(rlens.max())} "
-                                     f"(sum {int(rlens.sum())}), {tag}")
+                us_r, kvb, fl, f"16 sequences, contexts {int(rlens.min())}..{int(rlens.max())} "
+                               f"(sum {int(rlens.sum())}), {tag}", os_, on_)
             del ra_, rws
         del rpools
         return out
@@ -446,6 +562,7 @@ def main():
                    "chunk_size": chunk,
                    "top_k": top_k, "vocab": V, "acceptance": "greedy", "kv_bytes_per_step": layers * kv_bytes_layer},
         "verify_steps_per_s": round(1000.0 / ms_per_step, 2),
+        "ms_per_step_with_call_events": round(ms_per_step_events, 4),
         "hbm_frac_step": round(kv_gbs_step / HBM_PEAK_GBS, 4),
         "hbm_read_ceiling_gbs": round(ceiling, 1),
         "hbm_frac_step_of_read_ceiling": round(kv_gbs_step / ceiling, 4),

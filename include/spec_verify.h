@@ -59,7 +59,7 @@
 extern "C" {
 #endif
 
-#define SPEC_ABI_VERSION 4
+#define SPEC_ABI_VERSION 5
 
 /* Largest draft tree (nodes per sequence) any call accepts.  spec_tree_attention takes up to 256
  * nodes in index order, and up to this many when the tree is in preorder with subtree ends. */
@@ -88,6 +88,41 @@ int spec_abi_version(void);
 const char* spec_status_string(int status);
 /* (host) Thread-local text of the last failure on this thread; "" after a successful call. */
 const char* spec_last_error(void);
+
+/* ------------------------------------------------------------------------------------------
+ * The SPEC_DEBUG build and the debug record  [AS "Correctness first": per-row bookkeeping errors;
+ * VC "MTP": positive witnesses that every draft was really tested]
+ *
+ * libspec_verify_debug.so is this library built with SPEC_DEBUG.  In it, spec_tree_attention,
+ * spec_accept_greedy and spec_accept_rejection first run device-side checks of the device
+ * preconditions listed with each call, and the acceptance walks count what they did.  The results go
+ * to a debug record of SPEC_DEBUG_RECORD_BYTES bytes at the end of the call's workspace, at byte
+ * offset (the call's *_workspace_size) - SPEC_DEBUG_RECORD_BYTES, as uint32 words:
+ *   [0] error bits (SPEC_DBG_*): 0 when every checked precondition holds
+ *   [1] acceptance: rows of target logits whose reduction (greedy: argmax; rejection: row maximum)
+ *       this call computed and its walk read; Σ_b N_b when the call ran whole
+ *   [2] acceptance: draft tokens the walk tested against their parent's row; Σ_b (N_b - 1)
+ *   [3] 0
+ * (spec_tree_attention writes words 1..3 as 0.)  Every workspace size includes the record in both
+ * builds; the release build never writes it.  A call whose preconditions fail still runs (its kernels
+ * clamp indices, so nothing is read or written out of bounds); the record says what was wrong.  The
+ * record is written on the call's stream: read it after the call completes.  spec_accept_greedy_noalloc
+ * and the calls without a workspace run no checks.
+ * ------------------------------------------------------------------------------------------ */
+#define SPEC_DEBUG_RECORD_BYTES 256
+#define SPEC_DBG_PARENTS (1u << 0)      /* parents[i] outside 0..i-1 (i > 0), or a root parent other than -1 */
+#define SPEC_DBG_BLOCK_TABLE (1u << 1)  /* a block-table entry the call reads is outside 0..num_pages-1 */
+#define SPEC_DBG_NODE_OFFSETS (1u << 2) /* node_offsets[0] != 0, decreasing, or a tree above max_nodes */
+#define SPEC_DBG_CTX_LENS (1u << 3)     /* a ctx_lens entry outside 0..max_ctx_len */
+#define SPEC_DBG_SUBTREE_END (1u << 4)  /* subtree_end[i] outside i+1..N (sequence-local) */
+#define SPEC_DBG_TOKENS (1u << 5)       /* a non-root draft token outside 0..vocab-1 */
+#define SPEC_DBG_UNIFORMS (1u << 6)     /* a u_accept (non-root) or u_sample entry outside [0, 1) */
+#define SPEC_DBG_DRAFT_PROBS (1u << 7)  /* a draft probability negative or not finite */
+#define SPEC_DBG_CHILDREN (1u << 8)     /* a node with more than max_children children */
+#define SPEC_DBG_LOGITS (1u << 9)       /* a NaN target logit */
+
+/* 1 in the SPEC_DEBUG build (libspec_verify_debug.so), 0 in the release build. */
+int spec_debug_build(void);
 
 /* ------------------------------------------------------------------------------------------
  * Paged KV cache [DSC "Features": paged KV with a block table; AS "Layout"].

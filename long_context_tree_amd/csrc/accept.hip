@@ -438,6 +438,9 @@ __global__ __launch_bounds__(256) void walk_kernel(AcceptParams p) {
   __shared__ int stop_s, depth_s, bad_s, seg_s, bonus_s;
   __shared__ double base_s, thr_s, zlast_s;
   __shared__ double zs[9];
+#ifdef SPEC_DEBUG
+  __shared__ int dbg_rows_s, dbg_tests_s;   // witnesses: rows reduced in this call and read here, tests run
+#endif
   const int b = blockIdx.x;
   const int tid = threadIdx.x;
   int n0 = p.node_offsets[b];
@@ -452,6 +455,10 @@ __global__ __launch_bounds__(256) void walk_kernel(AcceptParams p) {
     return;
   }
   if (tid == 0) bad_s = 0;
+#ifdef SPEC_DEBUG
+  if (tid == 0) dbg_rows_s = dbg_tests_s = 0;
+  __syncthreads();
+#endif
   for (int i = tid; i < N; i += 256) {
     int pi = p.parents[n0 + i];
     par_s[i] = pi;
@@ -473,7 +480,16 @@ __global__ __launch_bounds__(256) void walk_kernel(AcceptParams p) {
       }
       for (; s < p.nseg; ++s) k0 = umax64(k0, sk[s]);
       amax_s[i] = key_index(umax64(umax64(k0, k1), umax64(k2, k3)));
+#ifdef SPEC_DEBUG
+      // the debug checks cleared every key: a row counts when all its segment keys were written again
+      bool fresh = true;
+      for (int q = 0; q < p.nseg; ++q) fresh = fresh && sk[q] != 0ull;
+      if (fresh) atomicAdd(&dbg_rows_s, 1);
+#endif
     }
+#ifdef SPEC_DEBUG
+    if (REJECT && p.node_key[n0 + i] != 0ull) atomicAdd(&dbg_rows_s, 1);   // row maximum written in this call
+#endif
   }
   __syncthreads();
   // child counts and sibling ranks: each parent entry is read once and compared with the nodes this
@@ -494,6 +510,9 @@ __global__ __launch_bounds__(256) void walk_kernel(AcceptParams p) {
     const int u = par_s[c];
     const int x = tok_s[c];
     bool ok = false;
+#ifdef SPEC_DEBUG
+    atomicAdd(&dbg_tests_s, 1);
+#endif
     if (x >= 0 && x < p.vocab) {
       if (!REJECT) {
         ok = (x == amax_s[u]);
@@ -527,6 +546,12 @@ __global__ __launch_bounds__(256) void walk_kernel(AcceptParams p) {
     }
   }
   __syncthreads();
+#ifdef SPEC_DEBUG
+  if (tid == 0 && p.dbg) {
+    atomicAdd(&p.dbg[1], (uint32_t)dbg_rows_s);
+    atomicAdd(&p.dbg[2], (uint32_t)dbg_tests_s);
+  }
+#endif
   if (REJECT) {
     // sampling order: at each node move to its first accepted child
     if (tid == 0) {
@@ -729,15 +754,20 @@ __global__ __launch_bounds__(256) void walk_kernel(AcceptParams p) {
 
 }  // namespace
 
-size_t greedy_ws_bytes(int batch, int max_nodes, int nseg) {
+// workspace: the call's arrays, then the debug record (last SPEC_DEBUG_RECORD_BYTES bytes)
+size_t greedy_keys_bytes(int batch, int max_nodes, int nseg) {
   return align_up(sizeof(unsigned long long) * (size_t)batch * max_nodes * nseg, 256);
+}
+
+size_t greedy_ws_bytes(int batch, int max_nodes, int nseg) {
+  return greedy_keys_bytes(batch, max_nodes, nseg) + SPEC_DEBUG_RECORD_BYTES;
 }
 
 size_t rejection_ws_bytes(int batch, int max_nodes, int nsegr, int max_children) {
   const size_t nodes = (size_t)batch * max_nodes, lv = (size_t)max_children + 1;
-  return greedy_ws_bytes(batch, max_nodes, nsegr) + align_up(sizeof(unsigned long long) * nodes, 256) +
+  return greedy_keys_bytes(batch, max_nodes, nsegr) + align_up(sizeof(unsigned long long) * nodes, 256) +
          align_up(sizeof(double) * nodes * lv * nsegr, 256) + align_up(sizeof(double) * nodes * lv, 256) +
-         align_up(sizeof(int32_t) * nodes, 256);
+         align_up(sizeof(int32_t) * nodes, 256) + SPEC_DEBUG_RECORD_BYTES;
 }
 
 hipError_t launch_accept_greedy(const AcceptParams& p, hipStream_t s) {

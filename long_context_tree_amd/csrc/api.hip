@@ -246,6 +246,12 @@ extern "C" {
 
 int spec_abi_version(void) { return SPEC_ABI_VERSION; }
 
+#ifdef SPEC_DEBUG
+int spec_debug_build(void) { return 1; }
+#else
+int spec_debug_build(void) { return 0; }
+#endif
+
 const char* spec_status_string(int status) {
   switch (status) {
     case SPEC_OK: return "SPEC_OK";
@@ -273,6 +279,13 @@ int spec_tree_attention(const spec_tree_attention_args* args, void* stream) {
   st = check_workspace(args->workspace, args->workspace_bytes, l.bytes, "spec_tree_attention");
   if (st != SPEC_OK) return st;
   const spec::AttnParams p = attn_params(args, l);
+#ifdef SPEC_DEBUG
+  {
+    uint32_t* rec = reinterpret_cast<uint32_t*>(static_cast<char*>(args->workspace) + l.plan.off_debug);
+    const hipError_t de = spec::launch_debug_attn_check(p, rec, static_cast<hipStream_t>(stream));
+    if (de != hipSuccess) return hip_fail(de, "spec_tree_attention debug checks");
+  }
+#endif
   const hipError_t e = spec::launch_tree_attention(p, l.plan, args->head_dim, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "spec_tree_attention launch");
   return ok();
@@ -344,7 +357,14 @@ int spec_accept_greedy(const spec_accept_greedy_args* args, void* stream) {
   const size_t need = spec::greedy_ws_bytes(args->batch, args->max_nodes, nseg_of(args->vocab));
   st = check_workspace(args->workspace, args->workspace_bytes, need, "spec_accept_greedy");
   if (st != SPEC_OK) return st;
-  const spec::AcceptParams p = accept_params(args);
+  spec::AcceptParams p = accept_params(args);
+#ifdef SPEC_DEBUG
+  {
+    p.dbg = reinterpret_cast<uint32_t*>(static_cast<char*>(args->workspace) + need - SPEC_DEBUG_RECORD_BYTES);
+    const hipError_t de = spec::launch_debug_accept_check(p, p.dbg, 0, static_cast<hipStream_t>(stream));
+    if (de != hipSuccess) return hip_fail(de, "spec_accept_greedy debug checks");
+  }
+#endif
   const hipError_t e = spec::launch_accept_greedy(p, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "spec_accept_greedy launch");
   return ok();
@@ -387,7 +407,7 @@ int spec_accept_rejection(const spec_accept_rejection_args* args, void* stream) 
   p.nseg = nsegr;                                 // rejection keeps its segment maxima per residual segment
   char* ws = static_cast<char*>(g.workspace);
   const size_t nodes = (size_t)g.batch * g.max_nodes, lv = (size_t)args->max_children + 1;
-  size_t off = spec::greedy_ws_bytes(g.batch, g.max_nodes, nsegr);
+  size_t off = spec::greedy_keys_bytes(g.batch, g.max_nodes, nsegr);
   p.node_key = reinterpret_cast<unsigned long long*>(ws + off);
   off += spec::align_up(sizeof(unsigned long long) * nodes, 256);
   p.seg_sum = reinterpret_cast<double*>(ws + off);
@@ -395,6 +415,13 @@ int spec_accept_rejection(const spec_accept_rejection_args* args, void* stream) 
   p.zsum = reinterpret_cast<double*>(ws + off);
   off += spec::align_up(sizeof(double) * nodes * lv, 256);
   p.n_children = reinterpret_cast<int32_t*>(ws + off);
+#ifdef SPEC_DEBUG
+  {
+    p.dbg = reinterpret_cast<uint32_t*>(ws + need - SPEC_DEBUG_RECORD_BYTES);
+    const hipError_t de = spec::launch_debug_accept_check(p, p.dbg, 1, static_cast<hipStream_t>(stream));
+    if (de != hipSuccess) return hip_fail(de, "spec_accept_rejection debug checks");
+  }
+#endif
   const hipError_t e = spec::launch_accept_rejection(p, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "spec_accept_rejection launch");
   return ok();

@@ -35,7 +35,7 @@ struct AttnPlan {
   int split_tiles = 0;   // tiles per split
   int max_splits = 0;    // ceil(max_tiles / split_tiles)
   int max_chunks = 0;    // ceil(max_ctx_len / chunk_size), 0 without salience
-  size_t off_part_o = 0, off_part_ml = 0, off_chunk = 0, off_lse2 = 0, bytes = 0;
+  size_t off_part_o = 0, off_part_ml = 0, off_chunk = 0, off_lse2 = 0, off_debug = 0, bytes = 0;
 };
 
 struct AttnParams {
@@ -110,8 +110,10 @@ struct AcceptParams {
   double* seg_sum;       // [batch*max_nodes][max_children+1][nsegr] residual sums per segment
   double* zsum;          // [batch*max_nodes][max_children+1] residual sums per level (fixed-order totals)
   int32_t* n_children;   // [batch*max_nodes]
+  uint32_t* dbg;         // the debug record (SPEC_DEBUG build: witness counters of the walk), else NULL
 };
-size_t greedy_ws_bytes(int batch, int max_nodes, int nseg);
+size_t greedy_keys_bytes(int batch, int max_nodes, int nseg);   // the segment-key array alone
+size_t greedy_ws_bytes(int batch, int max_nodes, int nseg);     // keys + the debug record
 size_t rejection_ws_bytes(int batch, int max_nodes, int nsegr, int max_children);
 hipError_t launch_accept_greedy(const AcceptParams& p, hipStream_t s);
 
@@ -161,6 +163,12 @@ struct DraftGatherParams {
   int32_t* out_len;      // [batch]
 };
 hipError_t launch_draft_gather(const DraftGatherParams& p, int head_dim, int rope, hipStream_t s);
+
+// ------------------------------------------------------------------------------------------
+// device-side precondition checks (run by the SPEC_DEBUG build only)
+// ------------------------------------------------------------------------------------------
+hipError_t launch_debug_attn_check(const AttnParams& p, uint32_t* rec, hipStream_t s);
+hipError_t launch_debug_accept_check(const AcceptParams& p, uint32_t* rec, int rejection, hipStream_t s);
 
 // ------------------------------------------------------------------------------------------
 // streaming-read probe

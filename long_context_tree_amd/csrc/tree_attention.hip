@@ -875,6 +875,8 @@ bool make_attn_plan(const spec_tree_attention_args* a, int num_cus, AttnPlan* pl
   off = align_up(off + sizeof(float) * (size_t)a->batch * a->max_nodes * a->num_q_heads, 256);
   pl.off_chunk = off;
   off = align_up(off + sizeof(float) * (size_t)a->batch * pl.max_chunks * a->max_nodes * a->num_q_heads, 256);
+  pl.off_debug = off;                 // the debug record, last
+  off += SPEC_DEBUG_RECORD_BYTES;
   pl.bytes = off;
   *plan = pl;
   return true;

@@ -15,19 +15,25 @@ import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libspec_verify.so")
+DEBUG_LIB_PATH = os.path.join(_HERE, "libspec_verify_debug.so")   # the SPEC_DEBUG build
 
 SPEC_OK = 0
 SPEC_DTYPE_BF16 = 0
 SPEC_DTYPE_F32 = 1
-ABI_VERSION = 4
+ABI_VERSION = 5
 MAX_TREE_NODES = 2048
 V_TOKEN_ROWS = 0   # spec_v_layout: V pages like K, [pages][kv_heads][page_size][head_dim]
 V_DIM_MAJOR = 1    # V pages [pages][kv_heads][head_dim][page_size]
 ROPE_NONE = 0      # spec_rope: K copied as stored
 ROPE_HALF = 1      # pairs (i, i + head_dim/2)
 ROPE_PAIRS = 2     # pairs (2i, 2i + 1)
+DEBUG_RECORD_BYTES = 256   # SPEC_DEBUG_RECORD_BYTES: the last bytes of every workspace
+DBG_BITS = {"parents": 1 << 0, "block_table": 1 << 1, "node_offsets": 1 << 2, "ctx_lens": 1 << 3,
+            "subtree_end": 1 << 4, "tokens": 1 << 5, "uniforms": 1 << 6, "draft_probs": 1 << 7,
+            "children": 1 << 8, "logits": 1 << 9}   # SPEC_DBG_*
 
 _lib = None
+_debug_lib = None
 
 
 class SpecError(RuntimeError):
@@ -36,48 +42,76 @@ class SpecError(RuntimeError):
         self.status = status
 
 
+def _load(path: str):
+    """Load one build of the library and declare its functions' argument and result types."""
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with `python -m long_context_tree_amd.build`")
+    L = ctypes.CDLL(path)
+    L.spec_abi_version.restype = ctypes.c_int
+    L.spec_status_string.restype = ctypes.c_char_p
+    L.spec_status_string.argtypes = [ctypes.c_int]
+    L.spec_last_error.restype = ctypes.c_char_p
+    for name, argt in (("spec_tree_attention", TreeAttentionArgs), ("spec_chunk_salience", ChunkSalienceArgs),
+                       ("spec_accept_greedy", AcceptGreedyArgs),
+                       ("spec_accept_rejection", AcceptRejectionArgs),
+                       ("spec_kv_commit", KvCommitArgs), ("spec_draft_gather", DraftGatherArgs)):
+        f = getattr(L, name)
+        f.restype = ctypes.c_int
+        f.argtypes = [ctypes.POINTER(argt), ctypes.c_void_p]
+    for name, argt in (("spec_tree_attention_workspace_size", TreeAttentionArgs),
+                       ("spec_accept_greedy_workspace_size", AcceptGreedyArgs),
+                       ("spec_accept_rejection_workspace_size", AcceptRejectionArgs)):
+        f = getattr(L, name)
+        f.restype = ctypes.c_size_t
+        f.argtypes = [ctypes.POINTER(argt)]
+    L.spec_read_probe.restype = ctypes.c_int
+    L.spec_read_probe.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p]
+    L.spec_tree_bundle_order.restype = ctypes.c_int
+    L.spec_tree_bundle_order.argtypes = [ctypes.c_void_p, ctypes.c_int32] + [ctypes.c_void_p] * 4
+    L.spec_controller_speedup.restype = ctypes.c_double
+    L.spec_controller_speedup.argtypes = [ctypes.c_double, ctypes.c_double, ctypes.c_int32]
+    L.spec_controller_choose.restype = ctypes.c_int32
+    L.spec_controller_choose.argtypes = [ctypes.c_double, ctypes.c_double, ctypes.c_int32]
+    L.spec_controller_init.restype = ctypes.c_int
+    L.spec_controller_init.argtypes = [ctypes.POINTER(DepthControllerState), ctypes.c_int32, ctypes.c_double,
+                                       ctypes.c_double, ctypes.c_double, ctypes.c_double, ctypes.c_int64,
+                                       ctypes.c_int64, ctypes.c_int32]
+    L.spec_controller_update.restype = ctypes.c_int
+    L.spec_controller_update.argtypes = [ctypes.POINTER(DepthControllerState), ctypes.c_int32, ctypes.c_int32,
+                                         ctypes.c_double, ctypes.c_double]
+    L.spec_debug_build.restype = ctypes.c_int
+    if L.spec_abi_version() != ABI_VERSION:
+        raise RuntimeError(f"libspec_verify ABI {L.spec_abi_version()} != binding ABI {ABI_VERSION}")
+    return L
+
+
 def lib():
     """The loaded library; raises if it has not been built (python -m long_context_tree_amd.build)."""
     global _lib
     if _lib is None:
-        if not os.path.exists(LIB_PATH):
-            raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m long_context_tree_amd.build`")
-        L = ctypes.CDLL(LIB_PATH)
-        L.spec_abi_version.restype = ctypes.c_int
-        L.spec_status_string.restype = ctypes.c_char_p
-        L.spec_status_string.argtypes = [ctypes.c_int]
-        L.spec_last_error.restype = ctypes.c_char_p
-        for name, argt in (("spec_tree_attention", TreeAttentionArgs), ("spec_chunk_salience", ChunkSalienceArgs),
-                           ("spec_accept_greedy", AcceptGreedyArgs), ("spec_accept_rejection", AcceptRejectionArgs),
-                           ("spec_kv_commit", KvCommitArgs), ("spec_draft_gather", DraftGatherArgs)):
-            f = getattr(L, name)
-            f.restype = ctypes.c_int
-            f.argtypes = [ctypes.POINTER(argt), ctypes.c_void_p]
-        for name, argt in (("spec_tree_attention_workspace_size", TreeAttentionArgs),
-                           ("spec_accept_greedy_workspace_size", AcceptGreedyArgs),
-                           ("spec_accept_rejection_workspace_size", AcceptRejectionArgs)):
-            f = getattr(L, name)
-            f.restype = ctypes.c_size_t
-            f.argtypes = [ctypes.POINTER(argt)]
-        L.spec_read_probe.restype = ctypes.c_int
-        L.spec_read_probe.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p]
-        L.spec_tree_bundle_order.restype = ctypes.c_int
-        L.spec_tree_bundle_order.argtypes = [ctypes.c_void_p, ctypes.c_int32] + [ctypes.c_void_p] * 4
-        L.spec_controller_speedup.restype = ctypes.c_double
-        L.spec_controller_speedup.argtypes = [ctypes.c_double, ctypes.c_double, ctypes.c_int32]
-        L.spec_controller_choose.restype = ctypes.c_int32
-        L.spec_controller_choose.argtypes = [ctypes.c_double, ctypes.c_double, ctypes.c_int32]
-        L.spec_controller_init.restype = ctypes.c_int
-        L.spec_controller_init.argtypes = [ctypes.POINTER(DepthControllerState), ctypes.c_int32, ctypes.c_double,
-                                           ctypes.c_double, ctypes.c_double, ctypes.c_double, ctypes.c_int64,
-                                           ctypes.c_int64, ctypes.c_int32]
-        L.spec_controller_update.restype = ctypes.c_int
-        L.spec_controller_update.argtypes = [ctypes.POINTER(DepthControllerState), ctypes.c_int32, ctypes.c_int32,
-                                             ctypes.c_double, ctypes.c_double]
-        if L.spec_abi_version() != ABI_VERSION:
-            raise RuntimeError(f"libspec_verify ABI {L.spec_abi_version()} != binding ABI {ABI_VERSION}")
-        _lib = L
+        _lib = _load(LIB_PATH)
     return _lib
+
+
+def debug_lib():
+    """The SPEC_DEBUG build (device-side precondition checks and acceptance witnesses in the debug record
+    at the end of each workspace); the same argument structs as lib()."""
+    global _debug_lib
+    if _debug_lib is None:
+        _debug_lib = _load(DEBUG_LIB_PATH)
+    return _debug_lib
+
+
+def debug_record(workspace: torch.Tensor, workspace_size: int):
+    """The four uint32 words of the debug record of a call whose workspace (uint8 tensor) had
+    workspace_size bytes required: (error bits, rows witnessed, drafts tested, 0)."""
+    w = workspace[workspace_size - DEBUG_RECORD_BYTES:workspace_size - DEBUG_RECORD_BYTES + 16]
+    return [int(x) & 0xFFFFFFFF for x in w.view(torch.int32).cpu().tolist()]
+
+
+def debug_bits_names(bits: int):
+    return sorted(k for k, v in DBG_BITS.items() if bits & v)
+
 
 
 def status_string(status: int) -> str:

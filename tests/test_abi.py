@@ -29,11 +29,13 @@ def test_exports_every_declared_symbol():
     spec = _lib()
     names = declared_functions()
     assert {"spec_tree_attention", "spec_chunk_salience", "spec_accept_greedy", "spec_accept_rejection"} <= set(names)
-    assert len(names) == 18, names
-    L = ctypes.CDLL(spec.LIB_PATH)
-    for n in names:
-        assert hasattr(L, n), n
-    assert spec.lib().spec_abi_version() == 4
+    assert len(names) == 19, names
+    for path in (spec.LIB_PATH, spec.DEBUG_LIB_PATH):
+        L = ctypes.CDLL(path)
+        for n in names:
+            assert hasattr(L, n), (path, n)
+    assert spec.lib().spec_abi_version() == 5 and spec.debug_lib().spec_abi_version() == 5
+    assert spec.lib().spec_debug_build() == 0 and spec.debug_lib().spec_debug_build() == 1
     assert spec.status_string(3) == "SPEC_ERR_WORKSPACE"
 
 
@@ -274,3 +276,19 @@ def test_read_probe_refuses_bad_arguments():
     base = buf.data_ptr() + (-buf.data_ptr()) % 16
     assert L.spec_read_probe(base, 40, sink.data_ptr(), None) == 1 and "bytes" in spec.last_error()
     assert L.spec_read_probe(base, 32, None, None) == 1 and "sink" in spec.last_error()
+
+
+def test_workspaces_end_with_the_debug_record():
+    """Every workspace size includes the 256-byte debug record at its end, in both builds (the same size)."""
+    spec = _lib()
+    a, keep = _attn_args(spec)
+    n1 = spec.lib().spec_tree_attention_workspace_size(ctypes.byref(a))
+    n2 = spec.debug_lib().spec_tree_attention_workspace_size(ctypes.byref(a))
+    assert n1 == n2 and n1 % 256 == 0 and n1 > spec.DEBUG_RECORD_BYTES
+    no = torch.tensor([0, 3], dtype=torch.int32)
+    par = torch.tensor([-1, 0, 1], dtype=torch.int32)
+    outs = spec._outs(1, 4, "cpu")
+    g = spec._greedy_args(no, par, torch.zeros(3, dtype=torch.int32), torch.zeros(3, 64), 3, 4, outs)
+    # 3 rows x 1 segment key (8 bytes each), padded to 256, then the record
+    assert spec.lib().spec_accept_greedy_workspace_size(ctypes.byref(g)) == 256 + spec.DEBUG_RECORD_BYTES
+    assert spec.debug_lib().spec_accept_greedy_workspace_size(ctypes.byref(g)) == 256 + spec.DEBUG_RECORD_BYTES
