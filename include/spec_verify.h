@@ -272,6 +272,25 @@ size_t spec_accept_greedy_workspace_size(const spec_accept_greedy_args* args);
 int spec_accept_greedy(const spec_accept_greedy_args* args, void* stream);
 
 /* ------------------------------------------------------------------------------------------
+ * spec_accept_greedy_noalloc  for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc).
+ *
+ * The same operation, outputs, preconditions and errors as spec_accept_greedy, except that
+ * args->workspace and args->workspace_bytes are ignored: the per-segment argmax keys live in a
+ * library-owned device array of SPEC_GREEDY_NOALLOC_SCRATCH_BYTES bytes, one per GPU, which each GPU
+ * the library runs on holds until the process ends.  A call whose workspace need
+ * (spec_accept_greedy_workspace_size) exceeds that size returns SPEC_ERR_UNSUPPORTED before anything
+ * is enqueued.  The call allocates nothing (no hipMalloc, hipFree or allocating library routine); its
+ * first call on a device looks the array's address up once, with that device current.  Every call on
+ * one GPU shares that GPU's array, so calls that overlap on one GPU (different streams, no ordering
+ * between them) race; calls ordered on one stream do not.  Nothing in the array needs clearing: each
+ * call writes every key it reads.
+ * ------------------------------------------------------------------------------------------ */
+#define SPEC_GREEDY_NOALLOC_SCRATCH_BYTES (4u << 20)
+
+int spec_accept_greedy_noalloc(const spec_accept_greedy_args* args, void* stream);
+
+/* ------------------------------------------------------------------------------------------
  * spec_accept_rejection  [AS "Correctness first", "The controller"; Leviathan et al. and
  * Chen et al. as cited there]
  *

@@ -7,11 +7,11 @@ bundle (preorder) order of a draft tree, and the draft-depth controller.
 """
 
 from .spec import (ROPE_HALF, ROPE_NONE, ROPE_PAIRS, V_DIM_MAJOR, V_TOKEN_ROWS, AttentionHandle, DepthController,
-                   SpecError, accept_greedy, accept_rejection, chunk_salience, controller_choose, controller_speedup,
+                   SpecError, accept_greedy, accept_greedy_noalloc, accept_rejection, chunk_salience, controller_choose, controller_speedup,
                    draft_gather, kv_commit, last_error, lib, read_probe, status_string, tree_attention,
                    tree_attention_args, tree_bundle_order)
 
 __all__ = ["ROPE_HALF", "ROPE_NONE", "ROPE_PAIRS", "V_DIM_MAJOR", "V_TOKEN_ROWS", "AttentionHandle",
-           "DepthController", "SpecError", "accept_greedy", "accept_rejection", "chunk_salience", "controller_choose",
+           "DepthController", "SpecError", "accept_greedy", "accept_greedy_noalloc", "accept_rejection", "chunk_salience", "controller_choose",
            "controller_speedup", "draft_gather", "kv_commit", "last_error", "lib", "read_probe", "status_string",
            "tree_attention", "tree_attention_args", "tree_bundle_order"]

@@ -8,6 +8,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 #include <string>
 
 #include "spec_internal.h"
@@ -367,6 +368,66 @@ int spec_accept_greedy(const spec_accept_greedy_args* args, void* stream) {
 #endif
   const hipError_t e = spec::launch_accept_greedy(p, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "spec_accept_greedy launch");
+  return ok();
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------------------------
+// spec_accept_greedy_noalloc: the greedy call with its segment keys in a file-scope device array
+// ---------------------------------------------------------------------------------------------
+namespace {
+
+constexpr size_t kScratchBytes = SPEC_GREEDY_NOALLOC_SCRATCH_BYTES;
+constexpr int kScratchDevices = 64;
+
+// Each GPU the library runs on holds its own copy.  In host code `scratch` names a host-side stand-in,
+// not a device address: only the per-device pointers from hipGetSymbolAddress are handed to kernels.
+__device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kScratchDevices] = {};
+
+// The device address of this device's `scratch`, looked up once per device (with that device current).
+int scratch_for_current_device(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "spec_accept_greedy_noalloc: hipGetDevice");
+  if (dev < 0 || dev >= kScratchDevices)
+    return fail(SPEC_ERR_UNSUPPORTED, "spec_accept_greedy_noalloc: device %d, supported are 0..%d", dev,
+                kScratchDevices - 1);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "spec_accept_greedy_noalloc: hipGetSymbolAddress(scratch)");
+    if (!ptr) return fail(SPEC_ERR_HIP, "spec_accept_greedy_noalloc: hipGetSymbolAddress(scratch) gave NULL");
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return SPEC_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int spec_accept_greedy_noalloc(const spec_accept_greedy_args* args, void* stream) {
+  int st = check_greedy(args);
+  if (st != SPEC_OK) return st;
+  const size_t need = spec::greedy_ws_bytes(args->batch, args->max_nodes, nseg_of(args->vocab));
+  if (need > kScratchBytes)
+    return fail(SPEC_ERR_UNSUPPORTED,
+                "spec_accept_greedy_noalloc: batch * max_nodes * ceil(vocab / %d) keys need %zu bytes, more than the "
+                "%zu-byte device array; use spec_accept_greedy with a workspace",
+                spec::kSegment, need, kScratchBytes);
+  void* ws = nullptr;
+  st = scratch_for_current_device(&ws);
+  if (st != SPEC_OK) return st;
+  spec::AcceptParams p = accept_params(args);
+  p.seg_key = static_cast<unsigned long long*>(ws);
+  const hipError_t e = spec::launch_accept_greedy(p, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "spec_accept_greedy_noalloc launch");
   return ok();
 }
 

@@ -22,6 +22,7 @@ SPEC_DTYPE_BF16 = 0
 SPEC_DTYPE_F32 = 1
 ABI_VERSION = 5
 MAX_TREE_NODES = 2048
+GREEDY_NOALLOC_SCRATCH_BYTES = 4 << 20   # SPEC_GREEDY_NOALLOC_SCRATCH_BYTES
 V_TOKEN_ROWS = 0   # spec_v_layout: V pages like K, [pages][kv_heads][page_size][head_dim]
 V_DIM_MAJOR = 1    # V pages [pages][kv_heads][head_dim][page_size]
 ROPE_NONE = 0      # spec_rope: K copied as stored
@@ -52,7 +53,7 @@ def _load(path: str):
     L.spec_status_string.argtypes = [ctypes.c_int]
     L.spec_last_error.restype = ctypes.c_char_p
     for name, argt in (("spec_tree_attention", TreeAttentionArgs), ("spec_chunk_salience", ChunkSalienceArgs),
-                       ("spec_accept_greedy", AcceptGreedyArgs),
+                       ("spec_accept_greedy", AcceptGreedyArgs), ("spec_accept_greedy_noalloc", AcceptGreedyArgs),
                        ("spec_accept_rejection", AcceptRejectionArgs),
                        ("spec_kv_commit", KvCommitArgs), ("spec_draft_gather", DraftGatherArgs)):
         f = getattr(L, name)
@@ -408,6 +409,17 @@ def accept_greedy(node_offsets, parents, draft_tokens, target_logits, *, max_nod
     ws = _workspace(need, target_logits.device, workspace)
     a.workspace, a.workspace_bytes = ws.data_ptr(), ws.numel()
     _check(lib().spec_accept_greedy(ctypes.byref(a), _stream(stream)), "spec_accept_greedy")
+    return outs
+
+
+def accept_greedy_noalloc(node_offsets, parents, draft_tokens, target_logits, *, max_nodes: int, max_path: int,
+                          outs=None, stream=None):
+    """accept_greedy with the library's own per-GPU device array in place of a workspace (no allocation in
+    the call; refused when the keys need more than GREEDY_NOALLOC_SCRATCH_BYTES).  Returns as accept_greedy."""
+    B = node_offsets.numel() - 1
+    outs = outs or _outs(B, max_path, target_logits.device)
+    a = _greedy_args(node_offsets, parents, draft_tokens, target_logits, max_nodes, max_path, outs)
+    _check(lib().spec_accept_greedy_noalloc(ctypes.byref(a), _stream(stream)), "spec_accept_greedy_noalloc")
     return outs
 
 

@@ -29,7 +29,7 @@ def test_exports_every_declared_symbol():
     spec = _lib()
     names = declared_functions()
     assert {"spec_tree_attention", "spec_chunk_salience", "spec_accept_greedy", "spec_accept_rejection"} <= set(names)
-    assert len(names) == 19, names
+    assert len(names) == 20, names
     for path in (spec.LIB_PATH, spec.DEBUG_LIB_PATH):
         L = ctypes.CDLL(path)
         for n in names:
@@ -276,6 +276,22 @@ def test_read_probe_refuses_bad_arguments():
     base = buf.data_ptr() + (-buf.data_ptr()) % 16
     assert L.spec_read_probe(base, 40, sink.data_ptr(), None) == 1 and "bytes" in spec.last_error()
     assert L.spec_read_probe(base, 32, None, None) == 1 and "sink" in spec.last_error()
+
+
+def test_greedy_noalloc_refuses_inputs_beyond_its_device_array():
+    """The no-allocation greedy call refuses, before any HIP call, an input whose segment keys need more
+    than its fixed device array, and says which call to use instead."""
+    spec = _lib()
+    no = torch.tensor([0, 3], dtype=torch.int32)
+    par = torch.tensor([-1, 0, 1], dtype=torch.int32)
+    tok = torch.zeros(3, dtype=torch.int32)
+    logits = torch.zeros(3, 64, dtype=torch.float32)
+    outs = spec._outs(1, 4, "cpu")
+    a = spec._greedy_args(no, par, tok, logits, 3, 4, outs)
+    a.max_nodes, a.vocab = 2048, 1 << 24                      # 2048 x 2048 segment keys: 32 MiB
+    assert spec.lib().spec_accept_greedy_noalloc(ctypes.byref(a), None) == 2
+    assert "device array" in spec.last_error() and "spec_accept_greedy" in spec.last_error()
+    assert spec.GREEDY_NOALLOC_SCRATCH_BYTES == 4 << 20
 
 
 def test_workspaces_end_with_the_debug_record():
