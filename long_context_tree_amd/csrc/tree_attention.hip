@@ -39,6 +39,8 @@
 //    over each context chunk; the salience pass turns these into attention mass once the row's
 //    final log-sum-exp is known (no second pass over K).
 //  * Splits write (max, sum, unnormalised O) partials; the merge kernel combines them (LSE merge).
+#include <type_traits>
+
 #include "spec_internal.h"
 
 namespace spec {
@@ -799,11 +801,628 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnParams p) {
   }
 }
 
+// ---------------------------------------------------------------------------------------------------
+// Software-pipelined variant for wide trees: 8 waves of 32 query rows (256 rows per work-group),
+// head_dim 128, V in token rows, chunk partials per 64-slot tile (or none).
+//
+// The per-tile work of tree_attn_kernel runs in phases: the QK^T MFMAs, then the softmax on the VALU,
+// then the P.V MFMAs.  Both waves that share a SIMD reach the same phase at the same time (one barrier
+// per tile), so the exps never run beside matrix work.  On gfx950 a wave's independent VALU
+// instructions issue in the shadow of its MFMAs: at up to about two VALU instructions per 16x16x32
+// MFMA they cost nearly nothing (measured with a throwaway microbenchmark).  This variant splits each
+// 64-slot tile into two 32-key halves and runs, per tile t, two blocks of 34 MFMAs each with the exps of
+// one half inside:
+//   B1: QK^T of (t, half 1) and P.V + chunk sums of (t-1, half 1)  |  exps of (t, half 0)
+//   B2: P.V + chunk sums of (t, half 0) and QK^T of (t+1, half 0)  |  exps of (t, half 1)
+// so tile t+1's K tile must be in LDS during tile t: K and V each have three LDS buffers (K(t+2) and
+// V(t+1) load while tile t is computed).  Scores, probabilities and accumulators keep the registers of
+// tree_attn_kernel (the two score halves and the two probability halves are reused in turn).  The
+// online softmax, the lazy rescaling and the chunk bookkeeping are those of tree_attn_kernel, taken per
+// half-tile.  Every tile runs the same two blocks: a tile that holds tree slots masks its scores between
+// them, the split's first tile multiplies a cleared V buffer by zero probabilities, and its last tile
+// computes scores it never uses, so that no second copy of the step (and no register spill) is needed.
+// On pages of >= 16 slots each wave's four direct-to-LDS loads of the next tiles go out one at a time
+// inside block B1, so the vector memory path takes them beside the matrix work.
+template <int PRE, int CH>
+__global__ __launch_bounds__(512, 1) void tree_attn_pipe_kernel(AttnParams p) {
+  constexpr int D = 128, W = 8, RB = 2, NT = W * 64, ROWS_WG = W * RB * 16;
+  constexpr int KS = D / 32;                    // k-steps of the QK^T product
+  constexpr int NB = D / 16;                    // 16-dim output blocks
+  constexpr int CPR = D / 8;                    // 16-byte chunks per K/V row
+  constexpr int TILE_EL = kTile * D;
+  constexpr int LOADS = 2 * kTile * CPR / NT;   // 16-byte loads per thread and tile step (K or V)
+  constexpr int KB = kTile * CPR / 64;          // 1 KiB blocks of a K (or V) tile
+  constexpr int ANC_N = kMaxNodes, ANC_W = ANC_N / 64, END_N = ANC_N * ANC_W * 2;
+  static_assert(KB % LOADS == 0, "a wave's loads must be all K or all V");
+
+  // three K and three V tile buffers, separate arrays so that alias analysis tells the buffers being read
+  // from the ones whose direct-to-LDS loads are in flight
+  __shared__ __attribute__((aligned(16))) uint16_t ka[TILE_EL], kb[TILE_EL], kc[TILE_EL];
+  __shared__ __attribute__((aligned(16))) uint16_t va[TILE_EL], vb[TILE_EL], vc[TILE_EL];
+  union TreeRel {
+    uint64_t anc[ANC_N][ANC_W];
+    int end[END_N];
+  };
+  __shared__ TreeRel rel_lds;
+  auto& anc_lds = rel_lds.anc;
+  auto& end_lds = rel_lds.end;
+  __shared__ int pg_lds[kMaxSplitPages];
+  auto swz = [](int r) -> int { return r & 15; };              // K rows
+  auto swzv_rows = [](int r) -> int { return (2 * r) & 15; };  // V rows (read transposed)
+
+  // ---- which (row group, split, KV head, sequence): as tree_attn_kernel ----
+  const int RG = p.row_groups;
+  const int n_units = p.batch * p.Hkv * p.max_splits;
+  const int wg = blockIdx.x;
+  const int rg = (wg >> 3) % RG;
+  const int unit = ((wg >> 3) / RG) * 8 + (wg & 7);
+  if (unit >= n_units) return;
+  const int split = unit % p.max_splits;
+  const int kvh = (unit / p.max_splits) % p.Hkv;
+  const int b = unit / (p.max_splits * p.Hkv);
+  int n0 = p.node_offsets[b];
+  int N = p.node_offsets[b + 1] - n0;
+  N = N < 0 ? 0 : (N > p.max_nodes ? p.max_nodes : N);
+  n0 = n0 < 0 ? 0 : (n0 > (p.batch - 1) * p.max_nodes ? (p.batch - 1) * p.max_nodes : n0);
+  int L = p.ctx_lens[b];
+  L = L < 0 ? 0 : (L > p.max_ctx ? p.max_ctx : L);
+  const int keys = L + N;
+  const int n_tiles = (keys + kTile - 1) / kTile;
+  const int t_begin = split * p.split_tiles;
+  int t_end = min(n_tiles, t_begin + p.split_tiles);
+  const int G = p.G;
+  const int rows = N * G;
+  const int row0 = rg * ROWS_WG;
+  if (t_begin >= t_end || row0 >= rows) return;
+  {
+    const int last_node = (min(row0 + ROWS_WG, rows) - 1) / G;
+    const int t_need = (L + last_node + 1 + kTile - 1) / kTile;
+    t_end = max(t_begin + 1, min(t_end, t_need));
+  }
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lm = lane & 15, lg = lane >> 4;
+  const int pshift = p.page_shift;
+
+  const int pg_first = (t_begin * kTile) >> pshift;
+  const int pg_count = (((keys < t_end * kTile ? keys : t_end * kTile) - 1) >> pshift) - pg_first + 1;
+  {
+    const int32_t* bt_row = p.block_table + (int64_t)b * p.bt_stride;
+    for (int i = tid; i < pg_count; i += NT) {
+      const int pg = bt_row[pg_first + i];
+      pg_lds[i] = (pg >= 0 && pg < p.num_pages) ? pg : -1;
+    }
+  }
+  const bool has_tree = t_end * kTile > L;
+  if (PRE && has_tree) {
+    for (int i = tid; i < N && i < END_N; i += NT) {
+      int e = p.subtree_end[n0 + i];
+      end_lds[i] = e <= i ? i + 1 : (e > N ? N : e);
+    }
+  } else if (has_tree) {
+    for (int i = tid; i < N && i < ANC_N; i += NT) {
+      uint64_t m[ANC_W];
+#pragma unroll
+      for (int w = 0; w < ANC_W; ++w) m[w] = 0;
+      int j = i;
+      for (int step = 0; step < N && j >= 0 && j < ANC_N; ++step) {
+#pragma unroll
+        for (int w = 0; w < ANC_W; ++w) m[w] |= (j >> 6) == w ? 1ull << (j & 63) : 0ull;
+        const int pj = p.parents[n0 + j];
+        if (pj >= j) break;
+        j = pj;
+      }
+#pragma unroll
+      for (int w = 0; w < ANC_W; ++w) anc_lds[i][w] = m[w];
+    }
+  }
+
+  // ---- this lane's query rows and their Q fragments ----
+  int node_r[RB];
+  bool valid_r[RB];
+  bf16x8 qreg[RB][KS];
+  const bool wave_active = row0 + wave * RB * 16 < rows;
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    const int row = row0 + (wave * RB + rb) * 16 + lm;
+    valid_r[rb] = row < rows;
+    node_r[rb] = valid_r[rb] ? row / G : 0;
+    const int head = valid_r[rb] ? kvh * G + row % G : 0;
+    const uint16_t* qp = p.q + ((int64_t)(n0 + node_r[rb]) * p.Hq + head) * D + 8 * lg;
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) {
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (valid_r[rb]) v = *reinterpret_cast<const u32x4*>(qp + 32 * kk);
+      qreg[rb][kk] = __builtin_bit_cast(bf16x8, v);
+    }
+  }
+  __syncthreads();                                  // page ids visible before the first tile load
+
+  // ---- tile loads: waves 0..3 load K tiles, waves 4..7 V tiles (16 consecutive keys per wave) ----
+  const uint16_t* kbase = p.k + (int64_t)kvh * p.head_stride;
+  const uint16_t* vbase = p.v + (int64_t)kvh * p.head_stride;
+  const uint32_t tstride = (uint32_t)p.token_stride;
+  const int pmask = (1 << pshift) - 1;
+  const bool wave_is_v = wave * LOADS >= KB;
+  uint32_t ld_voff[LOADS];
+#pragma unroll
+  for (int i = 0; i < LOADS; ++i) {
+    const int blk = wave * LOADS + i;
+    const int q = (blk * 64 + lane) % (kTile * CPR);
+    const int kt = q / CPR;
+    const int src = ((q % CPR) ^ (blk >= KB ? swzv_rows(kt) : swz(kt))) * 8;
+    const int row = pshift > 6 ? kt : (kt & pmask);
+    ld_voff[i] = ((uint32_t)row * tstride + (uint32_t)src) * 2u;
+  }
+  constexpr int KPL = 64 / CPR;                     // keys per load (4)
+  constexpr int GL = 16 / KPL < LOADS ? 16 / KPL : LOADS;
+  const bool grouped = pshift >= 4;
+  // this wave's share of tile t (K for waves 0..3, V for waves 4..7) into buf
+  auto issue = [&](int t, uint16_t* buf) __attribute__((always_inline)) {
+    const int key0 = t * kTile;
+    const uint16_t* base = wave_is_v ? vbase : kbase;
+    if (grouped) {
+      int pgs[LOADS / GL];
+#pragma unroll
+      for (int g = 0; g < LOADS / GL; ++g) {
+        const int key_w = key0 + (((wave * LOADS + g * GL) * 64) % (kTile * CPR)) / CPR;
+        int pi = (key_w >> pshift) - pg_first;
+        pi = pi < pg_count ? pi : pg_count - 1;
+        pgs[g] = pg_lds[pi];
+      }
+#pragma unroll
+      for (int g = 0; g < LOADS / GL; ++g) {
+        const int key_w = key0 + (((wave * LOADS + g * GL) * 64) % (kTile * CPR)) / CPR;
+        const int pg = __builtin_amdgcn_readfirstlane(pgs[g]);
+        const int first_key = pshift > 6 ? key0 : (key_w & ~pmask);
+        const int span = pshift > 6 ? kTile : (1 << pshift);
+        int valid = keys - first_key;
+        valid = valid < 0 ? 0 : (valid > span ? span : valid);
+        if (pg < 0) valid = 0;
+        const uint32_t rowb = pshift > 6 ? (uint32_t)(key0 & pmask) * tstride : 0u;
+        const uint16_t* bp = base + (uint64_t)(uint32_t)(pg < 0 ? 0 : pg) * (uint32_t)p.page_stride + rowb;
+#pragma unroll
+        for (int i = g * GL; i < (g + 1) * GL; ++i)
+          buffer_load_lds16(bp, (uint32_t)valid * tstride * 2u, buf + ((wave * LOADS + i) % KB) * 512, ld_voff[i]);
+      }
+      return;
+    }
+    int pgv[LOADS];
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) {
+      const int blk = wave * LOADS + i;
+      const int key_w = key0 + ((blk * 64) % (kTile * CPR)) / CPR;
+      int pi = (key_w >> pshift) - pg_first;
+      pi = pi < pg_count ? pi : pg_count - 1;
+      pgv[i] = pg_lds[pi];
+    }
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) {
+      const int blk = wave * LOADS + i;
+      const int pg = __builtin_amdgcn_readfirstlane(pgv[i]);
+      const int key_w = key0 + ((blk * 64) % (kTile * CPR)) / CPR;
+      const int first_key = pshift > 6 ? key0 : (key_w & ~pmask);
+      const int span = pshift > 6 ? kTile : (1 << pshift);
+      int valid = keys - first_key;
+      valid = valid < 0 ? 0 : (valid > span ? span : valid);
+      if (pg < 0) valid = 0;
+      const uint32_t rowb = pshift > 6 ? (uint32_t)(key0 & pmask) * tstride : 0u;
+      const uint16_t* bp = base + (uint64_t)(uint32_t)(pg < 0 ? 0 : pg) * (uint32_t)p.page_stride + rowb;
+      buffer_load_lds16(bp, (uint32_t)valid * tstride * 2u, buf + (blk % KB) * 512, ld_voff[i]);
+    }
+  };
+
+  // The grouped path (pages of >= 16 slots: a wave's 16 keys sit in one page) split in two, so that the
+  // loads can be spread over a block: the page lookup and the descriptor's base and byte range first
+  // (valid = false gives an empty range: the loads then write zeros, into a buffer nobody reads), then
+  // one 16-byte direct-to-LDS load at a time.
+  auto plan_grouped = [&](int t, bool valid_tile, const uint16_t*& bp, uint32_t& bytes) __attribute__((always_inline)) {
+    const int key0 = t * kTile;
+    const int key_w = key0 + (((wave * LOADS) * 64) % (kTile * CPR)) / CPR;
+    int pi = (key_w >> pshift) - pg_first;
+    pi = pi < pg_count ? pi : pg_count - 1;
+    pi = pi < 0 ? 0 : pi;
+    const int pg = __builtin_amdgcn_readfirstlane(pg_lds[pi]);
+    const int first_key = pshift > 6 ? key0 : (key_w & ~pmask);
+    const int span = pshift > 6 ? kTile : (1 << pshift);
+    int valid = keys - first_key;
+    valid = valid < 0 ? 0 : (valid > span ? span : valid);
+    if (pg < 0 || !valid_tile) valid = 0;
+    const uint32_t rowb = pshift > 6 ? (uint32_t)(key0 & pmask) * tstride : 0u;
+    bp = (wave_is_v ? vbase : kbase) + (uint64_t)(uint32_t)(pg < 0 ? 0 : pg) * (uint32_t)p.page_stride + rowb;
+    bytes = (uint32_t)valid * tstride * 2u;
+  };
+  auto load_one = [&](const uint16_t* bp, uint32_t bytes, uint16_t* buf, int i) __attribute__((always_inline)) {
+    buffer_load_lds16(bp, bytes, buf + ((wave * LOADS + i) % KB) * 512, ld_voff[i]);
+  };
+  static_assert(LOADS / GL == 1, "one page group per wave and tile");
+
+  // ---- operand offsets (as tree_attn_kernel with token-row V) ----
+  int k_off[KS];
+#pragma unroll
+  for (int kk = 0; kk < KS; ++kk) k_off[kk] = lm * D + 8 * ((4 * kk + lg) ^ swz(lm));
+  // chunk c = 2 nb + b0 of the row at key sits at position c ^ swz: with swz = 2 sh + s0 that is
+  // 2 (nb ^ sh) + (b0 ^ s0), so the offset of dim block nb is v_base[h] + (16 sh ^ 16 nb)
+  int v_base[2], v_sh16[2];
+#pragma unroll
+  for (int h2 = 0; h2 < 2; ++h2) {
+    const int key = 32 * h2 + 4 * lg + (lm >> 2);
+    const int sw = swzv_rows(key);
+    v_base[h2] = key * D + 4 * (lm & 1) + 8 * (((lm & 3) >> 1) ^ (sw & 1));
+    v_sh16[h2] = 16 * (sw >> 1);
+  }
+  const bf16x8 ones = bf16_splat8(0x3F803F80u, 0x3F803F80u);
+
+  f32x4 o[RB][NB];
+  float m_r[RB], l_r[RB], cacc[RB];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    m_r[rb] = kNegBig;
+    l_r[rb] = 0.f;
+    cacc[rb] = 0.f;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) o[rb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  const float c2 = p.scale_log2;
+  const int cs = p.chunk_size;
+  const int cs_shift = (cs > 0 && (cs & (cs - 1)) == 0) ? __builtin_ctz((unsigned)cs) : -1;
+  auto chunk_of = [&](int key) __attribute__((always_inline)) -> int { return cs_shift >= 0 ? key >> cs_shift : key / cs; };
+  const int row_stride_chunk = p.max_nodes * p.Hq;
+  const int st_rb = lg % RB;
+  const int st_row = row0 + (wave * RB + st_rb) * 16 + lm;
+  const bool st_ok = lg < RB && st_row < rows;
+  const int64_t st_col = st_ok ? (int64_t)(st_row / G) * p.Hq + kvh * G + st_row % G : 0;
+  float* cbase = p.chunk_lse2 + (int64_t)b * p.max_chunks * row_stride_chunk + st_col;
+
+  // score halves (keys 0..31 and 32..63 of a tile) and probability halves, reused in turn
+  f32x4 sA[RB][2], sB[RB][2];
+  bf16x8 pA[RB], pB[RB];
+  float eA[RB], eB[RB];                             // this lane's fp32 sums of a half's probabilities
+  float csum[RB];
+
+  // S^T half h of the tile in kt: rows of keys 32h .. 32h+31 (blocks j = 2h, 2h+1)
+  auto qk_half = [&](const uint16_t* kt, int h, f32x4 (&s)[RB][2]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj) s[rb][jj] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) {
+      bf16x8 kf[2];
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj)
+        kf[jj] = *reinterpret_cast<const bf16x8*>(kt + k_off[kk] + 16 * (2 * h + jj) * D);
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb)
+          s[rb][jj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[jj], qreg[rb][kk], s[rb][jj], 0, 0, 0);
+    }
+  };
+  // a half-tile's probabilities against the running max (bf16 P fragment, fp32 lane sum)
+  auto exps_half = [&](const f32x4 (&s)[RB][2], bf16x8 (&pout)[RB], float (&esum)[RB]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      const float mneg = -m_r[rb];
+      bf16x8 v;
+      float e0 = 0.f, e1 = 0.f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float x0 = __builtin_amdgcn_exp2f(fmaf(s[rb][0][i], c2, mneg));
+        const float x1 = __builtin_amdgcn_exp2f(fmaf(s[rb][1][i], c2, mneg));
+        e0 = i == 0 ? x0 : e0 + x0;
+        e1 = i == 0 ? x1 : e1 + x1;
+        v[i] = (__bf16)x0;
+        v[4 + i] = (__bf16)x1;
+      }
+      pout[rb] = v;
+      esum[rb] = e0 + e1;
+    }
+  };
+  // O^T += V^T . P^T for half h of the tile in vt
+  auto pv_half = [&](const uint16_t* vt, int h, const bf16x8 (&pin)[RB]) __attribute__((always_inline)) {
+    typedef short i16x4 __attribute__((ext_vector_type(4)));
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const int off = v_base[h] + (v_sh16[h] ^ (16 * nb));
+      const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(vt + off));
+      const i16x4 hi =
+          __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(vt + off + 16 * D));
+      const u32x2 lo2 = __builtin_bit_cast(u32x2, lo), hi2 = __builtin_bit_cast(u32x2, hi);
+      const u32x4 av = {lo2[0], lo2[1], hi2[0], hi2[1]};
+      const bf16x8 vf = __builtin_bit_cast(bf16x8, av);
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) o[rb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pin[rb], o[rb][nb], 0, 0, 0);
+    }
+  };
+  // chunk sums of half h (ones of the context slots of the half: a = all ones inside the context)
+  auto chunk_half = [&](const bf16x8 (&pin)[RB], const bf16x8& a) __attribute__((always_inline)) {
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+      csum[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pin[rb], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0)[0];
+  };
+  // ones of half h of the tile at key0, cleared at slots >= L (chunk sums cover context slots only)
+  auto ones_edge = [&](int key0, int h) -> bf16x8 {
+    bf16x8 a = ones;
+    int nv = L - key0;
+    asm volatile("" : "+s"(nv));
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int pk = 32 * h + (e < 4 ? 4 * lg + e : 12 + 4 * lg + e);
+      if (pk >= nv) a[e] = (__bf16)0.0f;
+    }
+    return a;
+  };
+  // tree mask of half h of tile t (keys >= L visible only to their descendants)
+  auto mask_half = [&](int t, int h, f32x4 (&s)[RB][2]) __attribute__((always_inline)) {
+    const int key0 = t * kTile;
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int key = key0 + 16 * (2 * h + jj) + 4 * lg + i;
+          bool vis = key < L;
+          if (!vis && key < keys && valid_r[rb]) {
+            const int tj = key - L;
+            if constexpr (PRE != 0)
+              vis = tj <= node_r[rb] && node_r[rb] < end_lds[tj];
+            else
+              vis = (anc_lds[node_r[rb]][(tj >> 6) & (ANC_W - 1)] >> (tj & 63)) & 1ull;
+          }
+          if (!vis) s[rb][jj][i] = -INFINITY;
+        }
+  };
+  // after a half's exps: when some probability exceeds 2^kRescale (the running max is stale), take the
+  // half's maxima, move the running max (rescaling O, l and the chunk accumulator) and redo the exps;
+  // then add the half's sums to l
+  auto settle_half = [&](const f32x4 (&s)[RB][2], bf16x8 (&pout)[RB], float (&esum)[RB]) __attribute__((always_inline)) {
+    bool big = false;
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) big |= esum[rb] > 0x1p8f;
+    static_assert(kRescale == 8.0f, "the sum test above is 2^kRescale");
+    if (__builtin_expect(__builtin_amdgcn_ballot_w64(big) != 0, 0)) {
+      bool resc = false;
+      float mt[RB];
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        float mx = fmaxf(fmaxf(s[rb][0][0], s[rb][0][1]), fmaxf(s[rb][0][2], s[rb][0][3]));
+        mx = fmaxf(fmaxf(mx, fmaxf(s[rb][1][0], s[rb][1][1])), fmaxf(s[rb][1][2], s[rb][1][3]));
+        mt[rb] = max4g(mx) * c2;
+        resc |= mt[rb] > m_r[rb] + kRescale;
+      }
+      if (__builtin_amdgcn_ballot_w64(resc) != 0) {
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+          const float mnew = mt[rb] > m_r[rb] + kRescale ? mt[rb] : m_r[rb];
+          const float alpha = __builtin_amdgcn_exp2f(m_r[rb] - mnew);
+          l_r[rb] *= alpha;
+          cacc[rb] *= alpha;
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb) o[rb][nb] *= alpha;
+          m_r[rb] = mnew;
+        }
+      }
+      exps_half(s, pout, esum);
+    }
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) l_r[rb] += esum[rb];
+  };
+  // chunk sums of a finished half join the accumulator; a 64-slot tile that ends a chunk stores the
+  // chunk's log2-sum-exp per row (one 128-byte store per wave)
+  auto chunk_add = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) cacc[rb] += csum[rb];
+  };
+  auto chunk_close = [&](int key0) __attribute__((always_inline)) {
+    const int c = chunk_of(key0);
+    const int cend = min((c + 1) * cs, L);
+    if (key0 + kTile >= cend) {
+      float v = m_r[0] + __builtin_amdgcn_logf(cacc[0]);
+#pragma unroll
+      for (int rb = 1; rb < RB; ++rb)
+        if (st_rb == rb) v = m_r[rb] + __builtin_amdgcn_logf(cacc[rb]);
+      if (st_ok) cbase[(int64_t)c * row_stride_chunk] = v;
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) cacc[rb] = 0.f;
+    }
+  };
+
+  // One interleaved block: 17 slots, each one MFMA pair (P.V of the V tile vt, half hv, with pin: dim
+  // blocks 0..7; then the chunk sums of pin against a_chunk; then QK^T of the K tile kt, half hk: k-steps
+  // 0..3 x key blocks 0..1), the LDS reads of the fragment three slots ahead, and one element's
+  // probability (fma, exp, add, bf16 convert) of the half-tile scores sin.  sched_barrier pins the order:
+  // about two VALU instructions per MFMA issue in the MFMAs' shadow.
+  auto run_block = [&](const uint16_t* vt, int hv, const bf16x8 (&pin)[RB], const bf16x8& a_chunk,
+                       const uint16_t* kt, int hk, f32x4 (&sout)[RB][2], const f32x4 (&sin)[RB][2],
+                       bf16x8 (&pout)[RB], float (&esum)[RB], auto&& slot_hook) __attribute__((always_inline)) {
+    typedef short i16x4 __attribute__((ext_vector_type(4)));
+    constexpr int NF = 17, AHEAD = 3;
+    bf16x8 fr[AHEAD + 1];
+    auto read_frag = [&](int f, bf16x8& out) __attribute__((always_inline)) {
+      if (f < NB) {                                // V^T fragment of dim block f (two transposing reads)
+        const int off = v_base[hv] + (v_sh16[hv] ^ (16 * f));
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(vt + off));
+        const i16x4 hi =
+            __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(vt + off + 16 * D));
+        const u32x2 lo2 = __builtin_bit_cast(u32x2, lo), hi2 = __builtin_bit_cast(u32x2, hi);
+        const u32x4 av = {lo2[0], lo2[1], hi2[0], hi2[1]};
+        out = __builtin_bit_cast(bf16x8, av);
+      } else if (f > NB) {                         // K fragment of k-step kk, key block jj
+        const int kk = (f - NB - 1) >> 1, jj = (f - NB - 1) & 1;
+        out = *reinterpret_cast<const bf16x8*>(kt + k_off[kk] + 16 * (2 * hk + jj) * D);
+      }
+    };
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj) sout[rb][jj] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float xs[RB][8];
+#pragma unroll
+    for (int f = 0; f < AHEAD; ++f) read_frag(f, fr[f]);
+#pragma unroll
+    for (int f = 0; f < NF; ++f) {
+      slot_hook(f);
+      if (f + AHEAD < NF) read_frag(f + AHEAD, fr[(f + AHEAD) % (AHEAD + 1)]);
+      const bf16x8& cur = fr[f % (AHEAD + 1)];
+      if (f < NB) {
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) o[rb][f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cur, pin[rb], o[rb][f], 0, 0, 0);
+      } else if (f == NB) {
+        if (CH) {
+#pragma unroll
+          for (int rb = 0; rb < RB; ++rb)
+            csum[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_chunk, pin[rb], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0)[0];
+        }
+      } else {
+        const int kk = (f - NB - 1) >> 1, jj = (f - NB - 1) & 1;
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb)
+          sout[rb][jj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cur, qreg[rb][kk], sout[rb][jj], 0, 0, 0);
+      }
+      if (f < 2 * 8) {                             // element e of row block rb of the P fragment
+        const int rb = f >> 3, e = f & 7;
+        const float x = __builtin_amdgcn_exp2f(fmaf(sin[rb][e >> 2][e & 3], c2, -m_r[rb]));
+        xs[rb][e] = x;
+        esum[rb] = e == 0 ? x : esum[rb] + x;
+        if (e & 1) {
+          pout[rb][e - 1] = (__bf16)xs[rb][e - 1];
+          pout[rb][e] = (__bf16)x;
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  // ---- the pipeline ----
+  // prologue: K(t0), V(t0) and K(t0 + 1) resident, V buffer 2 (the V "tile t0 - 1" of the first step)
+  // cleared, then the scores of (t0, half 0).  The first step's P.V of the previous tile multiplies that
+  // cleared buffer by P = 0, and its chunk sums are zero and never stored.
+  const int t0 = t_begin;
+  if (!wave_is_v) {
+    issue(t0, ka);
+    if (t0 + 1 < t_end) issue(t0 + 1, kb);
+  } else {
+    issue(t0, va);
+  }
+  for (int i = tid; i < TILE_EL / 8; i += NT) reinterpret_cast<u32x4*>(vc)[i] = u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) pB[rb] = bf16_splat8(0u, 0u);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  if (wave_active) qk_half(ka, 0, sA);
+
+  // Step of tile t; R = (t - t0) mod 3 selects the buffers: K(t) in slot R, K(t+1) in R+1, K(t+2) loads
+  // into R+2; V(t-1) in slot R+2, V(t) in R, V(t+1) loads into R+1 (slots mod 3).  Every tile runs the
+  // same two interleaved blocks; a tile holding slots >= L first masks its scores (between the blocks,
+  // where few registers are live), and the split's last tile computes scores of a tile it never uses.
+  auto kslot = [&](int i) __attribute__((always_inline)) -> uint16_t* { return i == 0 ? ka : (i == 1 ? kb : kc); };
+  auto vslot = [&](int i) __attribute__((always_inline)) -> uint16_t* { return i == 0 ? va : (i == 1 ? vb : vc); };
+  auto step = [&](int t, auto r_c) __attribute__((always_inline)) {
+    constexpr int R = decltype(r_c)::value;
+    uint16_t* kcur = kslot(R);
+    uint16_t* knext = kslot((R + 1) % 3);
+    uint16_t* vprev = vslot((R + 2) % 3);
+    uint16_t* vcur = vslot(R);
+    // this wave's share of K(t+2) (waves 0..3) or V(t+1) (waves 4..7); on the grouped path its four
+    // loads go out one at a time inside block B1, so the vector memory path takes them in the background
+    const int t_ld = wave_is_v ? t + 1 : t + 2;
+    uint16_t* ld_buf = wave_is_v ? vslot((R + 1) % 3) : kslot((R + 2) % 3);
+    const uint16_t* ld_bp = nullptr;
+    uint32_t ld_bytes = 0;
+    if (grouped) plan_grouped(t_ld, t_ld < t_end, ld_bp, ld_bytes);
+    else if (t_ld < t_end) issue(t_ld, ld_buf);
+    auto b1_hook = [&](int f) __attribute__((always_inline)) {
+      if ((f & 3) == 2 && f < 4 * LOADS) {
+        if (grouped) load_one(ld_bp, ld_bytes, ld_buf, f >> 2);
+      }
+    };
+    auto no_hook = [](int) {};
+    const int key0 = t * kTile;
+    const bool edge = key0 + kTile > L;             // holds slots >= L: the tree mask applies
+    const bool prev_edge = key0 > L;                // tile t - 1 holds slots >= L
+    if (wave_active) {
+      if (__builtin_expect(edge, 0)) mask_half(t, 0, sA);
+      const bf16x8 a_prev = (CH && __builtin_expect(prev_edge, 0)) ? ones_edge(key0 - kTile, 1) : ones;
+      // B1: P.V and chunk sums of (t-1, half 1), QK^T of (t, half 1) | exps of (t, half 0)
+      run_block(vprev, 1, pB, a_prev, kcur, 1, sB, sA, pA, eA, b1_hook);
+      // the exps' sums feed the rescale check right here, so they stay inside the block above; the chunk
+      // of tile t - 1 closes after it (a rescale scales the running max and the chunk sum together, so the
+      // stored log2-sum-exp is the same).  At t0 the sums of the cleared "tile t0 - 1" are zero.
+      if (CH) chunk_add();
+      settle_half(sA, pA, eA);
+      if (CH && t > t0 && key0 - kTile < L) chunk_close(key0 - kTile);
+      if (__builtin_expect(edge, 0)) mask_half(t, 1, sB);
+      const bf16x8 a_cur = (CH && __builtin_expect(edge, 0)) ? ones_edge(key0, 0) : ones;
+      // B2: P.V and chunk sums of (t, half 0), QK^T of (t+1, half 0) | exps of (t, half 1)
+      run_block(vcur, 0, pA, a_cur, knext, 0, sA, sB, pB, eB, no_hook);
+      if (CH) chunk_add();
+      settle_half(sB, pB, eB);
+    } else if (grouped) {
+      // a wave without rows still loads its share of the tiles
+#pragma unroll
+      for (int i = 0; i < LOADS; ++i) load_one(ld_bp, ld_bytes, ld_buf, i);
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this thread's loads of K(t+2) / V(t+1) landed
+    __syncthreads();
+  };
+  for (int t = t0; t < t_end; t += 3) {
+    step(t, std::integral_constant<int, 0>{});
+    if (t + 1 < t_end) step(t + 1, std::integral_constant<int, 1>{});
+    if (t + 2 < t_end) step(t + 2, std::integral_constant<int, 2>{});
+  }
+  // the last tile's half 1: P.V, chunk sums and its chunk
+  if (wave_active) {
+    const int tl = t_end - 1;
+    const int rl = (tl - t0) % 3;
+    const uint16_t* vl = rl == 0 ? va : (rl == 1 ? vb : vc);
+    pv_half(vl, 1, pB);
+    const int key0 = tl * kTile;
+    if (CH && key0 < L) {
+      chunk_half(pB, key0 + kTile > L ? ones_edge(key0, 1) : ones);
+      chunk_add();
+      chunk_close(key0);
+    }
+  }
+
+  if (!wave_active) return;
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    float l = l_r[rb];
+    l += __shfl_xor(l, 16);
+    l += __shfl_xor(l, 32);
+    l_r[rb] = l;
+  }
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    if (!valid_r[rb]) continue;
+    const int row = row0 + (wave * RB + rb) * 16 + lm;
+    const int64_t base = (((int64_t)b * p.Hkv + kvh) * p.max_splits + split) * p.rows_pad + row;
+    if (lg == 0) {
+      p.part_ml[base * 2 + 0] = m_r[rb];
+      p.part_ml[base * 2 + 1] = l_r[rb];
+    }
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) *reinterpret_cast<f32x4*>(&p.part_o[base * D + 16 * nb + 4 * lg]) = o[rb][nb];
+  }
+}
+
 template <int D, int W, int RB, int CM, int VT>
 hipError_t launch_d_w(const AttnParams& p, const AttnPlan& plan, hipStream_t s) {
   const int n_units = p.batch * p.Hkv * p.max_splits;
   const int grid = (int)(ceil_div(n_units, 8) * 8 * plan.row_groups);
-  if (p.subtree_end)
+  if constexpr (D == 128 && W == 8 && CM == 0 && VT == 0) {
+    // wide trees, head_dim 128, token-row V, 64-slot (or no) chunk partials: the software-pipelined kernel
+    if (p.subtree_end) {
+      if (p.chunk_size > 0) hipLaunchKernelGGL((tree_attn_pipe_kernel<1, 1>), dim3(grid), dim3(512), 0, s, p);
+      else hipLaunchKernelGGL((tree_attn_pipe_kernel<1, 0>), dim3(grid), dim3(512), 0, s, p);
+    } else {
+      if (p.chunk_size > 0) hipLaunchKernelGGL((tree_attn_pipe_kernel<0, 1>), dim3(grid), dim3(512), 0, s, p);
+      else hipLaunchKernelGGL((tree_attn_pipe_kernel<0, 0>), dim3(grid), dim3(512), 0, s, p);
+    }
+  } else if (p.subtree_end)
     hipLaunchKernelGGL((tree_attn_kernel<D, W, RB, CM, VT, 1>), dim3(grid), dim3(W * 64), 0, s, p);
   else
     hipLaunchKernelGGL((tree_attn_kernel<D, W, RB, CM, VT, 0>), dim3(grid), dim3(W * 64), 0, s, p);
