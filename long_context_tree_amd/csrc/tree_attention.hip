@@ -823,7 +823,7 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnParams p) {
 // computes scores it never uses, so that no second copy of the step (and no register spill) is needed.
 // On pages of >= 16 slots each wave's four direct-to-LDS loads of the next tiles go out one at a time
 // inside block B1, so the vector memory path takes them beside the matrix work.
-template <int PRE, int CH>
+template <int PRE, int CH, int GRP>
 __global__ __launch_bounds__(512, 1) void tree_attn_pipe_kernel(AttnParams p) {
   constexpr int D = 128, W = 8, RB = 2, NT = W * 64, ROWS_WG = W * RB * 16;
   constexpr int KS = D / 32;                    // k-steps of the QK^T product
@@ -835,10 +835,10 @@ __global__ __launch_bounds__(512, 1) void tree_attn_pipe_kernel(AttnParams p) {
   constexpr int ANC_N = kMaxNodes, ANC_W = ANC_N / 64, END_N = ANC_N * ANC_W * 2;
   static_assert(KB % LOADS == 0, "a wave's loads must be all K or all V");
 
-  // three K and three V tile buffers, separate arrays so that alias analysis tells the buffers being read
+  // four K and four V tile buffers, separate arrays so that alias analysis tells the buffers being read
   // from the ones whose direct-to-LDS loads are in flight
-  __shared__ __attribute__((aligned(16))) uint16_t ka[TILE_EL], kb[TILE_EL], kc[TILE_EL];
-  __shared__ __attribute__((aligned(16))) uint16_t va[TILE_EL], vb[TILE_EL], vc[TILE_EL];
+  __shared__ __attribute__((aligned(16))) uint16_t ka[TILE_EL], kb[TILE_EL], kc[TILE_EL], kd[TILE_EL];
+  __shared__ __attribute__((aligned(16))) uint16_t va[TILE_EL], vb[TILE_EL], vc[TILE_EL], vd[TILE_EL];
   union TreeRel {
     uint64_t anc[ANC_N][ANC_W];
     int end[END_N];
@@ -957,7 +957,10 @@ __global__ __launch_bounds__(512, 1) void tree_attn_pipe_kernel(AttnParams p) {
   }
   constexpr int KPL = 64 / CPR;                     // keys per load (4)
   constexpr int GL = 16 / KPL < LOADS ? 16 / KPL : LOADS;
-  const bool grouped = pshift >= 4;
+  // GRP: pages of >= 16 slots (a wave's 16 keys of a tile in one page).  A compile-time switch: a
+  // run-time test around the loads inside a block is a branch, and the compiler then sinks the block's
+  // exps below it, out of the MFMAs' shadow.
+  constexpr bool grouped = GRP != 0;
   // this wave's share of tile t (K for waves 0..3, V for waves 4..7) into buf
   auto issue = [&](int t, uint16_t* buf) __attribute__((always_inline)) {
     const int key0 = t * kTile;
@@ -1017,19 +1020,25 @@ __global__ __launch_bounds__(512, 1) void tree_attn_pipe_kernel(AttnParams p) {
   // loads can be spread over a block: the page lookup and the descriptor's base and byte range first
   // (valid = false gives an empty range: the loads then write zeros, into a buffer nobody reads), then
   // one 16-byte direct-to-LDS load at a time.
-  auto plan_grouped = [&](int t, bool valid_tile, const uint16_t*& bp, uint32_t& bytes) __attribute__((always_inline)) {
+  constexpr int KEY_W = (((LOADS * 64) % (kTile * CPR)) / CPR);   // keys of a tile per wave (16)
+  auto page_of_tile = [&](int t) __attribute__((always_inline)) -> int {   // this wave's page id in tile t
+    int pi = ((t * kTile + KEY_W * (wave & 3)) >> pshift) - pg_first;
+    pi = pi < pg_count ? pi : pg_count - 1;
+    return pg_lds[pi < 0 ? 0 : pi];
+  };
+  // branch-free (it runs inside an interleaved block): the descriptor covers the tile's slots in the
+  // page (pages longer than a tile) or the whole page from its first slot; a tile start is a multiple
+  // of kTile, so key0 & pmask is zero for pages of <= kTile slots
+  const int fk_mask = pshift > 6 ? ~(kTile - 1) : ~pmask;
+  const int span = pshift > 6 ? kTile : (1 << pshift);
+  auto plan_grouped = [&](int t, bool valid_tile, int pg_v, const uint16_t*& bp, uint32_t& bytes) __attribute__((always_inline)) {
     const int key0 = t * kTile;
     const int key_w = key0 + (((wave * LOADS) * 64) % (kTile * CPR)) / CPR;
-    int pi = (key_w >> pshift) - pg_first;
-    pi = pi < pg_count ? pi : pg_count - 1;
-    pi = pi < 0 ? 0 : pi;
-    const int pg = __builtin_amdgcn_readfirstlane(pg_lds[pi]);
-    const int first_key = pshift > 6 ? key0 : (key_w & ~pmask);
-    const int span = pshift > 6 ? kTile : (1 << pshift);
-    int valid = keys - first_key;
-    valid = valid < 0 ? 0 : (valid > span ? span : valid);
-    if (pg < 0 || !valid_tile) valid = 0;
-    const uint32_t rowb = pshift > 6 ? (uint32_t)(key0 & pmask) * tstride : 0u;
+    const int pg = __builtin_amdgcn_readfirstlane(pg_v);
+    const int first_key = key_w & fk_mask;
+    int valid = min(max(keys - first_key, 0), span);
+    valid = (pg < 0 || !valid_tile) ? 0 : valid;
+    const uint32_t rowb = (uint32_t)(key0 & pmask) * tstride;
     bp = (wave_is_v ? vbase : kbase) + (uint64_t)(uint32_t)(pg < 0 ? 0 : pg) * (uint32_t)p.page_stride + rowb;
     bytes = (uint32_t)valid * tstride * 2u;
   };
@@ -1216,6 +1225,8 @@ __global__ __launch_bounds__(512, 1) void tree_attn_pipe_kernel(AttnParams p) {
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) cacc[rb] += csum[rb];
   };
+  float st_val = 0.f;                               // a closed chunk's value, stored at the next step
+  int st_c = -1;
   auto chunk_close = [&](int key0) __attribute__((always_inline)) {
     const int c = chunk_of(key0);
     const int cend = min((c + 1) * cs, L);
@@ -1224,9 +1235,18 @@ __global__ __launch_bounds__(512, 1) void tree_attn_pipe_kernel(AttnParams p) {
 #pragma unroll
       for (int rb = 1; rb < RB; ++rb)
         if (st_rb == rb) v = m_r[rb] + __builtin_amdgcn_logf(cacc[rb]);
-      if (st_ok) cbase[(int64_t)c * row_stride_chunk] = v;
+      st_val = v;
+      st_c = c;
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) cacc[rb] = 0.f;
+    }
+  };
+  // the store of a closed chunk waits for the start of the next step, ahead of that step's tile loads,
+  // so that the counted wait closing the step never waits for it
+  auto chunk_flush = [&]() __attribute__((always_inline)) {
+    if (CH && st_c >= 0) {
+      if (st_ok) cbase[(int64_t)st_c * row_stride_chunk] = st_val;
+      st_c = -1;
     }
   };
 
@@ -1297,49 +1317,90 @@ __global__ __launch_bounds__(512, 1) void tree_attn_pipe_kernel(AttnParams p) {
   };
 
   // ---- the pipeline ----
-  // prologue: K(t0), V(t0) and K(t0 + 1) resident, V buffer 2 (the V "tile t0 - 1" of the first step)
-  // cleared, then the scores of (t0, half 0).  The first step's P.V of the previous tile multiplies that
-  // cleared buffer by P = 0, and its chunk sums are zero and never stored.
+  // Tiles load two steps ahead of their first use: during step t, K(t+3) and V(t+2).  On pages of >= 16
+  // slots every wave issues exactly LOADS loads per step (empty-range loads past the split's end), and
+  // direct-to-LDS loads complete in order among themselves, so the wait that closes step t,
+  // vmcnt(LOADS), covers the loads of step t - 1 (K(t+2), V(t+1)) and leaves this step's in flight; a
+  // chunk store counted in between only makes that wait longer.  Shorter pages wait for everything.
+  auto kslot = [&](int i) __attribute__((always_inline)) -> uint16_t* {
+    return i == 0 ? ka : (i == 1 ? kb : (i == 2 ? kc : kd));
+  };
+  auto vslot = [&](int i) __attribute__((always_inline)) -> uint16_t* {
+    return i == 0 ? va : (i == 1 ? vb : (i == 2 ? vc : vd));
+  };
+  auto issue_tile = [&](int t, uint16_t* buf) __attribute__((always_inline)) {
+    if (grouped) {
+      const uint16_t* bp;
+      uint32_t bytes;
+      plan_grouped(t, t < t_end, page_of_tile(t), bp, bytes);
+#pragma unroll
+      for (int i = 0; i < LOADS; ++i) load_one(bp, bytes, buf, i);
+    } else if (t < t_end) {
+      issue(t, buf);
+    }
+  };
+  // The barrier that closes a step.  __syncthreads() would also wait for every load in flight (its
+  // release fence covers the direct-to-LDS writes), so the wait and the barrier are written out: this
+  // thread's LDS writes done (lgkmcnt), the older tile loads landed, then s_barrier.  The asm's memory
+  // clobber keeps every memory access on its side of the barrier.
+  auto step_barrier = [&]() __attribute__((always_inline)) {
+    static_assert(LOADS == 4, "the counted wait below is LOADS");
+    if (grouped) asm volatile("s_waitcnt vmcnt(4) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    else asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  };
+  // prologue: K(t0 .. t0+2) and V(t0 .. t0+1) issued, K(t0), K(t0+1) and V(t0) resident, V buffer 3 (the
+  // V "tile t0 - 1" of the first step) cleared, then the scores of (t0, half 0).  The first step's P.V of
+  // the previous tile multiplies that cleared buffer by P = 0; its chunk sums are zero and never stored.
   const int t0 = t_begin;
   if (!wave_is_v) {
-    issue(t0, ka);
-    if (t0 + 1 < t_end) issue(t0 + 1, kb);
+    issue_tile(t0, ka);
+    issue_tile(t0 + 1, kb);
+    issue_tile(t0 + 2, kc);
   } else {
-    issue(t0, va);
+    issue_tile(t0, va);
+    issue_tile(t0 + 1, vb);
   }
-  for (int i = tid; i < TILE_EL / 8; i += NT) reinterpret_cast<u32x4*>(vc)[i] = u32x4{0u, 0u, 0u, 0u};
+  for (int i = tid; i < TILE_EL / 8; i += NT) reinterpret_cast<u32x4*>(vd)[i] = u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) pB[rb] = bf16_splat8(0u, 0u);
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
+  // the first step's load plan
+  int pg_pre = 0;
+  const uint16_t* ld_bp = nullptr;
+  uint32_t ld_bytes = 0;
+  if (grouped) {
+    const int t_first = wave_is_v ? t0 + 2 : t0 + 3;
+    plan_grouped(t_first, t_first < t_end, page_of_tile(t_first), ld_bp, ld_bytes);
+  }
+  step_barrier();
   if (wave_active) qk_half(ka, 0, sA);
 
-  // Step of tile t; R = (t - t0) mod 3 selects the buffers: K(t) in slot R, K(t+1) in R+1, K(t+2) loads
-  // into R+2; V(t-1) in slot R+2, V(t) in R, V(t+1) loads into R+1 (slots mod 3).  Every tile runs the
-  // same two interleaved blocks; a tile holding slots >= L first masks its scores (between the blocks,
-  // where few registers are live), and the split's last tile computes scores of a tile it never uses.
-  auto kslot = [&](int i) __attribute__((always_inline)) -> uint16_t* { return i == 0 ? ka : (i == 1 ? kb : kc); };
-  auto vslot = [&](int i) __attribute__((always_inline)) -> uint16_t* { return i == 0 ? va : (i == 1 ? vb : vc); };
+  // Step of tile t; R = (t - t0) mod 4 selects the buffers: K(t) in slot R, K(t+1) in R+1, K(t+2) in R+2
+  // (landing), K(t+3) loads into R+3; V(t-1) in slot R+3, V(t) in R, V(t+1) in R+1 (landing), V(t+2)
+  // loads into R+2 (slots mod 4).  Every tile runs the same two interleaved blocks; a tile holding slots
+  // >= L first masks its scores (between the blocks, where few registers are live), and the split's last
+  // tile computes scores of a tile it never uses.
   auto step = [&](int t, auto r_c) __attribute__((always_inline)) {
     constexpr int R = decltype(r_c)::value;
     uint16_t* kcur = kslot(R);
-    uint16_t* knext = kslot((R + 1) % 3);
-    uint16_t* vprev = vslot((R + 2) % 3);
+    uint16_t* knext = kslot((R + 1) % 4);
+    uint16_t* vprev = vslot((R + 3) % 4);
     uint16_t* vcur = vslot(R);
-    // this wave's share of K(t+2) (waves 0..3) or V(t+1) (waves 4..7); on the grouped path its four
-    // loads go out one at a time inside block B1, so the vector memory path takes them in the background
-    const int t_ld = wave_is_v ? t + 1 : t + 2;
-    uint16_t* ld_buf = wave_is_v ? vslot((R + 1) % 3) : kslot((R + 2) % 3);
-    const uint16_t* ld_bp = nullptr;
-    uint32_t ld_bytes = 0;
-    if (grouped) plan_grouped(t_ld, t_ld < t_end, ld_bp, ld_bytes);
-    else if (t_ld < t_end) issue(t_ld, ld_buf);
+    // this wave's share of K(t+3) (waves 0..3) or V(t+2) (waves 4..7).  On the grouped path its four
+    // loads go out one at a time at slots 2, 6, 10 and 14 of B1, so the vector memory path takes them
+    // beside the matrix work; the next step's page id is read from LDS at the start of B2 and its load
+    // plan made at the end of B2, away from the step boundary where all waves want the scalar unit.
+    // (Loads placed in B2 as well, or shared by all waves as K and V halves, measured slower.)
+    const int t_ld = wave_is_v ? t + 2 : t + 3;
+    uint16_t* ld_buf = wave_is_v ? vslot((R + 2) % 4) : kslot((R + 3) % 4);
+    chunk_flush();
+    if (!grouped && t_ld < t_end) issue(t_ld, ld_buf);
     auto b1_hook = [&](int f) __attribute__((always_inline)) {
-      if ((f & 3) == 2 && f < 4 * LOADS) {
-        if (grouped) load_one(ld_bp, ld_bytes, ld_buf, f >> 2);
-      }
+      if (grouped && (f & 3) == 2 && f < 16) load_one(ld_bp, ld_bytes, ld_buf, f >> 2);
     };
-    auto no_hook = [](int) {};
+    auto b2_hook = [&](int f) __attribute__((always_inline)) {
+      if (grouped && f == 0) pg_pre = page_of_tile(t_ld + 1);
+      if (grouped && f == 16) plan_grouped(t_ld + 1, t_ld + 1 < t_end, pg_pre, ld_bp, ld_bytes);
+    };
     const int key0 = t * kTile;
     const bool edge = key0 + kTile > L;             // holds slots >= L: the tree mask applies
     const bool prev_edge = key0 > L;                // tile t - 1 holds slots >= L
@@ -1357,35 +1418,40 @@ __global__ __launch_bounds__(512, 1) void tree_attn_pipe_kernel(AttnParams p) {
       if (__builtin_expect(edge, 0)) mask_half(t, 1, sB);
       const bf16x8 a_cur = (CH && __builtin_expect(edge, 0)) ? ones_edge(key0, 0) : ones;
       // B2: P.V and chunk sums of (t, half 0), QK^T of (t+1, half 0) | exps of (t, half 1)
-      run_block(vcur, 0, pA, a_cur, knext, 0, sA, sB, pB, eB, no_hook);
+      run_block(vcur, 0, pA, a_cur, knext, 0, sA, sB, pB, eB, b2_hook);
       if (CH) chunk_add();
       settle_half(sB, pB, eB);
     } else if (grouped) {
       // a wave without rows still loads its share of the tiles
 #pragma unroll
       for (int i = 0; i < LOADS; ++i) load_one(ld_bp, ld_bytes, ld_buf, i);
+      plan_grouped(t_ld + 1, t_ld + 1 < t_end, page_of_tile(t_ld + 1), ld_bp, ld_bytes);
     }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this thread's loads of K(t+2) / V(t+1) landed
-    __syncthreads();
+    step_barrier();                                 // K(t+2) / V(t+1) landed (this thread's loads)
   };
-  for (int t = t0; t < t_end; t += 3) {
+  for (int t = t0; t < t_end; t += 4) {
     step(t, std::integral_constant<int, 0>{});
     if (t + 1 < t_end) step(t + 1, std::integral_constant<int, 1>{});
     if (t + 2 < t_end) step(t + 2, std::integral_constant<int, 2>{});
+    if (t + 3 < t_end) step(t + 3, std::integral_constant<int, 3>{});
   }
   // the last tile's half 1: P.V, chunk sums and its chunk
   if (wave_active) {
     const int tl = t_end - 1;
-    const int rl = (tl - t0) % 3;
-    const uint16_t* vl = rl == 0 ? va : (rl == 1 ? vb : vc);
+    const uint16_t* vl = vslot((tl - t0) & 3);
     pv_half(vl, 1, pB);
     const int key0 = tl * kTile;
+    chunk_flush();
     if (CH && key0 < L) {
       chunk_half(pB, key0 + kTile > L ? ones_edge(key0, 1) : ones);
       chunk_add();
       chunk_close(key0);
+      chunk_flush();
     }
   }
+  // the loads of tiles past the split's end are still in flight: they must land before the work-group's
+  // LDS is handed to another work-group
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
   if (!wave_active) return;
 #pragma unroll
@@ -1415,12 +1481,14 @@ hipError_t launch_d_w(const AttnParams& p, const AttnPlan& plan, hipStream_t s) 
   const int grid = (int)(ceil_div(n_units, 8) * 8 * plan.row_groups);
   if constexpr (D == 128 && W == 8 && CM == 0 && VT == 0) {
     // wide trees, head_dim 128, token-row V, 64-slot (or no) chunk partials: the software-pipelined kernel
+    auto go = [&](auto kern) { hipLaunchKernelGGL(kern, dim3(grid), dim3(512), 0, s, p); };
+    const bool grp = p.page_shift >= 4;
     if (p.subtree_end) {
-      if (p.chunk_size > 0) hipLaunchKernelGGL((tree_attn_pipe_kernel<1, 1>), dim3(grid), dim3(512), 0, s, p);
-      else hipLaunchKernelGGL((tree_attn_pipe_kernel<1, 0>), dim3(grid), dim3(512), 0, s, p);
+      if (p.chunk_size > 0) grp ? go(tree_attn_pipe_kernel<1, 1, 1>) : go(tree_attn_pipe_kernel<1, 1, 0>);
+      else grp ? go(tree_attn_pipe_kernel<1, 0, 1>) : go(tree_attn_pipe_kernel<1, 0, 0>);
     } else {
-      if (p.chunk_size > 0) hipLaunchKernelGGL((tree_attn_pipe_kernel<0, 1>), dim3(grid), dim3(512), 0, s, p);
-      else hipLaunchKernelGGL((tree_attn_pipe_kernel<0, 0>), dim3(grid), dim3(512), 0, s, p);
+      if (p.chunk_size > 0) grp ? go(tree_attn_pipe_kernel<0, 1, 1>) : go(tree_attn_pipe_kernel<0, 1, 0>);
+      else grp ? go(tree_attn_pipe_kernel<0, 0, 1>) : go(tree_attn_pipe_kernel<0, 0, 0>);
     }
   } else if (p.subtree_end)
     hipLaunchKernelGGL((tree_attn_kernel<D, W, RB, CM, VT, 1>), dim3(grid), dim3(W * 64), 0, s, p);
