@@ -178,221 +178,6 @@ __global__ __launch_bounds__(256) void argmax_seg_kernel(AcceptParams p) {
   if (threadIdx.x == 0) p.seg_key[u * p.nseg + seg] = best;
 }
 
-__device__ __forceinline__ float row_max(const AcceptParams& p, int64_t u) { return key_value(p.node_key[u]); }
-
-// Normaliser k of node u: Z[0] = sum exp(l - M); Z[k] = sum max(0, res_{k-1} - q) (fixed-order totals)
-__device__ __forceinline__ double level_sum(const AcceptParams& p, int64_t u, int k) {
-  return p.zsum[u * (p.max_children + 1) + k];
-}
-
-// ---- rejection: per node, the row-maximum key over the segments (one wave per node); then the
-// level-0 segment sums, taken against each segment's own maximum m_s, are brought to the row maximum M:
-// sum exp(l - m_s) * exp(m_s - M) ----
-__global__ __launch_bounds__(64) void node_max_kernel(AcceptParams p) {
-  const int64_t u = blockIdx.x;
-  // seg_key has a row for every row of the grid: its reads go out together with the row-count read
-  const int tn = total_nodes(p);
-  // the first key and level-0 sum of each lane stay in registers for the rescale below
-  const int s_first = threadIdx.x;
-  double* s0 = p.seg_sum + u * (p.max_children + 1) * p.nsegr;
-  const unsigned long long k_first = s_first < p.nseg ? p.seg_key[u * p.nseg + s_first] : 0ull;
-  const double sum_first = s_first < p.nsegr ? s0[s_first] : 0.0;
-  unsigned long long k = k_first;
-  for (int s = s_first + 64; s < p.nseg; s += 64) k = umax64(k, p.seg_key[u * p.nseg + s]);
-  if (u >= tn) return;
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) k = umax64(k, shfl_xor_u64(k, off));
-  if (threadIdx.x == 0) p.node_key[u] = k;
-  const double M = (double)key_value(k);
-  for (int s = s_first; s < p.nsegr; s += 64) {
-    const double ms = (double)key_value(s == s_first ? k_first : p.seg_key[u * p.nseg + s]);
-    const double sum = s == s_first ? sum_first : s0[s];
-    s0[s] = ms > -INFINITY ? sum * exp(ms - M) : 0.0;
-  }
-}
-
-// Total of residual level r of node u over its segments, summed by one wave in a fixed order (lanes
-// stride the segments, then a butterfly): every caller gets the same bits.  Valid in every lane.
-__device__ __forceinline__ double level_total_wave(const AcceptParams& p, int64_t u, int r) {
-  const double* s = p.seg_sum + (u * (p.max_children + 1) + r) * p.nsegr;
-  double z = 0.0;
-  for (int i = threadIdx.x & 63; i < p.nsegr; i += 64) z += s[i];
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) z += __shfl_xor(z, off);
-  return z;
-}
-
-// A thread's run of kResPer consecutive vocabulary entries [a0, a1) of row u (a1 - a0 <= kResPer): the
-// logits as fp32 and, if want_q, the draft probabilities.  Every load is issued before any value is
-// used (one round trip to memory instead of one per entry); 16-byte loads where the run is whole and
-// aligned.  Entries at and past a1 are left 0.
-constexpr int kResPer = kResSegment / 256;
-static_assert(kResPer % 8 == 0, "a run is whole 16-byte loads of bf16 logits and of fp32 probabilities");
-
-__device__ __forceinline__ void load_run(const AcceptParams& p, int64_t u, int a0, int a1, bool want_q,
-                                         float (&lg)[kResPer], float (&qv)[kResPer]) {
-  const bool whole = a1 - a0 == kResPer;
-  if (p.bf16) {
-    const uint16_t* row = reinterpret_cast<const uint16_t*>(p.logits) + u * p.vocab + a0;
-    if (whole && ((uintptr_t)row & 15) == 0) {
-      u32x4 w[kResPer / 8];
-#pragma unroll
-      for (int j = 0; j < kResPer / 8; ++j) w[j] = *reinterpret_cast<const u32x4*>(row + 8 * j);
-#pragma unroll
-      for (int j = 0; j < kResPer / 8; ++j)
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          lg[8 * j + 2 * k] = __uint_as_float(w[j][k] << 16);
-          lg[8 * j + 2 * k + 1] = __uint_as_float(w[j][k] & 0xFFFF0000u);
-        }
-    } else {
-#pragma unroll
-      for (int i = 0; i < kResPer; ++i) lg[i] = a0 + i < a1 ? __uint_as_float((uint32_t)row[i] << 16) : 0.f;
-    }
-  } else {
-    const float* row = reinterpret_cast<const float*>(p.logits) + u * p.vocab + a0;
-    if (whole && ((uintptr_t)row & 15) == 0) {
-      u32x4 w[kResPer / 4];
-#pragma unroll
-      for (int j = 0; j < kResPer / 4; ++j) w[j] = *reinterpret_cast<const u32x4*>(row + 4 * j);
-#pragma unroll
-      for (int j = 0; j < kResPer / 4; ++j)
-#pragma unroll
-        for (int k = 0; k < 4; ++k) lg[4 * j + k] = __uint_as_float(w[j][k]);
-    } else {
-#pragma unroll
-      for (int i = 0; i < kResPer; ++i) lg[i] = a0 + i < a1 ? row[i] : 0.f;
-    }
-  }
-#pragma unroll
-  for (int i = 0; i < kResPer; ++i) qv[i] = 0.f;
-  if (want_q) {
-    const float* row = p.draft_probs + u * p.vocab + a0;
-    if (whole && ((uintptr_t)row & 15) == 0) {
-      u32x4 w[kResPer / 4];
-#pragma unroll
-      for (int j = 0; j < kResPer / 4; ++j) w[j] = *reinterpret_cast<const u32x4*>(row + 4 * j);
-#pragma unroll
-      for (int j = 0; j < kResPer / 4; ++j)
-#pragma unroll
-        for (int k = 0; k < 4; ++k) qv[4 * j + k] = __uint_as_float(w[j][k]);
-    } else {
-#pragma unroll
-      for (int i = 0; i < kResPer; ++i) qv[i] = a0 + i < a1 ? row[i] : 0.f;
-    }
-  }
-}
-
-// ---- rejection: per (node, residual segment) the maximum key and the level-0 sum sum exp(l - m_s)
-// against the segment's own maximum m_s, from one read of the logits (the row maximum is not known
-// yet; node_max_kernel rescales the sums to it) ----
-__global__ __launch_bounds__(256) void max_sum_seg_kernel(AcceptParams p) {
-  const int seg = blockIdx.x;
-  const int i = blockIdx.y;                       // the node within its sequence
-  const int b = blockIdx.z;
-  const int tn = total_nodes(p);
-  int n0 = p.node_offsets[b];
-  int N = p.node_offsets[b + 1] - n0;
-  N = N < 0 ? 0 : (N > p.max_nodes ? p.max_nodes : N);
-  n0 = n0 < 0 ? 0 : (n0 > (p.batch - 1) * p.max_nodes ? (p.batch - 1) * p.max_nodes : n0);
-  const int64_t u = (int64_t)n0 + i;
-  if (i >= N || u >= tn) return;
-  // segment 0 also counts the node's children (the later ones among the sequence's nodes whose parent
-  // is i), for the residual passes; its parent reads go out with the logit reads
-  int kids = 0;
-  if (seg == 0)
-    for (int j = 1 + (int)threadIdx.x; j < N && n0 + j < tn; j += 256) kids += (p.parents[n0 + j] == i && i < j) ? 1 : 0;
-  const int v0 = seg * kResSegment;
-  const int v1 = min(p.vocab, v0 + kResSegment);
-  const int a0 = min(v1, v0 + (int)threadIdx.x * kResPer), a1 = min(v1, a0 + kResPer);
-  float lg[kResPer], qv[kResPer];
-  load_run(p, u, a0, a1, false, lg, qv);
-  // this thread's largest logit, then the lowest index holding it (visited from the top down), packed once
-  float mv = -INFINITY;
-#pragma unroll
-  for (int i = 0; i < kResPer; ++i)
-    if (a0 + i < a1) mv = fmaxf(mv, lg[i]);
-  int idx = a0;
-#pragma unroll
-  for (int i = kResPer - 1; i >= 0; --i)
-    if (a0 + i < a1 && lg[i] == mv) idx = a0 + i;
-  unsigned long long best = a0 < a1 ? pack_key(mv, idx) : 0ull;
-  best = block_max_u64(best);
-  const double m = (double)key_value(best);
-  double acc = 0.0;                               // this thread's run, summed in order
-  if (m > -INFINITY) {                            // a segment of -inf logits has no mass
-    // branch-free: an entry past the end takes exp(-inf) = +0, which leaves the sum's bits unchanged,
-    // and the eight exps share their constants and interleave
-#pragma unroll
-    for (int i = 0; i < kResPer; ++i) acc += exp(a0 + i < a1 ? (double)lg[i] - m : -INFINITY);
-  }
-  acc = block_sum_f64(acc);
-  if (threadIdx.x == 0) {
-    p.seg_key[u * p.nseg + seg] = best;
-    p.seg_sum[u * (p.max_children + 1) * p.nsegr + seg] = acc;
-  }
-  if (seg == 0) {                                 // uniform in the work-group
-    const double k = block_sum_f64((double)kids); // exact: at most max_nodes
-    if (threadIdx.x == 0) p.n_children[u] = (int)k;
-  }
-}
-
-// ---- rejection: one residual level r >= 1 for every node that needs it ----
-__global__ __launch_bounds__(256) void residual_pass_kernel(AcceptParams p, int r) {
-  const int seg = blockIdx.x;
-  const int64_t u = blockIdx.y;
-  // both reads are issued before either test (n_children has an entry for every row of the grid)
-  const int tn = total_nodes(p);
-  const int nc = p.n_children[u];
-  if ((u >= tn) | (nc < r)) return;
-  extern __shared__ double rz_s[];                // [max_children + 1] reciprocals of the earlier levels' totals
-  const int v0 = seg * kResSegment;
-  const int v1 = min(p.vocab, v0 + kResSegment);
-  const int a0 = min(v1, v0 + (int)threadIdx.x * kResPer), a1 = min(v1, a0 + kResPer);
-  float lg[kResPer], qv[kResPer];
-  load_run(p, u, a0, a1, true, lg, qv);
-  const double M = (double)row_max(p, u);
-  double acc = 0.0;                               // this thread's run, summed in order
-  {
-    // the earlier levels' totals, summed here (wave w takes levels w, w + 4, ...; each in the order the
-    // walk's totals use), kept as reciprocals: a product with the reciprocal differs from the quotient
-    // by at most one fp64 rounding.  The first 9 are held in registers.
-    for (int k = threadIdx.x >> 6; k < r; k += 4) {
-      const double z = level_total_wave(p, u, k);
-      if ((threadIdx.x & 63) == 0) {
-        rz_s[k] = z > 0.0 ? 1.0 / z : 0.0;
-        if (seg == 0) p.zsum[u * (p.max_children + 1) + k] = z;   // for the walk (the same bits in every pass)
-      }
-    }
-    __syncthreads();
-    // the first 9 in registers: every index below is a constant after unrolling (an array indexed by a
-    // loop variable would live in scratch memory, one read per entry and level)
-    double Z[9];
-#pragma unroll
-    for (int k = 0; k < 9; ++k) Z[k] = k < r ? rz_s[k] : 0.0;
-    // branch-free over the run: an entry past the end has q = 0 and exp(-inf) = +0, so it adds +0
-#pragma unroll
-    for (int i = 0; i < kResPer; ++i) {
-      const double q = (double)qv[i];
-      double res = exp(a0 + i < a1 ? (double)lg[i] - M : -INFINITY) * Z[0];
-#pragma unroll
-      for (int k = 1; k < 9; ++k) {
-        if (k >= r) break;
-        const double d = fmax(0.0, res - q);
-        if (Z[k] > 0.0) res = d * Z[k];
-      }
-      for (int k = 9; k < r; ++k) {
-        const double d = fmax(0.0, res - q);
-        const double zk = rz_s[k];
-        if (zk > 0.0) res = d * zk;
-      }
-      acc += fmax(0.0, res - q);
-    }
-  }
-  acc = block_sum_f64(acc);
-  if (threadIdx.x == 0) p.seg_sum[(u * (p.max_children + 1) + r) * p.nsegr + seg] = acc;
-}
-
 // Child count and sibling rank (earlier siblings) of the nodes tid + 256 q, q < PER; flags a parent
 // array that is not topological or a node with more than max_children children.  Without COUNT (greedy)
 // only the parent-order checks run.
@@ -430,14 +215,20 @@ __device__ __forceinline__ void child_ranks(const int* par_s, int N, int tid, in
   }
 }
 
-// ---- per sequence: the walk and the bonus token ----
-template <bool REJECT>
-__global__ __launch_bounds__(256) void walk_kernel(AcceptParams p) {
-  __shared__ int par_s[kMaxTreeNodes], tok_s[kMaxTreeNodes], first_s[kMaxTreeNodes], nch_s[kMaxTreeNodes];
+// Outputs of a sequence whose tree, or whose call, could not be evaluated: num_accepted = -1.
+__device__ __forceinline__ void write_invalid(const AcceptParams& p, int b, int tid) {
+  for (int i = tid; i < p.max_path; i += 256) {
+    p.out_path_nodes[(int64_t)b * p.max_path + i] = -1;
+    p.out_tokens[(int64_t)b * p.max_path + i] = -1;
+  }
+  if (tid == 0) p.out_num_accepted[b] = -1;
+}
+
+// ---- greedy, per sequence: the walk and the bonus token ----
+__global__ __launch_bounds__(256) void greedy_walk_kernel(AcceptParams p) {
+  __shared__ int par_s[kMaxTreeNodes], tok_s[kMaxTreeNodes], nch_s[kMaxTreeNodes];
   __shared__ int rank_s[kMaxTreeNodes], amax_s[kMaxTreeNodes], path_s[kMaxTreeNodes];
-  __shared__ int stop_s, depth_s, bad_s, seg_s, bonus_s;
-  __shared__ double base_s, thr_s, zlast_s;
-  __shared__ double zs[9];
+  __shared__ int stop_s, depth_s, bad_s;
 #ifdef SPEC_DEBUG
   __shared__ int dbg_rows_s, dbg_tests_s;   // witnesses: rows reduced in this call and read here, tests run
 #endif
@@ -450,8 +241,7 @@ __global__ __launch_bounds__(256) void walk_kernel(AcceptParams p) {
   int32_t* o_path = p.out_path_nodes + (int64_t)b * p.max_path;
   int32_t* o_tok = p.out_tokens + (int64_t)b * p.max_path;
   if (N == 0) {
-    for (int i = tid; i < p.max_path; i += 256) { o_path[i] = -1; o_tok[i] = -1; }
-    if (tid == 0) p.out_num_accepted[b] = -1;
+    write_invalid(p, b, tid);
     return;
   }
   if (tid == 0) bad_s = 0;
@@ -460,90 +250,48 @@ __global__ __launch_bounds__(256) void walk_kernel(AcceptParams p) {
   __syncthreads();
 #endif
   for (int i = tid; i < N; i += 256) {
-    int pi = p.parents[n0 + i];
-    par_s[i] = pi;
-    int t = p.draft_tokens[n0 + i];
-    tok_s[i] = t;
-    first_s[i] = 0x7FFFFFFF;
-    if (!REJECT) {
-      // four independent accumulators, unrolled so that 16 segment loads (the whole row at V = 128K) are
-      // in flight together
-      const unsigned long long* sk = p.seg_key + (int64_t)(n0 + i) * p.nseg;
-      unsigned long long k0 = 0, k1 = 0, k2 = 0, k3 = 0;
-      int s = 0;
+    par_s[i] = p.parents[n0 + i];
+    tok_s[i] = p.draft_tokens[n0 + i];
+    // four independent accumulators, unrolled so that 16 segment loads (the whole row at V = 128K) are
+    // in flight together
+    const unsigned long long* sk = p.seg_key + (int64_t)(n0 + i) * p.nseg;
+    unsigned long long k0 = 0, k1 = 0, k2 = 0, k3 = 0;
+    int s = 0;
 #pragma unroll 4
-      for (; s + 4 <= p.nseg; s += 4) {
-        k0 = umax64(k0, sk[s]);
-        k1 = umax64(k1, sk[s + 1]);
-        k2 = umax64(k2, sk[s + 2]);
-        k3 = umax64(k3, sk[s + 3]);
-      }
-      for (; s < p.nseg; ++s) k0 = umax64(k0, sk[s]);
-      amax_s[i] = key_index(umax64(umax64(k0, k1), umax64(k2, k3)));
-#ifdef SPEC_DEBUG
-      // the debug checks cleared every key: a row counts when all its segment keys were written again
-      bool fresh = true;
-      for (int q = 0; q < p.nseg; ++q) fresh = fresh && sk[q] != 0ull;
-      if (fresh) atomicAdd(&dbg_rows_s, 1);
-#endif
+    for (; s + 4 <= p.nseg; s += 4) {
+      k0 = umax64(k0, sk[s]);
+      k1 = umax64(k1, sk[s + 1]);
+      k2 = umax64(k2, sk[s + 2]);
+      k3 = umax64(k3, sk[s + 3]);
     }
+    for (; s < p.nseg; ++s) k0 = umax64(k0, sk[s]);
+    amax_s[i] = key_index(umax64(umax64(k0, k1), umax64(k2, k3)));
 #ifdef SPEC_DEBUG
-    if (REJECT && p.node_key[n0 + i] != 0ull) atomicAdd(&dbg_rows_s, 1);   // row maximum written in this call
+    // the debug checks cleared every key: a row counts when all its segment keys were written again
+    bool fresh = true;
+    for (int q = 0; q < p.nseg; ++q) fresh = fresh && sk[q] != 0ull;
+    if (fresh) atomicAdd(&dbg_rows_s, 1);
 #endif
   }
   __syncthreads();
-  // child counts and sibling ranks: each parent entry is read once and compared with the nodes this
-  // thread owns (tid, tid + 256, ...): one node per thread for trees of <= 256 nodes, else up to 8
+  // the parent-order checks: each parent entry is read once and compared with the nodes this thread
+  // owns (tid, tid + 256, ...): one node per thread for trees of <= 256 nodes, else up to 8
   if (N <= 256)
-    child_ranks<1, REJECT>(par_s, N, tid, REJECT ? p.max_children : 0x7FFFFFFF, rank_s, nch_s, bad_s);
+    child_ranks<1, false>(par_s, N, tid, 0x7FFFFFFF, rank_s, nch_s, bad_s);
   else
-    child_ranks<kMaxTreeNodes / 256, REJECT>(par_s, N, tid, REJECT ? p.max_children : 0x7FFFFFFF, rank_s, nch_s,
-                                             bad_s);
+    child_ranks<kMaxTreeNodes / 256, false>(par_s, N, tid, 0x7FFFFFFF, rank_s, nch_s, bad_s);
   __syncthreads();
   if (bad_s) {
-    for (int i = tid; i < p.max_path; i += 256) { o_path[i] = -1; o_tok[i] = -1; }
-    if (tid == 0) p.out_num_accepted[b] = -1;
+    write_invalid(p, b, tid);
     return;
   }
-  // accept tests of every child, in parallel
+  // the edge tests, in parallel: a draft passes iff it is its parent's greedy token
   for (int c = 1 + tid; c < N; c += 256) {
-    const int u = par_s[c];
     const int x = tok_s[c];
-    bool ok = false;
 #ifdef SPEC_DEBUG
     atomicAdd(&dbg_tests_s, 1);
 #endif
-    if (x >= 0 && x < p.vocab) {
-      if (!REJECT) {
-        ok = (x == amax_s[u]);
-      } else {
-        const int64_t gu = n0 + u;
-        const int r = rank_s[c];
-        // every read of the test is issued before any is used: the first 9 level totals (entries past r
-        // repeat level r, which exists, and are not used), the row maximum, q(x) and the logit
-        double Z[9];
-#pragma unroll
-        for (int k = 0; k < 9; ++k) Z[k] = level_sum(p, gu, k < r ? k : r);
-        const double M = (double)row_max(p, gu);
-        const double qx = (double)p.draft_probs[gu * p.vocab + x];
-        const float lx = load_logit(p, gu, x);
-#pragma unroll
-        for (int k = 0; k < 9; ++k) Z[k] = Z[k] > 0.0 ? 1.0 / Z[k] : 0.0;   // reciprocals, as in the residual passes
-        const double e = exp((double)lx - M);
-        double res = e * Z[0];
-        for (int k = 1; k <= r; ++k) {
-          const double d = fmax(0.0, res - qx);
-          const double zk = k < 9 ? Z[k] : (level_sum(p, gu, k) > 0.0 ? 1.0 / level_sum(p, gu, k) : 0.0);
-          if (zk > 0.0) res = d * zk;
-        }
-        ok = (double)p.u_accept[n0 + c] * qx < res;
-      }
-    }
-    if (REJECT) {
-      if (ok) atomicMin(&first_s[u], c);
-    } else {
-      rank_s[c] = ok ? 1 : 0;                     // greedy: the edge test, reused below
-    }
+    rank_s[c] = (x >= 0 && x < p.vocab && x == amax_s[par_s[c]]) ? 1 : 0;
   }
   __syncthreads();
 #ifdef SPEC_DEBUG
@@ -552,204 +300,543 @@ __global__ __launch_bounds__(256) void walk_kernel(AcceptParams p) {
     atomicAdd(&p.dbg[2], (uint32_t)dbg_tests_s);
   }
 #endif
-  if (REJECT) {
-    // sampling order: at each node move to its first accepted child
-    if (tid == 0) {
-      int u = 0, d = 0;
-      path_s[0] = 0;
-      while (first_s[u] != 0x7FFFFFFF && d + 1 < kMaxTreeNodes) {
-        u = first_s[u];
-        path_s[++d] = u;
-      }
-      stop_s = u;
-      depth_s = d;
+  // node j is accepted iff every edge on its root path passed; keep the deepest accepted node, the lowest
+  // index among equally deep ones
+  unsigned long long best = 0;
+  for (int j = tid; j < N; j += 256) {
+    bool acc = true;
+    int d = 0, x = j;
+    while (x > 0 && d < N) {
+      acc = acc && rank_s[x] != 0;
+      x = par_s[x];
+      ++d;
     }
-  } else {
-    // greedy: node j is accepted iff every edge on its root path passed; keep the deepest
-    // accepted node, the lowest index among equally deep ones
-    unsigned long long best = 0;
-    for (int j = tid; j < N; j += 256) {
-      bool acc = true;
-      int d = 0, x = j;
-      while (x > 0 && d < N) {
-        acc = acc && rank_s[x] != 0;
-        x = par_s[x];
-        ++d;
-      }
-      if (acc) best = umax64(best, ((unsigned long long)d << 32) | (uint32_t)(0xFFFFu - j));
+    if (acc) best = umax64(best, ((unsigned long long)d << 32) | (uint32_t)(0xFFFFu - j));
+  }
+  best = block_max_u64(best);
+  if (tid == 0) {
+    const int f = 0xFFFF - (int)(best & 0xFFFFu);
+    const int d = (int)(best >> 32);
+    int x = f;
+    for (int k = d; k >= 0; --k) {
+      path_s[k] = x;
+      x = k > 0 ? par_s[x] : x;
     }
-    best = block_max_u64(best);
-    if (tid == 0) {
-      const int f = 0xFFFF - (int)(best & 0xFFFFu);
-      const int d = (int)(best >> 32);
-      int x = f;
-      for (int k = d; k >= 0; --k) {
-        path_s[k] = x;
-        x = k > 0 ? par_s[x] : x;
-      }
-      stop_s = f;
-      depth_s = d;
-    }
+    stop_s = f;
+    depth_s = d;
   }
   __syncthreads();
   const int u = stop_s, depth = depth_s;
   if (depth + 1 > p.max_path) {
-    for (int i = tid; i < p.max_path; i += 256) { o_path[i] = -1; o_tok[i] = -1; }
-    if (tid == 0) p.out_num_accepted[b] = -1;
+    write_invalid(p, b, tid);
     return;
   }
-  int bonus;
-  if (!REJECT) {
-    bonus = amax_s[u];
-  } else {
-    // inverse CDF of the residual left at u after all its children were rejected
-    const int64_t gu = n0 + u;
-    const int r = nch_s[u];
-    // the totals of levels < r were stored by the residual passes; level r's (no pass follows it for this
-    // node) is summed here by wave 0 in the passes' order, so it has the bits they would give it
-    if (tid < 64) {
-      const double z = level_total_wave(p, gu, r);
-      if (tid == 0) {
-        zlast_s = z;
-        if (r < 9) zs[r] = z;
-      }
-    }
-    if (tid < r && tid < 9) zs[tid] = level_sum(p, gu, tid);    // read in parallel
-    __syncthreads();
-    auto zsum_of = [&](int k) -> double { return k == r ? zlast_s : level_sum(p, gu, k); };
-    if (tid == 0) {
-      int lvl = 0;
-      for (int k = 0; k <= r; ++k) {
-        const double z = k < 9 ? zs[k] : zsum_of(k);
-        if (z > 0.0 || k == 0) lvl = k;             // a zero residual keeps the previous level
-      }
-      seg_s = lvl;                                  // the level, handed to the block below
-    }
-    __syncthreads();
-    {
-      // the segment where the cumulative residual passes u * total: each thread owns a run of consecutive
-      // segments; a fixed-order block scan of the run totals gives every run its starting point
-      const int lvl = seg_s;
-      const double* ss = p.seg_sum + (gu * (p.max_children + 1) + lvl) * p.nsegr;
-      const double rz = 1.0 / zsum_of(lvl);
-      const int per_s = (p.nsegr + 255) / 256;
-      const int s0 = min(tid * per_s, p.nsegr), s1 = min(s0 + per_s, p.nsegr);
-      double run_tot = 0.0;
-      for (int q = s0; q < s1; ++q) run_tot += ss[q] * rz;
-      double tot;
-      const double start = block_scan_excl_f64(run_tot, &tot);
-      const double thr = (double)p.u_sample[gu] * tot;
-      if (tid == 0) {
-        seg_s = 0x7FFFFFFF;
-        base_s = 0.0;
-        thr_s = thr;
-        bonus_s = 0x7FFFFFFF;
-      }
-      __syncthreads();
-      int my_q = -1;
-      double my_base = 0.0;
-      if (start <= thr && start + run_tot > thr) {
-        double base = start;
-        for (int q = s0; q < s1; ++q) {
-          const double w = ss[q] * rz;
-          if (base + w > thr) {
-            my_q = q;
-            my_base = base;
-            break;
-          }
-          base += w;
-        }
-        if (my_q < 0) {                             // rounding inside the run: its last segment with mass
-          for (int q = s1 - 1; q >= s0; --q)
-            if (ss[q] > 0.0) {
-              my_q = q;
-              break;
-            }
-          my_base = start;
-          for (int q = s0; q < my_q; ++q) my_base += ss[q] * rz;
-        }
-        if (my_q >= 0) atomicMin(&seg_s, my_q);     // rounding may let two runs claim: lowest wins
-      }
-      __syncthreads();
-      if (my_q >= 0 && my_q == seg_s) base_s = my_base;
-      if (tid == 0 && seg_s == 0x7FFFFFFF) {        // rounding left the threshold past the end: the last
-        double base = tot;                          // segment with mass
-        int seg = p.nsegr - 1;
-        for (int q = p.nsegr - 1; q >= 0; --q) {
-          base -= ss[q] * rz;
-          if (ss[q] > 0.0) {
-            seg = q;
-            break;
-          }
-        }
-        seg_s = seg;
-        base_s = base;
-      }
-    }
-    __syncthreads();
-    const int seg = seg_s;
-    const int v0 = seg * kResSegment;
-    const int v1 = min(p.vocab, v0 + kResSegment);
-    const int a0 = min(v1, v0 + tid * kResPer);
-    const int a1 = min(v1, a0 + kResPer);
-    float lg[kResPer], qr[kResPer];
-    load_run(p, gu, a0, a1, true, lg, qr);
-    const double M = (double)row_max(p, gu);
-    const float* q = p.draft_probs + gu * (int64_t)p.vocab;
-    double Z[9];
-    for (int k = 0; k <= r && k < 9; ++k) Z[k] = zs[k] > 0.0 ? 1.0 / zs[k] : 0.0;
-    auto res_from = [&](float l, float qf) -> double {
-      const double qv = (double)qf;
-      double res = exp((double)l - M) * Z[0];
-      for (int k = 1; k <= r; ++k) {
-        const double dd = fmax(0.0, res - qv);
-        const double zk = k < 9 ? Z[k] : (zsum_of(k) > 0.0 ? 1.0 / zsum_of(k) : 0.0);
-        if (zk > 0.0) res = dd * zk;
-      }
-      return res;
-    };
-    auto res_of = [&](int v) -> double { return res_from(load_logit(p, gu, v), q[v]); };
-    // this thread's run of the residual, evaluated once and kept for the claim below
-    double rv[kResPer];
-    double mine = 0.0;
-#pragma unroll
-    for (int i = 0; i < kResPer; ++i) {             // an entry past the end gives +0 (q = 0, exp(-inf) = +0)
-      rv[i] = res_from(a0 + i < a1 ? lg[i] : -INFINITY, qr[i]);
-      mine += rv[i];
-    }
-    double seg_tot;
-    const double lo = base_s + block_scan_excl_f64(mine, &seg_tot);
-    const double thr = thr_s;
-    if (a0 < a1 && lo + mine > thr && lo <= thr) {
-      double run = lo;
-      int pick = a1 - 1;
-      bool found = false;
-#pragma unroll
-      for (int i = 0; i < kResPer; ++i) {         // the first entry whose running sum passes thr
-        if (found || a0 + i >= a1) continue;
-        run += rv[i];
-        if (run > thr) {
-          pick = a0 + i;
-          found = true;
-        }
-      }
-      atomicMin(&bonus_s, pick);                    // rounding may let two threads claim: lowest wins
-    }
-    __syncthreads();
-    if (tid == 0 && bonus_s == 0x7FFFFFFF) {        // rounding: take the last token with mass in the segment
-      int pick = v0;
-      for (int v = v1 - 1; v >= v0; --v)
-        if (res_of(v) > 0.0) { pick = v; break; }
-      bonus_s = pick;
-    }
-    __syncthreads();
-    bonus = bonus_s;
-  }
+  const int bonus = amax_s[u];
   for (int i = tid; i < p.max_path; i += 256) {
     o_path[i] = i <= depth ? path_s[i] : -1;
     o_tok[i] = i < depth ? tok_s[path_s[i + 1]] : (i == depth ? bonus : -1);
   }
   if (tid == 0) p.out_num_accepted[b] = depth;
+}
+
+// ---------------------------------------------------------------------------------------------------
+// Rejection acceptance in one pass over the rows ("Adaptive Speculative Decoding", "Correctness first").
+//
+// One work-group per (node, 8192-token segment) loads its segment of the node's logits once: 32
+// consecutive entries per thread, held in registers as fp64 residual values from then on.  The node's
+// residual levels follow from those registers; the draft probabilities, which every level needs, are
+// read from L2 at each level instead of being held (holding them spilled).  The node's work-groups meet
+// once per level, each publishing its segment's value into a slot of its own and polling the others':
+//   sync 0: each segment's maximum m_s and sum exp(l - m_s) (fp64) -> the row maximum M = max m_s and
+//           Z_0 = sum_s (sum exp(l - m_s)) exp(m_s - M); res_0 = exp(l - m_s) exp(m_s - M) / Z_0
+//   sync r, r = 1 .. children: the segment sums of max(0, res_{r-1} - q) -> Z_r;
+//           res_r = max(0, res_{r-1} - q) / Z_r, or res_{r-1} again if Z_r = 0
+// The child of rank r (r earlier siblings) is tested against res_r at its token, by the thread that
+// holds that token, as soon as res_r exists; after the last level the node's bonus token (the inverse
+// CDF of its last residual at u_sample) is drawn by the work-group whose segment holds it.  Every node's
+// draw is made, whether or not the walk ends there: the decisions of one node depend on that node's
+// row alone.  The sequence counts its finished nodes; the last one walks the tree from the root (first
+// accepted child of each node) and writes the outputs.
+//
+// Totals over segments are summed by every work-group in one fixed order, so all of a node's work-groups
+// hold the same bits.  A node's work-groups are consecutive in the grid, and work-groups start in grid
+// order, so the ones that wait only wait for ones that have started or will start when a finished
+// work-group leaves: the waits end.  Each wait is also bounded; a wait that runs out (which the ordering
+// above rules out) marks the call's error word, and the walk then writes num_accepted = -1.
+// ---------------------------------------------------------------------------------------------------
+constexpr int kRejPer = kRejSegment / 256;        // consecutive vocabulary entries per thread
+static_assert(kRejPer % 8 == 0, "a run is whole 16-byte loads of bf16 logits and of fp32 probabilities");
+constexpr int kSpinLimit = 1 << 18;               // polls of a counter before a wait gives up
+
+// this thread's run [a0, a1) of row u of the draft probabilities (entries past a1 are 0).  They are read
+// again at every residual level, from L2, rather than held in registers through the exps.
+__device__ __forceinline__ void load_q_run(const AcceptParams& p, int64_t u, int a0, int a1, float (&qv)[kRejPer]) {
+  const float* row = p.draft_probs + u * p.vocab + a0;
+  if (a1 - a0 == kRejPer && ((uintptr_t)row & 15) == 0) {
+    u32x4 w[kRejPer / 4];
+#pragma unroll
+    for (int j = 0; j < kRejPer / 4; ++j) w[j] = *reinterpret_cast<const u32x4*>(row + 4 * j);
+#pragma unroll
+    for (int j = 0; j < kRejPer / 4; ++j)
+#pragma unroll
+      for (int k = 0; k < 4; ++k) qv[4 * j + k] = __uint_as_float(w[j][k]);
+  } else {
+#pragma unroll
+    for (int i = 0; i < kRejPer; ++i) qv[i] = a0 + i < a1 ? row[i] : 0.f;
+  }
+}
+
+// Values passed between work-groups are written and read with device-scope (sc1) stores and loads,
+// which are coherent across the XCDs' L2 caches.  A writer waits for its stores to complete (vmcnt)
+// before it counts its arrival, and a reader issues its loads only after it has seen the count, so the
+// loads find the stores.  (Release and acquire fences at device scope would write back and invalidate
+// the whole L2 on every arrival: measured ten times slower.)
+__device__ __forceinline__ void store_dev_u64(unsigned long long* a, unsigned long long v) {
+  __hip_atomic_store(a, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void store_dev_f64(double* a, double v) {
+  store_dev_u64(reinterpret_cast<unsigned long long*>(a), __builtin_bit_cast(unsigned long long, v));
+}
+__device__ __forceinline__ void store_dev_i32(int32_t* a, int32_t v) {
+  __hip_atomic_store(a, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ unsigned long long load_dev_u64(const unsigned long long* a) {
+  return __hip_atomic_load(a, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ double load_dev_f64(const double* a) {
+  return __builtin_bit_cast(double, load_dev_u64(reinterpret_cast<const unsigned long long*>(a)));
+}
+__device__ __forceinline__ int load_dev_i32(const int32_t* a) {
+  return __hip_atomic_load(a, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// A work-group's value for one sync of its node: every thread's stores of the call so far complete
+// (vmcnt), then thread 0 stores the value into the work-group's own slot.
+__device__ __forceinline__ void publish_f64(double* slot, double v) {
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  if (threadIdx.x == 0) store_dev_f64(slot, v);
+}
+
+// A sync of a node is its S work-groups' values: a slot holds kUnset until its work-group writes it (a
+// real value is a sum of non-negative terms, or NaN from NaN inputs, never kUnset).  The waiters poll
+// the S slots in parallel, so that the values arrive with the poll that sees them all.
+constexpr double kUnset = -1.0;
+
+// Polls until the S slots v[0 .. S) are all set, then returns their fixed-order total (thread t sums s
+// = t, t + 256, ... in order; then the block sum): every work-group gets the same bits.  A wait that
+// runs out marks *err (and, once *err is marked, no wait waits: the call's results are void anyway).
+__device__ double wait_total(const double* v, int S, uint32_t* err) {
+  for (int it = 0;; ++it) {
+    double part = 0.0;
+    bool ok = true;
+    for (int s = threadIdx.x; s < S; s += 256) {
+      const double x = load_dev_f64(v + s);
+      ok = ok && x != kUnset;
+      part += x;
+    }
+    if (__syncthreads_and(ok)) return block_sum_f64(part);
+    if (it + 1 == kSpinLimit || __hip_atomic_load(err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u) {
+      if (threadIdx.x == 0) __hip_atomic_fetch_or(err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      return block_sum_f64(part);
+    }
+    __builtin_amdgcn_s_sleep(1);
+  }
+}
+
+// Clears what the first sync of a rejection call reads (every row's segment keys and level-0 slots),
+// the sequence counters and the error word.  The slots of later levels are cleared by their own
+// work-groups before those publish level 0.
+__global__ __launch_bounds__(256) void rej_clear_kernel(AcceptParams p) {
+  const int64_t nk = (int64_t)p.batch * p.max_nodes * p.nsegr;
+  const int64_t lvS = (int64_t)(p.max_children + 1) * p.nsegr;
+  for (int64_t i = blockIdx.x * 256 + threadIdx.x; i < nk; i += gridDim.x * 256) {
+    p.seg_key[i] = 0ull;
+    p.seg_sum[(i / p.nsegr) * lvS + i % p.nsegr] = kUnset;
+  }
+  for (int i = blockIdx.x * 256 + threadIdx.x; i < p.batch + 1; i += gridDim.x * 256) p.sync_cnt[i] = 0u;
+}
+
+// BF16: bf16 logits, kept packed (two to a register) until their exps are taken
+template <bool BF16>
+__global__ __launch_bounds__(256, 3) void rejection_kernel(AcceptParams p) {
+  __shared__ int kids_s[kMaxTreeNodes];           // this node's children, in index order
+  __shared__ int wcnt_s[4];
+  __shared__ int claim_s, last_s;
+  __shared__ double base_s, thr_s;
+  const int seg = blockIdx.x;
+  const int S = p.nsegr;
+  const int i = blockIdx.y;                       // the node within its sequence
+  const int b = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tn = total_nodes(p);
+  int n0 = p.node_offsets[b];
+  int N = p.node_offsets[b + 1] - n0;
+  N = N < 0 ? 0 : (N > p.max_nodes ? p.max_nodes : N);
+  n0 = n0 < 0 ? 0 : (n0 > (p.batch - 1) * p.max_nodes ? (p.batch - 1) * p.max_nodes : n0);
+  const int64_t u = (int64_t)n0 + i;
+  if (N == 0 || n0 + N > tn) {                    // (uniform) a sequence without a tree: -1
+    if (seg == 0 && i == 0) write_invalid(p, b, tid);
+    return;
+  }
+  if (i >= N) return;                             // (uniform) no such node: no counter counts this group
+  uint32_t* seq_cnt = p.sync_cnt + b;
+  uint32_t* err = p.sync_cnt + p.batch;
+  const int lv = p.max_children + 1;
+
+  // ---- this node's children in index order (a child's rank is its position) ----
+  int nk = 0;
+  for (int j0 = i + 1; j0 < N; j0 += 256) {
+    const int j = j0 + tid;
+    const bool kid = j < N && p.parents[n0 + j] == i;
+    const unsigned long long m = __ballot(kid);
+    if (lane == 0) wcnt_s[wave] = __popcll(m);
+    __syncthreads();
+    int off = nk;
+    for (int w = 0; w < wave; ++w) off += wcnt_s[w];
+    if (kid) kids_s[off + __popcll(m & ((1ull << lane) - 1ull))] = j;
+    nk += wcnt_s[0] + wcnt_s[1] + wcnt_s[2] + wcnt_s[3];
+    __syncthreads();
+  }
+  const int nl = nk < p.max_children ? nk : p.max_children;   // residual levels past level 0 (more
+                                                                // children than max_children: the walk
+                                                                // reports the tree)
+  // ---- the run: logits, and the draft probabilities if a child will be tested ----
+  const int v0 = seg * kRejSegment, v1 = min(p.vocab, v0 + kRejSegment);
+  const int a0 = min(v1, v0 + tid * kRejPer), a1 = min(v1, a0 + kRejPer);
+  // the run's logits: BF16 packed two to a register, else fp32
+  constexpr int LW = BF16 ? kRejPer / 2 : kRejPer;
+  uint32_t lw[LW];
+  {
+    const bool whole = a1 - a0 == kRejPer;
+    const char* row = static_cast<const char*>(p.logits) + (u * p.vocab + a0) * (BF16 ? 2 : 4);
+    if (whole && ((uintptr_t)row & 15) == 0) {
+#pragma unroll
+      for (int j = 0; j < LW / 4; ++j) {
+        const u32x4 w = *reinterpret_cast<const u32x4*>(row + 16 * j);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) lw[4 * j + k] = w[k];
+      }
+    } else if (BF16) {
+      const uint16_t* r16 = reinterpret_cast<const uint16_t*>(row);
+#pragma unroll
+      for (int j = 0; j < LW; ++j) {
+        const uint32_t lo = a0 + 2 * j < a1 ? r16[2 * j] : 0u, hi = a0 + 2 * j + 1 < a1 ? r16[2 * j + 1] : 0u;
+        lw[j] = lo | (hi << 16);
+      }
+    } else {
+      const uint32_t* r32 = reinterpret_cast<const uint32_t*>(row);
+#pragma unroll
+      for (int j = 0; j < LW; ++j) lw[j] = a0 + j < a1 ? r32[j] : 0u;
+    }
+  }
+  auto logit = [&](int k) -> float {
+    if (BF16) return __uint_as_float((k & 1) ? (lw[k >> 1] & 0xFFFF0000u) : (lw[k >> 1] << 16));
+    return __uint_as_float(lw[k]);
+  };
+  float qv[kRejPer];
+
+  double* ssum = p.seg_sum + u * lv * S;          // [level][segment]
+  // this work-group's slots of levels 1 .. nl, cleared before it publishes level 0 (a work-group polls a
+  // level's slots only after it has seen every level-0 value)
+  for (int r = 1 + tid; r <= nl; r += 256) store_dev_f64(ssum + r * S + seg, kUnset);
+
+  // ---- sync 1: the segment's maximum m_s (largest logit, lowest index among exact ties) and its
+  // level-0 sum against it, sum exp(l - m_s) (fp64); then the row maximum M = max m_s and
+  // Z_0 = sum_s (sum exp(l - m_s)) exp(m_s - M) ----
+  double res[kRejPer];
+  unsigned long long mine_key;
+  {
+    float mv = -INFINITY;
+#pragma unroll
+    for (int k = 0; k < kRejPer; ++k)
+      if (a0 + k < a1) mv = fmaxf(mv, logit(k));
+    int idx = a0;
+#pragma unroll
+    for (int k = kRejPer - 1; k >= 0; --k)
+      if (a0 + k < a1 && logit(k) == mv) idx = a0 + k;
+    mine_key = block_max_u64(a0 < a1 ? pack_key(mv, idx) : 0ull);
+    const double ms = (double)key_value(mine_key);
+    double acc = 0.0;                             // an entry past the end takes exp(-inf) = +0
+#pragma unroll
+    for (int k = 0; k < kRejPer; ++k) {
+      res[k] = ms > -INFINITY ? exp(a0 + k < a1 ? (double)logit(k) - ms : -INFINITY) : 0.0;
+      acc += res[k];
+    }
+    acc = block_sum_f64(acc);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (tid == 0) {
+      store_dev_f64(ssum + seg, acc);
+      store_dev_u64(p.seg_key + u * S + seg, mine_key);
+    }
+  }
+  double M, z;
+  {
+    // poll the S (key, sum) pairs; once all are set, the maximum and the rescaled total
+    unsigned long long mk = 0;
+    for (int it = 0;; ++it) {
+      bool ok = true;
+      mk = 0;
+      for (int s2 = tid; s2 < S; s2 += 256) {
+        const unsigned long long k2 = load_dev_u64(p.seg_key + u * S + s2);
+        ok = ok && k2 != 0ull && load_dev_f64(ssum + s2) != kUnset;
+        mk = umax64(mk, k2);
+      }
+      if (__syncthreads_and(ok)) break;
+      if (it + 1 == kSpinLimit || __hip_atomic_load(err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u) {
+        if (tid == 0) __hip_atomic_fetch_or(err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        break;
+      }
+      __builtin_amdgcn_s_sleep(1);
+    }
+    mk = block_max_u64(mk);
+    if (seg == 0 && tid == 0) store_dev_u64(p.node_key + u, mk);
+    M = (double)key_value(mk);
+    double part = 0.0;                            // segment s scaled to M, in s order per thread
+    for (int s2 = tid; s2 < S; s2 += 256) {
+      const double ms = (double)key_value(load_dev_u64(p.seg_key + u * S + s2));
+      const double sm = load_dev_f64(ssum + s2);
+      part += ms > -INFINITY ? sm * exp(ms - M) : 0.0;
+    }
+    z = block_sum_f64(part);
+    // res_0 = exp(l - m_s) exp(m_s - M) / Z_0
+    const double ms = (double)key_value(mine_key);
+    const double sc = (ms > -INFINITY ? exp(ms - M) : 0.0) * (z > 0.0 ? 1.0 / z : 0.0);
+#pragma unroll
+    for (int k = 0; k < kRejPer; ++k) res[k] *= sc;
+  }
+  int lvl = 0;                                    // the residual level res holds (the last with mass)
+  double zl = z;
+
+  // the child of rank r against res_r at its token, by the thread that holds the token; a token outside
+  // the vocabulary is rejected, by segment 0
+  auto test_child = [&](int r) {
+    if (r >= nk) return;
+    const int c = kids_s[r];
+    const int x = p.draft_tokens[n0 + c];
+    if (x < 0 || x >= p.vocab) {
+      if (seg == 0 && tid == 0) {
+        store_dev_i32(p.acc_ok + n0 + c, 0);
+#ifdef SPEC_DEBUG
+        if (p.dbg) atomicAdd(&p.dbg[2], 1u);
+#endif
+      }
+      return;
+    }
+    if (x < a0 || x >= a1) return;
+    double rv = 0.0;
+#pragma unroll
+    for (int k = 0; k < kRejPer; ++k)
+      if (a0 + k == x) rv = res[k];
+    const double qx = (double)p.draft_probs[u * p.vocab + x];
+    store_dev_i32(p.acc_ok + n0 + c, (double)p.u_accept[n0 + c] * qx < rv ? 1 : 0);
+#ifdef SPEC_DEBUG
+    if (p.dbg) atomicAdd(&p.dbg[2], 1u);
+#endif
+  };
+  test_child(0);
+
+  // ---- syncs 2 + r: the residual levels ----
+  for (int r = 1; r <= nl; ++r) {
+    load_q_run(p, u, a0, a1, qv);
+    double acc = 0.0;
+#pragma unroll
+    for (int k = 0; k < kRejPer; ++k) acc += fmax(0.0, res[k] - (double)qv[k]);
+    acc = block_sum_f64(acc);
+    publish_f64(ssum + r * S + seg, acc);
+    z = wait_total(ssum + r * S, S, err);
+    if (z > 0.0) {                                // a zero residual keeps the previous level
+      const double rz = 1.0 / z;
+      load_q_run(p, u, a0, a1, qv);               // read again (L2): not held through the wait
+#pragma unroll
+      for (int k = 0; k < kRejPer; ++k) res[k] = fmax(0.0, res[k] - (double)qv[k]) * rz;
+      lvl = r;
+      zl = z;
+    }
+    test_child(r);
+  }
+
+  // ---- the bonus draw from res (level lvl): the segment where the cumulative residual passes
+  // u_sample * total (every work-group of the node finds the same one), then the entry inside it ----
+  {
+    const double* ss = ssum + lvl * S;
+    const double rz = 1.0 / zl;
+    // segment q's share of the residual: level 0's slots hold sums against the segment maximum
+    auto wseg = [&](int q) -> double {
+      const double v = load_dev_f64(ss + q);
+      if (lvl > 0) return v * rz;
+      const double ms = (double)key_value(load_dev_u64(p.seg_key + u * S + q));
+      return ms > -INFINITY ? v * exp(ms - M) * rz : 0.0;
+    };
+    // each thread owns a run of consecutive segments; a fixed-order block scan of the run totals gives
+    // every run its starting point
+    const int per_s = (S + 255) / 256;
+    const int s0 = min(tid * per_s, S), s1 = min(s0 + per_s, S);
+    double run_tot = 0.0;
+    for (int q = s0; q < s1; ++q) run_tot += wseg(q);
+    double tot;
+    const double start = block_scan_excl_f64(run_tot, &tot);
+    const double thr = (double)p.u_sample[u] * tot;
+    if (tid == 0) {
+      claim_s = 0x7FFFFFFF;
+      base_s = 0.0;
+      thr_s = thr;
+    }
+    __syncthreads();
+    int my_q = -1;
+    double my_base = 0.0;
+    if (start <= thr && start + run_tot > thr) {
+      double base = start;
+      for (int q = s0; q < s1; ++q) {
+        const double w = wseg(q);
+        if (base + w > thr) {
+          my_q = q;
+          my_base = base;
+          break;
+        }
+        base += w;
+      }
+      if (my_q < 0) {                             // rounding inside the run: its last segment with mass
+        for (int q = s1 - 1; q >= s0; --q)
+          if (load_dev_f64(ss + q) > 0.0) {
+            my_q = q;
+            break;
+          }
+        my_base = start;
+        for (int q = s0; q < my_q; ++q) my_base += wseg(q);
+      }
+      if (my_q >= 0) atomicMin(&claim_s, my_q);   // rounding may let two runs claim: lowest wins
+    }
+    __syncthreads();
+    if (my_q >= 0 && my_q == claim_s) base_s = my_base;
+    if (tid == 0 && claim_s == 0x7FFFFFFF) {      // rounding left the threshold past the end: the last
+      double base = tot;                          // segment with mass
+      int sg = S - 1;
+      for (int q = S - 1; q >= 0; --q) {
+        const double w = wseg(q);
+        base -= w;
+        if (w > 0.0) {
+          sg = q;
+          break;
+        }
+      }
+      claim_s = sg;
+      base_s = base;
+    }
+    __syncthreads();
+    if (claim_s == seg) {                         // (uniform) this segment holds the draw
+      double mine = 0.0;
+#pragma unroll
+      for (int k = 0; k < kRejPer; ++k) mine += res[k];
+      double seg_tot;
+      const double lo = base_s + block_scan_excl_f64(mine, &seg_tot);
+      const double th = thr_s;
+      if (tid == 0) claim_s = 0x7FFFFFFF;
+      __syncthreads();
+      if (a0 < a1 && lo + mine > th && lo <= th) {
+        double run = lo;
+        int pick = a1 - 1;
+        bool found = false;
+#pragma unroll
+        for (int k = 0; k < kRejPer; ++k) {       // the first entry whose running sum passes thr
+          if (found || a0 + k >= a1) continue;
+          run += res[k];
+          if (run > th) {
+            pick = a0 + k;
+            found = true;
+          }
+        }
+        atomicMin(&claim_s, pick);                // rounding may let two threads claim: lowest wins
+      }
+      __syncthreads();
+      if (claim_s == 0x7FFFFFFF) {                // rounding: the last entry with mass in the segment
+        int last = -1;
+#pragma unroll
+        for (int k = 0; k < kRejPer; ++k)
+          if (a0 + k < a1 && res[k] > 0.0) last = a0 + k;
+        const unsigned long long lk = last >= 0 ? (unsigned long long)(last + 1) : 0ull;
+        const unsigned long long mx = block_max_u64(lk);
+        if (tid == 0) claim_s = mx > 0 ? (int)mx - 1 : v0;
+        __syncthreads();
+      }
+      // the node is done: its tests were stored before its last sync, its draw just now.  The sequence
+      // counts its finished nodes; the last one walks the tree.
+      if (tid == 0) {
+        store_dev_i32(p.bonus_tok + u, claim_s);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        const uint32_t old = __hip_atomic_fetch_add(seq_cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        last_s = old + 1 == (uint32_t)N;
+      }
+      __syncthreads();
+    } else {
+      return;
+    }
+  }
+
+  // ---- the last node of the sequence to finish walks its tree ----
+  if (!last_s) return;
+  {
+    // the walk reuses the shared arrays: kids_s holds the parents
+    __shared__ int first_s[kMaxTreeNodes], rank_s[kMaxTreeNodes], nch_s[kMaxTreeNodes], path_s[kMaxTreeNodes];
+    __shared__ int bad_s, stop_s, depth_s;
+    int* par_s = kids_s;
+    if (tid == 0) bad_s = __hip_atomic_load(err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u;
+#ifdef SPEC_DEBUG
+    int rows_seen = 0;
+#endif
+    for (int j = tid; j < N; j += 256) {
+      par_s[j] = p.parents[n0 + j];
+      first_s[j] = 0x7FFFFFFF;
+#ifdef SPEC_DEBUG
+      rows_seen += load_dev_u64(p.node_key + n0 + j) != 0ull ? 1 : 0;   // row maximum written in this call
+#endif
+    }
+    __syncthreads();
+#ifdef SPEC_DEBUG
+    if (p.dbg) {
+      const double seen = block_sum_f64((double)rows_seen);
+      if (tid == 0) atomicAdd(&p.dbg[1], (uint32_t)seen);
+    }
+#endif
+    if (N <= 256)
+      child_ranks<1, true>(par_s, N, tid, p.max_children, rank_s, nch_s, bad_s);
+    else
+      child_ranks<kMaxTreeNodes / 256, true>(par_s, N, tid, p.max_children, rank_s, nch_s, bad_s);
+    __syncthreads();
+    if (bad_s) {
+      write_invalid(p, b, tid);
+      return;
+    }
+    // the first accepted child of each node (every earlier sibling was rejected)
+    for (int c = 1 + tid; c < N; c += 256)
+      if (load_dev_i32(p.acc_ok + n0 + c) != 0) atomicMin(&first_s[par_s[c]], c);
+    __syncthreads();
+    if (tid == 0) {
+      int x = 0, d = 0;
+      path_s[0] = 0;
+      while (first_s[x] != 0x7FFFFFFF && d + 1 < kMaxTreeNodes) {
+        x = first_s[x];
+        path_s[++d] = x;
+      }
+      stop_s = x;
+      depth_s = d;
+    }
+    __syncthreads();
+    const int depth = depth_s;
+    if (depth + 1 > p.max_path) {
+      write_invalid(p, b, tid);
+      return;
+    }
+    const int bonus = load_dev_i32(p.bonus_tok + n0 + stop_s);
+    int32_t* o_path = p.out_path_nodes + (int64_t)b * p.max_path;
+    int32_t* o_tok = p.out_tokens + (int64_t)b * p.max_path;
+    for (int k = tid; k < p.max_path; k += 256) {
+      o_path[k] = k <= depth ? path_s[k] : -1;
+      o_tok[k] = k < depth ? p.draft_tokens[n0 + path_s[k + 1]] : (k == depth ? bonus : -1);
+    }
+    if (tid == 0) p.out_num_accepted[b] = depth;
+  }
 }
 
 }  // namespace
@@ -763,11 +850,20 @@ size_t greedy_ws_bytes(int batch, int max_nodes, int nseg) {
   return greedy_keys_bytes(batch, max_nodes, nseg) + SPEC_DEBUG_RECORD_BYTES;
 }
 
-size_t rejection_ws_bytes(int batch, int max_nodes, int nsegr, int max_children) {
+RejectionLayout rejection_layout(int batch, int max_nodes, int nsegr, int max_children) {
   const size_t nodes = (size_t)batch * max_nodes, lv = (size_t)max_children + 1;
-  return greedy_keys_bytes(batch, max_nodes, nsegr) + align_up(sizeof(unsigned long long) * nodes, 256) +
-         align_up(sizeof(double) * nodes * lv * nsegr, 256) + align_up(sizeof(double) * nodes * lv, 256) +
-         align_up(sizeof(int32_t) * nodes, 256) + SPEC_DEBUG_RECORD_BYTES;
+  RejectionLayout l;
+  l.off_node_key = greedy_keys_bytes(batch, max_nodes, nsegr);
+  l.off_seg_sum = l.off_node_key + align_up(sizeof(unsigned long long) * nodes, 256);
+  l.off_acc_ok = l.off_seg_sum + align_up(sizeof(double) * nodes * lv * nsegr, 256);
+  l.off_bonus = l.off_acc_ok + align_up(sizeof(int32_t) * nodes, 256);
+  l.off_sync = l.off_bonus + align_up(sizeof(int32_t) * nodes, 256);
+  l.bytes = l.off_sync + align_up(sizeof(uint32_t) * (batch + 1), 256) + SPEC_DEBUG_RECORD_BYTES;
+  return l;
+}
+
+size_t rejection_ws_bytes(int batch, int max_nodes, int nsegr, int max_children) {
+  return rejection_layout(batch, max_nodes, nsegr, max_children).bytes;
 }
 
 hipError_t launch_accept_greedy(const AcceptParams& p, hipStream_t s) {
@@ -775,23 +871,17 @@ hipError_t launch_accept_greedy(const AcceptParams& p, hipStream_t s) {
   hipLaunchKernelGGL(argmax_seg_kernel, dim3(p.nseg, rows), dim3(256), 0, s, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(walk_kernel<false>, dim3(p.batch), dim3(256), 0, s, p);
+  hipLaunchKernelGGL(greedy_walk_kernel, dim3(p.batch), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 
 hipError_t launch_accept_rejection(const AcceptParams& p, hipStream_t s) {
-  const unsigned rows = (unsigned)(p.batch * p.max_nodes);
-  hipLaunchKernelGGL(max_sum_seg_kernel, dim3(p.nsegr, p.max_nodes, p.batch), dim3(256), 0, s, p);
+  const int n = p.batch * p.max_nodes * p.nsegr + p.batch + 1;
+  hipLaunchKernelGGL(rej_clear_kernel, dim3((unsigned)min(ceil_div(n, 256), (int64_t)1024)), dim3(256), 0, s, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(node_max_kernel, dim3(rows), dim3(64), 0, s, p);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  for (int r = 1; r <= p.max_children; ++r) {
-    hipLaunchKernelGGL(residual_pass_kernel, dim3(p.nsegr, rows), dim3(256),
-                       sizeof(double) * (size_t)(p.max_children + 1), s, p, r);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-  }
-  hipLaunchKernelGGL(walk_kernel<true>, dim3(p.batch), dim3(256), 0, s, p);
+  if (p.bf16) hipLaunchKernelGGL(rejection_kernel<true>, dim3(p.nsegr, p.max_nodes, p.batch), dim3(256), 0, s, p);
+  else hipLaunchKernelGGL(rejection_kernel<false>, dim3(p.nsegr, p.max_nodes, p.batch), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 

@@ -220,7 +220,7 @@ int check_greedy(const spec_accept_greedy_args* a) {
 }
 
 int nseg_of(int vocab) { return (int)spec::ceil_div(vocab, spec::kSegment); }
-int nsegr_of(int vocab) { return (int)spec::ceil_div(vocab, spec::kResSegment); }
+int nsegr_of(int vocab) { return (int)spec::ceil_div(vocab, spec::kRejSegment); }
 
 spec::AcceptParams accept_params(const spec_accept_greedy_args* a) {
   spec::AcceptParams p{};
@@ -467,15 +467,12 @@ int spec_accept_rejection(const spec_accept_rejection_args* args, void* stream) 
   p.nsegr = nsegr;
   p.nseg = nsegr;                                 // rejection keeps its segment maxima per residual segment
   char* ws = static_cast<char*>(g.workspace);
-  const size_t nodes = (size_t)g.batch * g.max_nodes, lv = (size_t)args->max_children + 1;
-  size_t off = spec::greedy_keys_bytes(g.batch, g.max_nodes, nsegr);
-  p.node_key = reinterpret_cast<unsigned long long*>(ws + off);
-  off += spec::align_up(sizeof(unsigned long long) * nodes, 256);
-  p.seg_sum = reinterpret_cast<double*>(ws + off);
-  off += spec::align_up(sizeof(double) * nodes * lv * nsegr, 256);
-  p.zsum = reinterpret_cast<double*>(ws + off);
-  off += spec::align_up(sizeof(double) * nodes * lv, 256);
-  p.n_children = reinterpret_cast<int32_t*>(ws + off);
+  const spec::RejectionLayout l = spec::rejection_layout(g.batch, g.max_nodes, nsegr, args->max_children);
+  p.node_key = reinterpret_cast<unsigned long long*>(ws + l.off_node_key);
+  p.seg_sum = reinterpret_cast<double*>(ws + l.off_seg_sum);
+  p.acc_ok = reinterpret_cast<int32_t*>(ws + l.off_acc_ok);
+  p.bonus_tok = reinterpret_cast<int32_t*>(ws + l.off_bonus);
+  p.sync_cnt = reinterpret_cast<uint32_t*>(ws + l.off_sync);
 #ifdef SPEC_DEBUG
   {
     p.dbg = reinterpret_cast<uint32_t*>(ws + need - SPEC_DEBUG_RECORD_BYTES);

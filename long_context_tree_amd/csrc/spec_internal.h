@@ -14,7 +14,7 @@ constexpr int kTile = 64;          // KV slots per attention tile
 constexpr int kMaxNodes = 256;     // tree nodes per sequence with ancestor bit masks (4 x 64 bits)
 constexpr int kMaxTreeNodes = SPEC_MAX_TREE_NODES;   // tree nodes per sequence otherwise
 constexpr int kSegment = 8192;     // vocabulary elements per argmax work-group
-constexpr int kResSegment = 2048;  // vocabulary elements per residual-sum work-group (rejection)
+constexpr int kRejSegment = 8192;  // vocabulary elements per rejection work-group
 constexpr int kMaxTopK = 8192;     // chunks sorted by one work-group for top-k
 constexpr int kMaxSplitPages = 1024;  // page ids of one attention split staged in LDS
 
@@ -108,10 +108,16 @@ struct AcceptParams {
   const float* u_sample;
   unsigned long long* node_key;   // [batch*max_nodes] row maximum key
   double* seg_sum;       // [batch*max_nodes][max_children+1][nsegr] residual sums per segment
-  double* zsum;          // [batch*max_nodes][max_children+1] residual sums per level (fixed-order totals)
-  int32_t* n_children;   // [batch*max_nodes]
+  int32_t* acc_ok;       // [batch*max_nodes] 1: the node's draft passed its accept test
+  int32_t* bonus_tok;    // [batch*max_nodes] the token drawn from the node's last residual
+  uint32_t* sync_cnt;    // [batch] sequence counters (finished nodes), then 1 error word
   uint32_t* dbg;         // the debug record (SPEC_DEBUG build: witness counters of the walk), else NULL
 };
+// byte offsets of the rejection workspace's arrays (seg_key first, at 0)
+struct RejectionLayout {
+  size_t off_node_key, off_seg_sum, off_acc_ok, off_bonus, off_sync, bytes;
+};
+RejectionLayout rejection_layout(int batch, int max_nodes, int nsegr, int max_children);
 size_t greedy_keys_bytes(int batch, int max_nodes, int nseg);   // the segment-key array alone
 size_t greedy_ws_bytes(int batch, int max_nodes, int nseg);     // keys + the debug record
 size_t rejection_ws_bytes(int batch, int max_nodes, int nsegr, int max_children);
