@@ -294,7 +294,7 @@ def main():
     else:
         roof = {"bound": "hbm", "achieved": round(hbm_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(hbm_gbs / HBM_PEAK_GBS, 4), "traffic": traffic}
-    roof.update({"kernel": "spec_tree_attention (tree_attn_kernel + attn_merge_kernel)",
+    roof.update({"kernel": "spec_tree_attention (tree_attn_pipe_kernel + attn_merge_kernel)",
                  "alg_bytes_per_launch": alg_bytes, "alg_flops_per_launch": alg_flops,
                  "launch_us_median": round(t_attn * 1e6, 2),
                  "launch_us_p10_p90": [round(float(np.percentile(attn_ms, 10)) * 1e3, 2),
