@@ -7,25 +7,13 @@
 // first" and "The controller"), generalised to siblings drawn i.i.d. from q.
 //
 // Both are HBM streams over the [nodes][vocab] logits (16-33 MB at vocab 128K), so the work is
-// spread over (vocab segment x node) work-groups with fixed-order reductions, and only the tree
-// walk itself runs in one work-group per sequence:
-//   argmax_seg     (greedy) per (node, 8192-token segment): the packed key (ordered value, ~index)
-//                  maximum, i.e. the largest logit with the lowest index among exact ties
-//   max_sum_seg    (rejection) per (node, 2048-token segment): the same key, and level 0's
-//                  sum exp(l - m_s) against the segment maximum m_s, from one read of the logits;
-//                  segment 0 also counts the node's children.  node_max then takes the row maximum
-//                  M and scales each sum by exp(m_s - M)
-//   residual_pass  (rejection) level r >= 1, for nodes with >= r children: sum max(0, res_{r-1} - q),
-//                  with res_{r-1} rebuilt per element from the earlier levels' normalisers
-//                  (all fp64, exp evaluated in fp64), whose totals every work-group sums in one fixed
-//                  order and segment 0 stores for the walk
-// Each thread of the rejection passes loads its run of 8 consecutive entries before using any of them,
-// so a pass costs one round trip to memory.
-//   walk           per sequence: accept tests of every child in parallel (a child is tested only
-//                  after all earlier siblings were rejected, so its residual level is its sibling
-//                  rank), first accepted child per node by LDS atomic-min, walk from the root,
-//                  then the bonus token (greedy: argmax; rejection: inverse CDF of the residual,
-//                  segment found from the segment sums, then an in-segment scan)
+// spread over (vocab segment x node) work-groups with fixed-order reductions:
+//   argmax_seg        (greedy) per (node, 8192-token segment): the packed key (ordered value, ~index)
+//                     maximum, i.e. the largest logit with the lowest index among exact ties
+//   greedy_walk       (greedy) per sequence: every edge test in parallel, the deepest accepted node,
+//                     the path and the argmax bonus token
+//   rejection_kernel  (rejection) per (node, 8192-token segment), all levels of the node in one
+//                     launch (see below), the walk by the sequence's last node to finish
 #include <type_traits>
 
 #include "spec_internal.h"
@@ -51,9 +39,49 @@ __device__ __forceinline__ int key_index(unsigned long long k) { return (int)(~(
 
 __device__ __forceinline__ unsigned long long umax64(unsigned long long a, unsigned long long b) { return a > b ? a : b; }
 
-__device__ __forceinline__ unsigned long long shfl_xor_u64(unsigned long long v, int m) {
-  const uint32_t lo = __shfl_xor((uint32_t)v, m), hi = __shfl_xor((uint32_t)(v >> 32), m);
+// Lane l's value from lane l ^ M within each half-wave (M < 32), by ds_swizzle in its bitmask mode:
+// the lane pattern is an immediate, so no lane-address register stays live through a kernel.
+template <int M>
+__device__ __forceinline__ uint32_t xor_lane(uint32_t v) {
+  static_assert(M > 0 && M < 32, "bitmask-mode swizzles stay within 32 lanes");
+  return (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, 0x1F | (M << 10));
+}
+template <int M>
+__device__ __forceinline__ unsigned long long xor_lane_u64(unsigned long long v) {
+  return ((unsigned long long)xor_lane<M>((uint32_t)(v >> 32)) << 32) | xor_lane<M>((uint32_t)v);
+}
+template <int M>
+__device__ __forceinline__ double xor_lane_f64(double v) {
+  return __builtin_bit_cast(double, xor_lane_u64<M>(__builtin_bit_cast(unsigned long long, v)));
+}
+__device__ __forceinline__ unsigned long long lane_u64(unsigned long long v, int l) {
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(v >> 32), l);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, l);
   return ((unsigned long long)hi << 32) | lo;
+}
+__device__ __forceinline__ double lane_f64(double v, int l) {
+  return __builtin_bit_cast(double, lane_u64(__builtin_bit_cast(unsigned long long, v), l));
+}
+
+// Wave maximum of a u64 key: butterflies within each half-wave, then the two halves (lanes 0 and 32).
+__device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long v) {
+  v = umax64(v, xor_lane_u64<16>(v));
+  v = umax64(v, xor_lane_u64<8>(v));
+  v = umax64(v, xor_lane_u64<4>(v));
+  v = umax64(v, xor_lane_u64<2>(v));
+  v = umax64(v, xor_lane_u64<1>(v));
+  return umax64(lane_u64(v, 0), lane_u64(v, 32));
+}
+
+// Wave fp64 sum in a fixed order: butterflies within each half-wave (the two lanes of a pair add the
+// same two values, so every lane of a half holds the same bits), then half 0 + half 1.
+__device__ __forceinline__ double wave_sum_f64(double v) {
+  v += xor_lane_f64<16>(v);
+  v += xor_lane_f64<8>(v);
+  v += xor_lane_f64<4>(v);
+  v += xor_lane_f64<2>(v);
+  v += xor_lane_f64<1>(v);
+  return lane_f64(v, 0) + lane_f64(v, 32);
 }
 
 __device__ __forceinline__ float load_logit(const AcceptParams& p, int64_t u, int v) {
@@ -73,11 +101,10 @@ __device__ __forceinline__ int total_nodes(const AcceptParams& p) {
 // Block-wide (256 threads) maximum of a u64 key; result valid in every thread.
 __device__ unsigned long long block_max_u64(unsigned long long v) {
   __shared__ unsigned long long red[4];
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v = umax64(v, shfl_xor_u64(v, off));
+  v = wave_max_u64(v);
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
   __syncthreads();
-  v = umax64(umax64(red[0], red[1]), umax64(red[2], red[3]));
+  v = lane_u64(umax64(umax64(red[0], red[1]), umax64(red[2], red[3])), 0);   // (uniform: scalar registers)
   __syncthreads();
   return v;
 }
@@ -85,11 +112,10 @@ __device__ unsigned long long block_max_u64(unsigned long long v) {
 // Block-wide (256 threads) fp64 sum in a fixed order; result valid in every thread.
 __device__ double block_sum_f64(double v) {
   __shared__ double red[4];
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+  v = wave_sum_f64(v);
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
   __syncthreads();
-  v = (red[0] + red[1]) + (red[2] + red[3]);
+  v = lane_f64((red[0] + red[1]) + (red[2] + red[3]), 0);   // (uniform: scalar registers)
   __syncthreads();
   return v;
 }
@@ -181,8 +207,8 @@ __global__ __launch_bounds__(256) void argmax_seg_kernel(AcceptParams p) {
 // Child count and sibling rank (earlier siblings) of the nodes tid + 256 q, q < PER; flags a parent
 // array that is not topological or a node with more than max_children children.  Without COUNT (greedy)
 // only the parent-order checks run.
-template <int PER, bool COUNT>
-__device__ __forceinline__ void child_ranks(const int* par_s, int N, int tid, int max_children, int* rank_s,
+template <int PER, bool COUNT, typename PT>
+__device__ __forceinline__ void child_ranks(const PT* par_s, int N, int tid, int max_children, int* rank_s,
                                             int* nch_s, int& bad_s) {
   int own_p[PER], rank[PER], nch[PER];
 #pragma unroll
@@ -343,14 +369,18 @@ __global__ __launch_bounds__(256) void greedy_walk_kernel(AcceptParams p) {
 // Rejection acceptance in one pass over the rows ("Adaptive Speculative Decoding", "Correctness first").
 //
 // One work-group per (node, 8192-token segment) loads its segment of the node's logits once: 32
-// consecutive entries per thread, held in registers as fp64 residual values from then on.  The node's
-// residual levels follow from those registers; the draft probabilities, which every level needs, are
-// read from L2 at each level instead of being held (holding them spilled).  The node's work-groups meet
-// once per level, each publishing its segment's value into a slot of its own and polling the others':
+// consecutive entries per thread, held in registers as fp64 residual values from then on, beside the
+// thread's 32 draft probabilities (fp32, read once, since every level subtracts the same row).  The
+// grid of a 64-node tree at vocabulary 128K is 1024 work-groups, which must all be resident at once
+// (four per compute unit, so at most 128 registers per lane).  The node's work-groups meet once per
+// level, each publishing its segment's value into a slot of its own and polling the others':
 //   sync 0: each segment's maximum m_s and sum exp(l - m_s) (fp64) -> the row maximum M = max m_s and
-//           Z_0 = sum_s (sum exp(l - m_s)) exp(m_s - M); res_0 = exp(l - m_s) exp(m_s - M) / Z_0
+//           Z_0 = sum_s (sum exp(l - m_s)) exp(m_s - M); res_0 = exp(l - M) / Z_0, evaluated per thread
+//           as exp(l - m_t) exp(m_t - M) / Z_0 with the thread's own maximum m_t (so that a thread's
+//           exps wait for its own loads only)
 //   sync r, r = 1 .. children: the segment sums of max(0, res_{r-1} - q) -> Z_r;
 //           res_r = max(0, res_{r-1} - q) / Z_r, or res_{r-1} again if Z_r = 0
+// Every exp is fp64 (exp_neg: table-driven, within ~2 ulp).
 // The child of rank r (r earlier siblings) is tested against res_r at its token, by the thread that
 // holds that token, as soon as res_r exists; after the last level the node's bonus token (the inverse
 // CDF of its last residual at u_sample) is drawn by the work-group whose segment holds it.  Every node's
@@ -358,8 +388,8 @@ __global__ __launch_bounds__(256) void greedy_walk_kernel(AcceptParams p) {
 // row alone.  The sequence counts its finished nodes; the last one walks the tree from the root (first
 // accepted child of each node) and writes the outputs.
 //
-// Totals over segments are summed by every work-group in one fixed order, so all of a node's work-groups
-// hold the same bits.  A node's work-groups are consecutive in the grid, and work-groups start in grid
+// Wave 0 of each work-group polls the node's slots and sums them in one fixed order, so all of a node's
+// work-groups hold the same bits.  A node's work-groups are consecutive in the grid, and work-groups start in grid
 // order, so the ones that wait only wait for ones that have started or will start when a finished
 // work-group leaves: the waits end.  Each wait is also bounded; a wait that runs out (which the ordering
 // above rules out) marks the call's error word, and the walk then writes num_accepted = -1.
@@ -367,6 +397,33 @@ __global__ __launch_bounds__(256) void greedy_walk_kernel(AcceptParams p) {
 constexpr int kRejPer = kRejSegment / 256;        // consecutive vocabulary entries per thread
 static_assert(kRejPer % 8 == 0, "a run is whole 16-byte loads of bf16 logits and of fp32 probabilities");
 constexpr int kSpinLimit = 1 << 18;               // polls of a counter before a wait gives up
+constexpr int kPreTests = 16;                     // children whose test inputs are read before level 0
+
+// exp(d) for d <= 0 in fp64, table-driven (P. T. P. Tang, "Table-driven implementation of the
+// exponential function in IEEE floating-point arithmetic", ACM TOMS 15(2), 1989):
+//   n = rint(d 256 / ln 2),  r = d - n (ln 2 / 256)  (|r| <= ln 2 / 512, the constant split in two
+//   parts so that r carries no cancellation error),  exp(d) = 2^(n >> 8) * 2^((n & 255) / 256) * e^r,
+// the middle factor from a 256-entry table (2^(j/256), built by every work-group at its start) and
+// e^r from its degree-4 Taylor polynomial, whose truncation error at |r| <= ln 2 / 512 is below
+// 4e-17 relative.  The result is within ~2 ulp of the exact value.  d below -746 gives +0 (as does
+// exp: the true value is below half the smallest subnormal); NaN gives NaN.
+constexpr int kExpTab = 256;
+constexpr double kExpInvStep = 0x1.71547652b82fep+8;     // 256 / ln 2
+constexpr double kExpStepHi = 0x1.62e42fefa39efp-9;      // ln 2 / 256, leading part
+constexpr double kExpStepLo = 0x1.abc9e3b39803fp-64;     // ln 2 / 256 - kExpStepHi
+
+__device__ __forceinline__ double exp_neg(double d, const double* tab) {
+  d = d < -746.0 ? -746.0 : d;
+  const double n = __builtin_rint(d * kExpInvStep);
+  double r = __builtin_fma(-n, kExpStepHi, d);
+  r = __builtin_fma(-n, kExpStepLo, r);
+  double e = __builtin_fma(r, 1.0 / 24.0, 1.0 / 6.0);
+  e = __builtin_fma(e, r, 0.5);
+  e = __builtin_fma(e, r, 1.0);
+  e = __builtin_fma(e, r, 1.0);
+  const int ni = (int)n;
+  return ldexp(tab[ni & (kExpTab - 1)] * e, ni >> 8);
+}
 
 // this thread's run [a0, a1) of row u of the draft probabilities (entries past a1 are 0).  They are read
 // again at every residual level, from L2, rather than held in registers through the exps.
@@ -418,30 +475,74 @@ __device__ __forceinline__ void publish_f64(double* slot, double v) {
   if (threadIdx.x == 0) store_dev_f64(slot, v);
 }
 
+// A uniform fp64 value in scalar registers (its bits from lane 0).
+__device__ __forceinline__ double uniform_f64(double v) { return lane_f64(v, 0); }
+
 // A sync of a node is its S work-groups' values: a slot holds kUnset until its work-group writes it (a
 // real value is a sum of non-negative terms, or NaN from NaN inputs, never kUnset).  The waiters poll
 // the S slots in parallel, so that the values arrive with the poll that sees them all.
 constexpr double kUnset = -1.0;
 
-// Polls until the S slots v[0 .. S) are all set, then returns their fixed-order total (thread t sums s
-// = t, t + 256, ... in order; then the block sum): every work-group gets the same bits.  A wait that
-// runs out marks *err (and, once *err is marked, no wait waits: the call's results are void anyway).
-__device__ double wait_total(const double* v, int S, uint32_t* err) {
-  for (int it = 0;; ++it) {
+// True when the call's error word is marked; read by one lane every 256 polls of a wait (the word is
+// one address for the whole grid, so that reading it on every poll would queue at its memory channel).
+__device__ __forceinline__ bool wait_abandoned(int it, const uint32_t* err) {
+  if (it + 1 == kSpinLimit) return true;
+  if ((it & 255) != 255) return false;
+  const uint32_t e = (threadIdx.x & 63) == 0 ? __hip_atomic_load(err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0u;
+  return __builtin_amdgcn_readfirstlane(e) != 0u;
+}
+
+// The total of one sync's S slots v[0 .. S).  Wave 0 polls them: with S <= 64, lane l watches slot l and
+// stops reading it once it holds a value, so that a round reads only the slots still missing; else each
+// round reads them all.  The total is summed in a fixed order (lane l: slots l, l + 64, ... in order,
+// then the wave sum), so every work-group of the node gets the same bits, and reaches the other waves
+// through LDS.  *mine: slot l's value in lane l of wave 0 (with S <= 64).  A wait that runs out marks
+// *err (and once *err is marked no wait waits: the call's results are void anyway).
+__device__ double wait_total(const double* v, int S, uint32_t* err, double* mine) {
+  __shared__ double tot_s;
+  const int tid = threadIdx.x;
+  if (tid < 64) {
     double part = 0.0;
-    bool ok = true;
-    for (int s = threadIdx.x; s < S; s += 256) {
-      const double x = load_dev_f64(v + s);
-      ok = ok && x != kUnset;
-      part += x;
+    if (S <= 64) {
+      double x = 0.0;
+      bool have = tid >= S;
+      for (int it = 0;; ++it) {
+        if (!have) {
+          x = load_dev_f64(v + tid);
+          have = x != kUnset;
+        }
+        if (__ballot(!have) == 0ull) break;
+        if (wait_abandoned(it, err)) {
+          if (tid == 0) __hip_atomic_fetch_or(err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          break;
+        }
+        __builtin_amdgcn_s_sleep(1);
+      }
+      part = tid < S ? x : 0.0;
+      *mine = part;
+    } else {
+      for (int it = 0;; ++it) {
+        bool ok = true;
+        part = 0.0;
+        for (int s = tid; s < S; s += 64) {
+          const double x = load_dev_f64(v + s);
+          ok = ok && x != kUnset;
+          part += x;
+        }
+        if (__ballot(!ok) == 0ull) break;
+        if (wait_abandoned(it, err)) {
+          if (tid == 0) __hip_atomic_fetch_or(err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          break;
+        }
+        __builtin_amdgcn_s_sleep(1);
+      }
     }
-    if (__syncthreads_and(ok)) return block_sum_f64(part);
-    if (it + 1 == kSpinLimit || __hip_atomic_load(err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u) {
-      if (threadIdx.x == 0) __hip_atomic_fetch_or(err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      return block_sum_f64(part);
-    }
-    __builtin_amdgcn_s_sleep(1);
+    const double t = wave_sum_f64(part);
+    if (tid == 0) tot_s = t;
   }
+  __syncthreads();
+  return uniform_f64(tot_s);                      // (read by every wave before the barriers of the next
+                                                  // level's sum, after which tot_s is written again)
 }
 
 // Clears what the first sync of a rejection call reads (every row's segment keys and level-0 slots),
@@ -459,16 +560,25 @@ __global__ __launch_bounds__(256) void rej_clear_kernel(AcceptParams p) {
 
 // BF16: bf16 logits, kept packed (two to a register) until their exps are taken
 template <bool BF16>
-__global__ __launch_bounds__(256, 3) void rejection_kernel(AcceptParams p) {
+__global__ __launch_bounds__(256, 4) void rejection_kernel(AcceptParams p) {
   __shared__ int kids_s[kMaxTreeNodes];           // this node's children, in index order
+  __shared__ int16_t par16_s[kMaxTreeNodes];      // the sequence's parents, for the walk
   __shared__ int wcnt_s[4];
   __shared__ int claim_s, last_s;
   __shared__ double base_s, thr_s;
+  __shared__ double etab[kExpTab];                // 2^(j/256)
+  __shared__ int ptok_s[kPreTests];               // the first children's tokens ...
+  __shared__ float pua_s[kPreTests];              // ... their u_accept ...
+  __shared__ double pthr_s[kPreTests];            // ... and u_accept * q_u(token)
+  __shared__ float mt_s[256];                     // each thread's own maximum m_t, kept through sync 1
+  // with S <= 64: segment l's key and its slot at level lvl, as wave 0 polled them
+  __shared__ unsigned long long k0_s[64];
+  __shared__ double sl_s[64];
   const int seg = blockIdx.x;
   const int S = p.nsegr;
   const int i = blockIdx.y;                       // the node within its sequence
   const int b = blockIdx.z;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int tn = total_nodes(p);
   int n0 = p.node_offsets[b];
   int N = p.node_offsets[b + 1] - n0;
@@ -483,12 +593,16 @@ __global__ __launch_bounds__(256, 3) void rejection_kernel(AcceptParams p) {
   uint32_t* seq_cnt = p.sync_cnt + b;
   uint32_t* err = p.sync_cnt + p.batch;
   const int lv = p.max_children + 1;
+  const float us = p.u_sample[u];                 // the bonus draw's uniform (read now, used last)
 
-  // ---- this node's children in index order (a child's rank is its position) ----
+  // ---- this node's children in index order (a child's rank is its position); the parents are kept
+  // for the walk (a value outside -1 .. N-1 as -2, which the walk's checks reject) ----
   int nk = 0;
-  for (int j0 = i + 1; j0 < N; j0 += 256) {
+  for (int j0 = 0; j0 < N; j0 += 256) {
     const int j = j0 + tid;
-    const bool kid = j < N && p.parents[n0 + j] == i;
+    const int pj = j < N ? p.parents[n0 + j] : -2;
+    if (j < N) par16_s[j] = (int16_t)(pj >= -1 && pj < N ? pj : -2);
+    const bool kid = j > i && j < N && pj == i;
     const unsigned long long m = __ballot(kid);
     if (lane == 0) wcnt_s[wave] = __popcll(m);
     __syncthreads();
@@ -501,14 +615,16 @@ __global__ __launch_bounds__(256, 3) void rejection_kernel(AcceptParams p) {
   const int nl = nk < p.max_children ? nk : p.max_children;   // residual levels past level 0 (more
                                                                 // children than max_children: the walk
                                                                 // reports the tree)
-  // ---- the run: logits, and the draft probabilities if a child will be tested ----
+  // ---- the run's logits ----
   const int v0 = seg * kRejSegment, v1 = min(p.vocab, v0 + kRejSegment);
   const int a0 = min(v1, v0 + tid * kRejPer), a1 = min(v1, a0 + kRejPer);
-  // the run's logits: BF16 packed two to a register, else fp32
+  const int nv = a1 - a0;                         // entries of the run inside the vocabulary
+  // the run's logits: BF16 packed two to a register, else fp32; entries past the end of the vocabulary
+  // read as -inf, so that they change no maximum and take exp(-inf) = +0 at every level
   constexpr int LW = BF16 ? kRejPer / 2 : kRejPer;
   uint32_t lw[LW];
   {
-    const bool whole = a1 - a0 == kRejPer;
+    const bool whole = nv == kRejPer;
     const char* row = static_cast<const char*>(p.logits) + (u * p.vocab + a0) * (BF16 ? 2 : 4);
     if (whole && ((uintptr_t)row & 15) == 0) {
 #pragma unroll
@@ -521,20 +637,34 @@ __global__ __launch_bounds__(256, 3) void rejection_kernel(AcceptParams p) {
       const uint16_t* r16 = reinterpret_cast<const uint16_t*>(row);
 #pragma unroll
       for (int j = 0; j < LW; ++j) {
-        const uint32_t lo = a0 + 2 * j < a1 ? r16[2 * j] : 0u, hi = a0 + 2 * j + 1 < a1 ? r16[2 * j + 1] : 0u;
+        const uint32_t lo = 2 * j < nv ? r16[2 * j] : 0xFF80u, hi = 2 * j + 1 < nv ? r16[2 * j + 1] : 0xFF80u;
         lw[j] = lo | (hi << 16);
       }
     } else {
       const uint32_t* r32 = reinterpret_cast<const uint32_t*>(row);
 #pragma unroll
-      for (int j = 0; j < LW; ++j) lw[j] = a0 + j < a1 ? r32[j] : 0u;
+      for (int j = 0; j < LW; ++j) lw[j] = j < nv ? r32[j] : 0xFF800000u;
     }
   }
   auto logit = [&](int k) -> float {
     if (BF16) return __uint_as_float((k & 1) ? (lw[k >> 1] & 0xFFFF0000u) : (lw[k >> 1] << 16));
     return __uint_as_float(lw[k]);
   };
-  float qv[kRejPer];
+  // the exp table, 2^(j/256), in LDS before any wave's first exp (this barrier waits for LDS only, not
+  // for the loads in flight)
+  etab[tid] = exp2((double)tid * (1.0 / kExpTab));
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  // the test inputs of the first kPreTests children, read during level 0 so that no level waits for
+  // them: the token and u_accept now, q_u(token) once the token is in (after the level-0 publish); the
+  // threshold u_accept * q_u(token) (fp64; 0 for a token outside the vocabulary) goes to LDS after sync 1
+  const int npre = nk < kPreTests ? nk : kPreTests;
+  int pre_x = -1;
+  float pre_ua = 0.f, pre_q = 0.f;
+  if (tid < npre) {
+    const int c = kids_s[tid];
+    pre_x = p.draft_tokens[n0 + c];
+    pre_ua = p.u_accept[n0 + c];
+  }
 
   double* ssum = p.seg_sum + u * lv * S;          // [level][segment]
   // this work-group's slots of levels 1 .. nl, cleared before it publishes level 0 (a work-group polls a
@@ -543,27 +673,46 @@ __global__ __launch_bounds__(256, 3) void rejection_kernel(AcceptParams p) {
 
   // ---- sync 1: the segment's maximum m_s (largest logit, lowest index among exact ties) and its
   // level-0 sum against it, sum exp(l - m_s) (fp64); then the row maximum M = max m_s and
-  // Z_0 = sum_s (sum exp(l - m_s)) exp(m_s - M) ----
+  // Z_0 = sum_s (sum exp(l - m_s)) exp(m_s - M).  Each thread first takes its exps against its own
+  // maximum m_t, so that they wait for its own loads only (no barrier before them); its sum is then
+  // rescaled by exp(m_t - m_s), and its entries by exp(m_t - M) / Z_0 after the sync ----
   double res[kRejPer];
   unsigned long long mine_key;
   {
-    float mv = -INFINITY;
+    float mv = -INFINITY;                         // m_t
 #pragma unroll
-    for (int k = 0; k < kRejPer; ++k)
-      if (a0 + k < a1) mv = fmaxf(mv, logit(k));
-    int idx = a0;
+    for (int k = 0; k < kRejPer; ++k) mv = fmaxf(mv, logit(k));
+    uint32_t at_max = 0;                          // bit k: entry k holds the maximum
 #pragma unroll
-    for (int k = kRejPer - 1; k >= 0; --k)
-      if (a0 + k < a1 && logit(k) == mv) idx = a0 + k;
-    mine_key = block_max_u64(a0 < a1 ? pack_key(mv, idx) : 0ull);
-    const double ms = (double)key_value(mine_key);
-    double acc = 0.0;                             // an entry past the end takes exp(-inf) = +0
+    for (int k = 0; k < kRejPer; ++k) at_max |= logit(k) == mv ? 1u << k : 0u;
+    at_max &= nv >= kRejPer ? ~0u : (1u << nv) - 1u;
+    const int kb = at_max ? __builtin_ctz(at_max) : 0;   // the lowest such entry
+    double at = 0.0;
+    if (mv > -INFINITY) {                         // else the run has no mass
+      // the logits are unpacked again from lw here, and the exps are scheduled four at a time: the
+      // unpacked copies from the maximum, or more exps in flight, would not fit beside res at the
+      // occupancy the grid needs
 #pragma unroll
-    for (int k = 0; k < kRejPer; ++k) {
-      res[k] = ms > -INFINITY ? exp(a0 + k < a1 ? (double)logit(k) - ms : -INFINITY) : 0.0;
-      acc += res[k];
+      for (int j = 0; j < LW; ++j) asm volatile("" : "+v"(lw[j]));
+      const double mt = mv;
+#pragma unroll
+      for (int k = 0; k < kRejPer; ++k) {
+        res[k] = exp_neg((double)logit(k) - mt, etab);
+        at += res[k];
+        if (k % 4 == 3) __builtin_amdgcn_sched_barrier(0);
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < kRejPer; ++k) res[k] = 0.0;
     }
-    acc = block_sum_f64(acc);
+    if (tid < npre) {                             // (out of registers through the sync)
+      ptok_s[tid] = pre_x;
+      pua_s[tid] = pre_ua;
+    }
+    mine_key = block_max_u64(nv > 0 ? pack_key(mv, a0 + kb) : 0ull);
+    const double ms = (double)key_value(mine_key);
+    const double acc = block_sum_f64(mv > -INFINITY ? at * exp_neg((double)mv - ms, etab) : 0.0);
+    mt_s[tid] = mv;
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     if (tid == 0) {
@@ -571,38 +720,84 @@ __global__ __launch_bounds__(256, 3) void rejection_kernel(AcceptParams p) {
       store_dev_u64(p.seg_key + u * S + seg, mine_key);
     }
   }
+  if (tid < npre) {
+    const int x = ptok_s[tid];
+    if (x >= 0 && x < p.vocab) pre_q = p.draft_probs[u * p.vocab + x];
+  }
   double M, z;
+  float qv[kRejPer];
   {
-    // poll the S (key, sum) pairs; once all are set, the maximum and the rescaled total
-    unsigned long long mk = 0;
-    for (int it = 0;; ++it) {
-      bool ok = true;
-      mk = 0;
-      for (int s2 = tid; s2 < S; s2 += 256) {
-        const unsigned long long k2 = load_dev_u64(p.seg_key + u * S + s2);
-        ok = ok && k2 != 0ull && load_dev_f64(ssum + s2) != kUnset;
-        mk = umax64(mk, k2);
+    // wave 0 polls the S (key, sum) pairs as wait_total polls a level's slots, then takes the row
+    // maximum M and Z_0 (lane l: segments l, l + 64, ... in order, then the wave sum), for every wave
+    __shared__ double m_sh, z_sh;
+    if (nl > 0) load_q_run(p, u, a0, a1, qv);
+    if (tid < 64) {
+      const unsigned long long* keys = p.seg_key + u * S;
+      unsigned long long mk = 0;
+      double part = 0.0;
+      if (S <= 64) {
+        unsigned long long kk = 0;
+        double sm = 0.0;
+        bool have = tid >= S;
+        for (int it = 0;; ++it) {
+          if (!have) {
+            kk = load_dev_u64(keys + tid);
+            sm = load_dev_f64(ssum + tid);
+            have = kk != 0ull && sm != kUnset;
+          }
+          if (__ballot(!have) == 0ull) break;
+          if (wait_abandoned(it, err)) {
+            if (tid == 0) __hip_atomic_fetch_or(err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            break;
+          }
+          __builtin_amdgcn_s_sleep(1);
+        }
+        if (tid >= S) kk = 0ull, sm = 0.0;
+        mk = wave_max_u64(kk);
+        M = (double)key_value(mk);
+        const double ms = (double)key_value(kk);
+        part = tid < S && ms > -INFINITY ? sm * exp_neg(ms - M, etab) : 0.0;
+        k0_s[tid] = kk;
+        sl_s[tid] = sm;
+      } else {
+        for (int it = 0;; ++it) {
+          bool ok = true;
+          mk = 0;
+          for (int s2 = tid; s2 < S; s2 += 64) {
+            const unsigned long long k2 = load_dev_u64(keys + s2);
+            ok = ok && k2 != 0ull && load_dev_f64(ssum + s2) != kUnset;
+            mk = umax64(mk, k2);
+          }
+          if (__ballot(!ok) == 0ull) break;
+          if (wait_abandoned(it, err)) {
+            if (tid == 0) __hip_atomic_fetch_or(err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            break;
+          }
+          __builtin_amdgcn_s_sleep(1);
+        }
+        mk = wave_max_u64(mk);
+        M = (double)key_value(mk);
+        for (int s2 = tid; s2 < S; s2 += 64) {
+          const double ms = (double)key_value(load_dev_u64(keys + s2));
+          const double sm = load_dev_f64(ssum + s2);
+          part += ms > -INFINITY ? sm * exp_neg(ms - M, etab) : 0.0;
+        }
       }
-      if (__syncthreads_and(ok)) break;
-      if (it + 1 == kSpinLimit || __hip_atomic_load(err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u) {
-        if (tid == 0) __hip_atomic_fetch_or(err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        break;
+      const double zz = wave_sum_f64(part);
+      if (tid == 0) {
+        m_sh = M;
+        z_sh = zz;
+        if (seg == 0) store_dev_u64(p.node_key + u, mk);
       }
-      __builtin_amdgcn_s_sleep(1);
     }
-    mk = block_max_u64(mk);
-    if (seg == 0 && tid == 0) store_dev_u64(p.node_key + u, mk);
-    M = (double)key_value(mk);
-    double part = 0.0;                            // segment s scaled to M, in s order per thread
-    for (int s2 = tid; s2 < S; s2 += 256) {
-      const double ms = (double)key_value(load_dev_u64(p.seg_key + u * S + s2));
-      const double sm = load_dev_f64(ssum + s2);
-      part += ms > -INFINITY ? sm * exp(ms - M) : 0.0;
-    }
-    z = block_sum_f64(part);
-    // res_0 = exp(l - m_s) exp(m_s - M) / Z_0
-    const double ms = (double)key_value(mine_key);
-    const double sc = (ms > -INFINITY ? exp(ms - M) : 0.0) * (z > 0.0 ? 1.0 / z : 0.0);
+    if (tid < npre) pthr_s[tid] = (double)pua_s[tid] * (double)pre_q;
+    __syncthreads();
+    M = uniform_f64(m_sh);
+    z = uniform_f64(z_sh);
+    // res_0 = exp(l - m_t) exp(m_t - M) / Z_0
+    const double rz = uniform_f64(z > 0.0 ? 1.0 / z : 0.0);
+    const float mt = mt_s[tid];
+    const double sc = mt > -INFINITY ? exp_neg((double)mt - M, etab) * rz : 0.0;
 #pragma unroll
     for (int k = 0; k < kRejPer; ++k) res[k] *= sc;
   }
@@ -614,7 +809,15 @@ __global__ __launch_bounds__(256, 3) void rejection_kernel(AcceptParams p) {
   auto test_child = [&](int r) {
     if (r >= nk) return;
     const int c = kids_s[r];
-    const int x = p.draft_tokens[n0 + c];
+    int x;
+    double thr;
+    if (r < kPreTests) {
+      x = ptok_s[r];
+      thr = pthr_s[r];
+    } else {
+      x = p.draft_tokens[n0 + c];
+      thr = x >= 0 && x < p.vocab ? (double)p.u_accept[n0 + c] * (double)p.draft_probs[u * p.vocab + x] : 0.0;
+    }
     if (x < 0 || x >= p.vocab) {
       if (seg == 0 && tid == 0) {
         store_dev_i32(p.acc_ok + n0 + c, 0);
@@ -625,12 +828,12 @@ __global__ __launch_bounds__(256, 3) void rejection_kernel(AcceptParams p) {
       return;
     }
     if (x < a0 || x >= a1) return;
+    const int kx = x - a0;
     double rv = 0.0;
 #pragma unroll
     for (int k = 0; k < kRejPer; ++k)
-      if (a0 + k == x) rv = res[k];
-    const double qx = (double)p.draft_probs[u * p.vocab + x];
-    store_dev_i32(p.acc_ok + n0 + c, (double)p.u_accept[n0 + c] * qx < rv ? 1 : 0);
+      if (k == kx) rv = res[k];
+    store_dev_i32(p.acc_ok + n0 + c, thr < rv ? 1 : 0);
 #ifdef SPEC_DEBUG
     if (p.dbg) atomicAdd(&p.dbg[2], 1u);
 #endif
@@ -638,21 +841,36 @@ __global__ __launch_bounds__(256, 3) void rejection_kernel(AcceptParams p) {
   test_child(0);
 
   // ---- syncs 2 + r: the residual levels ----
+  // A thread whose run still has residual mass (part > 0) replaces res by
+  // max(0, res - q) at once: the level's total is then > 0, and res_r is that times 1/Z_r.  A thread
+  // without keeps res_{r-1}: res_r is 0 there when Z_r > 0, and Z_r == 0 keeps the previous level.
   for (int r = 1; r <= nl; ++r) {
-    load_q_run(p, u, a0, a1, qv);
-    double acc = 0.0;
+    double part = 0.0;
 #pragma unroll
-    for (int k = 0; k < kRejPer; ++k) acc += fmax(0.0, res[k] - (double)qv[k]);
-    acc = block_sum_f64(acc);
-    publish_f64(ssum + r * S + seg, acc);
-    z = wait_total(ssum + r * S, S, err);
-    if (z > 0.0) {                                // a zero residual keeps the previous level
-      const double rz = 1.0 / z;
-      load_q_run(p, u, a0, a1, qv);               // read again (L2): not held through the wait
+    for (int k = 0; k < kRejPer; ++k) part += fmax(0.0, res[k] - (double)qv[k]);
+    const bool mass = part > 0.0;
+    if (mass) {
+      // (q is converted to fp64 again here rather than kept converted from the sum above: 32 more fp64
+      // values live at once would cost a quarter of the register file, i.e. the occupancy)
 #pragma unroll
-      for (int k = 0; k < kRejPer; ++k) res[k] = fmax(0.0, res[k] - (double)qv[k]) * rz;
+      for (int k = 0; k < kRejPer; ++k) asm volatile("" : "+v"(qv[k]));
+#pragma unroll
+      for (int k = 0; k < kRejPer; ++k) res[k] = fmax(0.0, res[k] - (double)qv[k]);
+    }
+    const double acc = block_sum_f64(part);
+    // a level's slots carry their own values: only the last one also vouches for the node's test
+    // stores (the walk reads them once the node has counted itself)
+    if (r == nl) publish_f64(ssum + r * S + seg, acc);
+    else if (tid == 0) store_dev_f64(ssum + r * S + seg, acc);
+    double s_mine = 0.0;
+    z = wait_total(ssum + r * S, S, err, &s_mine);
+    if (z > 0.0) {
+      const double rz = uniform_f64(1.0 / z);
+#pragma unroll
+      for (int k = 0; k < kRejPer; ++k) res[k] = mass ? res[k] * rz : 0.0;
       lvl = r;
       zl = z;
+      if (tid < 64) sl_s[tid] = s_mine;
     }
     test_child(r);
   }
@@ -661,13 +879,16 @@ __global__ __launch_bounds__(256, 3) void rejection_kernel(AcceptParams p) {
   // u_sample * total (every work-group of the node finds the same one), then the entry inside it ----
   {
     const double* ss = ssum + lvl * S;
-    const double rz = 1.0 / zl;
+    const double rz = uniform_f64(1.0 / zl);
     // segment q's share of the residual: level 0's slots hold sums against the segment maximum
+    // (with S <= 64, segment tid's values were kept from the polls; others are read again, with the
+    // same bits)
     auto wseg = [&](int q) -> double {
-      const double v = load_dev_f64(ss + q);
+      const bool kept = S <= 64 && q == tid;
+      const double v = kept ? sl_s[tid] : load_dev_f64(ss + q);
       if (lvl > 0) return v * rz;
-      const double ms = (double)key_value(load_dev_u64(p.seg_key + u * S + q));
-      return ms > -INFINITY ? v * exp(ms - M) * rz : 0.0;
+      const double ms = (double)key_value(kept ? k0_s[tid] : load_dev_u64(p.seg_key + u * S + q));
+      return ms > -INFINITY ? v * exp_neg(ms - M, etab) * rz : 0.0;
     };
     // each thread owns a run of consecutive segments; a fixed-order block scan of the run totals gives
     // every run its starting point
@@ -677,7 +898,7 @@ __global__ __launch_bounds__(256, 3) void rejection_kernel(AcceptParams p) {
     for (int q = s0; q < s1; ++q) run_tot += wseg(q);
     double tot;
     const double start = block_scan_excl_f64(run_tot, &tot);
-    const double thr = (double)p.u_sample[u] * tot;
+    const double thr = (double)us * tot;
     if (tid == 0) {
       claim_s = 0x7FFFFFFF;
       base_s = 0.0;
@@ -734,28 +955,28 @@ __global__ __launch_bounds__(256, 3) void rejection_kernel(AcceptParams p) {
       const double th = thr_s;
       if (tid == 0) claim_s = 0x7FFFFFFF;
       __syncthreads();
-      if (a0 < a1 && lo + mine > th && lo <= th) {
-        double run = lo;
-        int pick = a1 - 1;
+      if (nv > 0 && lo + mine > th && lo <= th) {
+        double run = lo;                          // (entries past the end hold +0: they pass nothing)
+        int kp = nv - 1;
         bool found = false;
 #pragma unroll
         for (int k = 0; k < kRejPer; ++k) {       // the first entry whose running sum passes thr
-          if (found || a0 + k >= a1) continue;
+          if (found) continue;
           run += res[k];
           if (run > th) {
-            pick = a0 + k;
+            kp = k;
             found = true;
           }
         }
-        atomicMin(&claim_s, pick);                // rounding may let two threads claim: lowest wins
+        atomicMin(&claim_s, a0 + kp);             // rounding may let two threads claim: lowest wins
       }
       __syncthreads();
       if (claim_s == 0x7FFFFFFF) {                // rounding: the last entry with mass in the segment
         int last = -1;
 #pragma unroll
         for (int k = 0; k < kRejPer; ++k)
-          if (a0 + k < a1 && res[k] > 0.0) last = a0 + k;
-        const unsigned long long lk = last >= 0 ? (unsigned long long)(last + 1) : 0ull;
+          if (res[k] > 0.0) last = k;
+        const unsigned long long lk = last >= 0 ? (unsigned long long)(a0 + last + 1) : 0ull;
         const unsigned long long mx = block_max_u64(lk);
         if (tid == 0) claim_s = mx > 0 ? (int)mx - 1 : v0;
         __syncthreads();
@@ -777,16 +998,15 @@ __global__ __launch_bounds__(256, 3) void rejection_kernel(AcceptParams p) {
   // ---- the last node of the sequence to finish walks its tree ----
   if (!last_s) return;
   {
-    // the walk reuses the shared arrays: kids_s holds the parents
+    // (the parents were read into LDS at the start)
     __shared__ int first_s[kMaxTreeNodes], rank_s[kMaxTreeNodes], nch_s[kMaxTreeNodes], path_s[kMaxTreeNodes];
     __shared__ int bad_s, stop_s, depth_s;
-    int* par_s = kids_s;
+    const int16_t* par_s = par16_s;
     if (tid == 0) bad_s = __hip_atomic_load(err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u;
 #ifdef SPEC_DEBUG
     int rows_seen = 0;
 #endif
     for (int j = tid; j < N; j += 256) {
-      par_s[j] = p.parents[n0 + j];
       first_s[j] = 0x7FFFFFFF;
 #ifdef SPEC_DEBUG
       rows_seen += load_dev_u64(p.node_key + n0 + j) != 0ull ? 1 : 0;   // row maximum written in this call
