@@ -325,6 +325,7 @@ int spec_chunk_salience(const spec_chunk_salience_args* args, void* stream) {
   p.node_offsets = a->node_offsets;
   p.batch = a->batch;
   p.Hq = a->num_q_heads;
+  p.Hkv = a->num_kv_heads;
   p.max_nodes = a->max_nodes;
   p.max_ctx = a->max_ctx_len;
   p.chunk_size = a->chunk_size;

@@ -11,7 +11,7 @@
 // scores over the chunk, and the merge leaves each row's final log2-sum-exp.  The mass of chunk c
 // is then  mean over rows of exp2(chunk_lse2[c][row] - lse2[row]).
 //   salience  one work-group per (sequence, chunk): a fixed-order sum over the rows of the chunk
-//             (contiguous in the workspace), scaled, written or accumulated
+//             (one contiguous run per KV head in the workspace), scaled, written or accumulated
 //   top-k     (top_k > 0) one work-group per sequence: bitonic sort of (mass desc, index asc) keys in LDS
 // Every reduction has a fixed order, so results are bitwise reproducible.
 #include "spec_internal.h"
@@ -30,8 +30,9 @@ __device__ __forceinline__ void seq_bounds(const SalienceParams& p, int b, int* 
 
 // One work-group per (sequence, kChunksPerWG chunks): for each chunk, every row's exp2(chunk_lse2 -
 // lse2) is summed in a fixed order (each thread a fixed set of rows, then a butterfly in each wave, then
-// the four waves in order), scaled by 1 / rows and written or accumulated.  Rows of a chunk are
-// contiguous, so the reads are 16-byte loads when the row stride allows.
+// the four waves in order), scaled by 1 / rows and written or accumulated.  The attention workspace keeps
+// a chunk's rows as one run per KV head (row node * G + g is query head kvh * G + g); with G a multiple of
+// 4 the reads are 16-byte loads (four rows of one node, four consecutive query heads).
 __global__ __launch_bounds__(256) void salience_kernel(SalienceParams p) {
   __shared__ float red[4];
   const int b = blockIdx.y;
@@ -40,9 +41,13 @@ __global__ __launch_bounds__(256) void salience_kernel(SalienceParams p) {
   seq_bounds(p, b, &N, &L);
   const int nch = (L + p.chunk_size - 1) / p.chunk_size;
   const int rows = N * p.Hq;
-  const int stride = p.max_nodes * p.Hq;
+  const int stride = p.max_nodes * p.Hq;          // lse2 row stride of a sequence
+  const int G = p.Hq / p.Hkv;
+  const int NG = N * G;                           // rows of one KV head
+  const int RS = p.max_nodes * G;                 // chunk stride of the workspace rows of one KV head
+  const int64_t kstride = (int64_t)p.ws_max_chunks * RS;
   const float* l2 = p.lse2 + (int64_t)b * stride;
-  const bool vec = (stride & 3) == 0;
+  const bool vec = (G & 3) == 0;
   for (int k = 0; k < kChunksPerWG; ++k) {
     const int c = blockIdx.x * kChunksPerWG + k;
     if (c >= p.max_chunks) return;
@@ -51,12 +56,17 @@ __global__ __launch_bounds__(256) void salience_kernel(SalienceParams p) {
       if (tid == 0 && !p.accumulate) *dst = 0.f;
       continue;
     }
-    const float* x = p.chunk_lse2 + ((int64_t)b * p.ws_max_chunks + c) * stride;
+    const float* x = p.chunk_lse2 + (int64_t)b * p.Hkv * kstride + (int64_t)c * RS;   // KV head 0's run
     const float prev = (p.accumulate && tid == 0) ? *dst : 0.f;   // read now, used after the reduction
     float acc = 0.f;
-    int r = 0;
     if (vec) {
-      const int nv = rows >> 2;
+      // element i of the run of 4-row groups: KV head i / n4, rows 4 (i % n4) .. + 3
+      const int n4 = NG >> 2, nv = p.Hkv * n4;
+      auto at = [&](int i, float4& a, float4& m) {
+        const int h = i / n4, r = 4 * (i - h * n4);
+        a = *reinterpret_cast<const float4*>(x + h * kstride + r);
+        m = *reinterpret_cast<const float4*>(l2 + (r / G) * p.Hq + h * G + r % G);
+      };
       auto add4 = [&](const float4& a, const float4& m) {
         acc += (__builtin_amdgcn_exp2f(a.x - m.x) + __builtin_amdgcn_exp2f(a.y - m.y)) +
                (__builtin_amdgcn_exp2f(a.z - m.z) + __builtin_amdgcn_exp2f(a.w - m.w));
@@ -66,18 +76,21 @@ __global__ __launch_bounds__(256) void salience_kernel(SalienceParams p) {
       for (; i + 3 * 256 < nv; i += 4 * 256) {
         float4 a[4], m[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          a[j] = *reinterpret_cast<const float4*>(x + 4 * (i + 256 * j));
-          m[j] = *reinterpret_cast<const float4*>(l2 + 4 * (i + 256 * j));
-        }
+        for (int j = 0; j < 4; ++j) at(i + 256 * j, a[j], m[j]);
 #pragma unroll
         for (int j = 0; j < 4; ++j) add4(a[j], m[j]);
       }
-      for (; i < nv; i += 256)
-        add4(*reinterpret_cast<const float4*>(x + 4 * i), *reinterpret_cast<const float4*>(l2 + 4 * i));
-      r = nv << 2;
+      for (; i < nv; i += 256) {
+        float4 a, m;
+        at(i, a, m);
+        add4(a, m);
+      }
+    } else {
+      for (int i = tid; i < rows; i += 256) {
+        const int h = i / NG, r = i - h * NG;
+        acc += __builtin_amdgcn_exp2f(x[h * kstride + r] - l2[(r / G) * p.Hq + h * G + r % G]);
+      }
     }
-    for (int i = r + tid; i < rows; i += 256) acc += __builtin_amdgcn_exp2f(x[i] - l2[i]);
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off);
     if (lane == 0) red[w] = acc;

@@ -11,6 +11,7 @@
 namespace spec {
 
 constexpr int kTile = 64;          // KV slots per attention tile
+constexpr int kRingFloats = 2048;  // chunk values a 4-wave attention work-group holds for one split
 constexpr int kMaxNodes = 256;     // tree nodes per sequence with ancestor bit masks (4 x 64 bits)
 constexpr int kMaxTreeNodes = SPEC_MAX_TREE_NODES;   // tree nodes per sequence otherwise
 constexpr int kSegment = 8192;     // vocabulary elements per argmax work-group
@@ -58,7 +59,7 @@ struct AttnParams {
   int split_tiles, max_splits, row_groups, rows_pad;
   float* part_o;         // [batch][Hkv][max_splits][rows_pad][D]
   float* part_ml;        // [batch][Hkv][max_splits][rows_pad][2]  (running max in log2 units, sum)
-  float* chunk_lse2;     // [batch][max_chunks][max_nodes * Hq]
+  float* chunk_lse2;     // [batch][Hkv][max_chunks][max_nodes * G]  (row node * G + g: query head kvh * G + g)
   float* lse2;           // [batch][max_nodes * Hq]
   uint16_t* out;         // bf16 [total_nodes][Hq][D]
   float* lse;            // [total_nodes][Hq] natural log, nullable
@@ -73,7 +74,7 @@ hipError_t launch_tree_attention(const AttnParams& p, const AttnPlan& plan, int 
 struct SalienceParams {
   const int32_t* ctx_lens;
   const int32_t* node_offsets;
-  int batch, Hq, max_nodes, max_ctx, chunk_size;
+  int batch, Hq, Hkv, max_nodes, max_ctx, chunk_size;
   int ws_max_chunks;     // chunk stride of the attention workspace
   const float* chunk_lse2;
   const float* lse2;

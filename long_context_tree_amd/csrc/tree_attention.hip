@@ -393,13 +393,14 @@ __global__ __launch_bounds__(W * 64, (W == 8 ? 1 : 2)) void tree_attn_kernel(Att
   // chunk of a context slot: a shift for power-of-two chunk sizes (no per-tile scalar division)
   const int cs_shift = (cs > 0 && (cs & (cs - 1)) == 0) ? __builtin_ctz((unsigned)cs) : -1;
   auto chunk_of = [&](int key) __attribute__((always_inline)) -> int { return cs_shift >= 0 ? key >> cs_shift : key / cs; };
-  const int row_stride_chunk = p.max_nodes * p.Hq;
+  // chunk partials: [sequence][KV head][chunk][row of the KV head], so that a wave's 32 rows of a chunk
+  // are 128 contiguous bytes, written by this work-group alone
+  const int row_stride_chunk = p.max_nodes * G;
   // chunk-partial rows: the lanes of group lg store row block lg (RB consecutive 16-row blocks, one store)
   const int st_rb = lg % RB;
   const int st_row = row0 + (wave * RB + st_rb) * 16 + lm;
   const bool st_ok = lg < RB && st_row < rows;
-  const int64_t st_col = st_ok ? (int64_t)(st_row / G) * p.Hq + kvh * G + st_row % G : 0;
-  float* cbase = p.chunk_lse2 + (int64_t)b * p.max_chunks * row_stride_chunk + st_col;
+  float* cbase = p.chunk_lse2 + ((int64_t)b * p.Hkv + kvh) * p.max_chunks * row_stride_chunk + (st_ok ? st_row : 0);
 
   // S (scores of the current tile) and P (its bf16 probabilities) live across the compute stages
   f32x4 s[RB][4];
@@ -591,6 +592,26 @@ __global__ __launch_bounds__(W * 64, (W == 8 ? 1 : 2)) void tree_attn_kernel(Att
   constexpr bool DEFER = CM != 2;
   float pend_v[NS];
   int pend_c = -1;
+  // With chunks of >= 64 slots (one value per row and chunk end) and token-row V, the values of a split
+  // collect in LDS instead and go out once, after the split's last tile: a store issued inside the tile
+  // loop would be waited for by the step's closing wait, and with HBM busy with the KV stream a store
+  // round trip is long.  The LDS holds kRingFloats values per work-group, kRingFloats / (32 * waves with
+  // rows) chunk ends per wave; the split length is capped to that (make_attn_plan), and a ring that still
+  // fills (it cannot under that cap) is written out at once.
+  constexpr bool RING = CM == 0 && VT == 0 && W == 4;
+  __shared__ float cring[RING ? kRingFloats : 1];
+  const int waves_used = min(W, (rows - row0 + RB * 16 - 1) / (RB * 16));
+  const int ring_cap = RING ? kRingFloats / (RB * 16 * (waves_used > 0 ? waves_used : 1)) : 0;
+  float* const cring_w = cring + (RING ? wave * ring_cap * RB * 16 : 0);   // this wave's slots (active waves)
+  const bool ring = RING;
+  int ring_n = 0, ring_c0 = 0;                      // values in the ring and the chunk of the first
+  auto ring_flush = [&]() __attribute__((always_inline)) {
+    for (int j = 0; j < ring_n; ++j) {
+      const float v = cring_w[j * RB * 16 + (lane & (RB * 16 - 1))];
+      if (st_ok) cbase[(int64_t)(ring_c0 + j) * row_stride_chunk] = v;
+    }
+    ring_n = 0;
+  };
   auto flush_chunks = [&]() __attribute__((always_inline)) {
     if (pend_c >= 0) {
 #pragma unroll
@@ -615,9 +636,16 @@ __global__ __launch_bounds__(W * 64, (W == 8 ? 1 : 2)) void tree_attn_kernel(Att
 #pragma unroll
         for (int rb = 1; rb < RB; ++rb)
           if (st_rb == rb) v = m_r[rb] + __builtin_amdgcn_logf(cacc[rb]);
-        pend_v[0] = v;
-        pend_c = c;
-        if (!DEFER) flush_chunks();
+        if (ring) {
+          if (ring_n == ring_cap) ring_flush();     // (not under the plan's split cap)
+          if (lane < RB * 16) cring_w[ring_n * RB * 16 + lane] = v;
+          ring_c0 = ring_n == 0 ? c : ring_c0;
+          ++ring_n;
+        } else {
+          pend_v[0] = v;
+          pend_c = c;
+          if (!DEFER) flush_chunks();
+        }
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) cacc[rb] = 0.f;
       }
@@ -697,6 +725,7 @@ __global__ __launch_bounds__(W * 64, (W == 8 ? 1 : 2)) void tree_attn_kernel(Att
   }
 
   flush_chunks();
+  if (ring && ring_n > 0) ring_flush();
   if (!wave_active) return;
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
@@ -1077,12 +1106,12 @@ __global__ __launch_bounds__(512, 1) void tree_attn_pipe_kernel(AttnParams p) {
   const int cs = p.chunk_size;
   const int cs_shift = (cs > 0 && (cs & (cs - 1)) == 0) ? __builtin_ctz((unsigned)cs) : -1;
   auto chunk_of = [&](int key) __attribute__((always_inline)) -> int { return cs_shift >= 0 ? key >> cs_shift : key / cs; };
-  const int row_stride_chunk = p.max_nodes * p.Hq;
+  // chunk partials: [sequence][KV head][chunk][row of the KV head] (a wave's 32 rows contiguous)
+  const int row_stride_chunk = p.max_nodes * G;
   const int st_rb = lg % RB;
   const int st_row = row0 + (wave * RB + st_rb) * 16 + lm;
   const bool st_ok = lg < RB && st_row < rows;
-  const int64_t st_col = st_ok ? (int64_t)(st_row / G) * p.Hq + kvh * G + st_row % G : 0;
-  float* cbase = p.chunk_lse2 + (int64_t)b * p.max_chunks * row_stride_chunk + st_col;
+  float* cbase = p.chunk_lse2 + ((int64_t)b * p.Hkv + kvh) * p.max_chunks * row_stride_chunk + (st_ok ? st_row : 0);
 
   // score halves (keys 0..31 and 32..63 of a tile) and probability halves, reused in turn
   f32x4 sA[RB][2], sB[RB][2];
@@ -1547,6 +1576,12 @@ bool make_attn_plan(const spec_tree_attention_args* a, int num_cus, AttnPlan* pl
     if (st < 8) st = 8;
   }
   if (st > cap_tiles) st = (int)cap_tiles;
+  if (a->chunk_size >= kTile && pl.waves == 4 && a->kv.v_layout != SPEC_V_DIM_MAJOR) {
+    // the 4-wave kernel keeps a split's chunk values in LDS: kRingFloats over 32 rows per wave with rows
+    const int waves_used = (int)ceil_div(rows < 128 ? rows : 128, 32);
+    const int64_t ring_tiles = (int64_t)(kRingFloats / (32 * waves_used)) * (a->chunk_size / kTile);
+    if (st > ring_tiles) st = (int)ring_tiles;
+  }
   st = (int)(ceil_div(st, align) * align);
   if (st > cap_tiles) st = (int)((cap_tiles / align) * align);
   if (st < 1) st = align;
