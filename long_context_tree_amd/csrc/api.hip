@@ -183,6 +183,8 @@ spec::AttnParams attn_params(const spec_tree_attention_args* a, const AttnLayout
   p.max_splits = l.plan.max_splits;
   p.row_groups = l.plan.row_groups;
   p.rows_pad = l.plan.rows_pad;
+  p.chunk_cs = l.plan.chunk_cs;
+  p.chunk_hs = l.plan.chunk_hs;
   char* ws = static_cast<char*>(a->workspace);
   p.part_o = reinterpret_cast<float*>(ws + l.plan.off_part_o);
   p.part_ml = reinterpret_cast<float*>(ws + l.plan.off_part_ml);
@@ -330,6 +332,8 @@ int spec_chunk_salience(const spec_chunk_salience_args* args, void* stream) {
   p.max_ctx = a->max_ctx_len;
   p.chunk_size = a->chunk_size;
   p.ws_max_chunks = l.ws_max_chunks;
+  p.chunk_cs = l.plan.chunk_cs;
+  p.chunk_hs = l.plan.chunk_hs;
   char* ws = static_cast<char*>(a->workspace);
   p.chunk_lse2 = reinterpret_cast<const float*>(ws + l.plan.off_chunk);
   p.lse2 = reinterpret_cast<const float*>(ws + l.plan.off_lse2);

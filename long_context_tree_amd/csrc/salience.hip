@@ -31,8 +31,8 @@ __device__ __forceinline__ void seq_bounds(const SalienceParams& p, int b, int* 
 // One work-group per (sequence, kChunksPerWG chunks): for each chunk, every row's exp2(chunk_lse2 -
 // lse2) is summed in a fixed order (each thread a fixed set of rows, then a butterfly in each wave, then
 // the four waves in order), scaled by 1 / rows and written or accumulated.  The attention workspace keeps
-// a chunk's rows as one run per KV head (row node * G + g is query head kvh * G + g); with G a multiple of
-// 4 the reads are 16-byte loads (four rows of one node, four consecutive query heads).
+// a chunk's rows, and the rows' final log2-sum-exps, as one run per KV head (row node * G + g is query
+// head kvh * G + g); with G a multiple of 4 the reads are 16-byte loads.
 __global__ __launch_bounds__(256) void salience_kernel(SalienceParams p) {
   __shared__ float red[4];
   const int b = blockIdx.y;
@@ -41,13 +41,11 @@ __global__ __launch_bounds__(256) void salience_kernel(SalienceParams p) {
   seq_bounds(p, b, &N, &L);
   const int nch = (L + p.chunk_size - 1) / p.chunk_size;
   const int rows = N * p.Hq;
-  const int stride = p.max_nodes * p.Hq;          // lse2 row stride of a sequence
   const int G = p.Hq / p.Hkv;
   const int NG = N * G;                           // rows of one KV head
-  const int RS = p.max_nodes * G;                 // chunk stride of the workspace rows of one KV head
-  const int64_t kstride = (int64_t)p.ws_max_chunks * RS;
-  const float* l2 = p.lse2 + (int64_t)b * stride;
-  const bool vec = (G & 3) == 0;
+  const int RS = p.max_nodes * G;                 // lse2 rows per KV head
+  const float* l2 = p.lse2 + (int64_t)b * p.Hkv * RS;
+  const bool vec = (G & 3) == 0;                  // (NG and RS are then multiples of 4)
   for (int k = 0; k < kChunksPerWG; ++k) {
     const int c = blockIdx.x * kChunksPerWG + k;
     if (c >= p.max_chunks) return;
@@ -56,40 +54,48 @@ __global__ __launch_bounds__(256) void salience_kernel(SalienceParams p) {
       if (tid == 0 && !p.accumulate) *dst = 0.f;
       continue;
     }
-    const float* x = p.chunk_lse2 + (int64_t)b * p.Hkv * kstride + (int64_t)c * RS;   // KV head 0's run
+    const float* x = p.chunk_lse2 + (int64_t)b * p.ws_max_chunks * p.Hkv * RS + (int64_t)c * p.chunk_cs;   // head 0
     const float prev = (p.accumulate && tid == 0) ? *dst : 0.f;   // read now, used after the reduction
     float acc = 0.f;
-    if (vec) {
-      // element i of the run of 4-row groups: KV head i / n4, rows 4 (i % n4) .. + 3
-      const int n4 = NG >> 2, nv = p.Hkv * n4;
-      auto at = [&](int i, float4& a, float4& m) {
-        const int h = i / n4, r = 4 * (i - h * n4);
-        a = *reinterpret_cast<const float4*>(x + h * kstride + r);
-        m = *reinterpret_cast<const float4*>(l2 + (r / G) * p.Hq + h * G + r % G);
-      };
+    // element (h, j) of the runs: KV head h, row (4-row group) j; each thread takes the flattened
+    // elements tid, tid + 256, ... in order, stepping (h, j) without a division
+    const int per = vec ? NG >> 2 : NG;           // elements per KV head
+    int h = 0, j = tid;
+    while (per > 0 && j >= per && h < p.Hkv) {
+      j -= per;
+      ++h;
+    }
+    auto next = [&]() {
+      j += 256;
+      while (j >= per && h < p.Hkv) {
+        j -= per;
+        ++h;
+      }
+    };
+    if (per > 0 && vec) {
       auto add4 = [&](const float4& a, const float4& m) {
         acc += (__builtin_amdgcn_exp2f(a.x - m.x) + __builtin_amdgcn_exp2f(a.y - m.y)) +
                (__builtin_amdgcn_exp2f(a.z - m.z) + __builtin_amdgcn_exp2f(a.w - m.w));
       };
-      int i = tid;
-      // four pairs of 16-byte loads in flight per round trip; the sum keeps the order i, i + 256, ...
-      for (; i + 3 * 256 < nv; i += 4 * 256) {
+      // up to four pairs of 16-byte loads in flight per round trip; the sum keeps the element order
+      while (h < p.Hkv) {
         float4 a[4], m[4];
+        int n = 0;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) at(i + 256 * j, a[j], m[j]);
+        for (int u = 0; u < 4; ++u) {
+          if (h < p.Hkv) {
+            a[u] = *reinterpret_cast<const float4*>(x + (int64_t)h * p.chunk_hs + 4 * j);
+            m[u] = *reinterpret_cast<const float4*>(l2 + h * RS + 4 * j);
+            n = u + 1;
+            next();
+          }
+        }
 #pragma unroll
-        for (int j = 0; j < 4; ++j) add4(a[j], m[j]);
+        for (int u = 0; u < 4; ++u)
+          if (u < n) add4(a[u], m[u]);
       }
-      for (; i < nv; i += 256) {
-        float4 a, m;
-        at(i, a, m);
-        add4(a, m);
-      }
-    } else {
-      for (int i = tid; i < rows; i += 256) {
-        const int h = i / NG, r = i - h * NG;
-        acc += __builtin_amdgcn_exp2f(x[h * kstride + r] - l2[(r / G) * p.Hq + h * G + r % G]);
-      }
+    } else if (per > 0) {
+      for (; h < p.Hkv; next()) acc += __builtin_amdgcn_exp2f(x[(int64_t)h * p.chunk_hs + j] - l2[h * RS + j]);
     }
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off);

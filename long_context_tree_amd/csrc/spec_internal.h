@@ -32,6 +32,8 @@ struct AttnPlan {
   int rows_wg = 0;       // query rows per work-group = waves * 32
   int row_groups = 0;    // work-groups sharing one KV range (rows of one KV head / rows_wg)
   int rows_pad = 0;      // row_groups * rows_wg
+  int chunk_cs = 0;      // chunk_lse2 strides (floats) of a chunk and of a KV head; see AttnParams
+  int chunk_hs = 0;
   int max_tiles = 0;     // ceil((max_ctx_len + max_nodes) / 64)
   int split_tiles = 0;   // tiles per split
   int max_splits = 0;    // ceil(max_tiles / split_tiles)
@@ -57,10 +59,13 @@ struct AttnParams {
   float scale_log2;      // scale * log2(e)
   int chunk_size, max_chunks;
   int split_tiles, max_splits, row_groups, rows_pad;
+  int chunk_cs, chunk_hs;  // chunk_lse2 strides (floats) of a chunk and of a KV head
   float* part_o;         // [batch][Hkv][max_splits][rows_pad][D]
   float* part_ml;        // [batch][Hkv][max_splits][rows_pad][2]  (running max in log2 units, sum)
-  float* chunk_lse2;     // [batch][Hkv][max_chunks][max_nodes * G]  (row node * G + g: query head kvh * G + g)
-  float* lse2;           // [batch][max_nodes * Hq]
+  float* chunk_lse2;     // per sequence max_chunks * Hkv * max_nodes * G floats; (chunk c, KV head h, row r =
+                         // node * G + g, query head h * G + g) at c * chunk_cs + h * chunk_hs + r: chunk-major
+                         // ([chunk][h][row]) when max_nodes * G is a multiple of 32, else [h][chunk][row]
+  float* lse2;           // [batch][Hkv][max_nodes * G], rows ordered as in chunk_lse2
   uint16_t* out;         // bf16 [total_nodes][Hq][D]
   float* lse;            // [total_nodes][Hq] natural log, nullable
 };
@@ -76,6 +81,7 @@ struct SalienceParams {
   const int32_t* node_offsets;
   int batch, Hq, Hkv, max_nodes, max_ctx, chunk_size;
   int ws_max_chunks;     // chunk stride of the attention workspace
+  int chunk_cs, chunk_hs;  // its strides (floats) of a chunk and of a KV head
   const float* chunk_lse2;
   const float* lse2;
   float* chunk_mass;     // [batch][max_chunks]

@@ -393,14 +393,15 @@ __global__ __launch_bounds__(W * 64, (W == 8 ? 1 : 2)) void tree_attn_kernel(Att
   // chunk of a context slot: a shift for power-of-two chunk sizes (no per-tile scalar division)
   const int cs_shift = (cs > 0 && (cs & (cs - 1)) == 0) ? __builtin_ctz((unsigned)cs) : -1;
   auto chunk_of = [&](int key) __attribute__((always_inline)) -> int { return cs_shift >= 0 ? key >> cs_shift : key / cs; };
-  // chunk partials: [sequence][KV head][chunk][row of the KV head], so that a wave's 32 rows of a chunk
-  // are 128 contiguous bytes, written by this work-group alone
-  const int row_stride_chunk = p.max_nodes * G;
+  // chunk partials (layout in AttnParams): a wave's 32 rows of a chunk are contiguous, in lines that
+  // only this work-group writes
+  const int row_stride_chunk = p.chunk_cs;
   // chunk-partial rows: the lanes of group lg store row block lg (RB consecutive 16-row blocks, one store)
   const int st_rb = lg % RB;
   const int st_row = row0 + (wave * RB + st_rb) * 16 + lm;
   const bool st_ok = lg < RB && st_row < rows;
-  float* cbase = p.chunk_lse2 + ((int64_t)b * p.Hkv + kvh) * p.max_chunks * row_stride_chunk + (st_ok ? st_row : 0);
+  float* cbase = p.chunk_lse2 + (int64_t)b * p.max_chunks * p.Hkv * p.max_nodes * G + (int64_t)kvh * p.chunk_hs +
+                 (st_ok ? st_row : 0);
 
   // S (scores of the current tile) and P (its bf16 probabilities) live across the compute stages
   f32x4 s[RB][4];
@@ -825,7 +826,7 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnParams p) {
   }
   if (lane == 0) {
     const float l2 = M + __builtin_amdgcn_logf(lsum);
-    p.lse2[(int64_t)b * per_seq + rem] = l2;
+    p.lse2[(int64_t)b * per_seq + (int64_t)kvh * p.max_nodes * p.G + row] = l2;   // [b][kvh][node * G + g]
     if (p.lse) p.lse[(int64_t)(n0 + node) * p.Hq + head] = l2 * 0.69314718055994530942f;
   }
 }
@@ -1106,12 +1107,13 @@ __global__ __launch_bounds__(512, 1) void tree_attn_pipe_kernel(AttnParams p) {
   const int cs = p.chunk_size;
   const int cs_shift = (cs > 0 && (cs & (cs - 1)) == 0) ? __builtin_ctz((unsigned)cs) : -1;
   auto chunk_of = [&](int key) __attribute__((always_inline)) -> int { return cs_shift >= 0 ? key >> cs_shift : key / cs; };
-  // chunk partials: [sequence][KV head][chunk][row of the KV head] (a wave's 32 rows contiguous)
-  const int row_stride_chunk = p.max_nodes * G;
+  // chunk partials (layout in AttnParams)
+  const int row_stride_chunk = p.chunk_cs;
   const int st_rb = lg % RB;
   const int st_row = row0 + (wave * RB + st_rb) * 16 + lm;
   const bool st_ok = lg < RB && st_row < rows;
-  float* cbase = p.chunk_lse2 + ((int64_t)b * p.Hkv + kvh) * p.max_chunks * row_stride_chunk + (st_ok ? st_row : 0);
+  float* cbase = p.chunk_lse2 + (int64_t)b * p.max_chunks * p.Hkv * p.max_nodes * G + (int64_t)kvh * p.chunk_hs +
+                 (st_ok ? st_row : 0);
 
   // score halves (keys 0..31 and 32..63 of a tile) and probability halves, reused in turn
   f32x4 sA[RB][2], sB[RB][2];
@@ -1596,7 +1598,16 @@ bool make_attn_plan(const spec_tree_attention_args* a, int num_cus, AttnPlan* pl
   pl.off_lse2 = off;
   off = align_up(off + sizeof(float) * (size_t)a->batch * a->max_nodes * a->num_q_heads, 256);
   pl.off_chunk = off;
-  off = align_up(off + sizeof(float) * (size_t)a->batch * pl.max_chunks * a->max_nodes * a->num_q_heads, 256);
+  {
+    // chunk partials: with whole 32-row blocks per KV head, chunk-major, so that a chunk's rows are one
+    // run for the salience pass and a wave's 32 rows one 128-byte line; otherwise KV-head-major, so that
+    // a work-group's values of consecutive chunks are one run (no line shared with another KV head)
+    const int rs = a->max_nodes * pl.G;
+    const bool chunk_major = rs % 32 == 0;
+    pl.chunk_cs = chunk_major ? a->num_kv_heads * rs : rs;
+    pl.chunk_hs = chunk_major ? rs : (pl.max_chunks > 0 ? pl.max_chunks : 1) * rs;
+  }
+  off = align_up(off + sizeof(float) * (size_t)a->batch * pl.max_chunks * a->num_kv_heads * a->max_nodes * pl.G, 256);
   pl.off_debug = off;                 // the debug record, last
   off += SPEC_DEBUG_RECORD_BYTES;
   pl.bytes = off;
