@@ -749,10 +749,15 @@ __global__ __launch_bounds__(W * 64, (W == 8 ? 1 : 2)) void tree_attn_kernel(Att
   }
 }
 
-// LSE merge of the split partials: one wave per (node, query head) row; each lane owns D/64 dims.
+// LSE merge of the split partials: one wave per (node, query head) row.  A split's D partial-output
+// values are read as D/4 16-byte pieces, so one wave-wide load covers 64/(D/4) splits and a lane keeps
+// up to kMergeLoads of them in flight: a row's splits arrive in a few round trips even when the rows are
+// few (a chain's 160 rows at 128K context hold ~60 splits each), which is what bounds this kernel there.
+constexpr int kMergeLoads = 16;
 template <int D>
 __global__ __launch_bounds__(256) void attn_merge_kernel(AttnParams p) {
-  constexpr int E = D / 64;
+  constexpr int F = D / 4;                        // lanes per split, four dims each
+  constexpr int P = 64 / F;                       // splits per wave-wide load
   const int lane = threadIdx.x & 63;
   const int64_t rid = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   const int per_seq = p.max_nodes * p.Hq;
@@ -772,6 +777,7 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnParams p) {
   const int kvh = head / p.G;
   const int row = node * p.G + head % p.G;
   const int64_t base0 = ((int64_t)b * p.Hkv + kvh) * p.max_splits * p.rows_pad + row;
+  const int sub = lane / F, d4 = lane % F;        // this lane's split within a load, and its four dims
 
   // every lane reads the (max, sum) of up to 64 splits at once; then per-split weights by shuffle
   float M = -INFINITY;
@@ -780,9 +786,7 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnParams p) {
   for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
 
   float lsum = 0.f;
-  float acc[E];
-#pragma unroll
-  for (int e = 0; e < E; ++e) acc[e] = 0.f;
+  f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
   for (int s0 = 0; s0 < nsp; s0 += 64) {
     const int s = s0 + lane;
     float w = 0.f, lw = 0.f;
@@ -795,34 +799,38 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnParams p) {
     for (int off = 32; off >= 1; off >>= 1) lw += __shfl_xor(lw, off);
     lsum += lw;
     const int cnt = min(64, nsp - s0);
-    int i = 0;
-    for (; i + 4 <= cnt; i += 4) {                // four splits in flight per iteration
-      float wv[4], x[4][E];
+    for (int i = 0; i < cnt; i += P * kMergeLoads) {
+      f32x4 x[kMergeLoads];
+      float wv[kMergeLoads];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        wv[u] = __shfl(w, i + u);
-        const int64_t bs = base0 + (int64_t)(s0 + i + u) * p.rows_pad;
-#pragma unroll
-        for (int e = 0; e < E; ++e) x[u][e] = p.part_o[bs * D + lane + 64 * e];
+      for (int u = 0; u < kMergeLoads; ++u) {
+        const int j = i + u * P + sub;            // the split (within this block of 64) of load u
+        wv[u] = __shfl(w, j & 63);
+        wv[u] = j < cnt ? wv[u] : 0.f;
+        x[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (j < cnt)
+          x[u] = *reinterpret_cast<const f32x4*>(&p.part_o[(base0 + (int64_t)(s0 + j) * p.rows_pad) * D + 4 * d4]);
       }
 #pragma unroll
-      for (int u = 0; u < 4; ++u)
-#pragma unroll
-        for (int e = 0; e < E; ++e) acc[e] += wv[u] * x[u][e];
-    }
-    for (; i < cnt; ++i) {
-      const float wi = __shfl(w, i);
-      const int64_t bs = base0 + (int64_t)(s0 + i) * p.rows_pad;
-#pragma unroll
-      for (int e = 0; e < E; ++e) acc[e] += wi * p.part_o[bs * D + lane + 64 * e];
+      for (int u = 0; u < kMergeLoads; ++u) acc += wv[u] * x[u];
     }
   }
-  const float inv = 1.0f / lsum;
-  uint16_t* op = p.out + ((int64_t)(n0 + node) * p.Hq + head) * D;
+  // the P lanes that hold the same four dims of different splits
 #pragma unroll
-  for (int e = 0; e < E; ++e) {
-    const __bf16 v = (__bf16)(acc[e] * inv);
-    op[lane + 64 * e] = __builtin_bit_cast(uint16_t, v);
+  for (int off = F; off < 64; off <<= 1) {
+    acc.x += __shfl_xor(acc.x, off);
+    acc.y += __shfl_xor(acc.y, off);
+    acc.z += __shfl_xor(acc.z, off);
+    acc.w += __shfl_xor(acc.w, off);
+  }
+  const float inv = 1.0f / lsum;
+  if (sub == 0) {
+    uint16_t* op = p.out + ((int64_t)(n0 + node) * p.Hq + head) * D + 4 * d4;
+    const uint32_t lo = __builtin_bit_cast(uint16_t, (__bf16)(acc.x * inv)) |
+                        ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)(acc.y * inv)) << 16);
+    const uint32_t hi = __builtin_bit_cast(uint16_t, (__bf16)(acc.z * inv)) |
+                        ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)(acc.w * inv)) << 16);
+    *reinterpret_cast<uint2*>(op) = make_uint2(lo, hi);
   }
   if (lane == 0) {
     const float l2 = M + __builtin_amdgcn_logf(lsum);
