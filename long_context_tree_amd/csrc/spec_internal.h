@@ -11,7 +11,7 @@
 namespace spec {
 
 constexpr int kTile = 64;          // KV slots per attention tile
-constexpr int kRingFloats = 2048;  // chunk values a 4-wave attention work-group holds for one split
+constexpr int kRingFloats = 2048;  // chunk values a 4-wave attention work-group holds between two writes
 constexpr int kMaxNodes = 256;     // tree nodes per sequence with ancestor bit masks (4 x 64 bits)
 constexpr int kMaxTreeNodes = SPEC_MAX_TREE_NODES;   // tree nodes per sequence otherwise
 constexpr int kSegment = 8192;     // vocabulary elements per argmax work-group

@@ -593,12 +593,11 @@ __global__ __launch_bounds__(W * 64, (W == 8 ? 1 : 2)) void tree_attn_kernel(Att
   constexpr bool DEFER = CM != 2;
   float pend_v[NS];
   int pend_c = -1;
-  // With chunks of >= 64 slots (one value per row and chunk end) and token-row V, the values of a split
-  // collect in LDS instead and go out once, after the split's last tile: a store issued inside the tile
-  // loop would be waited for by the step's closing wait, and with HBM busy with the KV stream a store
-  // round trip is long.  The LDS holds kRingFloats values per work-group, kRingFloats / (32 * waves with
-  // rows) chunk ends per wave; the split length is capped to that (make_attn_plan), and a ring that still
-  // fills (it cannot under that cap) is written out at once.
+  // With chunks of >= 64 slots (one value per row and chunk end) and token-row V, the values collect in
+  // LDS instead: a store issued inside a step would be waited for by the step's closing wait, and with HBM
+  // busy with the KV stream a store round trip is long.  The LDS holds kRingFloats values per work-group,
+  // kRingFloats / (32 * waves with rows) chunk ends per wave; a full ring is written out right after a
+  // step's closing wait, so that its stores land during the next step, and the rest after the split.
   constexpr bool RING = CM == 0 && VT == 0 && W == 4;
   __shared__ float cring[RING ? kRingFloats : 1];
   const int waves_used = min(W, (rows - row0 + RB * 16 - 1) / (RB * 16));
@@ -638,7 +637,7 @@ __global__ __launch_bounds__(W * 64, (W == 8 ? 1 : 2)) void tree_attn_kernel(Att
         for (int rb = 1; rb < RB; ++rb)
           if (st_rb == rb) v = m_r[rb] + __builtin_amdgcn_logf(cacc[rb]);
         if (ring) {
-          if (ring_n == ring_cap) ring_flush();     // (not under the plan's split cap)
+          if (ring_n == ring_cap) ring_flush();     // (not reached: a full ring goes out at the step's end)
           if (lane < RB * 16) cring_w[ring_n * RB * 16 + lane] = v;
           ring_c0 = ring_n == 0 ? c : ring_c0;
           ++ring_n;
@@ -718,7 +717,14 @@ __global__ __launch_bounds__(W * 64, (W == 8 ? 1 : 2)) void tree_attn_kernel(Att
       stage_pv(t, cur[1], pb);
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this thread's loads of the next tile landed
-    __syncthreads();
+    if constexpr (RING) {
+      // a full ring goes out here, after the wait: its stores have a whole step to land before the next
+      // step's wait.  The barrier waits for LDS only (a work-group fence would also wait for the stores).
+      if (ring_n == ring_cap) ring_flush();
+      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    } else {
+      __syncthreads();
+    }
   };
   for (int t = t_begin; t < t_end; t += 2) {
     step(t, kv_a, kv_b);
@@ -1586,12 +1592,6 @@ bool make_attn_plan(const spec_tree_attention_args* a, int num_cus, AttnPlan* pl
     if (st < 8) st = 8;
   }
   if (st > cap_tiles) st = (int)cap_tiles;
-  if (a->chunk_size >= kTile && pl.waves == 4 && a->kv.v_layout != SPEC_V_DIM_MAJOR) {
-    // the 4-wave kernel keeps a split's chunk values in LDS: kRingFloats over 32 rows per wave with rows
-    const int waves_used = (int)ceil_div(rows < 128 ? rows : 128, 32);
-    const int64_t ring_tiles = (int64_t)(kRingFloats / (32 * waves_used)) * (a->chunk_size / kTile);
-    if (st > ring_tiles) st = (int)ring_tiles;
-  }
   st = (int)(ceil_div(st, align) * align);
   if (st > cap_tiles) st = (int)((cap_tiles / align) * align);
   if (st < 1) st = align;
