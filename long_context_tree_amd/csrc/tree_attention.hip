@@ -759,7 +759,7 @@ __global__ __launch_bounds__(W * 64, (W == 8 ? 1 : 2)) void tree_attn_kernel(Att
 // values are read as D/4 16-byte pieces, so one wave-wide load covers 64/(D/4) splits and a lane keeps
 // up to kMergeLoads of them in flight: a row's splits arrive in a few round trips even when the rows are
 // few (a chain's 160 rows at 128K context hold ~60 splits each), which is what bounds this kernel there.
-constexpr int kMergeLoads = 16;
+constexpr int kMergeLoads = 8;
 template <int D>
 __global__ __launch_bounds__(256) void attn_merge_kernel(AttnParams p) {
   constexpr int F = D / 4;                        // lanes per split, four dims each
