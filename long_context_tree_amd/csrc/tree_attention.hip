@@ -595,22 +595,43 @@ __global__ __launch_bounds__(W * 64, (W == 8 ? 1 : 2)) void tree_attn_kernel(Att
   int pend_c = -1;
   // With chunks of >= 64 slots (one value per row and chunk end) and token-row V, the values collect in
   // LDS instead: a store issued inside a step would be waited for by the step's closing wait, and with HBM
-  // busy with the KV stream a store round trip is long.  The LDS holds kRingFloats values per work-group,
-  // kRingFloats / (32 * waves with rows) chunk ends per wave; a full ring is written out right after a
-  // step's closing wait, so that its stores land during the next step, and the rest after the split.
+  // busy with the KV stream a store round trip is long.  The LDS ring holds kRingFloats values,
+  // [chunk end][row - row0] with RS rows per chunk end (the work-group holds every row of its KV head:
+  // RS <= 128), i.e. in the layout's order of a chunk's rows.  When it is full, every thread of the
+  // work-group writes it out after a step's closing barrier, 16 bytes per store where the rows allow, and
+  // a second barrier keeps the next appends behind those reads; the stores land during the next step.
+  // The rest goes out after the split.
   constexpr bool RING = CM == 0 && VT == 0 && W == 4;
-  __shared__ float cring[RING ? kRingFloats : 1];
-  const int waves_used = min(W, (rows - row0 + RB * 16 - 1) / (RB * 16));
-  const int ring_cap = RING ? kRingFloats / (RB * 16 * (waves_used > 0 ? waves_used : 1)) : 0;
-  float* const cring_w = cring + (RING ? wave * ring_cap * RB * 16 : 0);   // this wave's slots (active waves)
-  const bool ring = RING;
-  int ring_n = 0, ring_c0 = 0;                      // values in the ring and the chunk of the first
+  __shared__ __attribute__((aligned(16))) float cring[RING ? kRingFloats : 4];
+  const int RS = p.max_nodes * G;                   // a chunk's rows of one KV head in the layout
+  const int ring_cap = RING ? kRingFloats / RS : 0; // chunk ends the ring holds (>= 16)
+  int ring_n = 0, ring_c0 = 0;                      // chunk ends in the ring, the first one's chunk
+  float* const gbase = p.chunk_lse2 + (int64_t)b * p.max_chunks * p.Hkv * p.max_nodes * G + (int64_t)kvh * p.chunk_hs + row0;
+  // (all threads) the ring's ring_n chunk ends -> chunk partials; rows past the sequence's own are not
+  // written
   auto ring_flush = [&]() __attribute__((always_inline)) {
-    for (int j = 0; j < ring_n; ++j) {
-      const float v = cring_w[j * RB * 16 + (lane & (RB * 16 - 1))];
-      if (st_ok) cbase[(int64_t)(ring_c0 + j) * row_stride_chunk] = v;
+    const float* src = cring;
+    const int n = ring_n * RS, nr = rows - row0;
+    if ((RS & 3) == 0 && (nr & 3) == 0) {
+      for (int i = 4 * tid; i < n; i += 4 * NT) {
+        const int j = i / RS, r = i - j * RS;
+        const f32x4 v = *reinterpret_cast<const f32x4*>(src + i);
+        if (r < nr) *reinterpret_cast<f32x4*>(gbase + (int64_t)(ring_c0 + j) * row_stride_chunk + r) = v;
+      }
+    } else {
+      for (int i = tid; i < n; i += NT) {
+        const int j = i / RS, r = i - j * RS;
+        if (r < nr) gbase[(int64_t)(ring_c0 + j) * row_stride_chunk + r] = src[i];
+      }
     }
     ring_n = 0;
+  };
+  // the chunk that tile t closes (its last context tile), or -1
+  auto close_of = [&](int t) __attribute__((always_inline)) -> int {
+    const int key0 = t * kTile;
+    if (cs <= 0 || key0 >= L) return -1;
+    const int c = chunk_of(key0);
+    return key0 + kTile >= min((c + 1) * cs, L) ? c : -1;
   };
   auto flush_chunks = [&]() __attribute__((always_inline)) {
     if (pend_c >= 0) {
@@ -636,11 +657,9 @@ __global__ __launch_bounds__(W * 64, (W == 8 ? 1 : 2)) void tree_attn_kernel(Att
 #pragma unroll
         for (int rb = 1; rb < RB; ++rb)
           if (st_rb == rb) v = m_r[rb] + __builtin_amdgcn_logf(cacc[rb]);
-        if (ring) {
-          if (ring_n == ring_cap) ring_flush();     // (not reached: a full ring goes out at the step's end)
-          if (lane < RB * 16) cring_w[ring_n * RB * 16 + lane] = v;
-          ring_c0 = ring_n == 0 ? c : ring_c0;
-          ++ring_n;
+        if constexpr (RING) {
+          // (the step's end counts the chunk end, in every wave)
+          if (st_ok) cring[ring_n * RS + (st_row - row0)] = v;
         } else {
           pend_v[0] = v;
           pend_c = c;
@@ -718,10 +737,19 @@ __global__ __launch_bounds__(W * 64, (W == 8 ? 1 : 2)) void tree_attn_kernel(Att
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this thread's loads of the next tile landed
     if constexpr (RING) {
-      // a full ring goes out here, after the wait: its stores have a whole step to land before the next
-      // step's wait.  The barrier waits for LDS only (a work-group fence would also wait for the stores).
-      if (ring_n == ring_cap) ring_flush();
+      const int c = close_of(t);
+      if (c >= 0) {
+        ring_c0 = ring_n == 0 ? c : ring_c0;
+        ++ring_n;
+      }
+      // the barriers wait for LDS only (a work-group fence would also wait for the ring's stores); after
+      // the first the step's chunk ends are in the ring, and a full ring goes out, to land during the
+      // next step
       asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      if (ring_n == ring_cap) {
+        ring_flush();
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      }
     } else {
       __syncthreads();
     }
@@ -732,7 +760,7 @@ __global__ __launch_bounds__(W * 64, (W == 8 ? 1 : 2)) void tree_attn_kernel(Att
   }
 
   flush_chunks();
-  if (ring && ring_n > 0) ring_flush();
+  if (RING && ring_n > 0) ring_flush();
   if (!wave_active) return;
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
