@@ -1617,7 +1617,13 @@ bool make_attn_plan(const spec_tree_attention_args* a, int num_cus, AttnPlan* pl
     const int64_t target = (int64_t)(num_cus > 0 ? num_cus : 256) * (pl.waves == 8 ? 1 : 2);
     int64_t want_splits = ceil_div(target, ranges);
     st = (int)ceil_div(pl.max_tiles, want_splits < 1 ? 1 : want_splits);
-    if (st < 8) st = 8;
+    if (st < 8) {
+      // short contexts: 8 tiles per split, unless the work-groups would then fill less than half of that
+      // round; the split length is then halved (down to 2 tiles) until they do, since a split's tiles run
+      // one after another (a 4K-token chain: 18 against 24 us)
+      st = 8;
+      while (st > 2 && ranges * ceil_div(pl.max_tiles, st) < target / 2) st /= 2;
+    }
   }
   if (st > cap_tiles) st = (int)cap_tiles;
   st = (int)(ceil_div(st, align) * align);
