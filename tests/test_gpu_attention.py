@@ -287,6 +287,40 @@ def test_rising_scores_rescale_mid_split(chunk, split, nodes, v_layout):
         compare_mass(mass.cpu().numpy().astype(np.float64)[0, :len(m_ref[0])], m_ref[0])
 
 
+@pytest.mark.parametrize("case_name,split", [("n32_g4", 64), ("chain_g3", 160), ("ragged_g2", 150), ("n32_g4", 0)])
+def test_chunk_ring_write_outs(case_name, split):
+    """Narrow trees (4-wave work-groups, token-row V, 64-slot chunks) collect a split's chunk values in an
+    LDS ring of 2048 values, [chunk end][row], and write it out whenever it fills: splits longer than
+    2048 / rows chunk ends.  n32_g4: 128 rows per KV head, 16 chunk ends per write-out, several inside each
+    64-tile split (16-byte stores).  chain_g3: G = 3, 15 rows (4-byte stores: rows not a multiple of 4),
+    136 chunk ends per write-out.  ragged_g2: max_nodes 8 with a 5-node tree, 16 rows per chunk end in the
+    layout but 10 of the sequence's own (4-byte stores, rows past the sequence's not written)."""
+    r = synth.rng_for(107, 0, 0)
+    if case_name == "n32_g4":
+        case = synth.attention_case(107, ctx_lens=[6000], trees=[synth.random_tree(r, 32, 6)], num_q_heads=32,
+                                    num_kv_heads=8, head_dim=128)
+    elif case_name == "chain_g3":
+        case = synth.attention_case(108, ctx_lens=[12000], trees=[synth.chain_tree(5)], num_q_heads=6,
+                                    num_kv_heads=2, head_dim=64)
+    else:
+        case = synth.attention_case(109, ctx_lens=[9000, 7000], trees=[synth.random_tree(r, 8, 3),
+                                                                       synth.random_tree(r, 5, 3)],
+                                    num_q_heads=4, num_kv_heads=2, head_dim=128)
+    print(f"case=ring {case_name} split={split}", flush=True)
+    out, lse, h, t = run_attention(case, chunk_size=64, split_tiles=split)
+    import long_context_tree_amd as lt
+    n_ch = -(-int(case.ctx_lens.max()) // 64)
+    mass = torch.full((len(case.ctx_lens), n_ch), 7.0, dtype=torch.float32, device=dev())
+    lt.chunk_salience(h, mass)
+    torch.cuda.synchronize()
+    o_ref, l_ref, m_ref = oracle_attention(case, 64)
+    compare_out(out, lse, o_ref, l_ref)
+    mg = mass.cpu().numpy().astype(np.float64)
+    for b, mr in enumerate(m_ref):
+        compare_mass(mg[b, :len(mr)], mr)
+        assert (mg[b, len(mr):] == 0).all()
+
+
 @pytest.mark.parametrize("ctx,k,kind,width", [
     (32768, 256, "ties", 0), (32768, 1, "ties", 0), (32768, 256, "equal", 0), (1600, 256, "ties", 0),
     (32768, 256, "zeros", 0), (32768, 200, "distinct", 0),
