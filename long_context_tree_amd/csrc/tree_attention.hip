@@ -783,17 +783,20 @@ __global__ __launch_bounds__(W * 64, (W == 8 ? 1 : 2)) void tree_attn_kernel(Att
   }
 }
 
-// LSE merge of the split partials: one wave per (node, query head) row.  A split's D partial-output
+// LSE merge of the split partials: one wave per (node, query head) row, or (SPLIT4, for calls with few
+// rows) one work-group per row whose four waves take a quarter of the splits each and combine through
+// LDS, so that a few rows with many splits still spread over the CUs.  A split's D partial-output
 // values are read as D/4 16-byte pieces, so one wave-wide load covers 64/(D/4) splits and a lane keeps
 // up to kMergeLoads of them in flight: a row's splits arrive in a few round trips even when the rows are
 // few (a chain's 160 rows at 128K context hold ~60 splits each), which is what bounds this kernel there.
 constexpr int kMergeLoads = 8;
-template <int D>
+template <int D, bool SPLIT4>
 __global__ __launch_bounds__(256) void attn_merge_kernel(AttnParams p) {
   constexpr int F = D / 4;                        // lanes per split, four dims each
   constexpr int P = 64 / F;                       // splits per wave-wide load
-  const int lane = threadIdx.x & 63;
-  const int64_t rid = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t rid = SPLIT4 ? (int64_t)blockIdx.x : (int64_t)blockIdx.x * 4 + wave;   // (SPLIT4: uniform
+                                                                                        // in the work-group)
   const int per_seq = p.max_nodes * p.Hq;
   const int b = (int)(rid / per_seq);
   if (b >= p.batch) return;
@@ -812,19 +815,25 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnParams p) {
   const int row = node * p.G + head % p.G;
   const int64_t base0 = ((int64_t)b * p.Hkv + kvh) * p.max_splits * p.rows_pad + row;
   const int sub = lane / F, d4 = lane % F;        // this lane's split within a load, and its four dims
+  int s_lo = 0, s_hi = nsp;                       // this wave's splits
+  if (SPLIT4) {
+    const int q = (nsp + 3) / 4;
+    s_lo = min(nsp, wave * q);
+    s_hi = min(nsp, s_lo + q);
+  }
 
   // every lane reads the (max, sum) of up to 64 splits at once; then per-split weights by shuffle
   float M = -INFINITY;
-  for (int s = lane; s < nsp; s += 64) M = fmaxf(M, p.part_ml[(base0 + (int64_t)s * p.rows_pad) * 2]);
+  for (int s = s_lo + lane; s < s_hi; s += 64) M = fmaxf(M, p.part_ml[(base0 + (int64_t)s * p.rows_pad) * 2]);
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
 
   float lsum = 0.f;
   f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-  for (int s0 = 0; s0 < nsp; s0 += 64) {
+  for (int s0 = s_lo; s0 < s_hi; s0 += 64) {
     const int s = s0 + lane;
     float w = 0.f, lw = 0.f;
-    if (s < nsp) {
+    if (s < s_hi) {
       const int64_t bs = base0 + (int64_t)s * p.rows_pad;
       w = __builtin_amdgcn_exp2f(p.part_ml[bs * 2] - M);
       lw = w * p.part_ml[bs * 2 + 1];
@@ -832,7 +841,7 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnParams p) {
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) lw += __shfl_xor(lw, off);
     lsum += lw;
-    const int cnt = min(64, nsp - s0);
+    const int cnt = min(64, s_hi - s0);
     for (int i = 0; i < cnt; i += P * kMergeLoads) {
       f32x4 x[kMergeLoads];
       float wv[kMergeLoads];
@@ -856,6 +865,29 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnParams p) {
     acc.y += __shfl_xor(acc.y, off);
     acc.z += __shfl_xor(acc.z, off);
     acc.w += __shfl_xor(acc.w, off);
+  }
+  if (SPLIT4) {
+    // the four waves' (max, sum, O) against the largest max (a wave without splits has max -inf and
+    // weight 0)
+    __shared__ float m_s[4], l_s[4];
+    __shared__ f32x4 a_s[4][F];
+    if (lane == 0) {
+      m_s[wave] = M;
+      l_s[wave] = lsum;
+    }
+    if (sub == 0) a_s[wave][d4] = acc;
+    __syncthreads();
+    if (wave != 0) return;
+    const float Mt = fmaxf(fmaxf(m_s[0], m_s[1]), fmaxf(m_s[2], m_s[3]));
+    lsum = 0.f;
+    acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const float sc = m_s[w] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_s[w] - Mt);
+      lsum += sc * l_s[w];
+      acc += sc * a_s[w][d4];
+    }
+    M = Mt;
   }
   const float inv = 1.0f / lsum;
   if (sub == 0) {
@@ -1570,7 +1602,11 @@ hipError_t launch_d_w(const AttnParams& p, const AttnPlan& plan, hipStream_t s) 
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t rows = (int64_t)p.batch * p.max_nodes * p.Hq;
-  hipLaunchKernelGGL((attn_merge_kernel<D>), dim3((unsigned)ceil_div(rows, 4)), dim3(256), 0, s, p);
+  // few rows (under 1024: fewer than 256 work-groups of four rows): one work-group per row
+  if (rows < 1024)
+    hipLaunchKernelGGL((attn_merge_kernel<D, true>), dim3((unsigned)rows), dim3(256), 0, s, p);
+  else
+    hipLaunchKernelGGL((attn_merge_kernel<D, false>), dim3((unsigned)ceil_div(rows, 4)), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 
