@@ -918,8 +918,8 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnParams p) {
 // one half inside:
 //   B1: QK^T of (t, half 1) and P.V + chunk sums of (t-1, half 1)  |  exps of (t, half 0)
 //   B2: P.V + chunk sums of (t, half 0) and QK^T of (t+1, half 0)  |  exps of (t, half 1)
-// so tile t+1's K tile must be in LDS during tile t: K and V each have three LDS buffers (K(t+2) and
-// V(t+1) load while tile t is computed).  Scores, probabilities and accumulators keep the registers of
+// so tile t+1's K tile must be in LDS during tile t.  K and V each have four LDS buffers: K(t+3) and
+// V(t+2) load while tile t is computed, two steps ahead of their first use.  Scores, probabilities and accumulators keep the registers of
 // tree_attn_kernel (the two score halves and the two probability halves are reused in turn).  The
 // online softmax, the lazy rescaling and the chunk bookkeeping are those of tree_attn_kernel, taken per
 // half-tile.  Every tile runs the same two blocks: a tile that holds tree slots masks its scores between
