@@ -83,21 +83,26 @@ __device__ __forceinline__ void buffer_load_lds16(const void* base, uint32_t num
 // compile-time switch: with a run-time flag the compiler versioned the tile loop on it, and that
 // build gave wrong results on the bit-mask path as well (cause not found), so the two mask sources are
 // separate instantiations.
-template <int D, int W, int RB, int CM, int VT, int PRE>
+// SW: (4-wave work-groups, token-row V, 64-slot chunks, <= 64 rows per KV head) waves 1 and 2 load the
+// tiles and wave 3 alone writes the chunk ring out.  Wave 3 issues no loads, so no step waits for its
+// stores: with HBM busy with the KV stream, a store round trip is longer than a step.
+template <int D, int W, int RB, int CM, int VT, int PRE, int SW = 0>
 __global__ __launch_bounds__(W * 64, (W == 8 ? 1 : 2)) void tree_attn_kernel(AttnParams p) {
+  static_assert(!SW || (W == 4 && CM == 0 && VT == 0), "the store wave is a variant of the 4-wave chunk ring");
   constexpr int NT = W * 64;
+  constexpr int NLW = SW ? 2 : W;               // waves that load tiles
   constexpr int ROWS_WG = W * RB * 16;
   constexpr int KS = D / 32;                    // k-steps of the QK^T product
   constexpr int NB = D / 16;                    // 16-dim output blocks
   constexpr int CPR = D / 8;                    // 16-byte chunks per K/V row
   constexpr int TILE_EL = kTile * D;            // bf16 elements of one K (or V) tile
-  constexpr int LOADS = 2 * kTile * CPR / NT;   // 16-byte direct-to-LDS loads per thread and tile (K and V)
+  constexpr int LOADS = 2 * kTile * CPR / (NLW * 64);   // 16-byte direct-to-LDS loads per loading thread and tile
   constexpr int KB = kTile * CPR / 64;          // 1 KiB blocks of a K (or V) tile
   constexpr int NS = CM == 2 ? 4 : (CM == 1 ? 2 : 1);   // row-sum fragments per row block
   // ancestor masks: a 4-wave work-group holds <= 128 rows, hence <= 128 nodes (two 64-bit words)
   constexpr int ANC_N = W == 8 ? kMaxNodes : 128;
   constexpr int ANC_W = ANC_N / 64;
-  static_assert((2 * kTile * CPR) % NT == 0 && (kTile * CPR) % 64 == 0, "tile must split evenly");
+  static_assert((2 * kTile * CPR) % (NLW * 64) == 0 && (kTile * CPR) % 64 == 0, "tile must split evenly");
 
   // K and V tiles, double-buffered, rows of D bf16 without padding; the 16-byte chunk c of key r sits at
   // position c ^ swz(r) of its row, which keeps both the MFMA operand reads and the transposing V reads
@@ -164,6 +169,8 @@ __global__ __launch_bounds__(W * 64, (W == 8 ? 1 : 2)) void tree_attn_kernel(Att
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: keeps load descriptors scalar
+  const bool loader = !SW || wave == 1 || wave == 2;            // this wave loads tiles
+  const int lwave = SW ? (wave == 2 ? 1 : 0) : wave;            // its place among the loading waves
   const int lm = lane & 15, lg = lane >> 4;
   const int pshift = p.page_shift;
 
@@ -226,8 +233,8 @@ __global__ __launch_bounds__(W * 64, (W == 8 ? 1 : 2)) void tree_attn_kernel(Att
   __syncthreads();                                  // page ids visible before the first tile load
 
   // ---- tile loads: straight from HBM into LDS, 16 bytes per lane, lanes in LDS order ----
-  // Load i of a wave fills LDS chunks [(wave * LOADS + i) * 64, +64) of the K tile (first half of the
-  // loads) or of the V tile: 64 / CPR consecutive keys of one page (page sizes >= 8), so each load is a
+  // Load i of loading wave lwave fills LDS chunks [(lwave * LOADS + i) * 64, +64) of the K tile (first
+  // half of the loads) or of the V tile: 64 / CPR consecutive keys of one page (page sizes >= 8), so each load is a
   // buffer load through a scalar descriptor of that page and each lane only adds a fixed offset (its
   // key's row and its swizzled source chunk).  The descriptor's byte range ends at the sequence's last
   // slot in the page, so slots past the sequence (and pages with an invalid id: empty range) read zeros.
@@ -246,7 +253,7 @@ __global__ __launch_bounds__(W * 64, (W == 8 ? 1 : 2)) void tree_attn_kernel(Att
   uint32_t ld_voff[LOADS];                          // bytes from the page (or, for pages > 64 slots, tile) start
 #pragma unroll
   for (int i = 0; i < LOADS; ++i) {
-    const int blk = wave * LOADS + i;
+    const int blk = lwave * LOADS + i;
     if (VT && blk >= KB) {
       // V load u = blk - KB fills 1 KiB of page block u >> v_ipp_l: dims from (u mod loads per page) * 512 / pe
       const int u = blk - KB;
@@ -268,7 +275,7 @@ __global__ __launch_bounds__(W * 64, (W == 8 ? 1 : 2)) void tree_attn_kernel(Att
   constexpr int KPL = 64 / CPR;                     // keys per load
   constexpr int GL = 16 / KPL < LOADS ? 16 / KPL : LOADS;   // loads per 16-key group
   static_assert(KB % LOADS == 0 && LOADS % GL == 0, "a wave's loads must be all K or all V, in whole groups");
-  const bool wave_is_v = wave * LOADS >= KB;
+  const bool wave_is_v = lwave * LOADS >= KB;
   const bool grouped = !(VT && wave_is_v) && pshift >= 4;
   auto issue_tile = [&](int t, uint16_t (*kv)[TILE_EL]) __attribute__((always_inline)) {
     const int key0 = t * kTile;
@@ -276,14 +283,14 @@ __global__ __launch_bounds__(W * 64, (W == 8 ? 1 : 2)) void tree_attn_kernel(Att
       int pgs[LOADS / GL];
 #pragma unroll
       for (int g = 0; g < LOADS / GL; ++g) {      // page ids of the groups (LDS reads issued together)
-        const int key_w = key0 + (((wave * LOADS + g * GL) * 64) % (kTile * CPR)) / CPR;
+        const int key_w = key0 + (((lwave * LOADS + g * GL) * 64) % (kTile * CPR)) / CPR;
         int pi = (key_w >> pshift) - pg_first;
         pi = pi < pg_count ? pi : pg_count - 1;
         pgs[g] = pg_lds[pi];
       }
 #pragma unroll
       for (int g = 0; g < LOADS / GL; ++g) {
-        const int key_w = key0 + (((wave * LOADS + g * GL) * 64) % (kTile * CPR)) / CPR;
+        const int key_w = key0 + (((lwave * LOADS + g * GL) * 64) % (kTile * CPR)) / CPR;
         const int pg = __builtin_amdgcn_readfirstlane(pgs[g]);
         const int first_key = pshift > 6 ? key0 : (key_w & ~pmask);
         const int span = pshift > 6 ? kTile : (1 << pshift);
@@ -294,7 +301,7 @@ __global__ __launch_bounds__(W * 64, (W == 8 ? 1 : 2)) void tree_attn_kernel(Att
         const uint16_t* b = (wave_is_v ? vbase : kbase) + (uint64_t)(uint32_t)(pg < 0 ? 0 : pg) * (uint32_t)p.page_stride + row0;
 #pragma unroll
         for (int i = g * GL; i < (g + 1) * GL; ++i)
-          buffer_load_lds16(b, (uint32_t)valid * tstride * 2u, &kv[wave_is_v ? 1 : 0][((wave * LOADS + i) % KB) * 512],
+          buffer_load_lds16(b, (uint32_t)valid * tstride * 2u, &kv[wave_is_v ? 1 : 0][((lwave * LOADS + i) % KB) * 512],
                             ld_voff[i]);
       }
       return;
@@ -303,7 +310,7 @@ __global__ __launch_bounds__(W * 64, (W == 8 ? 1 : 2)) void tree_attn_kernel(Att
     int pgv[LOADS];
 #pragma unroll
     for (int i = 0; i < LOADS; ++i) {
-      const int blk = wave * LOADS + i;
+      const int blk = lwave * LOADS + i;
       const int key_w = (VT && blk >= KB) ? key0 + (((blk - KB) >> v_ipp_l) << lpe) : key0 + ((blk * 64) % (kTile * CPR)) / CPR;
       int pi = (key_w >> pshift) - pg_first;
       pi = pi < pg_count ? pi : pg_count - 1;
@@ -311,7 +318,7 @@ __global__ __launch_bounds__(W * 64, (W == 8 ? 1 : 2)) void tree_attn_kernel(Att
     }
 #pragma unroll
     for (int i = 0; i < LOADS; ++i) {
-      const int blk = wave * LOADS + i;
+      const int blk = lwave * LOADS + i;
       const bool is_v = blk >= KB;
       uint16_t* dst = &kv[is_v ? 1 : 0][(blk % KB) * 512];
       const int pg = __builtin_amdgcn_readfirstlane(pgv[i]);
@@ -612,14 +619,15 @@ __global__ __launch_bounds__(W * 64, (W == 8 ? 1 : 2)) void tree_attn_kernel(Att
   auto ring_flush = [&]() __attribute__((always_inline)) {
     const float* src = cring;
     const int n = ring_n * RS, nr = rows - row0;
+    const int ft = SW ? lane : tid, fn = SW ? 64 : NT;   // the writing threads: the store wave, or all
     if ((RS & 3) == 0 && (nr & 3) == 0) {
-      for (int i = 4 * tid; i < n; i += 4 * NT) {
+      for (int i = 4 * ft; i < n; i += 4 * fn) {
         const int j = i / RS, r = i - j * RS;
         const f32x4 v = *reinterpret_cast<const f32x4*>(src + i);
         if (r < nr) *reinterpret_cast<f32x4*>(gbase + (int64_t)(ring_c0 + j) * row_stride_chunk + r) = v;
       }
     } else {
-      for (int i = tid; i < n; i += NT) {
+      for (int i = ft; i < n; i += fn) {
         const int j = i / RS, r = i - j * RS;
         if (r < nr) gbase[(int64_t)(ring_c0 + j) * row_stride_chunk + r] = src[i];
       }
@@ -693,11 +701,11 @@ __global__ __launch_bounds__(W * 64, (W == 8 ? 1 : 2)) void tree_attn_kernel(Att
   };
 
   // one barrier per tile: tile t+1 loads straight into the other buffer while tile t is computed
-  issue_tile(t_begin, kv_a);
+  if (loader) issue_tile(t_begin, kv_a);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   auto step = [&](int t, uint16_t (*cur)[TILE_EL], uint16_t (*nxt)[TILE_EL]) __attribute__((always_inline)) {
-    if (t + 1 < t_end) issue_tile(t + 1, nxt);
+    if (loader && t + 1 < t_end) issue_tile(t + 1, nxt);
     flush_chunks();
     if (VT && t * kTile + kTile > keys) {
       // the sequence's last tile: its dim-major V slots past the sequence hold whatever the page held
@@ -735,7 +743,8 @@ __global__ __launch_bounds__(W * 64, (W == 8 ? 1 : 2)) void tree_attn_kernel(Att
       for (int rb = 0; rb < RB; ++rb) l_r[rb] += esum[rb];
       stage_pv(t, cur[1], pb);
     }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this thread's loads of the next tile landed
+    // this thread's loads of the next tile landed (the store wave has none, and does not wait for its stores)
+    if (!SW || wave != 3) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     if constexpr (RING) {
       const int c = close_of(t);
       if (c >= 0) {
@@ -747,7 +756,8 @@ __global__ __launch_bounds__(W * 64, (W == 8 ? 1 : 2)) void tree_attn_kernel(Att
       // next step
       asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
       if (ring_n == ring_cap) {
-        ring_flush();
+        if (!SW || wave == 3) ring_flush();
+        ring_n = 0;
         asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
       }
     } else {
@@ -760,7 +770,7 @@ __global__ __launch_bounds__(W * 64, (W == 8 ? 1 : 2)) void tree_attn_kernel(Att
   }
 
   flush_chunks();
-  if (RING && ring_n > 0) ring_flush();
+  if (RING && ring_n > 0 && (!SW || wave == 3)) ring_flush();
   if (!wave_active) return;
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
@@ -1595,6 +1605,14 @@ hipError_t launch_d_w(const AttnParams& p, const AttnPlan& plan, hipStream_t s) 
       if (p.chunk_size > 0) grp ? go(tree_attn_pipe_kernel<0, 1, 1>) : go(tree_attn_pipe_kernel<0, 1, 0>);
       else grp ? go(tree_attn_pipe_kernel<0, 0, 1>) : go(tree_attn_pipe_kernel<0, 0, 0>);
     }
+  } else if constexpr (W == 4 && CM == 0 && VT == 0) {
+    // <= 64 rows per KV head (one or two waves with rows): the variant with a store wave
+    auto go = [&](auto kern) { hipLaunchKernelGGL(kern, dim3(grid), dim3(W * 64), 0, s, p); };
+    const bool sw = p.max_nodes * p.G <= 64;
+    if (p.subtree_end)
+      sw ? go(tree_attn_kernel<D, W, RB, CM, VT, 1, 1>) : go(tree_attn_kernel<D, W, RB, CM, VT, 1, 0>);
+    else
+      sw ? go(tree_attn_kernel<D, W, RB, CM, VT, 0, 1>) : go(tree_attn_kernel<D, W, RB, CM, VT, 0, 0>);
   } else if (p.subtree_end)
     hipLaunchKernelGGL((tree_attn_kernel<D, W, RB, CM, VT, 1>), dim3(grid), dim3(W * 64), 0, s, p);
   else
