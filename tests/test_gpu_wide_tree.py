@@ -46,6 +46,31 @@ def test_interval_mask_equals_bit_masks(v_layout, chunk):
     compare_out(b[0], b[1], o_ref, l_ref)
 
 
+@pytest.mark.parametrize("n,split", [(12, 64), (16, 0), (30, 48)])
+def test_interval_mask_narrow_trees_with_ring_write_outs(n, split):
+    """Preorder trees of <= 32 nodes at 4 query heads per KV head (4-wave work-groups; <= 64 rows take the
+    variant whose last wave writes the chunk values out), with splits long enough that the LDS ring of chunk
+    values is written out inside a split: interval and bit masks give the same bytes, and both match the
+    oracle."""
+    tree, end = _preorder_tree(530 + n, n, 5)
+    case = synth.attention_case(530 + n, ctx_lens=[5000], trees=[tree], num_q_heads=8, num_kv_heads=2,
+                                head_dim=128)
+    print(f"nodes={n} split={split}", flush=True)
+    a = run_attention(case, chunk_size=64, split_tiles=split)
+    b = run_attention(case, chunk_size=64, split_tiles=split, subtree_end=end)
+    import long_context_tree_amd as lt
+    ma = torch.zeros((1, -(-5000 // 64)), dtype=torch.float32, device=dev())
+    mb = torch.zeros_like(ma)
+    lt.chunk_salience(a[2], ma)
+    lt.chunk_salience(b[2], mb)
+    torch.cuda.synchronize()
+    assert torch.equal(a[0].view(torch.int16), b[0].view(torch.int16))
+    assert torch.equal(a[1], b[1]) and torch.equal(ma, mb)
+    o_ref, l_ref, m_ref = oracle_attention(case, 64)
+    compare_out(b[0], b[1], o_ref, l_ref)
+    compare_mass(mb.cpu().numpy()[0].astype(np.float64), m_ref[0])
+
+
 @pytest.mark.parametrize("n,depth,L,hq,hkv,d", [(300, 12, 1000, 8, 2, 128), (1000, 16, 3000, 4, 1, 128),
                                                 (2048, 20, 500, 4, 2, 64), (700, 40, 5000, 32, 8, 128)])
 def test_wide_tree_attention_matches_oracle(n, depth, L, hq, hkv, d):
