@@ -1367,14 +1367,14 @@ __global__ __launch_bounds__(512, 1) void tree_attn_pipe_kernel(AttnParams p) {
 
   // One interleaved block: 17 slots, each one MFMA pair (P.V of the V tile vt, half hv, with pin: dim
   // blocks 0..7; then the chunk sums of pin against a_chunk; then QK^T of the K tile kt, half hk: k-steps
-  // 0..3 x key blocks 0..1), the LDS reads of the fragment three slots ahead, and one element's
+  // 0..3 x key blocks 0..1), the LDS reads of the fragment two slots ahead, and one element's
   // probability (fma, exp, add, bf16 convert) of the half-tile scores sin.  sched_barrier pins the order:
   // about two VALU instructions per MFMA issue in the MFMAs' shadow.
   auto run_block = [&](const uint16_t* vt, int hv, const bf16x8 (&pin)[RB], const bf16x8& a_chunk,
                        const uint16_t* kt, int hk, f32x4 (&sout)[RB][2], const f32x4 (&sin)[RB][2],
                        bf16x8 (&pout)[RB], float (&esum)[RB], auto&& slot_hook) __attribute__((always_inline)) {
     typedef short i16x4 __attribute__((ext_vector_type(4)));
-    constexpr int NF = 17, AHEAD = 3;
+    constexpr int NF = 17, AHEAD = 2;
     bf16x8 fr[AHEAD + 1];
     auto read_frag = [&](int f, bf16x8& out) __attribute__((always_inline)) {
       if (f < NB) {                                // V^T fragment of dim block f (two transposing reads)
